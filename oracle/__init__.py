@@ -1,0 +1,313 @@
+"""CPU oracle for producer-fused NVFP4 activation quantization.
+
+TEST INFRASTRUCTURE ONLY.  The oracle defines, bit for bit, what the GPU
+library computes.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import it; the library never does.
+It shares no code, header, table or constant generator with the HIP path.
+
+The arithmetic lives in plain C (``nvfp4_oracle.c``, single-threaded,
+IEEE fp32 with FTZ/DAZ cleared).  This module compiles it with gcc, loads it
+with ctypes and converts numpy arrays.  ``silu_exact`` is an independent
+pure-Python derivation of the SiLU table used to pin the C one.
+
+Every function here follows the passages cited in ``nvfp4_oracle.c``:
+the FastVideo API page ``minimax_h3_nvfp4_fused`` (quantize, swiglu_quantize,
+new_quantized), TensorRT-LLM PR #21483 (Summary: producer-fused quantize), the
+FastVideo branch compare's ``minimax_h3_swiglu_quant.cuh`` (scale_fp8,
+scale_float, fp4_pair, quant_probe) and the FastVideo commit log (int64
+indexing, frame-index bounds contract).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from fractions import Fraction
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "nvfp4_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+GCC_FLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+             "-msse2", "-mfpmath=sse", "-fvisibility=hidden"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle into ``oracle/liboracle.so`` (always, when force)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        F = ctypes.c_float
+        sig = {
+            "orc_bf16_round": (None, [P, P, I64]),
+            "orc_e4m3_encode": (None, [P, P, I64]),
+            "orc_e4m3_value": (ctypes.c_double, [ctypes.c_uint8]),
+            "orc_e2m1_encode": (None, [P, P, I64]),
+            "orc_e2m1_value": (ctypes.c_double, [ctypes.c_uint8]),
+            "orc_scale_offset": (I64, [I64, I64, I64]),
+            "orc_padded_rows": (I64, [I64]),
+            "orc_global_scale": (F, [F]),
+            "orc_rms_rstd": (F, [P, I64, F]),
+            "orc_quantize_rows": (None, [P, I64, I64, F, P, P]),
+            "orc_nvfp4_quantize": (None, [P, I64, I64, F, P, P]),
+            "orc_rms_adaln_rows": (None, [P, I64, I64, P, P, P, P, I64, I64, P, F, F,
+                                          P, P, P, P, P, P]),
+            "orc_silu_table": (ctypes.c_int, [P]),
+            "orc_swiglu_rows": (None, [P, P, I64, I64, I64, P, P, F, P, P, P, P]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# --------------------------------------------------------------------------
+# codecs
+# --------------------------------------------------------------------------
+
+def bf16_round(f32) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (NaN -> 0x7FC0)."""
+    a = _c(f32, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    _load().orc_bf16_round(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def bf16_to_f32(u16) -> np.ndarray:
+    """bf16 bit patterns -> fp32 (exact)."""
+    return (np.asarray(u16, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def e4m3_encode(f32) -> np.ndarray:
+    """Non-negative fp32 -> E4M3 code, nearest, ties to even, saturating at 448."""
+    a = _c(f32, np.float32)
+    out = np.empty(a.shape, np.uint8)
+    _load().orc_e4m3_encode(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def e4m3_value(code: int) -> float:
+    return _load().orc_e4m3_value(int(code))
+
+
+def e2m1_encode(f32) -> np.ndarray:
+    """fp32 -> E2M1 4-bit code (sign bit 3), nearest, ties to even, saturating at 6."""
+    a = _c(f32, np.float32)
+    out = np.empty(a.shape, np.uint8)
+    _load().orc_e2m1_encode(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def e2m1_value(code: int) -> float:
+    return _load().orc_e2m1_value(int(code))
+
+
+def scale_offset(r: int, b: int, k: int) -> int:
+    return _load().orc_scale_offset(int(r), int(b), int(k))
+
+
+def scale_offsets(rows, k: int) -> np.ndarray:
+    """Swizzled byte offsets [len(rows), k/16] of every block of the given rows
+    (same layout as orc_scale_offset, vectorised)."""
+    r = np.asarray(rows, np.int64)[:, None]
+    b = np.arange(k // 16, dtype=np.int64)[None, :]
+    return (((r // 128) * (k // 64) + b // 4) * 512 + (r % 32) * 16 + ((r // 32) % 4) * 4 + b % 4)
+
+
+def padded_rows(m: int) -> int:
+    return _load().orc_padded_rows(int(m))
+
+
+def global_scale(global_amax: float) -> float:
+    return _load().orc_global_scale(float(global_amax))
+
+
+def rms_rstd(x_row_u16, eps: float) -> float:
+    a = _c(x_row_u16, np.uint16)
+    return _load().orc_rms_rstd(_ptr(a), a.size, float(eps))
+
+
+# --------------------------------------------------------------------------
+# producers
+# --------------------------------------------------------------------------
+
+def quantize_rows(y_u16, global_amax: float):
+    """Block-quantize bf16 rows: returns codes [n, k/2], plain-order scale bytes [n, k/16]."""
+    y = _c(y_u16, np.uint16)
+    n, k = y.shape
+    codes = np.empty((n, k // 2), np.uint8)
+    sb = np.empty((n, k // 16), np.uint8)
+    _load().orc_quantize_rows(_ptr(y), n, k, float(global_amax), _ptr(codes), _ptr(sb))
+    return codes, sb
+
+
+def nvfp4_quantize(x_u16, global_amax: float):
+    """Standalone quantize: codes [m, k/2] and swizzled scales [pad(m), k/16]."""
+    x = _c(x_u16, np.uint16)
+    m, k = x.shape
+    codes = np.empty((m, k // 2), np.uint8)
+    scales = np.empty((padded_rows(m), k // 16), np.uint8)
+    _load().orc_nvfp4_quantize(_ptr(x), m, k, float(global_amax), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def rms_adaln_rows(x_u16, w_u16, table_u16, frame_idx, eps: float, global_amax: float,
+                   row_ids=None, want_y: bool = False, scales_rows: int | None = None):
+    """RMSNorm + adaLN -> NVFP4 for rows of x.
+
+    table_u16: [T, 2, k] bf16 (shift, scale).  frame_idx: per-row frame.
+    row_ids: the rows' indices in the full tensor (default 0..n-1).
+    Returns dict(codes [n,k/2], scale_bytes [n,k/16], rstd [n], y [n,k] or None,
+    status, scales: swizzled [scales_rows, k/16] when scales_rows is given).
+    """
+    x = _c(x_u16, np.uint16)
+    n, k = x.shape
+    w = _c(w_u16, np.uint16)
+    tab = _c(table_u16, np.uint16)
+    t_frames = tab.shape[0]
+    idx = _c(frame_idx, np.int32)
+    rid = None if row_ids is None else _c(row_ids, np.int64)
+    codes = np.empty((n, k // 2), np.uint8)
+    sb = np.empty((n, k // 16), np.uint8)
+    rstd = np.empty(n, np.float32)
+    y = np.empty((n, k), np.uint16) if want_y else None
+    scales = None
+    if scales_rows is not None:
+        scales = np.zeros((scales_rows, k // 16), np.uint8)
+    status = np.zeros(1, np.uint32)
+    shift_ptr = tab.ctypes.data                    # table row t: shift at t*2k elements
+    scale_ptr = tab.ctypes.data + k * tab.itemsize  # ... and scale k elements further
+    _load().orc_rms_adaln_rows(_ptr(x), n, k, _ptr(rid), _ptr(w), shift_ptr, scale_ptr, 2 * k,
+                               t_frames, _ptr(idx), float(eps),
+                               float(global_amax), _ptr(codes), _ptr(sb), _ptr(scales), _ptr(rstd),
+                               _ptr(y), _ptr(status))
+    return dict(codes=codes, scale_bytes=sb, rstd=rstd, y=y, status=int(status[0]), scales=scales)
+
+
+_silu_cache = None
+
+
+def silu_table() -> np.ndarray:
+    """The 65536-entry bf16 SiLU table (C, long double, single rounding)."""
+    global _silu_cache
+    if _silu_cache is None:
+        t = np.empty(65536, np.uint16)
+        amb = _load().orc_silu_table(_ptr(t))
+        if amb:
+            raise RuntimeError("oracle SiLU table: %d entries undecidable in long double" % amb)
+        _silu_cache = t
+    return _silu_cache
+
+
+def swiglu_rows(up_u16, gate_u16, global_amax: float, row_ids=None, want_y: bool = False,
+                scales_rows: int | None = None):
+    """SwiGLU -> NVFP4: y = bf16(S[gate] * up), then the block quantizer.
+
+    up_u16 / gate_u16: [n, f] bf16 (views into a packed [n, 2f] are fine).
+    """
+    up = _c(up_u16, np.uint16)
+    gate = _c(gate_u16, np.uint16)
+    n, f = up.shape
+    table = silu_table()
+    rid = None if row_ids is None else _c(row_ids, np.int64)
+    codes = np.empty((n, f // 2), np.uint8)
+    sb = np.empty((n, f // 16), np.uint8)
+    y = np.empty((n, f), np.uint16) if want_y else None
+    scales = None
+    if scales_rows is not None:
+        scales = np.zeros((scales_rows, f // 16), np.uint8)
+    _load().orc_swiglu_rows(_ptr(up), _ptr(gate), f, n, f, _ptr(rid), _ptr(table),
+                            float(global_amax), _ptr(codes), _ptr(sb), _ptr(scales), _ptr(y))
+    return dict(codes=codes, scale_bytes=sb, y=y, scales=scales)
+
+
+# --------------------------------------------------------------------------
+# independent derivation of the SiLU table (exact decimal arithmetic)
+# --------------------------------------------------------------------------
+
+def _round_fraction_to_bf16(q: Fraction) -> int:
+    """Exact rational -> nearest bf16 bit pattern, ties to even."""
+    sign = 0x8000 if q < 0 else 0
+    a = -q if q < 0 else q
+    if a == 0:
+        return sign
+    # exponent E with 2^E <= a < 2^(E+1)
+    E = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** E > a:
+        E -= 1
+    elif Fraction(2) ** (E + 1) <= a:
+        E += 1
+    qexp = -133 if E < -126 else E - 7
+    n = a / (Fraction(2) ** qexp)
+    fl = n.numerator // n.denominator
+    frac = n - fl
+    if abs(frac - Fraction(1, 2)) < Fraction(1, 10 ** 45):
+        raise ArithmeticError("SiLU value too close to a bf16 midpoint for 60-digit evaluation")
+    if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    value = Fraction(fl) * Fraction(2) ** qexp
+    if value >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    # encode: value = fl * 2^qexp, fl <= 256
+    f = np.float32(float(value))  # exact: <= 9 significant bits, in fp32 range
+    return sign | int(np.array([f], np.float32).view(np.uint32)[0] >> 16)
+
+
+def silu_exact() -> np.ndarray:
+    """SiLU table from Python's decimal module (60 significant digits).
+
+    For |g| >= 100 the rounding is decided by a bound instead of evaluating:
+    g <= -100 gives |g| e^g < 2^-134 (half the smallest bf16 subnormal), so -0;
+    g >= 100 differs from g by a relative e^-100, far below half a bf16 ulp, so g.
+    """
+    import decimal
+    ctx = decimal.Context(prec=60)
+    out = np.empty(65536, np.uint16)
+    for g in range(65536):
+        e = (g >> 7) & 0xFF
+        if e == 0xFF:
+            out[g] = 0x7FC0 if (g & 0x7F) else (0x8000 if g & 0x8000 else 0x7F80)
+            continue
+        x = float(np.array([g << 16], np.uint32).view(np.float32)[0])
+        if x <= -100.0:
+            out[g] = 0x8000
+            continue
+        if x >= 100.0:
+            out[g] = g
+            continue
+        if x == 0.0:
+            out[g] = g  # silu(+-0) = +-0
+            continue
+        dx = decimal.Decimal(x)  # exact binary value
+        s = ctx.divide(dx, ctx.add(decimal.Decimal(1), ctx.exp(ctx.minus(dx))))
+        out[g] = _round_fraction_to_bf16(Fraction(s))
+    return out

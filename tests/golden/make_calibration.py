@@ -1,0 +1,68 @@
+"""Write tests/golden/calibration_amax.json: the static global amax of every workload.
+
+Calls only the CPU oracle (``oracle/``) and the seeded input generators
+(``workloads/``).  The static activation amax plays the role of the calibrated
+input amax of a static-NVFP4 Linear (FastVideo API page
+``minimax_h3_nvfp4_fused``, NVFP4DecoderLinear with act_scale="static"; the
+TensorRT-LLM fusions apply only to static NVFP4 scales).  For each workload:
+
+  rms_adaln_256x2048     max |y| of the oracle's own modulated output y
+  quantize_63240x7168    max |x| over 8,192 calibration rows (y = x)
+  rms_adaln_63240x7168   max |y| of the oracle on 8,192 calibration rows,
+  rms_adaln_300000x7168    frame index (r * T) // 8192
+  swiglu_16384x19456     max |y| of the oracle on 2,048 calibration rows
+
+Run:  python tests/golden/make_calibration.py
+"""
+import json
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+sys.path.insert(0, ROOT)
+
+import oracle  # noqa: E402
+import workloads  # noqa: E402
+
+
+def amax_of_bf16(u16) -> float:
+    return float(np.max(np.abs(oracle.bf16_to_f32(u16))))
+
+
+def calibrate(w: workloads.Workload) -> dict:
+    if w.kind == "rms_adaln":
+        if w.cal_rows == 0:
+            x, idx, how = w.x(), w.frame_idx(), "max|y| of the oracle over the workload itself"
+        else:
+            x, idx = w.calibration_x(), w.calibration_frame_idx()
+            how = "max|y| of the oracle over %d calibration rows" % w.cal_rows
+        res = oracle.rms_adaln_rows(x, w.weight(), w.table(), idx, w.eps, 1.0, want_y=True)
+        amax = amax_of_bf16(res["y"])
+    elif w.kind == "quantize":
+        amax = amax_of_bf16(w.calibration_x())
+        how = "max|x| over %d calibration rows" % w.cal_rows
+    elif w.kind == "swiglu":
+        o = w.calibration_x()
+        res = oracle.swiglu_rows(o[:, :w.k], o[:, w.k:], 1.0, want_y=True)
+        amax = amax_of_bf16(res["y"])
+        how = "max|y| of the oracle over %d calibration rows" % w.cal_rows
+    else:
+        raise ValueError(w.kind)
+    return {"global_amax": amax, "global_amax_hex": float(amax).hex(), "how": how}
+
+
+def main():
+    out = {}
+    for name, w in workloads.WORKLOADS.items():
+        out[name] = calibrate(w)
+        print(name, out[name]["global_amax"], flush=True)
+    path = os.path.join(ROOT, "tests", "golden", "calibration_amax.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1, sort_keys=True)
+        f.write("\n")
+
+
+if __name__ == "__main__":
+    main()

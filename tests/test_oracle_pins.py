@@ -1,0 +1,431 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks an oracle function against a library routine, an exhaustive
+or boundary-focused brute force, a closed form, a hand-worked fixture under
+tests/golden/ (with its citation), an invariant, or an exact-arithmetic
+derivation.  None of them needs a GPU.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def f32_from_bits(u):
+    return np.asarray(u, np.uint32).view(np.float32)
+
+
+def bits(f):
+    return np.asarray(f, np.float32).view(np.uint32)
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding: every fp32 input against torch's own conversion
+# --------------------------------------------------------------------------
+
+def _bf16_chunk(start, step):
+    u = np.arange(step, dtype=np.uint32) + np.uint32(start)
+    f = u.view(np.float32)
+    ours = oracle.bf16_round(f)
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    diff = np.nonzero(ours != ref)[0]
+    # torch keeps NaN payloads; the oracle canonicalises NaN to 0x7FC0.  Nothing else may differ.
+    nan_count = int(np.count_nonzero(((u & 0x7F800000) == 0x7F800000) & ((u & 0x7FFFFF) != 0)))
+    return (bool(np.all(np.isnan(f[diff]))) and bool(np.all(ours[diff] == 0x7FC0)),
+            len(diff) <= nan_count, start)
+
+
+def test_bf16_round_all_fp32_inputs_match_torch():
+    from concurrent.futures import ThreadPoolExecutor
+    step = 1 << 26
+    with ThreadPoolExecutor(4) as ex:
+        for only_nan, count_ok, start in ex.map(lambda s: _bf16_chunk(s, step), range(0, 1 << 32, step)):
+            assert only_nan and count_ok, hex(start)
+    nan_in = f32_from_bits(np.array([0x7FC00000, 0x7F800001, 0xFFFFFFFF], np.uint32))
+    assert np.all(oracle.bf16_round(nan_in) == 0x7FC0)
+
+
+# --------------------------------------------------------------------------
+# E4M3: decode table, encoder against a brute-force nearest search
+# --------------------------------------------------------------------------
+
+def e4m3_exact_value(code):
+    """OCP E4M3 (FN) value from the bit fields, as an exact fraction."""
+    e, m = (code >> 3) & 15, code & 7
+    if e == 0:
+        return Fraction(m, 512)
+    return Fraction(8 + m, 8) * Fraction(2) ** (e - 7)
+
+
+def test_e4m3_decode_all_finite_codes():
+    for c in range(127):
+        assert Fraction(oracle.e4m3_value(c)) == e4m3_exact_value(c)
+    assert oracle.e4m3_value(0x7E) == 448.0
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3_value(0x38) == 1.0
+    # strictly increasing: the encoder relies on it
+    vals = [oracle.e4m3_value(c) for c in range(127)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))
+
+
+E4M3_VALUES = np.array([float(e4m3_exact_value(c)) for c in range(127)])
+
+
+def brute_e4m3(x):
+    """Nearest of the 127 finite E4M3 values by exhaustive search, ties to the even code."""
+    x = np.asarray(x, np.float64)
+    d = np.abs(x[:, None] - E4M3_VALUES[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    # among the (at most two) nearest codes, prefer the even one
+    idx = np.where(cand.sum(axis=1) > 1,
+                   np.argmax(cand & (np.arange(127)[None, :] % 2 == 0), axis=1),
+                   np.argmax(cand, axis=1))
+    return idx.astype(np.uint8)
+
+
+def neighbourhood(points, ulps=3):
+    """fp32 values within +-ulps of each point (points as fp32)."""
+    p = bits(np.asarray(points, np.float32)).astype(np.int64)
+    offs = np.arange(-ulps, ulps + 1)
+    u = (p[:, None] + offs[None, :]).ravel()
+    u = u[(u >= 0) & (u < 0x7F800000)]
+    return f32_from_bits(u.astype(np.uint32))
+
+
+def test_e4m3_encoder_vs_bruteforce_at_every_boundary_and_random():
+    mids = (E4M3_VALUES[1:] + E4M3_VALUES[:-1]) / 2
+    pts = np.concatenate([neighbourhood(E4M3_VALUES), neighbourhood(mids.astype(np.float32), 4),
+                          neighbourhood([448.0, 464.0, 480.0, 2.0 ** -10, 2.0 ** -9], 8)])
+    g = np.random.Generator(np.random.PCG64(11))
+    rand = np.concatenate([
+        g.uniform(0, 500, 200000).astype(np.float32),
+        f32_from_bits(g.integers(0, 0x7F800000, 200000, dtype=np.uint32)),  # every exponent
+        np.exp2(g.uniform(-20, 10, 200000)).astype(np.float32)])
+    x = np.concatenate([pts, rand])
+    x = x[x < 1e6]  # beyond that brute force distances stop being informative; covered below
+    assert np.array_equal(oracle.e4m3_encode(x), brute_e4m3(x))
+    big = np.array([448.0, 449.0, 463.99, 464.0, 500.0, 1e6, 3.4e38, np.inf], np.float32)
+    assert np.all(oracle.e4m3_encode(big) == 0x7E)
+    assert np.all(oracle.e4m3_encode(np.array([0.0, -0.0, 2.0 ** -10, 1e-30], np.float32)) == 0)
+    assert oracle.e4m3_encode(np.array([2.0 ** -10 * 1.0000001], np.float32))[0] == 1
+
+
+def test_e4m3_encoder_monotone_over_a_dense_sweep():
+    u = np.arange(0, 0x44000000, 97, dtype=np.uint32)  # every 97th pattern up to 512
+    c = oracle.e4m3_encode(f32_from_bits(u))
+    assert np.all(np.diff(c.astype(np.int32)) >= 0)
+
+
+# --------------------------------------------------------------------------
+# E2M1: the interval table and a brute-force nearest search
+# --------------------------------------------------------------------------
+
+E2M1_MAG = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+
+
+def brute_e2m1(v):
+    v = np.asarray(v, np.float32)
+    a = np.abs(v.astype(np.float64))
+    d = np.abs(a[:, None] - E2M1_MAG[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    mag = np.where(cand.sum(axis=1) > 1, np.argmax(cand & (np.arange(8)[None, :] % 2 == 0), axis=1),
+                   np.argmax(cand, axis=1))
+    return (mag | np.where(np.signbit(v), 8, 0)).astype(np.uint8)
+
+
+def test_e2m1_interval_table():
+    # closed/open intervals of round-to-nearest-even with saturation at 6
+    cases = [(0.0, 0), (0.25, 0), (0.2500001, 1), (0.5, 1), (0.7499999, 1), (0.75, 2), (1.25, 2),
+             (1.2500001, 3), (1.7499999, 3), (1.75, 4), (2.5, 4), (2.5000002, 5), (3.4999998, 5),
+             (3.5, 6), (5.0, 6), (5.0000005, 7), (6.0, 7), (7.0, 7), (1e30, 7), (np.inf, 7)]
+    v = np.array([c[0] for c in cases], np.float32)
+    want = np.array([c[1] for c in cases], np.uint8)
+    assert np.array_equal(oracle.e2m1_encode(v), want)
+    assert np.array_equal(oracle.e2m1_encode(-v), want | 8)
+    assert oracle.e2m1_encode(np.array([-0.0], np.float32))[0] == 8
+    for c in range(16):
+        assert oracle.e2m1_value(c) == (-1 if c & 8 else 1) * E2M1_MAG[c & 7]
+
+
+def test_e2m1_encoder_vs_bruteforce():
+    mids = (E2M1_MAG[1:] + E2M1_MAG[:-1]) / 2
+    pts = np.concatenate([neighbourhood(E2M1_MAG, 4), neighbourhood(mids.astype(np.float32), 6)])
+    allbf16 = f32_from_bits(np.arange(65536, dtype=np.uint32) << 16)
+    allbf16 = allbf16[np.isfinite(allbf16)]
+    g = np.random.Generator(np.random.PCG64(12))
+    rand = np.concatenate([g.uniform(-7, 7, 300000).astype(np.float32),
+                           f32_from_bits(g.integers(0, 0x7F800000, 100000, dtype=np.uint32))])
+    v = np.concatenate([pts, -pts, allbf16, rand])
+    # fp64 distances are exact below 2^50; beyond, every value saturates to 6
+    small = np.abs(v) < 2.0 ** 50
+    assert np.array_equal(oracle.e2m1_encode(v[small]), brute_e2m1(v[small]))
+    assert np.array_equal(oracle.e2m1_encode(v[~small]), np.where(np.signbit(v[~small]), 15, 7))
+
+
+# --------------------------------------------------------------------------
+# swizzled scale layout
+# --------------------------------------------------------------------------
+
+def pages_nested_index(r, g, width):
+    """The swizzled index as the FastVideo branch compare's quant_probe nests it:
+    row tile, then 4-block group, then r%32, then (r/32)%4, then g%4."""
+    return (((((r // 128) * (width // 64) + g // 4) * 32 + r % 32) * 4 + (r // 32) % 4) * 4 + g % 4)
+
+
+def test_scale_offset_hand_worked_cases():
+    data = json.load(open(os.path.join(GOLDEN, "hand_worked_blocks.json")))["scale_offsets"]
+    for c in data["cases"]:
+        assert oracle.scale_offset(c["r"], c["b"], c["k"]) == c["offset"], c
+
+
+@pytest.mark.parametrize("k", [64, 128, 192, 7168, 19456])
+def test_scale_offset_equals_pages_nesting_and_is_a_bijection(k):
+    m = 300
+    pad = oracle.padded_rows(m)
+    offs = oracle.scale_offsets(np.arange(pad), k)
+    r = np.arange(pad)[:, None]
+    g = np.arange(k // 16)[None, :]
+    assert np.array_equal(offs, pages_nested_index(r, g, k))
+    for rr, bb in [(0, 0), (pad - 1, k // 16 - 1), (129, 7 % (k // 16))]:
+        assert oracle.scale_offset(rr, bb, k) == offs[rr, bb]
+    flat = np.sort(offs.ravel())
+    assert np.array_equal(flat, np.arange(pad * k // 16))
+
+
+def test_padded_rows():
+    assert [oracle.padded_rows(m) for m in (0, 1, 127, 128, 129, 63240, 300000)] == \
+        [0, 128, 128, 128, 256, 63360, 300032]
+
+
+# --------------------------------------------------------------------------
+# the block quantizer: hand-worked blocks, padding, dequantization bound
+# --------------------------------------------------------------------------
+
+def _block_values(vals):
+    out = []
+    for v in vals:
+        out.append(-0.0 if v == "-0" else float(v))
+    return np.array(out, np.float32)
+
+
+def test_hand_worked_blocks():
+    data = json.load(open(os.path.join(GOLDEN, "hand_worked_blocks.json")))
+    for blk in data["blocks"]:
+        row = np.zeros(64, np.float32)
+        row[:16] = _block_values(blk["values"])
+        y = oracle.bf16_round(row).reshape(1, 64)
+        codes, sb = oracle.quantize_rows(y, blk["global_amax"])
+        assert sb[0, 0] == blk["scale_code"], blk["name"]
+        assert codes[0, :8].tobytes().hex() == blk["packed_hex"], blk["name"]
+        nib = np.stack([codes[0, :8] & 15, codes[0, :8] >> 4], axis=1).ravel()
+        assert list(nib) == blk["codes"], blk["name"]
+
+
+def test_padding_rows_are_zero():
+    p = json.load(open(os.path.join(GOLDEN, "hand_worked_blocks.json")))["padding"]
+    g = np.random.Generator(np.random.PCG64(3))
+    x = oracle.bf16_round(g.standard_normal((p["m"], p["k"])).astype(np.float32) + 3.0)
+    codes, scales = oracle.nvfp4_quantize(x, 10.0)
+    assert codes.size == p["codes_bytes"] and scales.size == p["scale_bytes"]
+    nz = np.nonzero(scales.ravel())[0]
+    assert list(nz) == p["nonzero_scale_offsets"]
+
+
+def test_dequantization_error_bound():
+    g = np.random.Generator(np.random.PCG64(4))
+    n, k = 512, 256
+    x = g.standard_normal((n, k)).astype(np.float32) * np.exp2(g.integers(-6, 2, (n, 1))).astype(np.float32)
+    y = oracle.bf16_round(x)
+    yf = oracle.bf16_to_f32(y).astype(np.float64)
+    amax = 8.0
+    gsf = oracle.global_scale(amax)
+    assert gsf == np.float32(2688.0) / np.float32(amax)
+    codes, sb = oracle.quantize_rows(y, amax)
+    q = np.stack([codes & 15, codes >> 4], axis=-1).reshape(n, k)
+    qv = np.vectorize(oracle.e2m1_value)(q)
+    dec = np.vectorize(oracle.e4m3_value)(sb)
+    dec_e = np.repeat(dec, 16, axis=1)
+    s_e = np.repeat(sb, 16, axis=1)
+    ok = (s_e != 0) & (s_e != 0x7E)
+    deq = qv * dec_e / float(gsf)
+    spacing = np.where(np.abs(qv) < 2, 0.5, np.where(np.abs(qv) < 4, 1.0, 2.0))
+    # half a code spacing in the block's units, plus the two fp32 roundings (inv and y*inv);
+    # |v| <= 6 holds since the scale rounds to nearest with relative error <= 2^-4 ...
+    bound = 0.5 * spacing * dec_e / float(gsf) + 2.0 ** -22 * np.abs(yf)
+    v_over = np.abs(yf) * float(gsf) / dec_e
+    sel = ok & (v_over <= 6.0)
+    assert sel.sum() > 0.9 * sel.size
+    assert np.all(np.abs(yf - deq)[sel] <= bound[sel])
+    # ... which this checks directly: per normal-scale block max|v| <= 6 / (1 - 2^-4)
+    blocks_amax = np.abs(yf).reshape(n, k // 16, 16).max(axis=2)
+    normal = (sb >= 0x08) & (sb < 0x7E)
+    assert np.all((blocks_amax * float(gsf) / dec)[normal] <= 6.0 / (1 - 2.0 ** -4))
+
+
+# --------------------------------------------------------------------------
+# RMSNorm statistic and the adaLN rounding chain
+# --------------------------------------------------------------------------
+
+def test_rstd_equal_values_row_is_exact():
+    k = 7168
+    for c in [1.0, 0.5, 3.0, 0.125]:
+        x = oracle.bf16_round(np.full(k, c, np.float32))
+        # K * c^2 is exact in fp32 here, so the tree sums exactly and ms = c^2
+        want = np.float32(1.0) / np.sqrt(np.float32(c * c) + np.float32(1e-6))
+        assert oracle.rms_rstd(x, 1e-6) == want
+
+
+def test_rstd_zero_row():
+    for eps in [1e-6, 1e-5, 0.25]:
+        assert oracle.rms_rstd(np.zeros(2048, np.uint16), eps) == \
+            np.float32(1.0) / np.sqrt(np.float32(eps))
+
+
+def test_rstd_close_to_fp64():
+    g = np.random.Generator(np.random.PCG64(5))
+    for k in [512, 2048, 7168]:
+        x = oracle.bf16_round(g.standard_normal(k).astype(np.float32) * 3)
+        xf = oracle.bf16_to_f32(x).astype(np.float64)
+        ref = 1.0 / np.sqrt(np.mean(xf * xf) + 1e-6)
+        assert abs(oracle.rms_rstd(x, 1e-6) / ref - 1) < 1e-6
+
+
+def test_rstd_tree_order_is_the_documented_one():
+    """Rows whose fp32 sum depends on the order of the additions.  Lane L holds
+    chunk L (k = 512 gives one chunk per lane).  Lane 0 holds 2^24 (x = 4096);
+    two other lanes hold 1.0.  In fp32, 2^24 + 1 rounds back to 2^24 (tie to
+    even), while 1 + 1 = 2 and 2^24 + 2 are exact.  The butterfly pairs lanes
+    (0,1),(2,3) at distance 1, then (0,2) at distance 2:
+      ones on lanes 1 and 3: (2^24+1) -> 2^24, then 2^24 + 1 -> 2^24;
+      ones on lanes 2 and 3: 1 + 1 = 2 first, then 2^24 + 2 exactly.
+    A sequential left-to-right sum gives 2^24 in both cases."""
+    k = 512
+
+    def row(lanes):
+        x = np.zeros(k, np.float32)
+        x[0] = 4096.0
+        for L in lanes:
+            x[8 * L] = 1.0
+        return oracle.bf16_round(x)
+
+    eps = np.float32(1e-6)
+    want13 = np.float32(1.0) / np.sqrt(np.float32(2.0 ** 24 / 512) + eps)
+    want23 = np.float32(1.0) / np.sqrt(np.float32((2.0 ** 24 + 2) / 512) + eps)
+    assert want13 != want23
+    assert oracle.rms_rstd(row([1, 3]), 1e-6) == want13
+    assert oracle.rms_rstd(row([2, 3]), 1e-6) == want23
+
+
+def test_adaln_chain_reduces_to_bf16_of_x_times_rstd():
+    """With w = 1, scale = 0 and shift = 0 every later rounding is exact, so
+    y = bf16(x * rstd); checked with torch's fp32 multiply and bf16 cast."""
+    g = np.random.Generator(np.random.PCG64(6))
+    n, k = 8, 2048
+    x = oracle.bf16_round(g.standard_normal((n, k)).astype(np.float32))
+    w = oracle.bf16_round(np.ones(k, np.float32))
+    tab = np.zeros((2, 2, k), np.uint16)
+    res = oracle.rms_adaln_rows(x, w, tab, np.zeros(n, np.int32), 1e-6, 4.0, want_y=True)
+    xt = torch.from_numpy(oracle.bf16_to_f32(x).copy())
+    rt = torch.from_numpy(res["rstd"].copy())[:, None]
+    want = (xt * rt).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(res["y"], want)
+
+
+def test_adaln_chain_single_element_by_hand():
+    """One element traced through the chain with torch fp32 ops, each result cast to bf16."""
+    k = 512
+    g = np.random.Generator(np.random.PCG64(7))
+    x = oracle.bf16_round(g.standard_normal((1, k)).astype(np.float32))
+    w = oracle.bf16_round((1 + 0.1 * g.standard_normal(k)).astype(np.float32))
+    tab = oracle.bf16_round((0.1 * g.standard_normal((3, 2, k))).astype(np.float32))
+    res = oracle.rms_adaln_rows(x, w, tab, np.array([2], np.int32), 1e-6, 4.0, want_y=True)
+    B = torch.bfloat16
+
+    def t(a):
+        return torch.from_numpy(oracle.bf16_to_f32(a).copy())
+
+    n = (t(x[0]) * torch.tensor(res["rstd"][0])).to(B).float()
+    nw = (n * t(w)).to(B).float()
+    opl = (1.0 + t(tab[2, 1])).to(B).float()
+    mm = (nw * opl).to(B).float()
+    y = (mm + t(tab[2, 0])).to(B)
+    assert np.array_equal(res["y"][0], y.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_frame_index_out_of_range_zeroes_the_row_and_sets_status():
+    k = 512
+    g = np.random.Generator(np.random.PCG64(8))
+    x = oracle.bf16_round(g.standard_normal((3, k)).astype(np.float32))
+    w = oracle.bf16_round(np.ones(k, np.float32))
+    tab = oracle.bf16_round((0.1 * g.standard_normal((2, 2, k))).astype(np.float32))
+    res = oracle.rms_adaln_rows(x, w, tab, np.array([0, 2, -1], np.int32), 1e-6, 4.0, want_y=True,
+                                scales_rows=128)
+    assert res["status"] & 1
+    assert not res["codes"][1:].any() and not res["scale_bytes"][1:].any() and not res["y"][1:].any()
+    assert res["codes"][0].any()
+    ok = oracle.rms_adaln_rows(x[:1], w, tab, np.array([1], np.int32), 1e-6, 4.0)
+    assert ok["status"] == 0
+
+
+# --------------------------------------------------------------------------
+# SiLU table and the SwiGLU producer
+# --------------------------------------------------------------------------
+
+def test_silu_table_equals_exact_decimal_derivation():
+    assert np.array_equal(oracle.silu_table(), oracle.silu_exact())
+
+
+def test_silu_table_special_values():
+    t = oracle.silu_table()
+    assert t[0x0000] == 0x0000 and t[0x8000] == 0x8000
+    assert t[0x7F80] == 0x7F80 and t[0xFF80] == 0x8000 and t[0x7FC1] == 0x7FC0
+    # silu(1) = 0.7310585..., bf16 0x3F3B = 0.73046875; silu(-1) = -0.268941..., 0xBE8A = -0.26953125
+    assert t[0x3F80] == 0x3F3B and t[0xBF80] == 0xBE8A
+
+
+def test_swiglu_with_unit_up_returns_the_table():
+    gate = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((gate >> 7) & 0xFF) != 0xFF
+    gate = gate[finite][: (finite.sum() // 64) * 64].reshape(-1, 64)
+    up = np.full(gate.shape, 0x3F80, np.uint16)
+    res = oracle.swiglu_rows(up, gate, 4.0, want_y=True)
+    assert np.array_equal(res["y"], oracle.silu_table()[gate])
+
+
+def test_swiglu_product_rounding_vs_torch():
+    g = np.random.Generator(np.random.PCG64(9))
+    up = oracle.bf16_round(g.standard_normal((4, 256)).astype(np.float32))
+    gate = oracle.bf16_round(g.standard_normal((4, 256)).astype(np.float32))
+    res = oracle.swiglu_rows(up, gate, 4.0, want_y=True)
+    s = torch.from_numpy(oracle.bf16_to_f32(oracle.silu_table()[gate]).copy())
+    u = torch.from_numpy(oracle.bf16_to_f32(up).copy())
+    want = (s * u).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(res["y"], want)
+
+
+# --------------------------------------------------------------------------
+# whole-tensor quantize equals per-row quantize placed by the layout
+# --------------------------------------------------------------------------
+
+def test_tensor_quantize_matches_rows_and_layout():
+    g = np.random.Generator(np.random.PCG64(10))
+    m, k = 261, 192
+    x = oracle.bf16_round(g.standard_normal((m, k)).astype(np.float32))
+    codes, scales = oracle.nvfp4_quantize(x, 5.0)
+    c2, sb = oracle.quantize_rows(x, 5.0)
+    assert np.array_equal(codes, c2)
+    offs = oracle.scale_offsets(np.arange(m), k)
+    assert np.array_equal(scales.ravel()[offs], sb)
+    mask = np.ones(scales.size, bool)
+    mask[offs.ravel()] = False
+    assert not scales.ravel()[mask].any()

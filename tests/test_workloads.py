@@ -1,0 +1,61 @@
+"""Seeded input generators: determinism, shapes, chunk regeneration, calibration file."""
+import json
+import os
+
+import numpy as np
+
+import oracle
+import workloads
+
+
+def test_shapes_and_determinism():
+    w = workloads.get("rms_adaln_256x2048")
+    a, b = w.x(), w.x()
+    assert a.shape == (256, 2048) and a.dtype == np.uint16
+    assert np.array_equal(a, b)
+    assert w.weight().shape == (2048,) and w.table().shape == (8, 2, 2048)
+    assert np.array_equal(w.frame_idx(), np.arange(256) // 32)
+
+
+def test_chunk_regeneration_matches_full_draw():
+    w = workloads.Workload("t", 9, "rms_adaln", 9000, 512, frames=3, rows_per_frame=3000,
+                           outliers="cols36_x30")
+    full = w.x()
+    rows = np.array([0, 1, 4095, 4096, 8191, 8192, 8999])
+    assert np.array_equal(w.x_rows(rows), full[rows])
+
+
+def test_outlier_recipes():
+    w = workloads.get("rms_adaln_63240x7168")
+    cols = w.outlier_columns()
+    assert len(cols) == 36 and len(set(cols.tolist())) == 36
+    w1 = workloads.get("rms_adaln_256x2048")
+    x = oracle.bf16_to_f32(w1.x())
+    frac_big = np.mean(np.abs(x) > 6)  # N(0,1) beyond 6 sigma is ~2e-9; outliers are x20
+    assert 0.005 < frac_big < 0.015
+
+
+def test_frames_cover_the_table():
+    for name in ["rms_adaln_63240x7168", "rms_adaln_300000x7168"]:
+        w = workloads.get(name)
+        idx = w.frame_idx()
+        assert idx.min() == 0 and idx.max() == w.frames - 1
+        cal = w.calibration_frame_idx()
+        assert cal.min() == 0 and cal.max() == w.frames - 1
+
+
+def test_algorithmic_bytes():
+    w = workloads.get("rms_adaln_63240x7168")
+    assert w.algorithmic_bytes() == 1_161_646_080
+    assert workloads.get("swiglu_16384x19456").algorithmic_bytes() == 1_454_374_912
+    assert workloads.get("rms_adaln_300000x7168").algorithmic_bytes() == 5_510_414_336
+
+
+def test_calibration_file_reproduces_for_the_tiny_workload():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "calibration_amax.json")
+    data = json.load(open(path))
+    assert set(data) == set(workloads.WORKLOADS)
+    w = workloads.get("rms_adaln_256x2048")
+    res = oracle.rms_adaln_rows(w.x(), w.weight(), w.table(), w.frame_idx(), w.eps, 1.0, want_y=True)
+    amax = float(np.max(np.abs(oracle.bf16_to_f32(res["y"]))))
+    assert amax == data[w.name]["global_amax"] == workloads.calibration_amax(w.name)

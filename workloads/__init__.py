@@ -1,0 +1,210 @@
+"""Seeded synthetic inputs for the NVFP4 activation-quantization producers.
+
+This module holds input construction only: random draws, shapes, frame
+indices and the bf16 conversion of the drawn fp32 samples (done by torch's
+own ``Tensor.to(torch.bfloat16)``).  It contains none of the method's
+arithmetic, and both the CPU oracle and the GPU library consume what it
+produces.
+
+Workloads (shapes from the pages' H3 block: 56 heads x 128 = 7168 hidden,
+a 34x60 latent grid per frame over 31 frames = 63,240 tokens from
+544x960x124 video; SwiGLU hidden 19,456; and a 300,000-token shape past the
+2^31-element boundary reported in the FastVideo commit log):
+
+  rms_adaln_256x2048       tiny RMSNorm+adaLN (8 frames, frame = token // 32)
+  quantize_63240x7168      attention-output quantize (per-head std)
+  rms_adaln_63240x7168     RMSNorm+adaLN at the H3 block shape (31 frames)
+  swiglu_16384x19456       SwiGLU producer over a value-first [M, 2F] projection
+  rms_adaln_300000x7168    RMSNorm+adaLN over 2.15e9 elements (147 frames)
+
+Seeds: numpy ``PCG64``; the seed of role ``role`` in workload number ``i``
+(1..5 in the order above) is ``1000*i + role`` with roles 1 x, 2 weight,
+3 modulation table, 4 calibration rows, 5 outlier pick, 6 per-head std.
+Large tensors are drawn in 4096-row chunks, chunk ``c`` from
+``SeedSequence(1000*i + role).spawn(n_chunks)[c]``, so any chunk can be
+regenerated alone and chunks can be drawn in parallel threads.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+
+import numpy as np
+
+CHUNK_ROWS = 4096
+ROLE_X, ROLE_W, ROLE_TABLE, ROLE_CAL, ROLE_OUTLIER, ROLE_HEADSTD = 1, 2, 3, 4, 5, 6
+
+
+def to_bf16(a: np.ndarray) -> np.ndarray:
+    """fp32 samples -> bf16 bit patterns (uint16), via torch's conversion."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def rng(i: int, role: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(1000 * i + role))
+
+
+def _threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    number: int               # 1..5, selects the seeds
+    kind: str                 # "rms_adaln" | "quantize" | "swiglu"
+    m: int                    # rows (tokens)
+    k: int                    # output columns (hidden, or F for swiglu)
+    frames: int = 0           # modulation table rows (rms_adaln)
+    rows_per_frame: int = 0   # frame index = row // rows_per_frame
+    eps: float = 1e-6
+    outliers: str = ""        # "iid1pct_x20" | "cols36_x30" | ""
+    cal_rows: int = 0         # calibration rows for the static amax (0: from the data itself)
+    extra: dict = field(default_factory=dict)
+
+    # ---- sizes -------------------------------------------------------------
+    @property
+    def padded_rows(self) -> int:
+        return (self.m + 127) // 128 * 128
+
+    @property
+    def in_cols(self) -> int:
+        return 2 * self.k if self.kind == "swiglu" else self.k
+
+    def algorithmic_bytes(self) -> int:
+        """HBM bytes one pass must move: bf16 inputs once, packed codes once,
+        scale bytes over the padded rows (parameters not counted)."""
+        return (2 * self.m * self.in_cols + self.m * self.k // 2 + self.padded_rows * self.k // 16)
+
+    def param_bytes(self) -> int:
+        if self.kind == "rms_adaln":
+            return 2 * self.k + 2 * self.frames * 2 * self.k + 4 * self.m
+        return 0
+
+    # ---- generation ----------------------------------------------------------
+    def n_chunks(self, rows: int) -> int:
+        return (rows + CHUNK_ROWS - 1) // CHUNK_ROWS
+
+    def _chunk_f32(self, role: int, rows: int, c: int, cols_out: np.ndarray | None,
+                   head_std: np.ndarray | None) -> np.ndarray:
+        seeds = np.random.SeedSequence(1000 * self.number + role).spawn(self.n_chunks(rows))
+        g = np.random.Generator(np.random.PCG64(seeds[c]))
+        r = min(CHUNK_ROWS, rows - c * CHUNK_ROWS)
+        a = g.standard_normal((r, self.in_cols), dtype=np.float32)
+        if self.outliers == "iid1pct_x20":
+            mask = g.random((r, self.in_cols), dtype=np.float32) < 0.01
+            a[mask] *= 20.0
+        elif self.outliers == "cols36_x30":
+            a[:, cols_out] *= 30.0
+        if head_std is not None:
+            a *= np.repeat(head_std, 128)[None, :]
+        return a
+
+    def outlier_columns(self) -> np.ndarray | None:
+        if self.outliers != "cols36_x30":
+            return None
+        n = int(round(0.005 * self.k))
+        return np.sort(rng(self.number, ROLE_OUTLIER).choice(self.k, n, replace=False))
+
+    def head_std(self) -> np.ndarray | None:
+        if self.kind != "quantize":
+            return None
+        heads = self.k // 128
+        return (0.5 * rng(self.number, ROLE_HEADSTD).uniform(0.2, 2.0, heads)).astype(np.float32)
+
+    def _rows_bf16(self, role: int, rows: int, chunks=None, out: np.ndarray | None = None):
+        cols = self.outlier_columns()
+        hs = self.head_std()
+        idx = range(self.n_chunks(rows)) if chunks is None else chunks
+        idx = list(idx)
+
+        def one(c):
+            return c, to_bf16(self._chunk_f32(role, rows, c, cols, hs))
+
+        parts = {}
+        with ThreadPoolExecutor(_threads()) as ex:
+            for c, a in ex.map(one, idx):
+                if out is not None:
+                    out[c * CHUNK_ROWS:c * CHUNK_ROWS + a.shape[0]] = a
+                else:
+                    parts[c] = a
+        if out is not None:
+            return out
+        return np.concatenate([parts[c] for c in idx], axis=0)
+
+    def x(self, out: np.ndarray | None = None) -> np.ndarray:
+        """The full input [m, in_cols] as bf16 patterns."""
+        if out is None:
+            out = np.empty((self.m, self.in_cols), np.uint16)
+        return self._rows_bf16(ROLE_X, self.m, out=out)
+
+    def x_rows(self, rows) -> np.ndarray:
+        """Rows of the input regenerated from their chunks alone."""
+        rows = np.asarray(rows, np.int64)
+        chunks = sorted(set((rows // CHUNK_ROWS).tolist()))
+        blocks = self._rows_bf16(ROLE_X, self.m, chunks=chunks)
+        pos = {c: i for i, c in enumerate(chunks)}
+        starts = np.cumsum([0] + [min(CHUNK_ROWS, self.m - c * CHUNK_ROWS) for c in chunks])
+        sel = [starts[pos[int(r // CHUNK_ROWS)]] + int(r % CHUNK_ROWS) for r in rows]
+        return blocks[sel]
+
+    def calibration_x(self) -> np.ndarray:
+        return self._rows_bf16(ROLE_CAL, self.cal_rows)
+
+    def weight(self) -> np.ndarray:
+        return to_bf16(1.0 + 0.1 * rng(self.number, ROLE_W).standard_normal(self.k, dtype=np.float32))
+
+    def table(self) -> np.ndarray:
+        """[frames, 2, k] bf16: row t holds (shift, scale) of frame t."""
+        t = 0.1 * rng(self.number, ROLE_TABLE).standard_normal((self.frames, 2, self.k),
+                                                                dtype=np.float32)
+        return to_bf16(t)
+
+    def frame_idx(self, rows=None) -> np.ndarray:
+        r = np.arange(self.m, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+        return (r // self.rows_per_frame).astype(np.int32)
+
+    def calibration_frame_idx(self) -> np.ndarray:
+        r = np.arange(self.cal_rows, dtype=np.int64)
+        return ((r * self.frames) // self.cal_rows).astype(np.int32)
+
+    def sample_rows(self, n_random: int = 8192, head: int = 4096, tail: int = 4096) -> np.ndarray:
+        """First `head`, last `tail` and `n_random` seeded random rows (sorted, unique)."""
+        g = np.random.Generator(np.random.PCG64(1000 * self.number + 7))
+        parts = [np.arange(min(head, self.m)), np.arange(max(0, self.m - tail), self.m),
+                 g.choice(self.m, size=min(n_random, self.m), replace=False)]
+        return np.unique(np.concatenate(parts)).astype(np.int64)
+
+
+WORKLOADS = {
+    w.name: w for w in [
+        Workload("rms_adaln_256x2048", 1, "rms_adaln", 256, 2048, frames=8, rows_per_frame=32,
+                 outliers="iid1pct_x20"),
+        Workload("quantize_63240x7168", 2, "quantize", 63240, 7168, cal_rows=8192),
+        Workload("rms_adaln_63240x7168", 3, "rms_adaln", 63240, 7168, frames=31,
+                 rows_per_frame=2040, outliers="cols36_x30", cal_rows=8192),
+        Workload("swiglu_16384x19456", 4, "swiglu", 16384, 19456, cal_rows=2048),
+        Workload("rms_adaln_300000x7168", 5, "rms_adaln", 300000, 7168, frames=147,
+                 rows_per_frame=2041, outliers="cols36_x30", cal_rows=8192),
+    ]
+}
+
+BENCH_WORKLOAD = "rms_adaln_63240x7168"
+
+
+def get(name: str) -> Workload:
+    return WORKLOADS[name]
+
+
+def calibration_amax(name: str) -> float:
+    """The static global amax of a workload, read from the stored calibration
+    file (written by tests/golden/make_calibration.py from the CPU oracle)."""
+    import json
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "tests", "golden", "calibration_amax.json")
+    with open(path) as f:
+        data = json.load(f)
+    return float(np.float32(data[name]["global_amax"]))
