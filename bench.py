@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the producer-fused NVFP4 activation quantizer on one MI355X.
+
+One step = one pass of the fused RMSNorm + adaLN -> NVFP4 producer over the whole
+63,240 x 7168 bf16 activation of an H3 block (34x60 latent tokens x 31 frames, 56 heads x
+128), inputs resident in HBM, outputs: packed E2M1 codes + swizzled E4M3 scales.
+
+Prints ONE JSON line:
+  value      whole-job HBM throughput, algorithmic bytes / time per step (GB/s)
+  roofline   the kernel's algorithmic GB/s (per-launch HIP events) against 8 TB/s peak,
+             plus measured HBM traffic per launch from the committed rocprofv3 counter
+             summary when it was taken on the current kernel sources (else null)
+  cpu_baseline  the CPU oracle timed on a bounded row sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused RMSNorm+adaLN→NVFP4 HBM GB/s & % of peak at 63,240×7168 bf16"
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, vendor figure
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="rms_adaln_63240x7168")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=32768, help="rows of the oracle sample")
+    return p.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "nvfp4_activation_quantization_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(csrc, "*"))):
+        h.update(os.path.basename(path).encode())
+        h.update(open(path, "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from profiles/traffic_<workload>.txt, if it was measured on
+    the current kernel sources (its source_sha256 line), else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(float(kv["fetch_bytes_per_launch"])) + int(float(kv["write_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def make_inputs(wl, torch, amax):
+    import numpy as np
+    dev = "cuda:0"
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev)
+
+    if wl.kind == "rms_adaln":
+        x = up(wl.x())
+        args = dict(x=x, weight=up(wl.weight()), table=up(wl.table()),
+                    frame_idx=torch.from_numpy(wl.frame_idx()).to(dev))
+    else:
+        args = dict(x=up(wl.x()))
+    return args
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(rows are independent; see DESIGN.md for how the path would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nvfp4_activation_quantization_amd as nq
+    import workloads
+
+    wl = workloads.get(a.workload)
+    amax = workloads.calibration_amax(wl.name)
+    torch.cuda.set_device(0)
+    inp = make_inputs(wl, torch, amax)
+    codes, scales = nq.new_quantized(wl.m, wl.k, "cuda:0")
+    stream = torch.cuda.current_stream()
+
+    if wl.kind == "rms_adaln":
+        def step():
+            nq.rms_adaln_nvfp4(inp["x"], inp["weight"], inp["table"], inp["frame_idx"], wl.eps, amax,
+                               codes=codes, scales=scales, stream=stream)
+    elif wl.kind == "quantize":
+        def step():
+            nq.nvfp4_quantize(inp["x"], amax, codes=codes, scales=scales, stream=stream)
+    else:
+        def step():
+            nq.swiglu_nvfp4(inp["x"], amax, codes=codes, scales=scales, stream=stream)
+        nq.init()
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, per-launch events on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(a.steps)]
+    region0 = torch.cuda.Event(enable_timing=True)
+    region1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    region0.record(stream)
+    for i in range(a.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    region1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    region_ms = region0.elapsed_time(region1)
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kernel_ms = float(np.mean(per_launch_ms))
+    ms_per_step = region_ms / a.steps
+
+    alg_bytes = wl.algorithmic_bytes()
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
+
+    # practical ceiling for context: a device-to-device copy of the input bytes
+    x = inp["x"]
+    dst = torch.empty_like(x)
+    for _ in range(3):
+        dst.copy_(x)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        dst.copy_(x)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_ms = c0.elapsed_time(c1) / 10
+    copy_gbps = 2 * x.numel() * x.element_size() / (copy_ms * 1e-3) / 1e9
+    del dst
+
+    traffic = measured_traffic(wl.name)
+
+    out = {
+        "metric": METRIC if wl.name == "rms_adaln_63240x7168" else "NVFP4 producer HBM GB/s (%s)" % wl.name,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "rows": wl.m, "hidden": wl.k,
+                   "frames": wl.frames if wl.kind == "rms_adaln" else None,
+                   "algorithmic_bytes_per_step": alg_bytes, "global_amax": amax},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
+        "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
+        "rows_per_s": round(wl.m / (ms_per_step * 1e-3), 1),
+        "kernel_us": round(kernel_ms * 1e3, 2),
+        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "wall_s": round(wall, 3),
+    }
+
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, amax, a.cpu_rows, np)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, amax, rows, np):
+    """The CPU oracle (unchanged) on the first `rows` rows of the workload, split into
+    contiguous row blocks over the host's threads (rows are independent)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    rows = min(rows, wl.m)
+    sel = np.arange(rows)
+    x = wl.x_rows(sel)
+    if wl.kind == "rms_adaln":
+        w, table, idx = wl.weight(), wl.table(), wl.frame_idx(sel)
+
+        def part(se):
+            s, e = se
+            oracle.rms_adaln_rows(x[s:e], w, table, idx[s:e], wl.eps, amax)
+    elif wl.kind == "quantize":
+        def part(se):
+            s, e = se
+            oracle.quantize_rows(x[s:e], amax)
+    else:
+        oracle.silu_table()
+
+        def part(se):
+            s, e = se
+            oracle.swiglu_rows(x[s:e, :wl.k], x[s:e, wl.k:], amax)
+    step = (rows + 4 * threads - 1) // (4 * threads)
+    blocks = [(s, min(rows, s + step)) for s in range(0, rows, step)]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(part, blocks))
+    dt = time.perf_counter() - t0
+    bytes_per_row = wl.algorithmic_bytes() / wl.m
+    return {"value": round(rows * bytes_per_row / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "rows_per_s": round(rows / dt, 1), "seconds": round(dt, 3),
+            "sample": "first %d rows of %s, %d threads, row blocks" % (rows, wl.name, threads)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * nvfp4act.h -- C ABI of libnvfp4act.so: producer-fused NVFP4 activation
+ * quantization for AMD Instinct MI355X (gfx950).
+ *
+ * Three producers, each fused with the same NVFP4 block quantizer:
+ *   rms_adaln_nvfp4  RMSNorm (fp32 statistic) + adaLN modulation -> NVFP4
+ *   swiglu_nvfp4     SiLU(gate) * up                              -> NVFP4
+ *   nvfp4_quantize   identity (attention-output quantize)         -> NVFP4
+ *
+ * Sources: TensorRT-LLM PR #21483 "Fuse the MiniMax-H3 NVFP4 activation
+ * quantize into the AdaLN, SwiGLU and attention-output producers" (Summary);
+ * FastVideo API page "fastvideo.models.vaes.minimax_h3_nvfp4_fused" (module
+ * summary, new_quantized, quantize, swiglu_quantize); FastVideo branch compare
+ * "regen2k-nvfp4-decoder..fasth3-spark-exact-perf", minimax_h3_swiglu_quant.cuh
+ * (scale_fp8, scale_float, fp4_pair, quant_probe, launch_quant_probe) and
+ * h3_swiglu_gemm_binding.py (int status, nonzero -> error); FastVideo commit
+ * log "vae-parallel-decode" (int64 indexing past 2^31 elements, frame-index
+ * bounds contract).
+ *
+ * The NVFP4 format written by every entry point
+ * ---------------------------------------------
+ * Input rows of k bf16 values are cut into 16-element blocks.  With the
+ * global scale gsf = 2688 / global_amax (2688 = 448 * 6, IEEE fp32):
+ *   block scale   s   = E4M3(gsf * (max|y| * fp32(1/6))), round to nearest
+ *                       even, saturating at 448 (code 0x7E); OCP E4M3 codes
+ *   element code  q_i = E2M1(y_i * inv), inv = (s != 0) ? gsf / dec(s) : 0,
+ *                       round to nearest even, saturating at 6; bit 3 = sign
+ *                       of the product (so -0 encodes as 0x8)
+ * codes  [m, k/2] bytes, row-major; byte j of a row holds columns 2j (low
+ *        nibble) and 2j+1 (high nibble).
+ * scales [pad(m), k/16] bytes, pad(m) = ceil(m/128)*128, in the 128x4
+ *        swizzled layout: the scale of (row r, block b) is at byte
+ *        ((r/128)*(k/64) + b/4)*512 + (r%32)*16 + ((r/32)%4)*4 + b%4.
+ *        The bytes of rows m .. pad(m)-1 are written as 0.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All data pointers are device pointers (HIP device memory visible to the
+ *   current device).  bf16 data is passed as raw 16-bit patterns.
+ * - Every compute call is asynchronous on `stream` (a hipStream_t passed as
+ *   void*, NULL = the default stream), allocates nothing and never waits for
+ *   the device.  The one exception is the first swiglu_nvfp4 call on a device
+ *   (or an explicit nvfp4act_init), which builds the device's SiLU table once
+ *   and waits for it.
+ * - Ownership: the caller allocates and frees every buffer.  Inputs must stay
+ *   valid and unmodified, and outputs untouched, until the stream work is done.
+ *   The library writes only codes, scales and the non-NULL side outputs.
+ * - Errors: arguments are checked on the host before anything is launched; on
+ *   an error nothing is written and a nonzero status is returned (see
+ *   NVFP4ACT_* below).  m == 0 (with valid k) is a no-op that returns 0 before
+ *   any other check, so empty tensors may pass NULL pointers.  Faults inside a kernel
+ *   surface at the caller's next synchronisation.
+ * - Inputs are finite bf16.  Non-finite inputs are outside the contract.
+ * - Calls are stateless and thread-safe; sizes are int64 and all device
+ *   indexing is 64-bit (tensors past 2^31 elements are supported).
+ */
+#ifndef NVFP4ACT_H
+#define NVFP4ACT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define NVFP4ACT_OK            0
+#define NVFP4ACT_ERR_NULL      1  /* a required pointer is NULL                         */
+#define NVFP4ACT_ERR_SHAPE     2  /* m < 0, bad k / f / ld / num_frames / frame_stride   */
+#define NVFP4ACT_ERR_ALIGN     3  /* a pointer, row stride or frame stride not 16-byte aligned */
+#define NVFP4ACT_ERR_VALUE     4  /* global_amax not finite or too small; eps not finite or < 0 */
+#define NVFP4ACT_ERR_DEVICE    5  /* no usable gfx950 device is current                  */
+#define NVFP4ACT_ERR_LAUNCH    6  /* a HIP call failed; see nvfp4act_last_hip_error()   */
+#define NVFP4ACT_ERR_TABLE     7  /* the SiLU table could not be built exactly           */
+
+/* ceil(m / 128) * 128: rows of the swizzled scale buffer */
+int64_t nvfp4act_padded_rows(int64_t m);
+/* m * k / 2: bytes of the packed codes */
+int64_t nvfp4act_codes_bytes(int64_t m, int64_t k);
+/* padded_rows(m) * k / 16: bytes of the swizzled scales */
+int64_t nvfp4act_scales_bytes(int64_t m, int64_t k);
+/* 2688.0f / global_amax (IEEE fp32), the global scale the kernels use */
+float nvfp4act_global_scale(float global_amax);
+/* static text for a status code */
+const char* nvfp4act_status_string(int status);
+/* HIP error code behind the last NVFP4ACT_ERR_LAUNCH of the calling thread */
+int nvfp4act_last_hip_error(void);
+
+/* Build the per-device constant tables on the current device (the SiLU table
+   of swiglu_nvfp4) and wait for them.  Idempotent; optional (swiglu_nvfp4
+   calls it on first use).  Call it before capturing swiglu_nvfp4 into a HIP
+   graph.  Returns a status. */
+int nvfp4act_init(void);
+
+/* Standalone NVFP4 quantize of a bf16 tensor (the attention-output quantize).
+   FastVideo API page, quantize; TensorRT-LLM PR #21483, attention-output
+   quantize commit.
+     x       [m, k] bf16, row-major, contiguous, 16-byte aligned
+     m       rows, >= 0
+     k       columns, a positive multiple of 64
+     global_amax  static per-tensor amax (> 0, finite, 2688/global_amax finite)
+     codes   [m, k/2] bytes (16-byte aligned)
+     scales  [pad(m), k/16] bytes (16-byte aligned)
+   Returns a status. */
+int nvfp4_quantize(const void* x, int64_t m, int64_t k, float global_amax,
+                   void* codes, void* scales, void* stream);
+
+/* Fused RMSNorm + adaLN modulation -> NVFP4 (the AdaLN RMSNorm + modulation
+   producer of TensorRT-LLM PR #21483; every bf16 rounding of the op-by-op
+   eager path kept, FastVideo API page summary).  Per row r with t = frame_idx[r]:
+     rstd = 1 / sqrt(sum(x^2) / k + eps)   fp32, fixed reduction tree:
+            8 interleaved accumulators per lane over 8-element chunks
+            L, L+64, ... (fused multiply-add), folded pairwise, then a
+            butterfly over the 64 lanes at distances 1, 2, 4, ..., 32
+     y    = bf16(bf16(bf16(bf16(x*rstd) * w) * bf16(1 + scale[t])) + shift[t])
+   then the NVFP4 quantizer above.
+     x            [m, k] bf16 (16-byte aligned rows)
+     weight       [k] bf16 RMSNorm weight
+     shift, scale modulation rows: frame t's rows start at shift + t*frame_stride
+                  and scale + t*frame_stride elements (for a [T, 2, k] table of
+                  (shift, scale): shift = table, scale = table + k, frame_stride = 2k)
+     frame_stride elements between frames (>= k; frame_stride*2 a multiple of 16)
+     num_frames   T >= 1
+     frame_idx    [m] int32 frame of each row; must lie in [0, T).  A row with an
+                  index outside that range is written as all-zero codes and
+                  scale bytes (and a zero y_out row) and bit 0 of *status_word is
+                  set; nothing waits for the check (FastVideo commit log,
+                  modulation bounds contract).
+     eps          >= 0 and finite
+     m, k         m >= 0; k a positive multiple of 512
+     global_amax  as for nvfp4_quantize
+     codes, scales  outputs as for nvfp4_quantize
+     rstd_out     [m] fp32, nullable: the row statistic
+     y_out        [m, k] bf16, nullable: the pre-quantization activation
+     status_word  one uint32 in device memory, nullable; bits are only ever set
+                  (OR), so the caller clears it
+   Returns a status. */
+int rms_adaln_nvfp4(const void* x, const void* weight, const void* shift, const void* scale,
+                    int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx,
+                    float eps, int64_t m, int64_t k, float global_amax,
+                    void* codes, void* scales, float* rstd_out, void* y_out,
+                    uint32_t* status_word, void* stream);
+
+/* SwiGLU -> NVFP4 (FastVideo API page, swiglu_quantize; TensorRT-LLM PR
+   #21483, SiLU-and-mul producer):
+     y = bf16(S[gate] * up),  S[g] = bf16(g * sigmoid(g)) correctly rounded
+   then the NVFP4 quantizer above.
+     up, gate  row i at up + i*ld, gate + i*ld elements, f values each (for a
+               value-first [m, 2f] projection: gate = up + f, ld = 2f)
+     ld        row stride in elements (>= f; ld*2 a multiple of 16)
+     m, f      m >= 0; f a positive multiple of 64
+     global_amax, codes, scales  as for nvfp4_quantize (k = f)
+     y_out     [m, f] bf16, nullable
+   Returns a status. */
+int swiglu_nvfp4(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f,
+                 float global_amax, void* codes, void* scales, void* y_out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4ACT_H */

@@ -1,0 +1,197 @@
+"""Producer-fused NVFP4 activation quantization for MI355X (gfx950).
+
+Thin ctypes binding over ``libnvfp4act.so`` (C ABI in ``include/nvfp4act.h``).
+This module only turns torch tensors into pointers and sizes, calls the entry
+point of the same name on the current torch stream, and raises on a nonzero
+status: every step of the computation runs in the library's HIP kernels.
+If the library is missing the import fails loudly; there is no fallback.
+
+Entry points (see ``include/nvfp4act.h`` for the exact contract):
+  nvfp4_quantize(x, global_amax)                          standalone quantize
+  rms_adaln_nvfp4(x, weight, table, frame_idx, eps, global_amax)
+  swiglu_nvfp4(projection, global_amax)                   value-first [m, 2f]
+each returning ``(codes, scales)``: codes ``[m, k/2]`` uint8, scales
+``[pad(m), k/16]`` uint8 in the 128x4 swizzle (buffer shapes as the FastVideo
+API page's ``new_quantized``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libnvfp4act.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libnvfp4act.so is not built (run python -m nvfp4_activation_quantization_amd.build "
+                      "or __graft_entry__.build())")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P, _I64, _F, _I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int
+_SIGS = {
+    "nvfp4act_padded_rows": (_I64, [_I64]),
+    "nvfp4act_codes_bytes": (_I64, [_I64, _I64]),
+    "nvfp4act_scales_bytes": (_I64, [_I64, _I64]),
+    "nvfp4act_global_scale": (_F, [_F]),
+    "nvfp4act_status_string": (ctypes.c_char_p, [_I]),
+    "nvfp4act_last_hip_error": (_I, []),
+    "nvfp4act_init": (_I, []),
+    "nvfp4_quantize": (_I, [_P, _I64, _I64, _F, _P, _P, _P]),
+    "rms_adaln_nvfp4": (_I, [_P, _P, _P, _P, _I64, _I64, _P, _F, _I64, _I64, _F, _P, _P, _P, _P, _P, _P]),
+    "swiglu_nvfp4": (_I, [_P, _P, _I64, _I64, _I64, _F, _P, _P, _P, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+STATUS = {0: "ok", 1: "null", 2: "shape", 3: "align", 4: "value", 5: "device", 6: "launch", 7: "table"}
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int):
+        msg = _lib.nvfp4act_status_string(status).decode()
+        if status == 6:
+            msg += " (hip error %d)" % _lib.nvfp4act_last_hip_error()
+        super().__init__("nvfp4act status %d: %s" % (status, msg))
+        self.status = status
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise NVFP4Error(status)
+
+
+def library():
+    """The loaded ctypes library (raw C ABI)."""
+    return _lib
+
+
+def padded_rows(m: int) -> int:
+    return _lib.nvfp4act_padded_rows(m)
+
+
+def global_scale(global_amax: float) -> float:
+    return _lib.nvfp4act_global_scale(global_amax)
+
+
+def init() -> None:
+    """Build the per-device tables on the current device (optional; waits)."""
+    _check(_lib.nvfp4act_init())
+
+
+def new_quantized(m: int, k: int, device) -> tuple[torch.Tensor, torch.Tensor]:
+    """Output buffers for an [m, k] activation: codes [m, k/2], scales [pad(m), k/16]."""
+    codes = torch.empty((m, k // 2), dtype=torch.uint8, device=device)
+    scales = torch.empty((padded_rows(m), k // 16), dtype=torch.uint8, device=device)
+    return codes, scales
+
+
+def _bf16_ptr(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError("%s must hold bf16 values (bfloat16 or a 16-bit integer view)" % name)
+    if not t.is_cuda:
+        raise TypeError("%s must be a device tensor" % name)
+    return t.data_ptr()
+
+
+def _out_ptr(t, dtype, shape, name):
+    if t is None:
+        return 0
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError("%s must be a contiguous %s device tensor of shape %s" % (name, dtype, tuple(shape)))
+    return t.data_ptr()
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def nvfp4_quantize(x: torch.Tensor, global_amax: float, codes=None, scales=None, stream=None):
+    """Standalone NVFP4 quantize of a contiguous bf16 [m, k] tensor."""
+    m, k = x.shape
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if codes is None or scales is None:
+        codes, scales = new_quantized(m, k, x.device)
+    _check(_lib.nvfp4_quantize(_bf16_ptr(x, "x"), m, k, float(global_amax),
+                               _out_ptr(codes, torch.uint8, (m, k // 2), "codes"),
+                               _out_ptr(scales, torch.uint8, (padded_rows(m), k // 16), "scales"),
+                               _stream(stream, x.device)))
+    return codes, scales
+
+
+def rms_adaln_nvfp4(x: torch.Tensor, weight: torch.Tensor, table: torch.Tensor, frame_idx: torch.Tensor,
+                    eps: float, global_amax: float, codes=None, scales=None, rstd_out=None, y_out=None,
+                    status_word=None, stream=None):
+    """Fused RMSNorm + adaLN -> NVFP4.
+
+    x [m, k] bf16; weight [k] bf16; table [T, 2, k] bf16 holding (shift, scale) per
+    frame; frame_idx [m] int32.  Optional outputs: rstd_out [m] fp32, y_out [m, k]
+    bf16, status_word [1] int32/uint32 (bit 0: a frame index was out of range).
+    """
+    m, k = x.shape
+    if not x.is_contiguous() or not table.is_contiguous() or not weight.is_contiguous():
+        raise ValueError("x, weight and table must be contiguous")
+    if table.dim() != 3 or table.shape[1] != 2 or table.shape[2] != k:
+        raise ValueError("table must be [T, 2, k]")
+    if frame_idx.dtype != torch.int32 or not frame_idx.is_contiguous() or frame_idx.numel() != m:
+        raise ValueError("frame_idx must be a contiguous int32 tensor of m elements")
+    if codes is None or scales is None:
+        codes, scales = new_quantized(m, k, x.device)
+    tab = _bf16_ptr(table, "table")
+    sw = 0
+    if status_word is not None:
+        if status_word.dtype not in (torch.int32, torch.uint32) or not status_word.is_cuda:
+            raise ValueError("status_word must be a 32-bit device tensor")
+        sw = status_word.data_ptr()
+    _check(_lib.rms_adaln_nvfp4(
+        _bf16_ptr(x, "x"), _bf16_ptr(weight, "weight"), tab, tab + 2 * k, 2 * k, table.shape[0],
+        frame_idx.data_ptr(), float(eps), m, k, float(global_amax),
+        _out_ptr(codes, torch.uint8, (m, k // 2), "codes"),
+        _out_ptr(scales, torch.uint8, (padded_rows(m), k // 16), "scales"),
+        _out_ptr(rstd_out, torch.float32, (m,), "rstd_out"),
+        _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, k), "y_out") if y_out is not None else 0,
+        sw, _stream(stream, x.device)))
+    return codes, scales
+
+
+def swiglu_nvfp4(projection: torch.Tensor, global_amax: float, codes=None, scales=None, y_out=None,
+                 gate: torch.Tensor | None = None, stream=None):
+    """SwiGLU -> NVFP4.
+
+    With gate=None, projection is a value-first [m, 2f] tensor (up = first f columns,
+    gate = last f).  Otherwise projection is up [m, f] and gate [m, f], two views with
+    the same row stride (unit column stride).
+    """
+    if gate is None:
+        m, two_f = projection.shape
+        f = two_f // 2
+        if not projection.is_contiguous():
+            raise ValueError("projection must be contiguous")
+        up_ptr = _bf16_ptr(projection, "projection")
+        gate_ptr = up_ptr + 2 * f
+        ld = two_f
+    else:
+        m, f = projection.shape
+        if gate.shape != projection.shape or projection.stride(1) != 1 or gate.stride(1) != 1 \
+                or projection.stride(0) != gate.stride(0):
+            raise ValueError("up and gate must be [m, f] views with unit column stride and equal row stride")
+        up_ptr = _bf16_ptr(projection, "up")
+        gate_ptr = _bf16_ptr(gate, "gate")
+        ld = projection.stride(0)
+    if codes is None or scales is None:
+        codes, scales = new_quantized(m, f, projection.device)
+    _check(_lib.swiglu_nvfp4(up_ptr, gate_ptr, ld, m, f, float(global_amax),
+                             _out_ptr(codes, torch.uint8, (m, f // 2), "codes"),
+                             _out_ptr(scales, torch.uint8, (padded_rows(m), f // 16), "scales"),
+                             _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, f), "y_out")
+                             if y_out is not None else 0,
+                             _stream(stream, projection.device)))
+    return codes, scales

@@ -1,0 +1,196 @@
+// abi.cpp -- the C ABI of libnvfp4act.so (declared in include/nvfp4act.h): host-side
+// argument checks, per-device set-up and status reporting.  No compute happens here; each
+// entry point validates, then enqueues its kernel on the caller's stream.
+//
+// The status-code convention (int return, nonzero on failure, stream last) follows the
+// C-ABI launchers of the FastVideo branch compare (launch_quant_probe / launch_gemm_swiglu,
+// with h3_swiglu_gemm_binding.py raising on a nonzero code).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/nvfp4act.h"
+#include "kernels.hpp"
+
+namespace {
+
+using nvfp4act::DeviceInfo;
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceState {
+  bool probed = false;
+  bool usable = false;
+  bool silu_ready = false;
+  int silu_status = NVFP4ACT_OK;
+  DeviceInfo info{0};
+};
+
+std::mutex g_mutex;
+DeviceState g_dev[kMaxDevices];
+thread_local int t_last_hip_error = 0;
+
+int fail_hip(hipError_t e) {
+  t_last_hip_error = (int)e;
+  return NVFP4ACT_ERR_LAUNCH;
+}
+
+// Probe the current device once: gfx950, CU count, LDS attributes of the kernels.
+int current_device(const DeviceInfo** info, int* device_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return NVFP4ACT_ERR_DEVICE;
+  }
+  std::lock_guard<std::mutex> lock(g_mutex);
+  DeviceState& st = g_dev[dev];
+  if (!st.probed) {
+    st.probed = true;
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return NVFP4ACT_ERR_DEVICE;
+    }
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return NVFP4ACT_ERR_DEVICE;
+    st.info.cu_count = prop.multiProcessorCount;
+    hipError_t e = nvfp4act::prepare_rms_adaln();
+    if (e == hipSuccess) e = nvfp4act::prepare_swiglu();
+    if (e != hipSuccess) {
+      st.probed = false;
+      return fail_hip(e);
+    }
+    st.usable = true;
+  }
+  if (!st.usable) return NVFP4ACT_ERR_DEVICE;
+  *info = &st.info;
+  if (device_out) *device_out = dev;
+  return NVFP4ACT_OK;
+}
+
+int ensure_silu_table(int dev) {
+  std::lock_guard<std::mutex> lock(g_mutex);
+  DeviceState& st = g_dev[dev];
+  if (st.silu_ready) return NVFP4ACT_OK;
+  if (st.silu_status != NVFP4ACT_OK) return st.silu_status;
+  unsigned int ambiguous = 0;
+  hipError_t e = nvfp4act::build_silu_table(&ambiguous);
+  if (e != hipSuccess) return fail_hip(e);
+  if (ambiguous != 0) {
+    st.silu_status = NVFP4ACT_ERR_TABLE;
+    return st.silu_status;
+  }
+  st.silu_ready = true;
+  return NVFP4ACT_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_amax(float global_amax) {
+  if (!std::isfinite(global_amax) || !(global_amax > 0.0f)) return NVFP4ACT_ERR_VALUE;
+  if (!std::isfinite(2688.0f / global_amax)) return NVFP4ACT_ERR_VALUE;
+  return NVFP4ACT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t nvfp4act_padded_rows(int64_t m) { return m <= 0 ? 0 : (m + 127) / 128 * 128; }
+
+int64_t nvfp4act_codes_bytes(int64_t m, int64_t k) { return m * k / 2; }
+
+int64_t nvfp4act_scales_bytes(int64_t m, int64_t k) { return nvfp4act_padded_rows(m) * k / 16; }
+
+float nvfp4act_global_scale(float global_amax) { return 2688.0f / global_amax; }
+
+const char* nvfp4act_status_string(int status) {
+  switch (status) {
+    case NVFP4ACT_OK: return "ok";
+    case NVFP4ACT_ERR_NULL: return "a required pointer is NULL";
+    case NVFP4ACT_ERR_SHAPE: return "bad shape (m < 0, or k / f / ld / num_frames / frame_stride invalid)";
+    case NVFP4ACT_ERR_ALIGN: return "pointer, row stride or frame stride not 16-byte aligned";
+    case NVFP4ACT_ERR_VALUE: return "global_amax or eps out of range";
+    case NVFP4ACT_ERR_DEVICE: return "no usable gfx950 device is current";
+    case NVFP4ACT_ERR_LAUNCH: return "a HIP call failed (see nvfp4act_last_hip_error)";
+    case NVFP4ACT_ERR_TABLE: return "the SiLU table could not be built exactly";
+    default: return "unknown status";
+  }
+}
+
+int nvfp4act_last_hip_error(void) { return t_last_hip_error; }
+
+int nvfp4act_init(void) {
+  const DeviceInfo* info = nullptr;
+  int dev = -1;
+  int st = current_device(&info, &dev);
+  if (st != NVFP4ACT_OK) return st;
+  return ensure_silu_table(dev);
+}
+
+int nvfp4_quantize(const void* x, int64_t m, int64_t k, float global_amax, void* codes, void* scales,
+                   void* stream) {
+  if (m < 0 || k <= 0 || k % 64 != 0) return NVFP4ACT_ERR_SHAPE;
+  if (m == 0) return NVFP4ACT_OK;
+  if (!x || !codes || !scales) return NVFP4ACT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return NVFP4ACT_ERR_ALIGN;
+  int st = check_amax(global_amax);
+  if (st != NVFP4ACT_OK) return st;
+  const DeviceInfo* info = nullptr;
+  st = current_device(&info, nullptr);
+  if (st != NVFP4ACT_OK) return st;
+  hipError_t e = nvfp4act::launch_quantize(x, m, k, global_amax, codes, scales,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
+}
+
+int rms_adaln_nvfp4(const void* x, const void* weight, const void* shift, const void* scale,
+                    int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx, float eps,
+                    int64_t m, int64_t k, float global_amax, void* codes, void* scales, float* rstd_out,
+                    void* y_out, uint32_t* status_word, void* stream) {
+  if (m < 0 || k <= 0 || k % 512 != 0 || num_frames < 1 || frame_stride < k) return NVFP4ACT_ERR_SHAPE;
+  if (m == 0) return NVFP4ACT_OK;
+  if (!x || !weight || !shift || !scale || !frame_idx || !codes || !scales) return NVFP4ACT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(weight) || !aligned16(shift) || !aligned16(scale) ||
+      !aligned16(codes) || !aligned16(scales) || (frame_stride * 2) % 16 != 0 ||
+      (rstd_out && (reinterpret_cast<uintptr_t>(rstd_out) & 3u)) || (y_out && !aligned16(y_out)) ||
+      (reinterpret_cast<uintptr_t>(frame_idx) & 3u) ||
+      (status_word && (reinterpret_cast<uintptr_t>(status_word) & 3u)))
+    return NVFP4ACT_ERR_ALIGN;
+  int st = check_amax(global_amax);
+  if (st != NVFP4ACT_OK) return st;
+  if (!std::isfinite(eps) || eps < 0.0f) return NVFP4ACT_ERR_VALUE;
+  const DeviceInfo* info = nullptr;
+  st = current_device(&info, nullptr);
+  if (st != NVFP4ACT_OK) return st;
+  hipError_t e = nvfp4act::launch_rms_adaln(x, weight, shift, scale, frame_stride, num_frames,
+                                            frame_idx, eps, m, k, global_amax, codes, scales,
+                                            rstd_out, y_out, status_word, *info,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
+}
+
+int swiglu_nvfp4(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f, float global_amax,
+                 void* codes, void* scales, void* y_out, void* stream) {
+  if (m < 0 || f <= 0 || f % 64 != 0 || ld < f) return NVFP4ACT_ERR_SHAPE;
+  if (m == 0) return NVFP4ACT_OK;
+  if (!up || !gate || !codes || !scales) return NVFP4ACT_ERR_NULL;
+  if (!aligned16(up) || !aligned16(gate) || !aligned16(codes) || !aligned16(scales) ||
+      (ld * 2) % 16 != 0 || (y_out && !aligned16(y_out)))
+    return NVFP4ACT_ERR_ALIGN;
+  int st = check_amax(global_amax);
+  if (st != NVFP4ACT_OK) return st;
+  const DeviceInfo* info = nullptr;
+  int dev = -1;
+  st = current_device(&info, &dev);
+  if (st != NVFP4ACT_OK) return st;
+  st = ensure_silu_table(dev);
+  if (st != NVFP4ACT_OK) return st;
+  hipError_t e = nvfp4act::launch_swiglu(up, gate, ld, m, f, global_amax, codes, scales, y_out, *info,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// common.hpp -- device building blocks shared by the NVFP4 producer kernels.
+//
+// The NVFP4 format (FastVideo API page "fastvideo.models.vaes.minimax_h3_nvfp4_fused",
+// module summary and new_quantized; FastVideo branch compare, minimax_h3_swiglu_quant.cuh,
+// quant_probe): 16-element blocks, an E4M3 block scale under a global fp32 scale, E2M1
+// element codes packed two per byte (even column low), scales in the 128x4 swizzle.
+//
+// Work decomposition used by every kernel: one 64-lane wavefront owns one row at a
+// time.  The row is cut into 8-element chunks (16 bytes of bf16); lane L handles chunks
+// L, L+64, L+128, ... so each wavefront load is a contiguous 1 KiB.  A 16-element block is
+// chunk pair (2b, 2b+1), i.e. lanes (L, L^1): its amax is exchanged with one DPP move.
+// Four consecutive blocks live on lanes 8q..8q+7; lane 8q assembles their four scale
+// bytes and writes them as one 32-bit word, which in the swizzled layout is contiguous.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4act {
+
+constexpr int kWave = 64;
+constexpr uint32_t kRcp6Bits = 0x3E2AAAABu;   // fp32 nearest to 1/6
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---- bf16 ----------------------------------------------------------------------------
+
+// The two bf16 values of a packed word as exact fp32 (element 0 in the low half).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round two fp32 values to bf16 (nearest, ties to even; gfx950 v_cvt_pk_bf16_f32,
+// which matches the integer rule on every non-NaN fp32 input) and pack them.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// ---- E4M3 / E2M1 ---------------------------------------------------------------------
+
+// E4M3 code of a non-negative fp32, nearest-even, saturating at 448.  v_cvt_pk_fp8_f32
+// rounds to nearest-even on gfx950 (OCP E4M3) but turns values beyond 448 into NaN, so
+// the input is clamped first.
+__device__ __forceinline__ uint32_t e4m3_code(float sf) {
+  float c = __builtin_fminf(sf, 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+}
+
+// Exact value of an E4M3 code 0..126: exponent field 0 is m * 2^-9, else 2^(e-7)(1+m/8).
+__device__ __forceinline__ float e4m3_value(uint32_t s) {
+  uint32_t e = (s >> 3) & 15u, mant = s & 7u;
+  if (e == 0) return (float)mant * 0.001953125f;
+  return __uint_as_float(((e + 120u) << 23) | (mant << 20));
+}
+
+// Eight E2M1 codes of v[0..7] packed into one word (v[0] in bits 0..3).  The gfx950
+// scaled fp4 conversion with scale 1.0 rounds nearest-even, saturates at 6 and keeps
+// the sign of zero, like the specification, on every non-NaN fp32 input.
+__device__ __forceinline__ uint32_t pack_e2m1x8(const float* v) {
+  uint32_t w = 0;
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+  return w;
+}
+
+// ---- cross-lane ----------------------------------------------------------------------
+
+// Value of lane L^1 (DPP quad_perm [1,0,3,2]).
+__device__ __forceinline__ float lane_xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+
+// ---- global scale and inverse-scale table ----------------------------------------------
+
+// gsf = 2688 / global_amax, IEEE fp32 (every lane computes the same value).
+__device__ __forceinline__ float global_scale(float global_amax) { return 2688.0f / global_amax; }
+
+// Fill inv[0..127] with gsf / dec(s) (0 for s == 0); needs a barrier before use.
+__device__ __forceinline__ void fill_inverse_table(float* inv, float gsf, int tid) {
+  if (tid < 128) inv[tid] = (tid == 0) ? 0.0f : gsf / e4m3_value((uint32_t)tid);
+}
+
+// ---- the block quantizer for one chunk --------------------------------------------------
+
+// y[0..7]: this lane's half of a 16-element block (its partner lane holds the other
+// half).  Returns the packed codes of the 8 elements and sets *scale to the block's
+// E4M3 code (the same value on both lanes of the pair).
+__device__ __forceinline__ uint32_t quantize_chunk(const float* y, float gsf, const float* inv_tab,
+                                                   uint32_t* scale) {
+  float a = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(y[0]), __builtin_fabsf(y[1])),
+                            __builtin_fmaxf(__builtin_fabsf(y[2]), __builtin_fabsf(y[3])));
+  float b = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(y[4]), __builtin_fabsf(y[5])),
+                            __builtin_fmaxf(__builtin_fabsf(y[6]), __builtin_fabsf(y[7])));
+  float amax = __builtin_fmaxf(a, b);
+  amax = __builtin_fmaxf(amax, lane_xor1(amax));
+  const float rcp6 = __uint_as_float(kRcp6Bits);
+  uint32_t s = e4m3_code(gsf * (amax * rcp6));
+  float inv = inv_tab[s];
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = y[i] * inv;
+  *scale = s;
+  return pack_e2m1x8(v);
+}
+
+// Lanes 8q (q = 0..7) gather the scale bytes of lanes 8q, 8q+2, 8q+4, 8q+6 (blocks
+// 4q'..4q'+3 of the current group of 32 blocks) into one little-endian word.
+__device__ __forceinline__ uint32_t gather_scales4(uint32_t s) {
+  uint32_t t = s | (__shfl_down(s, 2, kWave) << 8);
+  return t | (__shfl_down(t, 4, kWave) << 16);
+}
+
+// Byte offset, in the swizzled scale buffer, of block 0 of row r (k columns); block b
+// (b % 4 == 0) of the row is at row_scale_base(r, k) + (b / 4) * 512.
+__device__ __forceinline__ int64_t row_scale_base(int64_t r, int64_t k) {
+  return (r >> 7) * (k >> 6) * 512 + (r & 31) * 16 + ((r >> 5) & 3) * 4;
+}
+
+// Zero the scale bytes of row r (a padding row, or a row written as zeros).
+__device__ __forceinline__ void zero_row_scales(uint8_t* scales, int64_t r, int64_t k, int lane) {
+  int64_t base = row_scale_base(r, k);
+  for (int64_t q = lane; q < (k >> 6); q += kWave)
+    *reinterpret_cast<uint32_t*>(scales + base + q * 512) = 0u;
+}
+
+// ---- streaming loads ------------------------------------------------------------------
+
+// 16-byte load that is not expected to be re-read (non-temporal hint).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---- workgroup -> work-unit mapping ---------------------------------------------------
+
+// Workgroups are dispatched round-robin over the 8 XCDs.  Kernels launch 8 * per
+// workgroups and remap the launch index so that the workgroups of one XCD take
+// consecutive work units (consecutive rows): the scale bytes of a 128-row tile then meet
+// in one XCD's L2 and leave it as whole lines.  The map is a bijection of [0, 8*per);
+// units >= the real unit count are idle.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int64_t xcd_unit(int64_t per) {
+  int64_t bid = blockIdx.x;
+  return (bid % kXcds) * per + bid / kXcds;
+}
+
+}  // namespace nvfp4act

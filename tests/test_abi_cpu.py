@@ -1,0 +1,105 @@
+"""The C-ABI library without a GPU: it loads, exports every function include/nvfp4act.h
+declares, and its host-side argument checks return the documented status codes.
+
+Every call here fails validation before anything is launched (or is an m == 0 no-op),
+so the fake device pointers below are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4act.h")
+
+import nvfp4_activation_quantization_amd as nq  # noqa: E402
+
+lib = nq.library()
+A = 0x10000           # a 16-byte aligned fake address (never dereferenced)
+U = 0x10008           # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:int|int64_t|float|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert set(names) >= {"nvfp4_quantize", "rms_adaln_nvfp4", "swiglu_nvfp4", "nvfp4act_init"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(nq.EXPORTED) == set(names)
+
+
+def test_size_helpers():
+    assert [nq.padded_rows(m) for m in (0, 1, 128, 129, 63240, 300000)] == [0, 128, 128, 256, 63360, 300032]
+    assert lib.nvfp4act_codes_bytes(63240, 7168) == 63240 * 3584
+    assert lib.nvfp4act_scales_bytes(63240, 7168) == 63360 * 448
+    assert nq.global_scale(2688.0) == 1.0
+    assert lib.nvfp4act_status_string(2).decode().startswith("bad shape")
+
+
+def q(x=A, m=4, k=64, amax=1.0, codes=A, scales=A):
+    return lib.nvfp4_quantize(x, m, k, amax, codes, scales, None)
+
+
+def test_quantize_status_codes():
+    assert q(x=None) == 1 and q(codes=None) == 1 and q(scales=None) == 1
+    assert q(m=-1) == 2 and q(k=48) == 2 and q(k=0) == 2
+    assert q(x=U) == 3 and q(codes=U) == 3 and q(scales=U) == 3
+    for bad in (0.0, -1.0, float("inf"), float("nan"), 1e-37):
+        assert q(amax=bad) == 4, bad
+    assert q(m=0) == 0
+
+
+def rms(**kw):
+    a = dict(x=A, w=A, shift=A, scale=A, fs=1024, nf=2, idx=A, eps=1e-6, m=4, k=512, amax=1.0,
+             codes=A, scales=A, rstd=None, y=None, st=None)
+    a.update(kw)
+    return lib.rms_adaln_nvfp4(a["x"], a["w"], a["shift"], a["scale"], a["fs"], a["nf"], a["idx"],
+                               a["eps"], a["m"], a["k"], a["amax"], a["codes"], a["scales"], a["rstd"],
+                               a["y"], a["st"], None)
+
+
+def test_rms_adaln_status_codes():
+    for key in ("x", "w", "shift", "scale", "idx", "codes", "scales"):
+        assert rms(**{key: None}) == 1, key
+    assert rms(m=-1) == 2 and rms(k=448) == 2 and rms(k=64) == 2 and rms(nf=0) == 2 and rms(fs=511) == 2
+    for key in ("x", "w", "shift", "scale", "codes", "scales", "y"):
+        assert rms(**{key: U}) == 3, key
+    assert rms(fs=1028) == 3 and rms(idx=A + 2) == 3 and rms(rstd=A + 1) == 3
+    assert rms(amax=0.0) == 4 and rms(eps=-1e-6) == 4 and rms(eps=float("nan")) == 4
+    assert rms(m=0) == 0
+
+
+def sw(**kw):
+    a = dict(up=A, gate=A, ld=128, m=4, f=64, amax=1.0, codes=A, scales=A, y=None)
+    a.update(kw)
+    return lib.swiglu_nvfp4(a["up"], a["gate"], a["ld"], a["m"], a["f"], a["amax"], a["codes"], a["scales"],
+                            a["y"], None)
+
+
+def test_swiglu_status_codes():
+    for key in ("up", "gate", "codes", "scales"):
+        assert sw(**{key: None}) == 1, key
+    assert sw(m=-1) == 2 and sw(f=32) == 2 and sw(ld=32) == 2
+    assert sw(up=U) == 3 and sw(ld=132) == 3 and sw(y=U) == 3
+    assert sw(amax=float("inf")) == 4
+    assert sw(m=0) == 0
+
+
+def test_valid_call_without_a_gpu_reports_no_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible: a valid call would launch on fake pointers")
+    assert q() == 5 and rms() == 5 and sw() == 5
+    assert lib.nvfp4act_init() == 5
+
+
+def test_binding_raises_on_status():
+    with pytest.raises(nq.NVFP4Error) as e:
+        nq._check(2)
+    assert e.value.status == 2 and "bad shape" in str(e.value)
