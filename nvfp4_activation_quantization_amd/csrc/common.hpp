@@ -18,6 +18,21 @@
 
 namespace nvfp4act {
 
+// Pointers known to address global memory: loads and stores through them compile to
+// global_* instructions rather than flat_* (pointers that reach a kernel inside a struct
+// argument are otherwise treated as generic).  The qualifier only exists for the gfx950
+// pass; the host pass of the same source sees plain pointers.
+#if defined(__HIP_DEVICE_COMPILE__)
+#define NVFP4_GLOBAL __attribute__((address_space(1)))
+#else
+#define NVFP4_GLOBAL
+#endif
+
+template <class T>
+__device__ __forceinline__ NVFP4_GLOBAL T* global_ptr(T* p) {
+  return (NVFP4_GLOBAL T*)p;
+}
+
 constexpr int kWave = 64;
 constexpr uint32_t kRcp6Bits = 0x3E2AAAABu;   // fp32 nearest to 1/6
 
@@ -37,6 +52,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// bf16(f) as an fp32 value, in one instruction: converting the pair (0, f) puts bf16(f)
+// in the upper half and +0 in the lower half, which is exactly the fp32 encoding of the
+// rounded value.
+__device__ __forceinline__ float round_bf16(float f) {
+  return __uint_as_float(pack_bf16x2(0.0f, f));
+}
+
+// Pack two values that are already bf16-exact fp32 numbers (upper halves of a and b).
+__device__ __forceinline__ uint32_t pack_exact_bf16x2(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
 // ---- E4M3 / E2M1 ---------------------------------------------------------------------
 
 // E4M3 code of a non-negative fp32, nearest-even, saturating at 448.  v_cvt_pk_fp8_f32
@@ -44,7 +71,8 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // the input is clamped first.
 __device__ __forceinline__ uint32_t e4m3_code(float sf) {
   float c = __builtin_fminf(sf, 448.0f);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, 0, false) & 0xFFu;
+  // bytes 0 and 1 receive the code; the rest keeps c's bits and is masked off
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, __float_as_int(c), false) & 0xFFu;
 }
 
 // Exact value of an E4M3 code 0..126: exponent field 0 is m * 2^-9, else 2^(e-7)(1+m/8).
@@ -58,7 +86,7 @@ __device__ __forceinline__ float e4m3_value(uint32_t s) {
 // scaled fp4 conversion with scale 1.0 rounds nearest-even, saturates at 6 and keeps
 // the sign of zero, like the specification, on every non-NaN fp32 input.
 __device__ __forceinline__ uint32_t pack_e2m1x8(const float* v) {
-  uint32_t w = 0;
+  uint32_t w = __float_as_uint(v[0]);     // every byte is overwritten below
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0], v[1], 1.0f, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
@@ -69,8 +97,8 @@ __device__ __forceinline__ uint32_t pack_e2m1x8(const float* v) {
 // ---- cross-lane ----------------------------------------------------------------------
 
 // Value of lane L^1 (DPP quad_perm [1,0,3,2]).
-__device__ __forceinline__ float lane_xor1(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+__device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
 }
 
 // ---- global scale and inverse-scale table ----------------------------------------------
@@ -85,20 +113,23 @@ __device__ __forceinline__ void fill_inverse_table(float* inv, float gsf, int ti
 
 // ---- the block quantizer for one chunk --------------------------------------------------
 
-// y[0..7]: this lane's half of a 16-element block (its partner lane holds the other
+// y[0..7]: this lane's half of a 16-element block (its partner lane L^1 holds the other
 // half).  Returns the packed codes of the 8 elements and sets *scale to the block's
 // E4M3 code (the same value on both lanes of the pair).
 __device__ __forceinline__ uint32_t quantize_chunk(const float* y, float gsf, const float* inv_tab,
                                                    uint32_t* scale) {
-  float a = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(y[0]), __builtin_fabsf(y[1])),
-                            __builtin_fmaxf(__builtin_fabsf(y[2]), __builtin_fabsf(y[3])));
-  float b = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(y[4]), __builtin_fabsf(y[5])),
-                            __builtin_fmaxf(__builtin_fabsf(y[6]), __builtin_fabsf(y[7])));
-  float amax = __builtin_fmaxf(a, b);
-  amax = __builtin_fmaxf(amax, lane_xor1(amax));
+  float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(y[0]), __builtin_fabsf(y[1])),
+                               __builtin_fabsf(y[2]));
+  amax = __builtin_fmaxf(__builtin_fmaxf(amax, __builtin_fabsf(y[3])), __builtin_fabsf(y[4]));
+  amax = __builtin_fmaxf(__builtin_fmaxf(amax, __builtin_fabsf(y[5])), __builtin_fabsf(y[6]));
+  amax = __builtin_fmaxf(amax, __builtin_fabsf(y[7]));
+  // the partner lane's half: amax >= 0, so the larger bit pattern is the larger value
+  uint32_t ab = __float_as_uint(amax);
+  ab = __builtin_elementwise_max(ab, lane_xor1(ab));
+  amax = __uint_as_float(ab);
   const float rcp6 = __uint_as_float(kRcp6Bits);
-  uint32_t s = e4m3_code(gsf * (amax * rcp6));
-  float inv = inv_tab[s];
+  const uint32_t s = e4m3_code(gsf * (amax * rcp6));
+  const float inv = inv_tab[s];
   float v[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = y[i] * inv;
@@ -106,11 +137,20 @@ __device__ __forceinline__ uint32_t quantize_chunk(const float* y, float gsf, co
   return pack_e2m1x8(v);
 }
 
-// Lanes 8q (q = 0..7) gather the scale bytes of lanes 8q, 8q+2, 8q+4, 8q+6 (blocks
-// 4q'..4q'+3 of the current group of 32 blocks) into one little-endian word.
-__device__ __forceinline__ uint32_t gather_scales4(uint32_t s) {
-  uint32_t t = s | (__shfl_down(s, 2, kWave) << 8);
-  return t | (__shfl_down(t, 4, kWave) << 16);
+// Scale-byte gather: lanes 8q (q = 0..7) collect the codes of lanes 8q, 8q+2, 8q+4, 8q+6
+// (four consecutive blocks) into one little-endian word.  The two byte-address operands
+// of ds_bpermute are per-lane constants made once by scale_gather_addresses().
+struct GatherAddr {
+  int plus2, plus4;
+};
+
+__device__ __forceinline__ GatherAddr scale_gather_addresses(int lane) {
+  return GatherAddr{((lane + 2) & 63) * 4, ((lane + 4) & 63) * 4};
+}
+
+__device__ __forceinline__ uint32_t gather_scales4(uint32_t s, const GatherAddr& g) {
+  uint32_t t = s | ((uint32_t)__builtin_amdgcn_ds_bpermute(g.plus2, (int)s) << 8);
+  return t | ((uint32_t)__builtin_amdgcn_ds_bpermute(g.plus4, (int)t) << 16);
 }
 
 // Byte offset, in the swizzled scale buffer, of block 0 of row r (k columns); block b
@@ -121,9 +161,9 @@ __device__ __forceinline__ int64_t row_scale_base(int64_t r, int64_t k) {
 
 // Zero the scale bytes of row r (a padding row, or a row written as zeros).
 __device__ __forceinline__ void zero_row_scales(uint8_t* scales, int64_t r, int64_t k, int lane) {
-  int64_t base = row_scale_base(r, k);
+  NVFP4_GLOBAL uint8_t* base = global_ptr(scales) + row_scale_base(r, k);
   for (int64_t q = lane; q < (k >> 6); q += kWave)
-    *reinterpret_cast<uint32_t*>(scales + base + q * 512) = 0u;
+    *reinterpret_cast<NVFP4_GLOBAL uint32_t*>(base + q * 512) = 0u;
 }
 
 // ---- streaming loads ------------------------------------------------------------------
@@ -132,7 +172,7 @@ __device__ __forceinline__ void zero_row_scales(uint8_t* scales, int64_t r, int6
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 load_stream(const uint4* p) {
-  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const NVFP4_GLOBAL u32x4*>(global_ptr(p)));
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 

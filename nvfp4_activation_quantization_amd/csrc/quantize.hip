@@ -25,6 +25,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint4* __restr
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  const GatherAddr ga = scale_gather_addresses(lane);
   const float gsf = global_scale(global_amax);
   fill_inverse_table(inv_tab, gsf, tid);
   __syncthreads();
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint4* __restr
                       bf16_lo(v[u].z), bf16_hi(v[u].z), bf16_lo(v[u].w), bf16_hi(v[u].w)};
         uint32_t s;
         uint32_t q = quantize_chunk(y, gsf, inv_tab, &s);
-        uint32_t s4 = gather_scales4(s);
+        uint32_t s4 = gather_scales4(s, ga);
         if (c < chunks) {
           cr[c] = q;
           if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(scales + sbase + c * 64) = s4;

@@ -5,12 +5,12 @@
 //   y    = bf16(bf16(bf16(bf16(x * rstd) * w) * bf16(1 + scale[t])) + shift[t])
 // followed by the NVFP4 block quantizer.
 //
-// One workgroup of 8 wavefronts per CU, persistent over a contiguous range of rows.
-// The RMSNorm weight and the current frame's modulation row are staged once in LDS as
-// fp32 (bf16(1 + scale) precomputed); a frame change restages it behind two barriers.
-// A row whose frame is not the staged one (possible only for unsorted frame indices)
-// reads its modulation row from global memory instead.  Each wavefront holds its row in
-// registers between the statistic and the output pass, so x is read from HBM once.
+// One workgroup per CU, persistent over a contiguous range of rows.  The RMSNorm weight
+// and the current frame's modulation row are staged once in LDS as fp32 (bf16(1 + scale)
+// precomputed); a frame change restages them behind two barriers.  A row whose frame is
+// not the staged one (possible only for unsorted frame indices) reads its modulation row
+// from global memory instead.  Each wavefront holds its row in registers between the
+// statistic and the output pass, so x is read from HBM once.
 //
 // The statistic uses the fixed tree of the specification: lane L owns chunks L + 64j,
 // keeps 8 accumulators (fused multiply-add), folds them pairwise, and a butterfly over the
@@ -22,9 +22,7 @@ namespace nvfp4act {
 
 namespace {
 
-constexpr int kThreads = 512;
-constexpr int kWaves = kThreads / kWave;
-constexpr int kMaxStagedK = 8192;       // 12 * k + 512 bytes of LDS
+constexpr int kMaxStagedK = 8192;       // LDS: 12 * k + 512 bytes
 
 struct RmsArgs {
   const uint4* x;
@@ -50,23 +48,16 @@ __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
   f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
-// Round 8 fp32 values to bf16: packed words in p, the rounded values back in f.
-__device__ __forceinline__ void round8(float* f, uint32_t* p) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    p[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
-    f[2 * i] = bf16_lo(p[i]);
-    f[2 * i + 1] = bf16_hi(p[i]);
-  }
+__device__ __forceinline__ void split8(const float4& a, const float4& b, float* f) {
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// The statistic of a row held as per-lane chunks v[0..n) (chunk L + 64j in v[j]).
+// The statistic of a row held as per-lane chunks (chunk L + 64j in v[j]).
 template <int N>
-__device__ __forceinline__ float row_rstd(const uint4* v, int n, int64_t k, float eps) {
+__device__ __forceinline__ float row_rstd(const uint4* v, int64_t k, float eps) {
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < N; ++j) {
-    if (N == 0 && j >= n) break;
     float f[8];
     unpack8(v[j], f);
 #pragma unroll
@@ -75,78 +66,105 @@ __device__ __forceinline__ float row_rstd(const uint4* v, int n, int64_t k, floa
   float s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) s = s + __shfl_xor(s, d, kWave);
-  float ms = s / (float)k;
-  return 1.0f / sqrtf(ms + eps);
+  return 1.0f / sqrtf(s / (float)k + eps);
 }
 
-// adaLN modulation and quantization of one chunk c of row r.
-//   x8   : the chunk's 8 inputs as fp32;  w8, opl8, sh8 : parameters as fp32
-__device__ __forceinline__ void emit_chunk(const RmsArgs& a, int64_t r, int64_t c, int lane,
-                                           const float* x8, const float* w8, const float* opl8,
-                                           const float* sh8, float rstd, float gsf,
-                                           const float* inv_tab, int64_t sbase) {
-  float f[8];
-  uint32_t p[4];
+// y = bf16(bf16(bf16(bf16(x * rstd) * w) * opl) + shift) for the 8 elements of a chunk;
+// every rounding yields the fp32 encoding of the bf16 result directly (round_bf16).
+__device__ __forceinline__ void modulate8(const float* x8, const float* w8, const float* o8,
+                                          const float* h8, float rstd, float* y) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = x8[e] * rstd;
-  round8(f, p);                                      // n  = bf16(x * rstd)
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = f[e] * w8[e];
-  round8(f, p);                                      // nw = bf16(n * w)
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = f[e] * opl8[e];
-  round8(f, p);                                      // m  = bf16(nw * bf16(1 + scale))
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = f[e] + sh8[e];
-  round8(f, p);                                      // y  = bf16(m + shift)
+  for (int e = 0; e < 8; ++e) {
+    float n = round_bf16(x8[e] * rstd);
+    float nw = round_bf16(n * w8[e]);
+    float mm = round_bf16(nw * o8[e]);
+    y[e] = round_bf16(mm + h8[e]);
+  }
+}
+
+// Per-row output cursors of one lane: chunk j of the lane is chunk c = lane + 64 j.
+struct RowOut {
+  NVFP4_GLOBAL uint32_t* codes;    // codes of chunk c at codes[64 j]
+  NVFP4_GLOBAL uint8_t* scales;    // swizzled scale word of chunk c (lanes 8q) at scales + 4096 j
+  NVFP4_GLOBAL uint4* y;           // y_out of chunk c at y[64 j], or null
+};
+
+__device__ __forceinline__ RowOut make_row_out(uint32_t* codes, uint8_t* scales, uint4* y_out, int64_t k,
+                                               int64_t r, int lane) {
+  const int64_t chunks = k >> 3;
+  RowOut o;
+  o.codes = global_ptr(codes) + r * chunks + lane;
+  o.scales = global_ptr(scales) + row_scale_base(r, k) + (int64_t)lane * 64;
+  o.y = y_out ? global_ptr(y_out) + r * chunks + lane : nullptr;
+  return o;
+}
+
+__device__ __forceinline__ RowOut row_out(const RmsArgs& a, int64_t r, int lane) {
+  return make_row_out(a.codes, a.scales, a.y_out, a.k, r, lane);
+}
+
+// Quantize chunk j of a row and store its codes, its scale word and y_out.
+__device__ __forceinline__ void store_chunk(const RowOut& o, int j, int lane, const float* y, float gsf,
+                                            const float* inv_tab, const GatherAddr& ga) {
   uint32_t s;
-  uint32_t q = quantize_chunk(f, gsf, inv_tab, &s);
-  uint32_t s4 = gather_scales4(s);
-  a.codes[r * (a.k >> 3) + c] = q;
-  if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(a.scales + sbase + c * 64) = s4;
-  if (a.y_out) a.y_out[r * (a.k >> 3) + c] = make_uint4(p[0], p[1], p[2], p[3]);
+  const uint32_t q = quantize_chunk(y, gsf, inv_tab, &s);
+  const uint32_t s4 = gather_scales4(s, ga);
+  o.codes[kWave * j] = q;
+  if ((lane & 7) == 0) *reinterpret_cast<NVFP4_GLOBAL uint32_t*>(o.scales + (int64_t)4096 * j) = s4;
+  if (o.y)
+    o.y[kWave * j] = make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
+                                pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
 }
 
 // Write row r as zeros (frame index outside [0, num_frames)).
 __device__ void zero_row(const RmsArgs& a, int64_t r, int lane) {
   const int64_t chunks = a.k >> 3;
   for (int64_t c = lane; c < chunks; c += kWave) {
-    a.codes[r * chunks + c] = 0u;
-    if (a.y_out) a.y_out[r * chunks + c] = make_uint4(0, 0, 0, 0);
+    global_ptr(a.codes)[r * chunks + c] = 0u;
+    if (a.y_out) global_ptr(a.y_out)[r * chunks + c] = make_uint4(0, 0, 0, 0);
   }
   zero_row_scales(a.scales, r, a.k, lane);
   if (lane == 0 && a.status) atomicOr(a.status, 1u);
 }
 
-__device__ __forceinline__ void load_frame_chunk(const RmsArgs& a, int64_t t, int64_t c, float* opl8,
-                                                 float* sh8) {
-  uint4 sc = *reinterpret_cast<const uint4*>(a.scale + t * a.frame_stride + 8 * c);
-  uint4 sh = *reinterpret_cast<const uint4*>(a.shift + t * a.frame_stride + 8 * c);
-  float tmp[8];
-  uint32_t p[4];
-  unpack8(sc, tmp);
+// The modulation row of frame t, chunk c, as fp32: o8 = bf16(1 + scale), h8 = shift.
+__device__ __forceinline__ void load_frame_chunk(const uint16_t* shift, const uint16_t* scale,
+                                                 int64_t frame_stride, int64_t t, int64_t c, float* o8,
+                                                 float* h8) {
+  const uint4 sc = *reinterpret_cast<const NVFP4_GLOBAL uint4*>(global_ptr(scale) + t * frame_stride + 8 * c);
+  const uint4 sh = *reinterpret_cast<const NVFP4_GLOBAL uint4*>(global_ptr(shift) + t * frame_stride + 8 * c);
+  unpack8(sc, o8);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) tmp[e] = 1.0f + tmp[e];
-  round8(tmp, p);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) opl8[e] = tmp[e];
-  unpack8(sh, sh8);
+  for (int e = 0; e < 8; ++e) o8[e] = round_bf16(1.0f + o8[e]);
+  unpack8(sh, h8);
 }
 
-// ---- the staged kernel (k <= kMaxStagedK, CPL = k / 512 chunks per lane) ------------------
+__device__ __forceinline__ void load_frame_chunk(const RmsArgs& a, int64_t t, int64_t c, float* o8,
+                                                 float* h8) {
+  load_frame_chunk(a.shift, a.scale, a.frame_stride, t, c, o8, h8);
+}
 
 // A row whose frame is not the staged one: re-read x (an L2 hit in practice) and the
-// frame's modulation row from global memory, one chunk at a time.
-__device__ __noinline__ void emit_row_unstaged(const RmsArgs& a, int64_t r, int64_t t, int lane,
-                                               const float* w_f, float rstd, float gsf,
-                                               const float* inv_tab, int64_t sbase) {
-  const uint4* xr = a.x + r * (a.k >> 3);
+// frame's modulation row from global memory, one chunk at a time.  Out of line and with
+// plain arguments, so the kernel's hot loop is not shaped by this rare path.
+__device__ __noinline__ void emit_row_unstaged(const uint4* x, const uint16_t* shift,
+                                               const uint16_t* scale, int64_t frame_stride, uint32_t* codes,
+                                               uint8_t* scales, uint4* y_out, int64_t k, int64_t r,
+                                               int64_t t, const float4* wA, const float4* wB, float rstd,
+                                               float gsf, const float* inv_tab) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const NVFP4_GLOBAL uint4* xr = global_ptr(x) + r * (k >> 3);
+  const RowOut o = make_row_out(codes, scales, y_out, k, r, lane);
+  const GatherAddr ga = scale_gather_addresses(lane);
 #pragma unroll 1
-  for (int64_t c = lane; c < (a.k >> 3); c += kWave) {
-    float x8[8], o8[8], h8[8];
+  for (int j = 0; j < (int)(k >> 9); ++j) {
+    const int64_t c = lane + (int64_t)kWave * j;
+    float x8[8], w8[8], o8[8], h8[8], y[8];
     unpack8(xr[c], x8);
-    load_frame_chunk(a, t, c, o8, h8);
-    emit_chunk(a, r, c, lane, x8, w_f + 8 * c, o8, h8, rstd, gsf, inv_tab, sbase);
+    split8(wA[c], wB[c], w8);
+    load_frame_chunk(shift, scale, frame_stride, t, c, o8, h8);
+    modulate8(x8, w8, o8, h8, rstd, y);
+    store_chunk(o, j, lane, y, gsf, inv_tab, ga);
   }
 }
 
@@ -156,100 +174,131 @@ __device__ __forceinline__ void load_row(uint4* v, const uint4* xr, int lane) {
   for (int j = 0; j < CPL; ++j) v[j] = load_stream(xr + lane + kWave * j);
 }
 
-template <int CPL>
-__global__ __launch_bounds__(kThreads) void rms_adaln_staged(RmsArgs a) {
-  extern __shared__ float lds[];
-  float* inv_tab = lds;
-  float* w_f = lds + 128;
-  float* opl_f = w_f + a.k;
-  float* sh_f = opl_f + a.k;
+// ---- the staged kernel (k <= kMaxStagedK, CPL = k / 512 chunks per lane) ------------------
+//
+// LDS: inverse-scale table (128 fp32), then six fp32 arrays of float4 indexed by chunk:
+// weight elements 0-3 and 4-7, bf16(1 + scale) 0-3 / 4-7, shift 0-3 / 4-7.  Lane L reads
+// chunk L + 64j, so each ds_read_b128 of a wavefront is one contiguous 1 KiB.
+//
+// THREADS = 512 (8 wavefronts, up to 256 VGPRs) double-buffers rows: the next row's loads
+// are in flight while the current row is processed.  THREADS = 1024 (16 wavefronts, 128
+// VGPRs) holds one row per wavefront and hides latency with more wavefronts.
+
+template <int CPL, int THREADS, bool DB>
+__global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a) {
+  constexpr int kWaves = THREADS / kWave;
+  extern __shared__ float4 lds4[];
+  float* inv_tab = reinterpret_cast<float*>(lds4);
+  const int64_t chunks = a.k >> 3;
+  float4* wA = lds4 + 32;                 // 128 floats = 32 float4
+  float4* wB = wA + chunks;
+  float4* oA = wB + chunks;
+  float4* oB = oA + chunks;
+  float4* hA = oB + chunks;
+  float4* hB = hA + chunks;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int64_t chunks = a.k >> 3;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const GatherAddr ga = scale_gather_addresses(lane);
+  const NVFP4_GLOBAL uint4* x = global_ptr(a.x);
 
   const int64_t unit = xcd_unit(a.per);
   const int64_t r_begin = unit * a.rows_per_unit;
   if (r_begin >= a.padded) return;                      // idle workgroup (uniform)
   const int64_t r_end = (r_begin + a.rows_per_unit < a.padded) ? r_begin + a.rows_per_unit : a.padded;
+  const int64_t m = a.m;
 
-  // Each wavefront double-buffers its rows: the next row's loads are in flight while the
-  // current row is normalised, modulated and quantized.
-  uint4 cur[CPL], nxt[CPL];
-  {
+  uint4 bufA[CPL];
+  uint4 bufB[DB ? CPL : 1];
+  if (DB) {
     const int64_t r = r_begin + wave;
-    if (r < r_end && r < a.m) load_row<CPL>(cur, a.x + r * chunks, lane);
+    if (r < r_end && r < m) load_row<CPL>(bufA, reinterpret_cast<const uint4*>(x + r * chunks), lane);
   }
 
   const float gsf = global_scale(a.global_amax);
   fill_inverse_table(inv_tab, gsf, tid);
-  for (int64_t c = tid; c < chunks; c += kThreads) {
+  for (int64_t c = tid; c < chunks; c += THREADS) {
     float f[8];
-    unpack8(*reinterpret_cast<const uint4*>(a.w + 8 * c), f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) w_f[8 * c + e] = f[e];
+    unpack8(*reinterpret_cast<const NVFP4_GLOBAL uint4*>(global_ptr(a.w) + 8 * c), f);
+    wA[c] = make_float4(f[0], f[1], f[2], f[3]);
+    wB[c] = make_float4(f[4], f[5], f[6], f[7]);
   }
   __syncthreads();
 
   int64_t staged = -1;
-  for (int64_t g = r_begin; g < r_end; g += kWaves) {
-    const int64_t r = g + wave;
-    const int64_t rn = r + kWaves;
-    if (rn < r_end && rn < a.m) load_row<CPL>(nxt, a.x + rn * chunks, lane);
 
+  // One group of kWaves rows: restage the frame if needed (uniform), then each wavefront
+  // processes its row held in cur; with DB the row kWaves further is loaded into nxt first.
+  auto group = [&](int64_t g, uint4* cur, uint4* nxt) {
+    const int64_t r = g + wave;
+    if (DB) {
+      const int64_t rn = r + kWaves;
+      if (rn < r_end && rn < m) load_row<CPL>(nxt, reinterpret_cast<const uint4*>(x + rn * chunks), lane);
+    } else {
+      if (r < r_end && r < m) load_row<CPL>(cur, reinterpret_cast<const uint4*>(x + r * chunks), lane);
+    }
     int64_t want = staged;
-    if (g < a.m) {
-      int64_t t = a.frame_idx[g];
+    if (g < m) {
+      const int64_t t = global_ptr(a.frame_idx)[g];
       if (t >= 0 && t < a.num_frames) want = t;
     }
-    if (want != staged) {                               // uniform over the workgroup
+    if (want != staged) {
       __syncthreads();
-      for (int64_t c = tid; c < chunks; c += kThreads) {
+      for (int64_t c = tid; c < chunks; c += THREADS) {
         float o8[8], h8[8];
         load_frame_chunk(a, want, c, o8, h8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          opl_f[8 * c + e] = o8[e];
-          sh_f[8 * c + e] = h8[e];
-        }
+        oA[c] = make_float4(o8[0], o8[1], o8[2], o8[3]);
+        oB[c] = make_float4(o8[4], o8[5], o8[6], o8[7]);
+        hA[c] = make_float4(h8[0], h8[1], h8[2], h8[3]);
+        hB[c] = make_float4(h8[4], h8[5], h8[6], h8[7]);
       }
       __syncthreads();
       staged = want;
     }
-
-    if (r < r_end) {
-      if (r >= a.m) {
-        zero_row_scales(a.scales, r, a.k, lane);
-      } else {
-        const float rstd = row_rstd<CPL>(cur, CPL, a.k, a.eps);
-        if (lane == 0 && a.rstd_out) a.rstd_out[r] = rstd;
-        const int64_t t = a.frame_idx[r];
-        if (t < 0 || t >= a.num_frames) {
-          zero_row(a, r, lane);
-        } else {
-          const int64_t sbase = row_scale_base(r, a.k);
-          // Keep the row packed between the two passes: without this the compiler keeps
-          // the fp32 values unpacked for the statistic alive into the output pass.
-#pragma unroll
-          for (int j = 0; j < CPL; ++j)
-            asm volatile("" : "+v"(cur[j].x), "+v"(cur[j].y), "+v"(cur[j].z), "+v"(cur[j].w));
-          if (t == staged) {
-#pragma unroll
-            for (int j = 0; j < CPL; ++j) {
-              const int64_t c = lane + kWave * j;
-              float x8[8];
-              unpack8(cur[j], x8);
-              emit_chunk(a, r, c, lane, x8, w_f + 8 * c, opl_f + 8 * c, sh_f + 8 * c, rstd, gsf,
-                         inv_tab, sbase);
-            }
-          } else {
-            emit_row_unstaged(a, r, t, lane, w_f, rstd, gsf, inv_tab, sbase);
-          }
-        }
-      }
+    if (r >= r_end) return;
+    if (r >= m) {
+      zero_row_scales(a.scales, r, a.k, lane);
+      return;
     }
+    const float rstd = row_rstd<CPL>(cur, a.k, a.eps);
+    if (lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
+    const int64_t t = global_ptr(a.frame_idx)[r];
+    if (t < 0 || t >= a.num_frames) {
+      zero_row(a, r, lane);
+      return;
+    }
+    if (t != staged) {
+      emit_row_unstaged(a.x, a.shift, a.scale, a.frame_stride, a.codes, a.scales, a.y_out, a.k, r, t, wA, wB,
+                        rstd, gsf, inv_tab);
+      return;
+    }
+    // Keep the row packed between the two passes: without this the compiler keeps the
+    // fp32 values unpacked for the statistic alive into the output pass.
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) cur[j] = nxt[j];
+    for (int j = 0; j < CPL; ++j)
+      asm volatile("" : "+v"(cur[j].x), "+v"(cur[j].y), "+v"(cur[j].z), "+v"(cur[j].w));
+    const RowOut o = row_out(a, r, lane);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + kWave * j;
+      float x8[8], w8[8], o8[8], h8[8], y[8];
+      unpack8(cur[j], x8);
+      split8(wA[c], wB[c], w8);
+      split8(oA[c], oB[c], o8);
+      split8(hA[c], hB[c], h8);
+      modulate8(x8, w8, o8, h8, rstd, y);
+      store_chunk(o, j, lane, y, gsf, inv_tab, ga);
+    }
+  };
+
+  if (DB) {
+    // two groups per iteration so the buffers swap roles without register copies
+    for (int64_t g = r_begin; g < r_end; g += 2 * kWaves) {
+      group(g, bufA, bufB);
+      if (g + kWaves < r_end) group(g + kWaves, bufB, bufA);
+    }
+  } else {
+    for (int64_t g = r_begin; g < r_end; g += kWaves) group(g, bufA, bufA);
   }
 }
 
@@ -270,7 +319,7 @@ __global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
     zero_row_scales(a.scales, r, a.k, lane);
     return;
   }
-  const uint4* xr = a.x + r * chunks;
+  const NVFP4_GLOBAL uint4* xr = global_ptr(a.x) + r * chunks;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int64_t c = lane; c < chunks; c += kWave) {
     float f[8];
@@ -282,40 +331,55 @@ __global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
 #pragma unroll
   for (int d = 1; d < kWave; d <<= 1) s = s + __shfl_xor(s, d, kWave);
   const float rstd = 1.0f / sqrtf(s / (float)a.k + a.eps);
-  if (lane == 0 && a.rstd_out) a.rstd_out[r] = rstd;
-  const int64_t t = a.frame_idx[r];
+  if (lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
+  const int64_t t = global_ptr(a.frame_idx)[r];
   if (t < 0 || t >= a.num_frames) {
     zero_row(a, r, lane);
     return;
   }
-  const int64_t sbase = row_scale_base(r, a.k);
-  for (int64_t c = lane; c < chunks; c += kWave) {
-    float x8[8], w8[8], o8[8], h8[8];
+  const RowOut o = row_out(a, r, lane);
+  const GatherAddr ga = scale_gather_addresses(lane);
+  for (int j = 0; j < (int)(chunks >> 6); ++j) {
+    const int64_t c = lane + (int64_t)kWave * j;
+    float x8[8], w8[8], o8[8], h8[8], y[8];
     unpack8(xr[c], x8);
-    unpack8(*reinterpret_cast<const uint4*>(a.w + 8 * c), w8);
+    unpack8(*reinterpret_cast<const NVFP4_GLOBAL uint4*>(global_ptr(a.w) + 8 * c), w8);
     load_frame_chunk(a, t, c, o8, h8);
-    emit_chunk(a, r, c, lane, x8, w8, o8, h8, rstd, gsf, inv_tab, sbase);
+    modulate8(x8, w8, o8, h8, rstd, y);
+    store_chunk(o, j, lane, y, gsf, inv_tab, ga);
   }
 }
 
+// Launch shape of the staged kernel (compile-time; see the kernel comment).
+#ifndef NVFP4ACT_RMS_THREADS
+#define NVFP4ACT_RMS_THREADS 512
+#endif
+#ifndef NVFP4ACT_RMS_DOUBLE_BUFFER
+#define NVFP4ACT_RMS_DOUBLE_BUFFER 1
+#endif
+constexpr int kStagedThreads = NVFP4ACT_RMS_THREADS;
+constexpr bool kStagedDoubleBuffer = NVFP4ACT_RMS_DOUBLE_BUFFER != 0;
+
 template <int CPL>
 hipError_t launch_staged(const RmsArgs& a, const DeviceInfo& dev, hipStream_t stream) {
-  const size_t lds = (128 + 3 * (size_t)a.k) * sizeof(float);
+  constexpr int kWaves = kStagedThreads / kWave;
+  const size_t lds = (size_t)512 + 96 * (size_t)(a.k >> 3);
   RmsArgs b = a;
   const int64_t groups = (a.padded + kWaves - 1) / kWaves;
   int64_t units = dev.cu_count < groups ? dev.cu_count : groups;
   b.per = (units + kXcds - 1) / kXcds;
   units = b.per * kXcds;
   b.rows_per_unit = (a.padded + units - 1) / units;
-  hipLaunchKernelGGL(rms_adaln_staged<CPL>, dim3((uint32_t)units), dim3(kThreads), lds, stream, b);
+  hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, kStagedDoubleBuffer>), dim3((uint32_t)units),
+                     dim3(kStagedThreads), lds, stream, b);
   return hipGetLastError();
 }
 
 template <int CPL>
 hipError_t allow_lds() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&rms_adaln_staged<CPL>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)((128 + 3 * kMaxStagedK) * sizeof(float)));
+  return hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&rms_adaln_staged<CPL, kStagedThreads, kStagedDoubleBuffer>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, (int)(512 + 12 * kMaxStagedK));
 }
 
 }  // namespace

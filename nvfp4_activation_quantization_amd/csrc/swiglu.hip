@@ -82,6 +82,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restric
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
+  const GatherAddr ga = scale_gather_addresses(lane);
 
   const int64_t unit = xcd_unit(per);
   const int64_t r_begin = unit * rows_per_unit;
@@ -123,13 +124,13 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restric
         for (int q = 0; q < 4; ++q) {
           const float s0 = __uint_as_float((uint32_t)table[gw[q] & 0xFFFFu] << 16);
           const float s1 = __uint_as_float((uint32_t)table[gw[q] >> 16] << 16);
-          p[q] = pack_bf16x2(s0 * bf16_lo(uw[q]), s1 * bf16_hi(uw[q]));
-          y[2 * q] = bf16_lo(p[q]);
-          y[2 * q + 1] = bf16_hi(p[q]);
+          y[2 * q] = round_bf16(s0 * bf16_lo(uw[q]));
+          y[2 * q + 1] = round_bf16(s1 * bf16_hi(uw[q]));
+          p[q] = pack_exact_bf16x2(y[2 * q], y[2 * q + 1]);
         }
         uint32_t s;
         const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
-        const uint32_t s4 = gather_scales4(s);
+        const uint32_t s4 = gather_scales4(s, ga);
         if (c < chunks) {
           codes[r * chunks + c] = code;
           if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(scales + sbase + c * 64) = s4;
