@@ -12,7 +12,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "../../include/nvfp4act.h"
+#include "nvfp4act.h"
 #include "kernels.hpp"
 
 namespace {

@@ -137,20 +137,12 @@ __device__ __forceinline__ uint32_t quantize_chunk(const float* y, float gsf, co
   return pack_e2m1x8(v);
 }
 
-// Scale-byte gather: lanes 8q (q = 0..7) collect the codes of lanes 8q, 8q+2, 8q+4, 8q+6
-// (four consecutive blocks) into one little-endian word.  The two byte-address operands
-// of ds_bpermute are per-lane constants made once by scale_gather_addresses().
-struct GatherAddr {
-  int plus2, plus4;
-};
-
-__device__ __forceinline__ GatherAddr scale_gather_addresses(int lane) {
-  return GatherAddr{((lane + 2) & 63) * 4, ((lane + 4) & 63) * 4};
-}
-
-__device__ __forceinline__ uint32_t gather_scales4(uint32_t s, const GatherAddr& g) {
-  uint32_t t = s | ((uint32_t)__builtin_amdgcn_ds_bpermute(g.plus2, (int)s) << 8);
-  return t | ((uint32_t)__builtin_amdgcn_ds_bpermute(g.plus4, (int)t) << 16);
+// Where a lane writes its block's scale byte.  Chunk c = lane + 64 j holds half of block
+// b = c / 2, whose byte sits at row_scale_base + (c / 8) * 512 + (c / 2) % 4, i.e. at
+// row_scale_base + scale_lane_offset(lane) + 4096 j.  Both lanes of a block store the same
+// byte to the same address, so no cross-lane gather is needed.
+__device__ __forceinline__ int64_t scale_lane_offset(int lane) {
+  return (int64_t)(lane >> 3) * 512 + ((lane >> 1) & 3);
 }
 
 // Byte offset, in the swizzled scale buffer, of block 0 of row r (k columns); block b
@@ -178,16 +170,51 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
 
 // ---- workgroup -> work-unit mapping ---------------------------------------------------
 
-// Workgroups are dispatched round-robin over the 8 XCDs.  Kernels launch 8 * per
-// workgroups and remap the launch index so that the workgroups of one XCD take
-// consecutive work units (consecutive rows): the scale bytes of a 128-row tile then meet
-// in one XCD's L2 and leave it as whole lines.  The map is a bijection of [0, 8*per);
-// units >= the real unit count are idle.
+// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  Two maps
+// keep the scale bytes of a 128-row tile (whose 128-byte lines collect bytes from 32
+// different rows) inside one L2 while they are written:
 constexpr int kXcds = 8;
 
+// Non-persistent grids: launch 8 * per workgroups; the workgroups of one XCD take
+// consecutive work units.  A bijection of [0, 8*per); units >= the real count are idle.
 __device__ __forceinline__ int64_t xcd_unit(int64_t per) {
   int64_t bid = blockIdx.x;
   return (bid % kXcds) * per + bid / kXcds;
+}
+
+// Persistent grids of 8 * W workgroups (one per CU) with `waves` rows per step each:
+// XCD x owns rows [x * rows_per_xcd, (x+1) * rows_per_xcd); at step s its W workgroups
+// process the W * waves consecutive rows starting at x * rows_per_xcd + s * W * waves
+// together, so every tile of the step is finished within the step.
+struct XcdSteps {
+  int64_t first;      // first row of this workgroup's slot in step 0
+  int64_t end;        // end of this XCD's rows (clamped to the padded row count)
+  int64_t step;       // rows per step of the whole XCD
+};
+
+__device__ __forceinline__ XcdSteps xcd_steps(int64_t rows_per_xcd, int64_t padded, int waves) {
+  const int64_t bid = blockIdx.x;
+  const int64_t w_count = gridDim.x / kXcds;
+  const int64_t xcd = bid % kXcds, w = bid / kXcds;
+  XcdSteps s;
+  const int64_t begin = xcd * rows_per_xcd;
+  s.end = (begin + rows_per_xcd < padded) ? begin + rows_per_xcd : padded;
+  s.step = w_count * waves;
+  s.first = begin + w * waves;
+  return s;
+}
+
+// Host side: workgroups per XCD and rows per XCD for a persistent launch.
+inline void plan_xcd_steps(int64_t padded, int cu_count, int waves, int64_t* wgs_per_xcd,
+                           int64_t* rows_per_xcd) {
+  const int64_t per_xcd = (padded + kXcds - 1) / kXcds;
+  int64_t w = cu_count / kXcds;
+  if (w < 1) w = 1;
+  const int64_t need = (per_xcd + waves - 1) / waves;
+  if (need < w) w = need;
+  const int64_t step = w * waves;
+  *wgs_per_xcd = w;
+  *rows_per_xcd = (per_xcd + step - 1) / step * step;
 }
 
 }  // namespace nvfp4act

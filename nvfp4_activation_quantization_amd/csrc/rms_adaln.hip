@@ -24,6 +24,24 @@ namespace {
 
 constexpr int kMaxStagedK = 8192;       // LDS: 12 * k + 512 bytes
 
+#ifndef NVFP4ACT_RMS_CONTIGUOUS
+#define NVFP4ACT_RMS_CONTIGUOUS 0
+#endif
+
+#if NVFP4ACT_RMS_CONTIGUOUS
+// Alternative row map: each workgroup takes one contiguous range of rows.
+__device__ __forceinline__ XcdSteps contiguous_rows(int64_t padded, int waves) {
+  const int64_t units = gridDim.x, per = units / kXcds;
+  const int64_t unit = xcd_unit(per);
+  const int64_t rows = (padded + units - 1) / units;
+  XcdSteps s;
+  s.first = unit * rows;
+  s.end = (s.first + rows < padded) ? s.first + rows : padded;
+  s.step = waves;
+  return s;
+}
+#endif
+
 struct RmsArgs {
   const uint4* x;
   const uint16_t* w;
@@ -40,7 +58,7 @@ struct RmsArgs {
   float* rstd_out;
   uint4* y_out;
   uint32_t* status;
-  int64_t rows_per_unit, per;
+  int64_t rows_per_xcd;
 };
 
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
@@ -85,7 +103,7 @@ __device__ __forceinline__ void modulate8(const float* x8, const float* w8, cons
 // Per-row output cursors of one lane: chunk j of the lane is chunk c = lane + 64 j.
 struct RowOut {
   NVFP4_GLOBAL uint32_t* codes;    // codes of chunk c at codes[64 j]
-  NVFP4_GLOBAL uint8_t* scales;    // swizzled scale word of chunk c (lanes 8q) at scales + 4096 j
+  NVFP4_GLOBAL uint8_t* scales;    // scale byte of chunk c's block at scales[4096 j]
   NVFP4_GLOBAL uint4* y;           // y_out of chunk c at y[64 j], or null
 };
 
@@ -94,7 +112,7 @@ __device__ __forceinline__ RowOut make_row_out(uint32_t* codes, uint8_t* scales,
   const int64_t chunks = k >> 3;
   RowOut o;
   o.codes = global_ptr(codes) + r * chunks + lane;
-  o.scales = global_ptr(scales) + row_scale_base(r, k) + (int64_t)lane * 64;
+  o.scales = global_ptr(scales) + row_scale_base(r, k) + scale_lane_offset(lane);
   o.y = y_out ? global_ptr(y_out) + r * chunks + lane : nullptr;
   return o;
 }
@@ -103,17 +121,24 @@ __device__ __forceinline__ RowOut row_out(const RmsArgs& a, int64_t r, int lane)
   return make_row_out(a.codes, a.scales, a.y_out, a.k, r, lane);
 }
 
-// Quantize chunk j of a row and store its codes, its scale word and y_out.
-__device__ __forceinline__ void store_chunk(const RowOut& o, int j, int lane, const float* y, float gsf,
-                                            const float* inv_tab, const GatherAddr& ga) {
+// Quantize chunk j of a row and store its codes, its block's scale byte and (when Y)
+// y_out.  No branches, so consecutive chunks can be scheduled together.
+template <bool Y>
+__device__ __forceinline__ void emit_chunk(const RowOut& o, int j, const float* y, float gsf,
+                                           const float* inv_tab) {
   uint32_t s;
   const uint32_t q = quantize_chunk(y, gsf, inv_tab, &s);
-  const uint32_t s4 = gather_scales4(s, ga);
   o.codes[kWave * j] = q;
-  if ((lane & 7) == 0) *reinterpret_cast<NVFP4_GLOBAL uint32_t*>(o.scales + (int64_t)4096 * j) = s4;
-  if (o.y)
+  o.scales[(int64_t)4096 * j] = (uint8_t)s;
+  if (Y)
     o.y[kWave * j] = make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
                                 pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
+}
+
+__device__ __forceinline__ void store_chunk(const RowOut& o, int j, const float* y, float gsf,
+                                            const float* inv_tab) {
+  if (o.y) emit_chunk<true>(o, j, y, gsf, inv_tab);
+  else emit_chunk<false>(o, j, y, gsf, inv_tab);
 }
 
 // Write row r as zeros (frame index outside [0, num_frames)).
@@ -155,7 +180,6 @@ __device__ __noinline__ void emit_row_unstaged(const uint4* x, const uint16_t* s
   const int lane = threadIdx.x & (kWave - 1);
   const NVFP4_GLOBAL uint4* xr = global_ptr(x) + r * (k >> 3);
   const RowOut o = make_row_out(codes, scales, y_out, k, r, lane);
-  const GatherAddr ga = scale_gather_addresses(lane);
 #pragma unroll 1
   for (int j = 0; j < (int)(k >> 9); ++j) {
     const int64_t c = lane + (int64_t)kWave * j;
@@ -164,7 +188,7 @@ __device__ __noinline__ void emit_row_unstaged(const uint4* x, const uint16_t* s
     split8(wA[c], wB[c], w8);
     load_frame_chunk(shift, scale, frame_stride, t, c, o8, h8);
     modulate8(x8, w8, o8, h8, rstd, y);
-    store_chunk(o, j, lane, y, gsf, inv_tab, ga);
+    store_chunk(o, j, y, gsf, inv_tab);
   }
 }
 
@@ -184,8 +208,8 @@ __device__ __forceinline__ void load_row(uint4* v, const uint4* xr, int lane) {
 // are in flight while the current row is processed.  THREADS = 1024 (16 wavefronts, 128
 // VGPRs) holds one row per wavefront and hides latency with more wavefronts.
 
-template <int CPL, int THREADS, bool DB>
-__global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a) {
+template <int CPL, int THREADS, bool DB, bool Y>
+__global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a, const int32_t* __restrict__ frame_idx) {
   constexpr int kWaves = THREADS / kWave;
   extern __shared__ float4 lds4[];
   float* inv_tab = reinterpret_cast<float*>(lds4);
@@ -199,21 +223,29 @@ __global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const GatherAddr ga = scale_gather_addresses(lane);
   const NVFP4_GLOBAL uint4* x = global_ptr(a.x);
 
-  const int64_t unit = xcd_unit(a.per);
-  const int64_t r_begin = unit * a.rows_per_unit;
-  if (r_begin >= a.padded) return;                      // idle workgroup (uniform)
-  const int64_t r_end = (r_begin + a.rows_per_unit < a.padded) ? r_begin + a.rows_per_unit : a.padded;
+#if NVFP4ACT_RMS_CONTIGUOUS
+  const XcdSteps st = contiguous_rows(a.padded, kWaves);
+#else
+  const XcdSteps st = xcd_steps(a.rows_per_xcd, a.padded, kWaves);
+#endif
+  if (st.first >= st.end) return;                       // idle workgroup (uniform)
+  const int64_t r_end = st.end;
   const int64_t m = a.m;
+  // Last real row of this XCD's range: rows past it (padding rows, or beyond the range)
+  // are never processed, and their loads read this row instead so every load is
+  // unconditional (a conditional load would turn the row buffers into loop phis).
+  const int64_t r_last = (r_end < m ? r_end : m) - 1;
+  const bool has_rows = st.first < m;                   // uniform
+
+  auto row_ptr = [&](int64_t r) {
+    return reinterpret_cast<const uint4*>(x + (r <= r_last ? r : r_last) * chunks);
+  };
 
   uint4 bufA[CPL];
   uint4 bufB[DB ? CPL : 1];
-  if (DB) {
-    const int64_t r = r_begin + wave;
-    if (r < r_end && r < m) load_row<CPL>(bufA, reinterpret_cast<const uint4*>(x + r * chunks), lane);
-  }
+  if (DB && has_rows) load_row<CPL>(bufA, row_ptr(st.first + wave), lane);
 
   const float gsf = global_scale(a.global_amax);
   fill_inverse_table(inv_tab, gsf, tid);
@@ -231,15 +263,13 @@ __global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a) {
   // processes its row held in cur; with DB the row kWaves further is loaded into nxt first.
   auto group = [&](int64_t g, uint4* cur, uint4* nxt) {
     const int64_t r = g + wave;
-    if (DB) {
-      const int64_t rn = r + kWaves;
-      if (rn < r_end && rn < m) load_row<CPL>(nxt, reinterpret_cast<const uint4*>(x + rn * chunks), lane);
-    } else {
-      if (r < r_end && r < m) load_row<CPL>(cur, reinterpret_cast<const uint4*>(x + r * chunks), lane);
+    if (has_rows) {
+      if (DB) load_row<CPL>(nxt, row_ptr(r + st.step), lane);
+      else load_row<CPL>(cur, row_ptr(r), lane);
     }
     int64_t want = staged;
     if (g < m) {
-      const int64_t t = global_ptr(a.frame_idx)[g];
+      const int64_t t = frame_idx[g];
       if (t >= 0 && t < a.num_frames) want = t;
     }
     if (want != staged) {
@@ -262,7 +292,7 @@ __global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a) {
     }
     const float rstd = row_rstd<CPL>(cur, a.k, a.eps);
     if (lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
-    const int64_t t = global_ptr(a.frame_idx)[r];
+    const int64_t t = frame_idx[r];
     if (t < 0 || t >= a.num_frames) {
       zero_row(a, r, lane);
       return;
@@ -287,18 +317,22 @@ __global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a) {
       split8(oA[c], oB[c], o8);
       split8(hA[c], hB[c], h8);
       modulate8(x8, w8, o8, h8, rstd, y);
-      store_chunk(o, j, lane, y, gsf, inv_tab, ga);
+      emit_chunk<Y>(o, j, y, gsf, inv_tab);
+#if NVFP4ACT_RMS_CHUNK_FENCE
+      __builtin_amdgcn_sched_barrier(0);   // bound cross-chunk interleaving (registers)
+#endif
     }
   };
 
   if (DB) {
-    // two groups per iteration so the buffers swap roles without register copies
-    for (int64_t g = r_begin; g < r_end; g += 2 * kWaves) {
+    // Two groups per iteration, both unconditional, so the buffers swap roles without
+    // register copies; a group past the range only prefetches (a clamped row) and returns.
+    for (int64_t g = st.first; g < r_end; g += 2 * st.step) {
       group(g, bufA, bufB);
-      if (g + kWaves < r_end) group(g + kWaves, bufB, bufA);
+      group(g + st.step, bufB, bufA);
     }
   } else {
-    for (int64_t g = r_begin; g < r_end; g += kWaves) group(g, bufA, bufA);
+    for (int64_t g = st.first; g < r_end; g += st.step) group(g, bufA, bufA);
   }
 }
 
@@ -338,7 +372,6 @@ __global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
     return;
   }
   const RowOut o = row_out(a, r, lane);
-  const GatherAddr ga = scale_gather_addresses(lane);
   for (int j = 0; j < (int)(chunks >> 6); ++j) {
     const int64_t c = lane + (int64_t)kWave * j;
     float x8[8], w8[8], o8[8], h8[8], y[8];
@@ -346,16 +379,22 @@ __global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
     unpack8(*reinterpret_cast<const NVFP4_GLOBAL uint4*>(global_ptr(a.w) + 8 * c), w8);
     load_frame_chunk(a, t, c, o8, h8);
     modulate8(x8, w8, o8, h8, rstd, y);
-    store_chunk(o, j, lane, y, gsf, inv_tab, ga);
+    store_chunk(o, j, y, gsf, inv_tab);
   }
 }
 
 // Launch shape of the staged kernel (compile-time; see the kernel comment).
 #ifndef NVFP4ACT_RMS_THREADS
-#define NVFP4ACT_RMS_THREADS 512
+#define NVFP4ACT_RMS_THREADS 768
+#endif
+#ifndef NVFP4ACT_RMS_CONTIGUOUS
+#define NVFP4ACT_RMS_CONTIGUOUS 0
+#endif
+#ifndef NVFP4ACT_RMS_CHUNK_FENCE
+#define NVFP4ACT_RMS_CHUNK_FENCE 0
 #endif
 #ifndef NVFP4ACT_RMS_DOUBLE_BUFFER
-#define NVFP4ACT_RMS_DOUBLE_BUFFER 1
+#define NVFP4ACT_RMS_DOUBLE_BUFFER 0
 #endif
 constexpr int kStagedThreads = NVFP4ACT_RMS_THREADS;
 constexpr bool kStagedDoubleBuffer = NVFP4ACT_RMS_DOUBLE_BUFFER != 0;
@@ -365,21 +404,28 @@ hipError_t launch_staged(const RmsArgs& a, const DeviceInfo& dev, hipStream_t st
   constexpr int kWaves = kStagedThreads / kWave;
   const size_t lds = (size_t)512 + 96 * (size_t)(a.k >> 3);
   RmsArgs b = a;
-  const int64_t groups = (a.padded + kWaves - 1) / kWaves;
-  int64_t units = dev.cu_count < groups ? dev.cu_count : groups;
-  b.per = (units + kXcds - 1) / kXcds;
-  units = b.per * kXcds;
-  b.rows_per_unit = (a.padded + units - 1) / units;
-  hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, kStagedDoubleBuffer>), dim3((uint32_t)units),
-                     dim3(kStagedThreads), lds, stream, b);
+  int64_t wgs_per_xcd = 0;
+  plan_xcd_steps(a.padded, dev.cu_count, kWaves, &wgs_per_xcd, &b.rows_per_xcd);
+  const int64_t units = wgs_per_xcd * kXcds;
+  if (a.y_out)
+    hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, kStagedDoubleBuffer, true>), dim3((uint32_t)units),
+                       dim3(kStagedThreads), lds, stream, b, a.frame_idx);
+  else
+    hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, kStagedDoubleBuffer, false>), dim3((uint32_t)units),
+                       dim3(kStagedThreads), lds, stream, b, a.frame_idx);
   return hipGetLastError();
 }
 
 template <int CPL>
 hipError_t allow_lds() {
+  const int bytes = 512 + 12 * kMaxStagedK;
+  hipError_t e = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&rms_adaln_staged<CPL, kStagedThreads, kStagedDoubleBuffer, false>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess) return e;
   return hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&rms_adaln_staged<CPL, kStagedThreads, kStagedDoubleBuffer>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, (int)(512 + 12 * kMaxStagedK));
+      reinterpret_cast<const void*>(&rms_adaln_staged<CPL, kStagedThreads, kStagedDoubleBuffer, true>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
 }  // namespace
@@ -419,8 +465,7 @@ hipError_t launch_rms_adaln(const void* x, const void* weight, const void* shift
   a.rstd_out = rstd_out;
   a.y_out = static_cast<uint4*>(y_out);
   a.status = status_word;
-  a.rows_per_unit = 0;
-  a.per = 0;
+  a.rows_per_xcd = 0;
   switch (k / 512) {
     case 1: return launch_staged<1>(a, dev, stream);
     case 2: return launch_staged<2>(a, dev, stream);

@@ -70,24 +70,64 @@ __global__ void silu_table_kernel() {
   g_silu_table[g] = (uint16_t)out;
 }
 
+// SwiGLU + quantize of kUnroll x 64 consecutive chunks of one row starting at chunk c0.
+template <bool Tail>
+__device__ __forceinline__ void swiglu_span(const NVFP4_GLOBAL uint4* ur, const NVFP4_GLOBAL uint4* gr,
+                                            NVFP4_GLOBAL uint32_t* cr, NVFP4_GLOBAL uint8_t* sr,
+                                            NVFP4_GLOBAL uint4* yr, int64_t c0, int64_t chunks, int lane,
+                                            const uint16_t* table, float gsf, const float* inv_tab) {
+  uint4 u[kUnroll], g[kUnroll];
+#pragma unroll
+  for (int i = 0; i < kUnroll; ++i) {
+    const int64_t c = c0 + i * kWave + lane;
+    if (!Tail || c < chunks) {
+      u[i] = load_stream(reinterpret_cast<const uint4*>(ur + c));
+      g[i] = load_stream(reinterpret_cast<const uint4*>(gr + c));
+    } else {
+      u[i] = make_uint4(0, 0, 0, 0);
+      g[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kUnroll; ++i) {
+    const int64_t c = c0 + i * kWave + lane;
+    const uint32_t gw[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
+    const uint32_t uw[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+    float y[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float s0 = __uint_as_float((uint32_t)table[gw[q] & 0xFFFFu] << 16);
+      const float s1 = __uint_as_float((uint32_t)table[gw[q] >> 16] << 16);
+      y[2 * q] = round_bf16(s0 * bf16_lo(uw[q]));
+      y[2 * q + 1] = round_bf16(s1 * bf16_hi(uw[q]));
+    }
+    uint32_t s;
+    const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
+    if (!Tail || c < chunks) {
+      cr[c0 + i * kWave] = code;
+      sr[(c0 / 8 + 8 * i) * 512] = (uint8_t)s;
+      if (yr)
+        yr[c0 + i * kWave] = make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
+                                        pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
+    }
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restrict__ up,
                                                           const uint4* __restrict__ gate, int64_t ld8,
                                                           int64_t m, int64_t f, int64_t padded,
                                                           float global_amax, uint32_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales, uint4* y_out,
-                                                          int64_t rows_per_unit, int64_t per) {
+                                                          int64_t rows_per_xcd) {
   extern __shared__ uint4 lds4[];
   uint16_t* table = reinterpret_cast<uint16_t*>(lds4);
   float* inv_tab = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lds4) + kTableBytes);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const GatherAddr ga = scale_gather_addresses(lane);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
 
-  const int64_t unit = xcd_unit(per);
-  const int64_t r_begin = unit * rows_per_unit;
-  if (r_begin >= padded) return;                          // idle workgroup (uniform)
-  const int64_t r_end = (r_begin + rows_per_unit < padded) ? r_begin + rows_per_unit : padded;
+  const XcdSteps st = xcd_steps(rows_per_xcd, padded, kWaves);
+  if (st.first >= st.end) return;                         // idle workgroup (uniform)
 
   const float gsf = global_scale(global_amax);
   fill_inverse_table(inv_tab, gsf, tid);
@@ -96,48 +136,23 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restric
   __syncthreads();
 
   const int64_t chunks = f >> 3;
-  for (int64_t r = r_begin + wave; r < r_end; r += kWaves) {
+  const int64_t span = kWave * kUnroll;
+  const int64_t full = chunks / span * span;
+  for (int64_t g = st.first; g < st.end; g += st.step) {
+    const int64_t r = g + wave;
+    if (r >= st.end) break;
     if (r >= m) {
       zero_row_scales(scales, r, f, lane);
       continue;
     }
-    const uint4* ur = up + r * ld8;
-    const uint4* gr = gate + r * ld8;
-    const int64_t sbase = row_scale_base(r, f);
-    for (int64_t c0 = 0; c0 < chunks; c0 += kWave * kUnroll) {
-      uint4 u[kUnroll], g[kUnroll];
-#pragma unroll
-      for (int i = 0; i < kUnroll; ++i) {
-        const int64_t c = c0 + i * kWave + lane;
-        const bool ok = c < chunks;
-        u[i] = ok ? load_stream(ur + c) : make_uint4(0, 0, 0, 0);
-        g[i] = ok ? load_stream(gr + c) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int i = 0; i < kUnroll; ++i) {
-        const int64_t c = c0 + i * kWave + lane;
-        const uint32_t gw[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
-        const uint32_t uw[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
-        float y[8];
-        uint32_t p[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float s0 = __uint_as_float((uint32_t)table[gw[q] & 0xFFFFu] << 16);
-          const float s1 = __uint_as_float((uint32_t)table[gw[q] >> 16] << 16);
-          y[2 * q] = round_bf16(s0 * bf16_lo(uw[q]));
-          y[2 * q + 1] = round_bf16(s1 * bf16_hi(uw[q]));
-          p[q] = pack_exact_bf16x2(y[2 * q], y[2 * q + 1]);
-        }
-        uint32_t s;
-        const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
-        const uint32_t s4 = gather_scales4(s, ga);
-        if (c < chunks) {
-          codes[r * chunks + c] = code;
-          if ((lane & 7) == 0) *reinterpret_cast<uint32_t*>(scales + sbase + c * 64) = s4;
-          if (y_out) y_out[r * chunks + c] = make_uint4(p[0], p[1], p[2], p[3]);
-        }
-      }
-    }
+    const NVFP4_GLOBAL uint4* ur = global_ptr(up) + r * ld8;
+    const NVFP4_GLOBAL uint4* gr = global_ptr(gate) + r * ld8;
+    NVFP4_GLOBAL uint32_t* cr = global_ptr(codes) + r * chunks + lane;
+    NVFP4_GLOBAL uint8_t* sr = global_ptr(scales) + row_scale_base(r, f) + scale_lane_offset(lane);
+    NVFP4_GLOBAL uint4* yr = y_out ? global_ptr(y_out) + r * chunks + lane : nullptr;
+    for (int64_t c0 = 0; c0 < full; c0 += span)
+      swiglu_span<false>(ur, gr, cr, sr, yr, c0, chunks, lane, table, gsf, inv_tab);
+    if (full < chunks) swiglu_span<true>(ur, gr, cr, sr, yr, full, chunks, lane, table, gsf, inv_tab);
   }
 }
 
@@ -164,15 +179,13 @@ hipError_t launch_swiglu(const void* up, const void* gate, int64_t ld, int64_t m
                          float global_amax, void* codes, void* scales, void* y_out,
                          const DeviceInfo& dev, hipStream_t stream) {
   const int64_t padded = (m + 127) / 128 * 128;
-  const int64_t groups = (padded + kWaves - 1) / kWaves;
-  int64_t units = dev.cu_count < groups ? dev.cu_count : groups;
-  const int64_t per = (units + kXcds - 1) / kXcds;
-  units = per * kXcds;
-  const int64_t rows_per_unit = (padded + units - 1) / units;
+  int64_t wgs_per_xcd = 0, rows_per_xcd = 0;
+  plan_xcd_steps(padded, dev.cu_count, kWaves, &wgs_per_xcd, &rows_per_xcd);
+  const int64_t units = wgs_per_xcd * kXcds;
   hipLaunchKernelGGL(swiglu_kernel, dim3((uint32_t)units), dim3(kThreads), kTableBytes + 512, stream,
                      static_cast<const uint4*>(up), static_cast<const uint4*>(gate), ld / 8, m, f, padded,
                      global_amax, static_cast<uint32_t*>(codes), static_cast<uint8_t*>(scales),
-                     static_cast<uint4*>(y_out), rows_per_unit, per);
+                     static_cast<uint4*>(y_out), rows_per_xcd);
   return hipGetLastError();
 }
 
