@@ -22,25 +22,8 @@ namespace nvfp4act {
 
 namespace {
 
-constexpr int kMaxStagedK = 8192;       // LDS: 12 * k + 512 bytes
 
-#ifndef NVFP4ACT_RMS_CONTIGUOUS
-#define NVFP4ACT_RMS_CONTIGUOUS 0
-#endif
 
-#if NVFP4ACT_RMS_CONTIGUOUS
-// Alternative row map: each workgroup takes one contiguous range of rows.
-__device__ __forceinline__ XcdSteps contiguous_rows(int64_t padded, int waves) {
-  const int64_t units = gridDim.x, per = units / kXcds;
-  const int64_t unit = xcd_unit(per);
-  const int64_t rows = (padded + units - 1) / units;
-  XcdSteps s;
-  s.first = unit * rows;
-  s.end = (s.first + rows < padded) ? s.first + rows : padded;
-  s.step = waves;
-  return s;
-}
-#endif
 
 struct RmsArgs {
   const uint4* x;
@@ -58,7 +41,6 @@ struct RmsArgs {
   float* rstd_out;
   uint4* y_out;
   uint32_t* status;
-  int64_t rows_per_xcd;
 };
 
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
@@ -105,6 +87,7 @@ struct RowOut {
   NVFP4_GLOBAL uint32_t* codes;    // codes of chunk c at codes[64 j]
   NVFP4_GLOBAL uint8_t* scales;    // scale byte of chunk c's block at scales[4096 j]
   NVFP4_GLOBAL uint4* y;           // y_out of chunk c at y[64 j], or null
+  uint8_t* scales_lds;             // the same byte in the tile's LDS scale block (TILE)
 };
 
 __device__ __forceinline__ RowOut make_row_out(uint32_t* codes, uint8_t* scales, uint4* y_out, int64_t k,
@@ -114,6 +97,7 @@ __device__ __forceinline__ RowOut make_row_out(uint32_t* codes, uint8_t* scales,
   o.codes = global_ptr(codes) + r * chunks + lane;
   o.scales = global_ptr(scales) + row_scale_base(r, k) + scale_lane_offset(lane);
   o.y = y_out ? global_ptr(y_out) + r * chunks + lane : nullptr;
+  o.scales_lds = nullptr;
   return o;
 }
 
@@ -121,34 +105,42 @@ __device__ __forceinline__ RowOut row_out(const RmsArgs& a, int64_t r, int lane)
   return make_row_out(a.codes, a.scales, a.y_out, a.k, r, lane);
 }
 
-// Quantize chunk j of a row and store its codes, its block's scale byte and (when Y)
-// y_out.  No branches, so consecutive chunks can be scheduled together.
-template <bool Y>
+// Quantize chunk j of a row and store its codes, its block's scale byte (into the tile's
+// LDS block with TILE, else to memory) and, with Y, y_out.  No branches, so consecutive
+// chunks can be scheduled together.
+template <bool Y, bool TILE>
 __device__ __forceinline__ void emit_chunk(const RowOut& o, int j, const float* y, float gsf,
                                            const float* inv_tab) {
   uint32_t s;
   const uint32_t q = quantize_chunk(y, gsf, inv_tab, &s);
   o.codes[kWave * j] = q;
-  o.scales[(int64_t)4096 * j] = (uint8_t)s;
+  if (TILE) o.scales_lds[4096 * j] = (uint8_t)s;
+  else o.scales[(int64_t)4096 * j] = (uint8_t)s;
   if (Y)
     o.y[kWave * j] = make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
                                 pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
 }
 
 __device__ __forceinline__ void store_chunk(const RowOut& o, int j, const float* y, float gsf,
-                                            const float* inv_tab) {
-  if (o.y) emit_chunk<true>(o, j, y, gsf, inv_tab);
-  else emit_chunk<false>(o, j, y, gsf, inv_tab);
+                                            const float* inv_tab, bool tile) {
+  if (tile) {
+    if (o.y) emit_chunk<true, true>(o, j, y, gsf, inv_tab);
+    else emit_chunk<false, true>(o, j, y, gsf, inv_tab);
+  } else {
+    if (o.y) emit_chunk<true, false>(o, j, y, gsf, inv_tab);
+    else emit_chunk<false, false>(o, j, y, gsf, inv_tab);
+  }
 }
 
-// Write row r as zeros (frame index outside [0, num_frames)).
-__device__ void zero_row(const RmsArgs& a, int64_t r, int lane) {
+// Write row r as zeros (frame index outside [0, num_frames)); its scale bytes go to
+// memory only when they are not gathered in a zeroed LDS tile block.
+__device__ void zero_row(const RmsArgs& a, int64_t r, int lane, bool scales_too) {
   const int64_t chunks = a.k >> 3;
   for (int64_t c = lane; c < chunks; c += kWave) {
     global_ptr(a.codes)[r * chunks + c] = 0u;
     if (a.y_out) global_ptr(a.y_out)[r * chunks + c] = make_uint4(0, 0, 0, 0);
   }
-  zero_row_scales(a.scales, r, a.k, lane);
+  if (scales_too) zero_row_scales(a.scales, r, a.k, lane);
   if (lane == 0 && a.status) atomicOr(a.status, 1u);
 }
 
@@ -172,14 +164,12 @@ __device__ __forceinline__ void load_frame_chunk(const RmsArgs& a, int64_t t, in
 // A row whose frame is not the staged one: re-read x (an L2 hit in practice) and the
 // frame's modulation row from global memory, one chunk at a time.  Out of line and with
 // plain arguments, so the kernel's hot loop is not shaped by this rare path.
-__device__ __noinline__ void emit_row_unstaged(const uint4* x, const uint16_t* shift,
-                                               const uint16_t* scale, int64_t frame_stride, uint32_t* codes,
-                                               uint8_t* scales, uint4* y_out, int64_t k, int64_t r,
-                                               int64_t t, const float4* wA, const float4* wB, float rstd,
-                                               float gsf, const float* inv_tab) {
+__device__ __noinline__ void emit_row_unstaged(const uint4* x, const uint16_t* shift, const uint16_t* scale,
+                                               int64_t frame_stride, RowOut o, int64_t k, int64_t r, int64_t t,
+                                               const float4* wA, const float4* wB, float rstd, float gsf,
+                                               const float* inv_tab, bool tile) {
   const int lane = threadIdx.x & (kWave - 1);
   const NVFP4_GLOBAL uint4* xr = global_ptr(x) + r * (k >> 3);
-  const RowOut o = make_row_out(codes, scales, y_out, k, r, lane);
 #pragma unroll 1
   for (int j = 0; j < (int)(k >> 9); ++j) {
     const int64_t c = lane + (int64_t)kWave * j;
@@ -188,7 +178,7 @@ __device__ __noinline__ void emit_row_unstaged(const uint4* x, const uint16_t* s
     split8(wA[c], wB[c], w8);
     load_frame_chunk(shift, scale, frame_stride, t, c, o8, h8);
     modulate8(x8, w8, o8, h8, rstd, y);
-    store_chunk(o, j, y, gsf, inv_tab);
+    store_chunk(o, j, y, gsf, inv_tab, tile);
   }
 }
 
@@ -200,15 +190,18 @@ __device__ __forceinline__ void load_row(uint4* v, const uint4* xr, int lane) {
 
 // ---- the staged kernel (k <= kMaxStagedK, CPL = k / 512 chunks per lane) ------------------
 //
-// LDS: inverse-scale table (128 fp32), then six fp32 arrays of float4 indexed by chunk:
-// weight elements 0-3 and 4-7, bf16(1 + scale) 0-3 / 4-7, shift 0-3 / 4-7.  Lane L reads
-// chunk L + 64j, so each ds_read_b128 of a wavefront is one contiguous 1 KiB.
+// LDS: inverse-scale table (128 fp32); six fp32 arrays of float4 indexed by chunk (weight
+// elements 0-3 and 4-7, bf16(1 + scale) 0-3 / 4-7, shift 0-3 / 4-7), so each ds_read_b128
+// of a wavefront is one contiguous 1 KiB; and, with TILE, the swizzled scale block of the
+// current 128-row tile (8k bytes).
 //
-// THREADS = 512 (8 wavefronts, up to 256 VGPRs) double-buffers rows: the next row's loads
-// are in flight while the current row is processed.  THREADS = 1024 (16 wavefronts, 128
-// VGPRs) holds one row per wavefront and hides latency with more wavefronts.
+// Each workgroup takes whole 128-row tiles (tile t, t + grid, ...).  Its wavefronts take
+// the tile's rows round-robin, one row at a time held in registers.  With TILE the scale
+// bytes are gathered in LDS and the tile's block, which is contiguous in the swizzled
+// layout, leaves with full-width 16-byte stores (padding rows stay zero); without TILE
+// (when the block does not fit next to the parameters) each byte is stored directly.
 
-template <int CPL, int THREADS, bool DB, bool Y>
+template <int CPL, int THREADS, bool Y, bool TILE>
 __global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a, const int32_t* __restrict__ frame_idx) {
   constexpr int kWaves = THREADS / kWave;
   extern __shared__ float4 lds4[];
@@ -220,32 +213,15 @@ __global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a, const int
   float4* oB = oA + chunks;
   float4* hA = oB + chunks;
   float4* hB = hA + chunks;
+  uint4* tile_sc = reinterpret_cast<uint4*>(hB + chunks);   // 128 rows x k/16 = 8k bytes = k/2 uint4
+  const int64_t tile_words = a.k >> 1;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const NVFP4_GLOBAL uint4* x = global_ptr(a.x);
-
-#if NVFP4ACT_RMS_CONTIGUOUS
-  const XcdSteps st = contiguous_rows(a.padded, kWaves);
-#else
-  const XcdSteps st = xcd_steps(a.rows_per_xcd, a.padded, kWaves);
-#endif
-  if (st.first >= st.end) return;                       // idle workgroup (uniform)
-  const int64_t r_end = st.end;
   const int64_t m = a.m;
-  // Last real row of this XCD's range: rows past it (padding rows, or beyond the range)
-  // are never processed, and their loads read this row instead so every load is
-  // unconditional (a conditional load would turn the row buffers into loop phis).
-  const int64_t r_last = (r_end < m ? r_end : m) - 1;
-  const bool has_rows = st.first < m;                   // uniform
-
-  auto row_ptr = [&](int64_t r) {
-    return reinterpret_cast<const uint4*>(x + (r <= r_last ? r : r_last) * chunks);
-  };
-
-  uint4 bufA[CPL];
-  uint4 bufB[DB ? CPL : 1];
-  if (DB && has_rows) load_row<CPL>(bufA, row_ptr(st.first + wave), lane);
+  const int64_t ntiles = a.padded >> 7;
+  if ((int64_t)blockIdx.x >= ntiles) return;            // idle workgroup (uniform)
 
   const float gsf = global_scale(a.global_amax);
   fill_inverse_table(inv_tab, gsf, tid);
@@ -255,84 +231,84 @@ __global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a, const int
     wA[c] = make_float4(f[0], f[1], f[2], f[3]);
     wB[c] = make_float4(f[4], f[5], f[6], f[7]);
   }
+  if (TILE)
+    for (int64_t i = tid; i < tile_words; i += THREADS) tile_sc[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   int64_t staged = -1;
-
-  // One group of kWaves rows: restage the frame if needed (uniform), then each wavefront
-  // processes its row held in cur; with DB the row kWaves further is loaded into nxt first.
-  auto group = [&](int64_t g, uint4* cur, uint4* nxt) {
-    const int64_t r = g + wave;
-    if (has_rows) {
-      if (DB) load_row<CPL>(nxt, row_ptr(r + st.step), lane);
-      else load_row<CPL>(cur, row_ptr(r), lane);
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t base = tile << 7;
+    for (int64_t g = base; g < base + 128; g += kWaves) {
+      // restage the modulation row when the group's first row needs another frame (uniform)
+      int64_t want = staged;
+      if (g < m) {
+        const int64_t t = frame_idx[g];
+        if (t >= 0 && t < a.num_frames) want = t;
+      }
+      if (want != staged) {
+        __syncthreads();
+        for (int64_t c = tid; c < chunks; c += THREADS) {
+          float o8[8], h8[8];
+          load_frame_chunk(a, want, c, o8, h8);
+          oA[c] = make_float4(o8[0], o8[1], o8[2], o8[3]);
+          oB[c] = make_float4(o8[4], o8[5], o8[6], o8[7]);
+          hA[c] = make_float4(h8[0], h8[1], h8[2], h8[3]);
+          hB[c] = make_float4(h8[4], h8[5], h8[6], h8[7]);
+        }
+        __syncthreads();
+        staged = want;
+      }
+      const int64_t r = g + wave;
+      if (r >= base + 128) continue;
+      if (r >= m) {
+        if (!TILE) zero_row_scales(a.scales, r, a.k, lane);   // TILE: already zero in LDS
+        continue;
+      }
+      uint4 cur[CPL];
+      load_row<CPL>(cur, reinterpret_cast<const uint4*>(x + r * chunks), lane);
+      const float rstd = row_rstd<CPL>(cur, a.k, a.eps);
+      if (lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
+      const int64_t t = frame_idx[r];
+      if (t < 0 || t >= a.num_frames) {
+        zero_row(a, r, lane, !TILE);
+        continue;
+      }
+      RowOut o = row_out(a, r, lane);
+      if (TILE) o.scales_lds = reinterpret_cast<uint8_t*>(tile_sc) + (row_scale_base(r, a.k) & 511) +
+                               scale_lane_offset(lane);
+      if (t != staged) {
+        emit_row_unstaged(a.x, a.shift, a.scale, a.frame_stride, o, a.k, r, t, wA, wB, rstd, gsf, inv_tab,
+                          TILE);
+        continue;
+      }
+      // Keep the row packed between the two passes: without this the compiler keeps the
+      // fp32 values unpacked for the statistic alive into the output pass.
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+        asm volatile("" : "+v"(cur[j].x), "+v"(cur[j].y), "+v"(cur[j].z), "+v"(cur[j].w));
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        const int c = lane + kWave * j;
+        float x8[8], w8[8], o8[8], h8[8], y[8];
+        unpack8(cur[j], x8);
+        split8(wA[c], wB[c], w8);
+        split8(oA[c], oB[c], o8);
+        split8(hA[c], hB[c], h8);
+        modulate8(x8, w8, o8, h8, rstd, y);
+        emit_chunk<Y, TILE>(o, j, y, gsf, inv_tab);
+      }
     }
-    int64_t want = staged;
-    if (g < m) {
-      const int64_t t = frame_idx[g];
-      if (t >= 0 && t < a.num_frames) want = t;
-    }
-    if (want != staged) {
+    if (TILE) {
+      // the tile's scale block is complete: copy it out and zero it for the next tile (each
+      // thread clears exactly the words it copied, so no barrier is needed in between)
       __syncthreads();
-      for (int64_t c = tid; c < chunks; c += THREADS) {
-        float o8[8], h8[8];
-        load_frame_chunk(a, want, c, o8, h8);
-        oA[c] = make_float4(o8[0], o8[1], o8[2], o8[3]);
-        oB[c] = make_float4(o8[4], o8[5], o8[6], o8[7]);
-        hA[c] = make_float4(h8[0], h8[1], h8[2], h8[3]);
-        hB[c] = make_float4(h8[4], h8[5], h8[6], h8[7]);
+      NVFP4_GLOBAL uint4* dst = reinterpret_cast<NVFP4_GLOBAL uint4*>(global_ptr(a.scales) + tile * (a.k >> 6) * 512);
+      for (int64_t i = tid; i < tile_words; i += THREADS) {
+        dst[i] = tile_sc[i];
+        tile_sc[i] = make_uint4(0, 0, 0, 0);
       }
       __syncthreads();
-      staged = want;
     }
-    if (r >= r_end) return;
-    if (r >= m) {
-      zero_row_scales(a.scales, r, a.k, lane);
-      return;
-    }
-    const float rstd = row_rstd<CPL>(cur, a.k, a.eps);
-    if (lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
-    const int64_t t = frame_idx[r];
-    if (t < 0 || t >= a.num_frames) {
-      zero_row(a, r, lane);
-      return;
-    }
-    if (t != staged) {
-      emit_row_unstaged(a.x, a.shift, a.scale, a.frame_stride, a.codes, a.scales, a.y_out, a.k, r, t, wA, wB,
-                        rstd, gsf, inv_tab);
-      return;
-    }
-    // Keep the row packed between the two passes: without this the compiler keeps the
-    // fp32 values unpacked for the statistic alive into the output pass.
-#pragma unroll
-    for (int j = 0; j < CPL; ++j)
-      asm volatile("" : "+v"(cur[j].x), "+v"(cur[j].y), "+v"(cur[j].z), "+v"(cur[j].w));
-    const RowOut o = row_out(a, r, lane);
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = lane + kWave * j;
-      float x8[8], w8[8], o8[8], h8[8], y[8];
-      unpack8(cur[j], x8);
-      split8(wA[c], wB[c], w8);
-      split8(oA[c], oB[c], o8);
-      split8(hA[c], hB[c], h8);
-      modulate8(x8, w8, o8, h8, rstd, y);
-      emit_chunk<Y>(o, j, y, gsf, inv_tab);
-#if NVFP4ACT_RMS_CHUNK_FENCE
-      __builtin_amdgcn_sched_barrier(0);   // bound cross-chunk interleaving (registers)
-#endif
-    }
-  };
-
-  if (DB) {
-    // Two groups per iteration, both unconditional, so the buffers swap roles without
-    // register copies; a group past the range only prefetches (a clamped row) and returns.
-    for (int64_t g = st.first; g < r_end; g += 2 * st.step) {
-      group(g, bufA, bufB);
-      group(g + st.step, bufB, bufA);
-    }
-  } else {
-    for (int64_t g = st.first; g < r_end; g += st.step) group(g, bufA, bufA);
   }
 }
 
@@ -368,7 +344,7 @@ __global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
   if (lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
   const int64_t t = global_ptr(a.frame_idx)[r];
   if (t < 0 || t >= a.num_frames) {
-    zero_row(a, r, lane);
+    zero_row(a, r, lane, true);
     return;
   }
   const RowOut o = row_out(a, r, lane);
@@ -379,53 +355,48 @@ __global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
     unpack8(*reinterpret_cast<const NVFP4_GLOBAL uint4*>(global_ptr(a.w) + 8 * c), w8);
     load_frame_chunk(a, t, c, o8, h8);
     modulate8(x8, w8, o8, h8, rstd, y);
-    store_chunk(o, j, y, gsf, inv_tab);
+    store_chunk(o, j, y, gsf, inv_tab, false);
   }
 }
 
-// Launch shape of the staged kernel (compile-time; see the kernel comment).
-#ifndef NVFP4ACT_RMS_THREADS
-#define NVFP4ACT_RMS_THREADS 768
-#endif
-#ifndef NVFP4ACT_RMS_CONTIGUOUS
-#define NVFP4ACT_RMS_CONTIGUOUS 0
-#endif
-#ifndef NVFP4ACT_RMS_CHUNK_FENCE
-#define NVFP4ACT_RMS_CHUNK_FENCE 0
-#endif
-#ifndef NVFP4ACT_RMS_DOUBLE_BUFFER
-#define NVFP4ACT_RMS_DOUBLE_BUFFER 0
-#endif
-constexpr int kStagedThreads = NVFP4ACT_RMS_THREADS;
-constexpr bool kStagedDoubleBuffer = NVFP4ACT_RMS_DOUBLE_BUFFER != 0;
+// Launch shape of the staged kernel: 12 wavefronts (3 per SIMD, up to 170 VGPRs each).
+constexpr int kStagedThreads = 768;
+
+// The tile's scale block (128 rows x k/16 bytes) is staged in LDS when it fits beside the
+// parameters (k <= 7680).
+constexpr size_t kLdsLimit = 160 * 1024;
+inline size_t staged_lds_bytes(int64_t k, bool tile) { return 512 + 12 * (size_t)k + (tile ? 8 * (size_t)k : 0); }
 
 template <int CPL>
 hipError_t launch_staged(const RmsArgs& a, const DeviceInfo& dev, hipStream_t stream) {
-  constexpr int kWaves = kStagedThreads / kWave;
-  const size_t lds = (size_t)512 + 96 * (size_t)(a.k >> 3);
-  RmsArgs b = a;
-  int64_t wgs_per_xcd = 0;
-  plan_xcd_steps(a.padded, dev.cu_count, kWaves, &wgs_per_xcd, &b.rows_per_xcd);
-  const int64_t units = wgs_per_xcd * kXcds;
-  if (a.y_out)
-    hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, kStagedDoubleBuffer, true>), dim3((uint32_t)units),
-                       dim3(kStagedThreads), lds, stream, b, a.frame_idx);
-  else
-    hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, kStagedDoubleBuffer, false>), dim3((uint32_t)units),
-                       dim3(kStagedThreads), lds, stream, b, a.frame_idx);
+  const bool tile = staged_lds_bytes(a.k, true) <= kLdsLimit;
+  const size_t lds = staged_lds_bytes(a.k, tile);
+  const int64_t ntiles = a.padded >> 7;
+  const int64_t grid = ntiles < dev.cu_count ? ntiles : dev.cu_count;
+  const dim3 g((uint32_t)grid), b(kStagedThreads);
+  if (tile) {
+    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, true, true>), g, b, lds, stream, a, a.frame_idx);
+    else hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, false, true>), g, b, lds, stream, a, a.frame_idx);
+  } else {
+    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, true, false>), g, b, lds, stream, a, a.frame_idx);
+    else hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, false, false>), g, b, lds, stream, a, a.frame_idx);
+  }
   return hipGetLastError();
+}
+
+template <int CPL, bool Y, bool TILE>
+hipError_t allow_lds_one() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&rms_adaln_staged<CPL, kStagedThreads, Y, TILE>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
 }
 
 template <int CPL>
 hipError_t allow_lds() {
-  const int bytes = 512 + 12 * kMaxStagedK;
-  hipError_t e = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&rms_adaln_staged<CPL, kStagedThreads, kStagedDoubleBuffer, false>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&rms_adaln_staged<CPL, kStagedThreads, kStagedDoubleBuffer, true>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  hipError_t e = allow_lds_one<CPL, false, false>();
+  if (e == hipSuccess) e = allow_lds_one<CPL, true, false>();
+  if (e == hipSuccess) e = allow_lds_one<CPL, false, true>();
+  if (e == hipSuccess) e = allow_lds_one<CPL, true, true>();
+  return e;
 }
 
 }  // namespace
@@ -465,7 +436,6 @@ hipError_t launch_rms_adaln(const void* x, const void* weight, const void* shift
   a.rstd_out = rstd_out;
   a.y_out = static_cast<uint4*>(y_out);
   a.status = status_word;
-  a.rows_per_xcd = 0;
   switch (k / 512) {
     case 1: return launch_staged<1>(a, dev, stream);
     case 2: return launch_staged<2>(a, dev, stream);
