@@ -5,8 +5,9 @@
 //
 // S is a 65,536-entry bf16 table indexed by the gate's bit pattern, built once per
 // device in fp64 by silu_table_kernel.  Each workgroup (one per CU, persistent over a
-// contiguous range of rows) copies the 128 KiB table into LDS; every element then costs
-// one LDS lookup, one multiply and one bf16 rounding before the quantizer.
+// set of 128-row x 512-column tiles) copies the 128 KiB table into LDS; every element then
+// costs one LDS lookup, one multiply and one bf16 rounding before the quantizer.  Each
+// tile's scale bytes are gathered in LDS and leave with 16-byte stores.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -19,8 +20,10 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kUnroll = 4;
 constexpr size_t kTableBytes = 65536 * sizeof(uint16_t);
+constexpr int kTileCols = 512;                     // 64 chunks: one per lane per row
+constexpr int kRowBatch = 4;                       // rows per wavefront in flight
+constexpr int kScaleBytes = kTileCols / 64 * 512;  // 4 KiB
 
 // Round hi + lo to bf16, nearest-even.  lo is a tiny residual that only breaks an exact
 // tie of hi; otherwise a value within 2^-36 of a midpoint (in units of the bf16 quantum)
@@ -70,89 +73,99 @@ __global__ void silu_table_kernel() {
   g_silu_table[g] = (uint16_t)out;
 }
 
-// SwiGLU + quantize of kUnroll x 64 consecutive chunks of one row starting at chunk c0.
-template <bool Tail>
-__device__ __forceinline__ void swiglu_span(const NVFP4_GLOBAL uint4* ur, const NVFP4_GLOBAL uint4* gr,
-                                            NVFP4_GLOBAL uint32_t* cr, NVFP4_GLOBAL uint8_t* sr,
-                                            NVFP4_GLOBAL uint4* yr, int64_t c0, int64_t chunks, int lane,
-                                            const uint16_t* table, float gsf, const float* inv_tab) {
-  uint4 u[kUnroll], g[kUnroll];
+// One 128-row x kTileCols tile: each wavefront takes rows wave, wave + 16, ... (8 rows),
+// kRowBatch at a time; scale bytes go to the tile's LDS block.
+__device__ __forceinline__ void swiglu_tile(const uint4* up, const uint4* gate, int64_t ld8, int64_t m,
+                                            int64_t row_chunks, uint32_t* codes, uint4* y_out,
+                                            int64_t tile_row, int64_t c0, int64_t tchunks, int lane, int wave,
+                                            const uint16_t* table, float gsf, const float* inv_tab,
+                                            uint8_t* sc_lane) {
+  const int64_t r0 = tile_row << 7;
+  const int64_t rows = (m - r0 < 128) ? (m - r0 > 0 ? m - r0 : 0) : 128;
+  const int64_t c = c0 + lane;
+  const bool lane_ok = lane < tchunks;
+  for (int64_t rb = wave * kRowBatch; rb < rows; rb += kWaves * kRowBatch) {
+    uint4 u[kRowBatch], g[kRowBatch];
 #pragma unroll
-  for (int i = 0; i < kUnroll; ++i) {
-    const int64_t c = c0 + i * kWave + lane;
-    if (!Tail || c < chunks) {
-      u[i] = load_stream(reinterpret_cast<const uint4*>(ur + c));
-      g[i] = load_stream(reinterpret_cast<const uint4*>(gr + c));
-    } else {
-      u[i] = make_uint4(0, 0, 0, 0);
-      g[i] = make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < kRowBatch; ++i) {
+      const int64_t r = r0 + rb + i;
+      if (rb + i < rows && lane_ok) {
+        u[i] = load_stream(reinterpret_cast<const uint4*>(global_ptr(up) + r * ld8 + c));
+        g[i] = load_stream(reinterpret_cast<const uint4*>(global_ptr(gate) + r * ld8 + c));
+      } else {
+        u[i] = make_uint4(0, 0, 0, 0);
+        g[i] = make_uint4(0, 0, 0, 0);
+      }
     }
-  }
 #pragma unroll
-  for (int i = 0; i < kUnroll; ++i) {
-    const int64_t c = c0 + i * kWave + lane;
-    const uint32_t gw[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
-    const uint32_t uw[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
-    float y[8];
+    for (int i = 0; i < kRowBatch; ++i) {
+      const int64_t rr = rb + i;
+      const uint32_t gw[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
+      const uint32_t uw[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+      float y[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float s0 = __uint_as_float((uint32_t)table[gw[q] & 0xFFFFu] << 16);
-      const float s1 = __uint_as_float((uint32_t)table[gw[q] >> 16] << 16);
-      y[2 * q] = round_bf16(s0 * bf16_lo(uw[q]));
-      y[2 * q + 1] = round_bf16(s1 * bf16_hi(uw[q]));
-    }
-    uint32_t s;
-    const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
-    if (!Tail || c < chunks) {
-      cr[c0 + i * kWave] = code;
-      sr[(c0 / 8 + 8 * i) * 512] = (uint8_t)s;
-      if (yr)
-        yr[c0 + i * kWave] = make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
-                                        pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
+      for (int q = 0; q < 4; ++q) {
+        const float s0 = __uint_as_float((uint32_t)table[gw[q] & 0xFFFFu] << 16);
+        const float s1 = __uint_as_float((uint32_t)table[gw[q] >> 16] << 16);
+        y[2 * q] = round_bf16(s0 * bf16_lo(uw[q]));
+        y[2 * q + 1] = round_bf16(s1 * bf16_hi(uw[q]));
+      }
+      uint32_t s;
+      const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
+      if (rr < rows && lane_ok) {
+        const int64_t r = r0 + rr;
+        global_ptr(codes)[r * row_chunks + c] = code;
+        sc_lane[(rr & 31) * 16 + ((rr >> 5) & 3) * 4] = (uint8_t)s;
+        if (y_out)
+          global_ptr(y_out)[r * row_chunks + c] =
+              make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
+                         pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
+      }
     }
   }
 }
 
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restrict__ up,
                                                           const uint4* __restrict__ gate, int64_t ld8,
-                                                          int64_t m, int64_t f, int64_t padded,
-                                                          float global_amax, uint32_t* __restrict__ codes,
+                                                          int64_t m, int64_t f, float global_amax,
+                                                          uint32_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales, uint4* y_out,
-                                                          int64_t rows_per_xcd) {
+                                                          int64_t col_tiles, int64_t ntiles) {
   extern __shared__ uint4 lds4[];
   uint16_t* table = reinterpret_cast<uint16_t*>(lds4);
   float* inv_tab = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lds4) + kTableBytes);
+  uint4* tile_sc = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(lds4) + kTableBytes + 512);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-
-  const XcdSteps st = xcd_steps(rows_per_xcd, padded, kWaves);
-  if (st.first >= st.end) return;                         // idle workgroup (uniform)
+  if ((int64_t)blockIdx.x >= ntiles) return;              // idle workgroup (uniform)
 
   const float gsf = global_scale(global_amax);
   fill_inverse_table(inv_tab, gsf, tid);
   const uint4* src = reinterpret_cast<const uint4*>(g_silu_table);
   for (int i = tid; i < (int)(kTableBytes / 16); i += kThreads) lds4[i] = src[i];
+  for (int i = tid; i < kScaleBytes / 16; i += kThreads) tile_sc[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  const int64_t chunks = f >> 3;
-  const int64_t span = kWave * kUnroll;
-  const int64_t full = chunks / span * span;
-  for (int64_t g = st.first; g < st.end; g += st.step) {
-    const int64_t r = g + wave;
-    if (r >= st.end) break;
-    if (r >= m) {
-      zero_row_scales(scales, r, f, lane);
-      continue;
+  const int64_t row_chunks = f >> 3;
+  uint8_t* sc_lane = reinterpret_cast<uint8_t*>(tile_sc) + scale_lane_offset(lane);
+  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
+    const int64_t tile_row = t / col_tiles, col_tile = t % col_tiles;
+    const int64_t c0 = col_tile * (kTileCols / 8);
+    const int64_t tchunks = (row_chunks - c0 < kTileCols / 8) ? row_chunks - c0 : kTileCols / 8;
+    swiglu_tile(up, gate, ld8, m, row_chunks, codes, y_out, tile_row, c0, tchunks, lane, wave, table, gsf,
+                inv_tab, sc_lane);
+    __syncthreads();
+    // copy the tile's scale slice out and zero it for the next tile (each thread clears
+    // exactly the words it copied)
+    NVFP4_GLOBAL uint4* dst = reinterpret_cast<NVFP4_GLOBAL uint4*>(
+        global_ptr(scales) + (tile_row * (f >> 6) + c0 / 8) * 512);
+    const int words = (int)(tchunks / 8) * 32;
+    for (int i = tid; i < words; i += kThreads) {
+      dst[i] = tile_sc[i];
+      tile_sc[i] = make_uint4(0, 0, 0, 0);
     }
-    const NVFP4_GLOBAL uint4* ur = global_ptr(up) + r * ld8;
-    const NVFP4_GLOBAL uint4* gr = global_ptr(gate) + r * ld8;
-    NVFP4_GLOBAL uint32_t* cr = global_ptr(codes) + r * chunks + lane;
-    NVFP4_GLOBAL uint8_t* sr = global_ptr(scales) + row_scale_base(r, f) + scale_lane_offset(lane);
-    NVFP4_GLOBAL uint4* yr = y_out ? global_ptr(y_out) + r * chunks + lane : nullptr;
-    for (int64_t c0 = 0; c0 < full; c0 += span)
-      swiglu_span<false>(ur, gr, cr, sr, yr, c0, chunks, lane, table, gsf, inv_tab);
-    if (full < chunks) swiglu_span<true>(ur, gr, cr, sr, yr, full, chunks, lane, table, gsf, inv_tab);
+    __syncthreads();
   }
 }
 
@@ -172,20 +185,20 @@ hipError_t build_silu_table(unsigned int* ambiguous) {
 
 hipError_t prepare_swiglu() {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&swiglu_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kTableBytes + 512));
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kTableBytes + 512 + kScaleBytes));
 }
 
 hipError_t launch_swiglu(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f,
                          float global_amax, void* codes, void* scales, void* y_out,
                          const DeviceInfo& dev, hipStream_t stream) {
-  const int64_t padded = (m + 127) / 128 * 128;
-  int64_t wgs_per_xcd = 0, rows_per_xcd = 0;
-  plan_xcd_steps(padded, dev.cu_count, kWaves, &wgs_per_xcd, &rows_per_xcd);
-  const int64_t units = wgs_per_xcd * kXcds;
-  hipLaunchKernelGGL(swiglu_kernel, dim3((uint32_t)units), dim3(kThreads), kTableBytes + 512, stream,
-                     static_cast<const uint4*>(up), static_cast<const uint4*>(gate), ld / 8, m, f, padded,
-                     global_amax, static_cast<uint32_t*>(codes), static_cast<uint8_t*>(scales),
-                     static_cast<uint4*>(y_out), rows_per_xcd);
+  const int64_t tile_rows = (m + 127) / 128;
+  const int64_t col_tiles = (f + kTileCols - 1) / kTileCols;
+  const int64_t ntiles = tile_rows * col_tiles;
+  const int64_t grid = ntiles < dev.cu_count ? ntiles : dev.cu_count;
+  hipLaunchKernelGGL(swiglu_kernel, dim3((uint32_t)grid), dim3(kThreads), kTableBytes + 512 + kScaleBytes, stream,
+                     static_cast<const uint4*>(up), static_cast<const uint4*>(gate), ld / 8, m, f, global_amax,
+                     static_cast<uint32_t*>(codes), static_cast<uint8_t*>(scales), static_cast<uint4*>(y_out),
+                     col_tiles, ntiles);
   return hipGetLastError();
 }
 
