@@ -68,11 +68,11 @@ __device__ __forceinline__ uint32_t pack_exact_bf16x2(float lo, float hi) {
 
 // E4M3 code of a non-negative fp32, nearest-even, saturating at 448.  v_cvt_pk_fp8_f32
 // rounds to nearest-even on gfx950 (OCP E4M3) but turns values beyond 448 into NaN, so
-// the input is clamped first.
+// the input is clamped first.  The pair (c, 0) converts to (code, 0x00) in the low half
+// and the upper half comes from the zero `old` operand, so the word is the code itself.
 __device__ __forceinline__ uint32_t e4m3_code(float sf) {
   float c = __builtin_fminf(sf, 448.0f);
-  // bytes 0 and 1 receive the code; the rest keeps c's bits and is masked off
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, c, __float_as_int(c), false) & 0xFFu;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false);
 }
 
 // Exact value of an E4M3 code 0..126: exponent field 0 is m * 2^-9, else 2^(e-7)(1+m/8).
@@ -96,9 +96,27 @@ __device__ __forceinline__ uint32_t pack_e2m1x8(const float* v) {
 
 // ---- cross-lane ----------------------------------------------------------------------
 
-// Value of lane L^1 (DPP quad_perm [1,0,3,2]).
-__device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);
+// max(v, value of lane L^1) for non-negative fp32 bit patterns (DPP quad_perm
+// [1,0,3,2]; with 0, the identity of the unsigned max, as the old value the move folds
+// into the max as one DPP instruction).
+__device__ __forceinline__ uint32_t max_with_lane_xor1(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  return __builtin_elementwise_max(v, o);
+}
+
+// max(|a|, |b|, |c|) and max(t, |b|, |c|) as single v_max3_f32 instructions with abs
+// source modifiers.  (Written out because the compiler lowers fabs of a value that was
+// bit-cast from an integer, as every bf16-rounded value here is, to a separate AND.)
+// Inputs are finite, where this equals the IEEE maximum of the magnitudes.
+__device__ __forceinline__ float abs_max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max_abs2(float t, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(t), "v"(b), "v"(c));
+  return r;
 }
 
 // ---- global scale and inverse-scale table ----------------------------------------------
@@ -118,15 +136,12 @@ __device__ __forceinline__ void fill_inverse_table(float* inv, float gsf, int ti
 // E4M3 code (the same value on both lanes of the pair).
 __device__ __forceinline__ uint32_t quantize_chunk(const float* y, float gsf, const float* inv_tab,
                                                    uint32_t* scale) {
-  float amax = __builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(y[0]), __builtin_fabsf(y[1])),
-                               __builtin_fabsf(y[2]));
-  amax = __builtin_fmaxf(__builtin_fmaxf(amax, __builtin_fabsf(y[3])), __builtin_fabsf(y[4]));
-  amax = __builtin_fmaxf(__builtin_fmaxf(amax, __builtin_fabsf(y[5])), __builtin_fabsf(y[6]));
-  amax = __builtin_fmaxf(amax, __builtin_fabsf(y[7]));
+  float amax = abs_max3(y[0], y[1], y[2]);
+  amax = max_abs2(amax, y[3], y[4]);
+  amax = max_abs2(amax, y[5], y[6]);
+  amax = max_abs2(amax, y[7], y[7]);
   // the partner lane's half: amax >= 0, so the larger bit pattern is the larger value
-  uint32_t ab = __float_as_uint(amax);
-  ab = __builtin_elementwise_max(ab, lane_xor1(ab));
-  amax = __uint_as_float(ab);
+  amax = __uint_as_float(max_with_lane_xor1(__float_as_uint(amax)));
   const float rcp6 = __uint_as_float(kRcp6Bits);
   const uint32_t s = e4m3_code(gsf * (amax * rcp6));
   const float inv = inv_tab[s];

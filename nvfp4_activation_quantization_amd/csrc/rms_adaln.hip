@@ -87,7 +87,7 @@ struct RowOut {
   NVFP4_GLOBAL uint32_t* codes;    // codes of chunk c at codes[64 j]
   NVFP4_GLOBAL uint8_t* scales;    // scale byte of chunk c's block at scales[4096 j]
   NVFP4_GLOBAL uint4* y;           // y_out of chunk c at y[64 j], or null
-  uint8_t* scales_lds;             // the same byte in the tile's LDS scale block (TILE)
+  uint8_t* scales_lds;             // the same byte in the tile's padded LDS block, at [4224 j] (TILE)
 };
 
 __device__ __forceinline__ RowOut make_row_out(uint32_t* codes, uint8_t* scales, uint4* y_out, int64_t k,
@@ -114,7 +114,7 @@ __device__ __forceinline__ void emit_chunk(const RowOut& o, int j, const float* 
   uint32_t s;
   const uint32_t q = quantize_chunk(y, gsf, inv_tab, &s);
   o.codes[kWave * j] = q;
-  if (TILE) o.scales_lds[4096 * j] = (uint8_t)s;
+  if (TILE) o.scales_lds[4224 * j] = (uint8_t)s;
   else o.scales[(int64_t)4096 * j] = (uint8_t)s;
   if (Y)
     o.y[kWave * j] = make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
@@ -182,39 +182,58 @@ __device__ __noinline__ void emit_row_unstaged(const uint4* x, const uint16_t* s
   }
 }
 
-template <int CPL>
-__device__ __forceinline__ void load_row(uint4* v, const uint4* xr, int lane) {
-#pragma unroll
-  for (int j = 0; j < CPL; ++j) v[j] = load_stream(xr + lane + kWave * j);
+// The float4 at byte offset base + off of the dynamic LDS block.
+__device__ __forceinline__ float4 lds_f4(const float4* lds, uint32_t base, uint32_t off) {
+  return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(lds) + base + off);
 }
 
-// ---- the staged kernel (k <= kMaxStagedK, CPL = k / 512 chunks per lane) ------------------
+template <int CPL>
+__device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr, int lane) {
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) v[j] = load_stream(reinterpret_cast<const uint4*>(xr + lane + kWave * j));
+}
+
+// ---- the staged kernel (k <= 8192, CPL = k / 512 chunks per lane) -------------------------
+//
+// One workgroup of 8 wavefronts per CU, persistent over 128-row tiles (tile t, t + grid,
+// ...).  Wavefront w takes rows 8i + w (i = 0..15) of each tile, so the eight rows in
+// flight at any time are consecutive and share a frame except at frame boundaries, and
+// every wavefront has the same 16 rows of work per tile.
+//
+// Each wavefront keeps its current row unpacked to fp32 in registers (8 CPL values per
+// lane) from the statistic to the output pass, so every element is unpacked once; right
+// after the statistic it issues the loads of its next row (4 CPL registers), which then
+// arrive while the output pass runs.
 //
 // LDS: inverse-scale table (128 fp32); six fp32 arrays of float4 indexed by chunk (weight
 // elements 0-3 and 4-7, bf16(1 + scale) 0-3 / 4-7, shift 0-3 / 4-7), so each ds_read_b128
 // of a wavefront is one contiguous 1 KiB; and, with TILE, the swizzled scale block of the
-// current 128-row tile (8k bytes).
-//
-// Each workgroup takes whole 128-row tiles (tile t, t + grid, ...).  Its wavefronts take
-// the tile's rows round-robin, one row at a time held in registers.  With TILE the scale
-// bytes are gathered in LDS and the tile's block, which is contiguous in the swizzled
-// layout, leaves with full-width 16-byte stores (padding rows stay zero); without TILE
-// (when the block does not fit next to the parameters) each byte is stored directly.
+// current 128-row tile (8k bytes), with a 16-byte pad after every 512 bytes: the eight
+// 4-byte groups a wavefront writes for one chunk are 512 bytes apart in the layout, which
+// would put them all in one LDS bank.  With TILE the scale bytes are gathered in LDS and the
+// tile's block, which is contiguous in the swizzled layout, leaves with 16-byte stores
+// (padding rows stay zero); without TILE (when the block does not fit beside the
+// parameters) each byte is stored directly.
 
-template <int CPL, int THREADS, bool Y, bool TILE>
-__global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a, const int32_t* __restrict__ frame_idx) {
-  constexpr int kWaves = THREADS / kWave;
+constexpr int kStagedWaves = 8;
+constexpr int kStagedThreads = kStagedWaves * kWave;
+constexpr int kRowsPerWave = 128 / kStagedWaves;
+
+template <int CPL, bool Y, bool TILE>
+__global__ __launch_bounds__(kStagedThreads) void rms_adaln_staged(RmsArgs a, const int32_t* __restrict__ frame_idx) {
+  constexpr int kChunks = CPL * kWave;          // chunks per row (k / 8)
+  constexpr int kTileWords = kChunks * 4;        // 128 rows x k/16 bytes, in uint4
+  constexpr int kTileLdsWords = kTileWords / 32 * 33;   // with one padding uint4 per 32
+  constexpr int kK = kChunks * 8;
   extern __shared__ float4 lds4[];
   float* inv_tab = reinterpret_cast<float*>(lds4);
-  const int64_t chunks = a.k >> 3;
   float4* wA = lds4 + 32;                 // 128 floats = 32 float4
-  float4* wB = wA + chunks;
-  float4* oA = wB + chunks;
-  float4* oB = oA + chunks;
-  float4* hA = oB + chunks;
-  float4* hB = hA + chunks;
-  uint4* tile_sc = reinterpret_cast<uint4*>(hB + chunks);   // 128 rows x k/16 = 8k bytes = k/2 uint4
-  const int64_t tile_words = a.k >> 1;
+  float4* wB = wA + kChunks;
+  float4* oA = wB + kChunks;
+  float4* oB = oA + kChunks;
+  float4* hA = oB + kChunks;
+  float4* hB = hA + kChunks;
+  uint4* tile_sc = reinterpret_cast<uint4*>(hB + kChunks);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -222,23 +241,40 @@ __global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a, const int
   const int64_t m = a.m;
   const int64_t ntiles = a.padded >> 7;
   if ((int64_t)blockIdx.x >= ntiles) return;            // idle workgroup (uniform)
+  // Byte offsets of this lane's chunk 0 in wA, oA and hA.  Each array pair (A, B) and its
+  // 64-lane steps then lie within the 16-bit immediate offset of one ds_read_b128 base;
+  // hiding the three bases from the optimiser keeps it from materialising one address per
+  // array and chunk (the arrays together span more than the immediate range).
+  constexpr uint32_t kArray = kChunks * 16;
+  uint32_t pw = 512 + 16 * lane, po = pw + 2 * kArray, ph = pw + 4 * kArray;
+  asm volatile("" : "+v"(pw), "+v"(po), "+v"(ph));
+
+  // the first row of this wavefront is in flight while the parameters are staged
+  // (loads are unconditional: a row past the end re-reads row m - 1, which is never used)
+  uint4 nxt[CPL];
+  {
+    const int64_t r0 = ((int64_t)blockIdx.x << 7) + wave;
+    load_row<CPL>(nxt, x + (r0 < m ? r0 : m - 1) * kChunks, lane);
+  }
 
   const float gsf = global_scale(a.global_amax);
   fill_inverse_table(inv_tab, gsf, tid);
-  for (int64_t c = tid; c < chunks; c += THREADS) {
+  for (int c = tid; c < kChunks; c += kStagedThreads) {
     float f[8];
     unpack8(*reinterpret_cast<const NVFP4_GLOBAL uint4*>(global_ptr(a.w) + 8 * c), f);
     wA[c] = make_float4(f[0], f[1], f[2], f[3]);
     wB[c] = make_float4(f[4], f[5], f[6], f[7]);
   }
   if (TILE)
-    for (int64_t i = tid; i < tile_words; i += THREADS) tile_sc[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < kTileLdsWords; i += kStagedThreads) tile_sc[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   int64_t staged = -1;
   for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int64_t base = tile << 7;
-    for (int64_t g = base; g < base + 128; g += kWaves) {
+    const int64_t next_first = ((tile + gridDim.x) << 7) + wave;   // this wave's row in the next tile
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int64_t g = base + kStagedWaves * i;
       // restage the modulation row when the group's first row needs another frame (uniform)
       int64_t want = staged;
       if (g < m) {
@@ -247,7 +283,7 @@ __global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a, const int
       }
       if (want != staged) {
         __syncthreads();
-        for (int64_t c = tid; c < chunks; c += THREADS) {
+        for (int c = tid; c < kChunks; c += kStagedThreads) {
           float o8[8], h8[8];
           load_frame_chunk(a, want, c, o8, h8);
           oA[c] = make_float4(o8[0], o8[1], o8[2], o8[3]);
@@ -259,14 +295,26 @@ __global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a, const int
         staged = want;
       }
       const int64_t r = g + wave;
-      if (r >= base + 128) continue;
-      if (r >= m) {
-        if (!TILE) zero_row_scales(a.scales, r, a.k, lane);   // TILE: already zero in LDS
+      if (r >= m) {                        // a padding row (and so is every later row)
+        if (!TILE) zero_row_scales(a.scales, r, kK, lane);   // TILE: already zero in LDS
         continue;
       }
-      uint4 cur[CPL];
-      load_row<CPL>(cur, reinterpret_cast<const uint4*>(x + r * chunks), lane);
-      const float rstd = row_rstd<CPL>(cur, a.k, a.eps);
+      // the row arrives (loaded one row earlier): unpack it once, take the statistic
+      float xf[CPL][8];
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) unpack8(nxt[j], xf[j]);
+      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < CPL; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(xf[j][e], xf[j][e], acc[e]);
+      // prefetch this wavefront's next row
+      const int64_t rn = (i + 1 < kRowsPerWave) ? r + kStagedWaves : next_first;
+      load_row<CPL>(nxt, x + (rn < m ? rn : m - 1) * kChunks, lane);
+      float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+#pragma unroll
+      for (int d = 1; d < kWave; d <<= 1) sum = sum + __shfl_xor(sum, d, kWave);
+      const float rstd = 1.0f / sqrtf(sum / (float)kK + a.eps);
       if (lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
       const int64_t t = frame_idx[r];
       if (t < 0 || t >= a.num_frames) {
@@ -274,27 +322,20 @@ __global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a, const int
         continue;
       }
       RowOut o = row_out(a, r, lane);
-      if (TILE) o.scales_lds = reinterpret_cast<uint8_t*>(tile_sc) + (row_scale_base(r, a.k) & 511) +
-                               scale_lane_offset(lane);
+      if (TILE) o.scales_lds = reinterpret_cast<uint8_t*>(tile_sc) + (row_scale_base(r, kK) & 511) +
+                               (lane >> 3) * 528 + ((lane >> 1) & 3);
       if (t != staged) {
-        emit_row_unstaged(a.x, a.shift, a.scale, a.frame_stride, o, a.k, r, t, wA, wB, rstd, gsf, inv_tab,
+        emit_row_unstaged(a.x, a.shift, a.scale, a.frame_stride, o, kK, r, t, wA, wB, rstd, gsf, inv_tab,
                           TILE);
         continue;
       }
-      // Keep the row packed between the two passes: without this the compiler keeps the
-      // fp32 values unpacked for the statistic alive into the output pass.
-#pragma unroll
-      for (int j = 0; j < CPL; ++j)
-        asm volatile("" : "+v"(cur[j].x), "+v"(cur[j].y), "+v"(cur[j].z), "+v"(cur[j].w));
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
-        const int c = lane + kWave * j;
-        float x8[8], w8[8], o8[8], h8[8], y[8];
-        unpack8(cur[j], x8);
-        split8(wA[c], wB[c], w8);
-        split8(oA[c], oB[c], o8);
-        split8(hA[c], hB[c], h8);
-        modulate8(x8, w8, o8, h8, rstd, y);
+        float w8[8], o8[8], h8[8], y[8];
+        split8(lds_f4(lds4, pw, 1024 * j), lds_f4(lds4, pw, kArray + 1024 * j), w8);
+        split8(lds_f4(lds4, po, 1024 * j), lds_f4(lds4, po, kArray + 1024 * j), o8);
+        split8(lds_f4(lds4, ph, 1024 * j), lds_f4(lds4, ph, kArray + 1024 * j), h8);
+        modulate8(xf[j], w8, o8, h8, rstd, y);
         emit_chunk<Y, TILE>(o, j, y, gsf, inv_tab);
       }
     }
@@ -302,10 +343,10 @@ __global__ __launch_bounds__(THREADS) void rms_adaln_staged(RmsArgs a, const int
       // the tile's scale block is complete: copy it out and zero it for the next tile (each
       // thread clears exactly the words it copied, so no barrier is needed in between)
       __syncthreads();
-      NVFP4_GLOBAL uint4* dst = reinterpret_cast<NVFP4_GLOBAL uint4*>(global_ptr(a.scales) + tile * (a.k >> 6) * 512);
-      for (int64_t i = tid; i < tile_words; i += THREADS) {
-        dst[i] = tile_sc[i];
-        tile_sc[i] = make_uint4(0, 0, 0, 0);
+      NVFP4_GLOBAL uint4* dst = reinterpret_cast<NVFP4_GLOBAL uint4*>(global_ptr(a.scales) + tile * (kK >> 6) * 512);
+      for (int i = tid; i < kTileWords; i += kStagedThreads) {
+        dst[i] = tile_sc[i + (i >> 5)];
+        tile_sc[i + (i >> 5)] = make_uint4(0, 0, 0, 0);
       }
       __syncthreads();
     }
@@ -359,13 +400,12 @@ __global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
   }
 }
 
-// Launch shape of the staged kernel: 12 wavefronts (3 per SIMD, up to 170 VGPRs each).
-constexpr int kStagedThreads = 768;
-
 // The tile's scale block (128 rows x k/16 bytes) is staged in LDS when it fits beside the
 // parameters (k <= 7680).
 constexpr size_t kLdsLimit = 160 * 1024;
-inline size_t staged_lds_bytes(int64_t k, bool tile) { return 512 + 12 * (size_t)k + (tile ? 8 * (size_t)k : 0); }
+inline size_t staged_lds_bytes(int64_t k, bool tile) {
+  return 512 + 12 * (size_t)k + (tile ? 8 * (size_t)k / 32 * 33 : 0);
+}
 
 template <int CPL>
 hipError_t launch_staged(const RmsArgs& a, const DeviceInfo& dev, hipStream_t stream) {
@@ -375,18 +415,18 @@ hipError_t launch_staged(const RmsArgs& a, const DeviceInfo& dev, hipStream_t st
   const int64_t grid = ntiles < dev.cu_count ? ntiles : dev.cu_count;
   const dim3 g((uint32_t)grid), b(kStagedThreads);
   if (tile) {
-    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, true, true>), g, b, lds, stream, a, a.frame_idx);
-    else hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, false, true>), g, b, lds, stream, a, a.frame_idx);
+    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, true, true>), g, b, lds, stream, a, a.frame_idx);
+    else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, true>), g, b, lds, stream, a, a.frame_idx);
   } else {
-    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, true, false>), g, b, lds, stream, a, a.frame_idx);
-    else hipLaunchKernelGGL((rms_adaln_staged<CPL, kStagedThreads, false, false>), g, b, lds, stream, a, a.frame_idx);
+    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, true, false>), g, b, lds, stream, a, a.frame_idx);
+    else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, false>), g, b, lds, stream, a, a.frame_idx);
   }
   return hipGetLastError();
 }
 
 template <int CPL, bool Y, bool TILE>
 hipError_t allow_lds_one() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&rms_adaln_staged<CPL, kStagedThreads, Y, TILE>),
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&rms_adaln_staged<CPL, Y, TILE>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
 }
 
