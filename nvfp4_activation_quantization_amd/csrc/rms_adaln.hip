@@ -52,21 +52,30 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, float* 
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// The statistic of a row held as per-lane chunks (chunk L + 64j in v[j]).
-template <int N>
-__device__ __forceinline__ float row_rstd(const uint4* v, int64_t k, float eps) {
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < N; ++j) {
-    float f[8];
-    unpack8(v[j], f);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(f[e], f[e], acc[e]);
-  }
-  float s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) s = s + __shfl_xor(s, d, kWave);
-  return 1.0f / sqrtf(s / (float)k + eps);
+// Butterfly sum over the 64 lanes: for s = 1, 2, 4, 8, 16, 32 every lane replaces v by
+// v + v[lane ^ s] (IEEE fp32 adds; both lanes of a pair compute the same sum, so every
+// lane ends with the same value).  The partner values come from DPP and the gfx950 row
+// swaps rather than LDS permutes: s = 1, 2 are quad permutations; s = 4 is row_shl:4 on
+// the even 4-lane banks of each 16-lane row and row_shr:4 on the odd ones; s = 8 is
+// row_ror:8; s = 16 and 32 use v_permlane16_swap / v_permlane32_swap, whose two results
+// are the lane's value and its partner's.
+__device__ __forceinline__ float lane_sum_butterfly(float v) {
+  uint32_t u = __float_as_uint(v);
+  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0xB1, 0xF, 0xF, false));
+  u = __float_as_uint(v);
+  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x4E, 0xF, 0xF, false));
+  u = __float_as_uint(v);
+  int t = __builtin_amdgcn_update_dpp((int)u, (int)u, 0x104, 0xF, 0x5, false);   // banks 0, 2: lane + 4
+  t = __builtin_amdgcn_update_dpp(t, (int)u, 0x114, 0xF, 0xA, false);            // banks 1, 3: lane - 4
+  v = v + __uint_as_float((uint32_t)t);
+  u = __float_as_uint(v);
+  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x128, 0xF, 0xF, false));
+  u = __float_as_uint(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  u = __float_as_uint(v);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
 }
 
 // y = bf16(bf16(bf16(bf16(x * rstd) * w) * opl) + shift) for the 8 elements of a chunk;
@@ -311,9 +320,8 @@ __global__ __launch_bounds__(kStagedThreads) void rms_adaln_staged(RmsArgs a, co
       // prefetch this wavefront's next row
       const int64_t rn = (i + 1 < kRowsPerWave) ? r + kStagedWaves : next_first;
       load_row<CPL>(nxt, x + (rn < m ? rn : m - 1) * kChunks, lane);
-      float sum = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-#pragma unroll
-      for (int d = 1; d < kWave; d <<= 1) sum = sum + __shfl_xor(sum, d, kWave);
+      const float sum = lane_sum_butterfly(((acc[0] + acc[1]) + (acc[2] + acc[3])) +
+                                           ((acc[4] + acc[5]) + (acc[6] + acc[7])));
       const float rstd = 1.0f / sqrtf(sum / (float)kK + a.eps);
       if (lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
       const int64_t t = frame_idx[r];
@@ -378,9 +386,8 @@ __global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(f[e], f[e], acc[e]);
   }
-  float s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) s = s + __shfl_xor(s, d, kWave);
+  const float s = lane_sum_butterfly(((acc[0] + acc[1]) + (acc[2] + acc[3])) +
+                                     ((acc[4] + acc[5]) + (acc[6] + acc[7])));
   const float rstd = 1.0f / sqrtf(s / (float)a.k + a.eps);
   if (lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
   const int64_t t = global_ptr(a.frame_idx)[r];
