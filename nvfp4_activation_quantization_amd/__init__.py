@@ -25,7 +25,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libnvfp4act.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libnvfp4act.so is not built (run python -m nvfp4_activation_quantization_amd.build "
+    raise ImportError("libnvfp4act.so is not built (run python nvfp4_activation_quantization_amd/build.py "
                       "or __graft_entry__.build())")
 
 _lib = ctypes.CDLL(LIB_PATH)

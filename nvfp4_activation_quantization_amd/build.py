@@ -1,6 +1,7 @@
 """Build libnvfp4act.so (HIP kernels + C ABI) for gfx950 with hipcc, in-tree.
 
-Usage: python -m nvfp4_activation_quantization_amd.build
+Usage: python nvfp4_activation_quantization_amd/build.py   (a plain script: the package itself
+       refuses to import until the library exists)
 """
 from __future__ import annotations
 
