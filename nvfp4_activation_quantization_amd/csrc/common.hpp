@@ -131,6 +131,27 @@ __device__ __forceinline__ void fill_inverse_table(float* inv, float gsf, int ti
 
 // ---- the block quantizer for one chunk --------------------------------------------------
 
+// The E4M3 scale code of the 16-element block whose halves y[0..7] are on lanes L and L^1
+// (the same value on both lanes of the pair).
+__device__ __forceinline__ uint32_t block_scale_code(const float* y, float gsf) {
+  float amax = abs_max3(y[0], y[1], y[2]);
+  amax = max_abs2(amax, y[3], y[4]);
+  amax = max_abs2(amax, y[5], y[6]);
+  amax = max_abs2(amax, y[7], y[7]);
+  // the partner lane's half: amax >= 0, so the larger bit pattern is the larger value
+  amax = __uint_as_float(max_with_lane_xor1(__float_as_uint(amax)));
+  const float rcp6 = __uint_as_float(kRcp6Bits);
+  return e4m3_code(gsf * (amax * rcp6));
+}
+
+// The packed E2M1 codes of y[0..7] under the inverse scale inv (gsf / dec(s), or 0).
+__device__ __forceinline__ uint32_t encode_chunk(const float* y, float inv) {
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = y[i] * inv;
+  return pack_e2m1x8(v);
+}
+
 // y[0..7]: this lane's half of a 16-element block (its partner lane L^1 holds the other
 // half).  Returns the packed codes of the 8 elements and sets *scale to the block's
 // E4M3 code (the same value on both lanes of the pair).

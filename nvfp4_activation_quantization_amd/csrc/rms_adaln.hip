@@ -48,8 +48,18 @@ __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
   f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
-__device__ __forceinline__ void split8(const float4& a, const float4& b, float* f) {
-  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+// The 8 values of a chunk from its four float2 planes (elements 0-1, 2-3, 4-5, 6-7).
+__device__ __forceinline__ void split8(const float2& a, const float2& b, const float2& c, const float2& d,
+                                       float* f) {
+  f[0] = a.x; f[1] = a.y; f[2] = b.x; f[3] = b.y; f[4] = c.x; f[5] = c.y; f[6] = d.x; f[7] = d.y;
+}
+
+// Store the 8 values of chunk c into four float2 planes of `chunks` entries each.
+__device__ __forceinline__ void store_planes(float2* planes, int chunks, int c, const float* f) {
+  planes[c] = make_float2(f[0], f[1]);
+  planes[chunks + c] = make_float2(f[2], f[3]);
+  planes[2 * chunks + c] = make_float2(f[4], f[5]);
+  planes[3 * chunks + c] = make_float2(f[6], f[7]);
 }
 
 // Butterfly sum over the 64 lanes: for s = 1, 2, 4, 8, 16, 32 every lane replaces v by
@@ -175,7 +185,7 @@ __device__ __forceinline__ void load_frame_chunk(const RmsArgs& a, int64_t t, in
 // plain arguments, so the kernel's hot loop is not shaped by this rare path.
 __device__ __noinline__ void emit_row_unstaged(const uint4* x, const uint16_t* shift, const uint16_t* scale,
                                                int64_t frame_stride, RowOut o, int64_t k, int64_t r, int64_t t,
-                                               const float4* wA, const float4* wB, float rstd, float gsf,
+                                               const float2* wp, float rstd, float gsf,
                                                const float* inv_tab, bool tile) {
   const int lane = threadIdx.x & (kWave - 1);
   const NVFP4_GLOBAL uint4* xr = global_ptr(x) + r * (k >> 3);
@@ -184,16 +194,42 @@ __device__ __noinline__ void emit_row_unstaged(const uint4* x, const uint16_t* s
     const int64_t c = lane + (int64_t)kWave * j;
     float x8[8], w8[8], o8[8], h8[8], y[8];
     unpack8(xr[c], x8);
-    split8(wA[c], wB[c], w8);
+    const int chunks = (int)(k >> 3);
+    split8(wp[c], wp[chunks + c], wp[2 * chunks + c], wp[3 * chunks + c], w8);
     load_frame_chunk(shift, scale, frame_stride, t, c, o8, h8);
     modulate8(x8, w8, o8, h8, rstd, y);
     store_chunk(o, j, y, gsf, inv_tab, tile);
   }
 }
 
-// The float4 at byte offset base + off of the dynamic LDS block.
-__device__ __forceinline__ float4 lds_f4(const float4* lds, uint32_t base, uint32_t off) {
-  return *reinterpret_cast<const float4*>(reinterpret_cast<const char*>(lds) + base + off);
+// The float2 at byte offset base + off of the dynamic LDS block.
+__device__ __forceinline__ float2 lds_f2(const float4* lds, uint32_t base, uint32_t off) {
+  return *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(lds) + base + off);
+}
+
+// The twelve float2 parameter values of chunk j (weight, 1 + scale, shift; four planes
+// each) from the LDS plane bases of this lane.
+__device__ __forceinline__ void load_params(const float4* lds, uint32_t pw, uint32_t po, uint32_t ph,
+                                            uint32_t plane, int j, float2* p) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    p[q] = lds_f2(lds, pw, q * plane + 512 * j);
+    p[4 + q] = lds_f2(lds, po, q * plane + 512 * j);
+    p[8 + q] = lds_f2(lds, ph, q * plane + 512 * j);
+  }
+}
+
+// Encode chunk j (its y, scale code s and inverse scale inv) and store its codes, its
+// block's scale byte (into the tile's LDS block with TILE, else to memory) and, with Y,
+// y_out.
+template <bool Y, bool TILE>
+__device__ __forceinline__ void emit_encoded(const RowOut& o, int j, const float* y, float inv, uint32_t s) {
+  o.codes[kWave * j] = encode_chunk(y, inv);
+  if (TILE) o.scales_lds[4224 * j] = (uint8_t)s;
+  else o.scales[(int64_t)4096 * j] = (uint8_t)s;
+  if (Y)
+    o.y[kWave * j] = make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
+                                pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
 }
 
 template <int CPL>
@@ -214,9 +250,9 @@ __device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr,
 // after the statistic it issues the loads of its next row (4 CPL registers), which then
 // arrive while the output pass runs.
 //
-// LDS: inverse-scale table (128 fp32); six fp32 arrays of float4 indexed by chunk (weight
-// elements 0-3 and 4-7, bf16(1 + scale) 0-3 / 4-7, shift 0-3 / 4-7), so each ds_read_b128
-// of a wavefront is one contiguous 1 KiB; and, with TILE, the swizzled scale block of the
+// LDS: inverse-scale table (128 fp32); twelve fp32 planes of float2 indexed by chunk (weight
+// elements 0-1, 2-3, 4-5, 6-7, then bf16(1 + scale) and shift alike), so each ds_read_b64
+// of a wavefront is one contiguous 512 bytes; and, with TILE, the swizzled scale block of the
 // current 128-row tile (8k bytes), with a 16-byte pad after every 512 bytes: the eight
 // 4-byte groups a wavefront writes for one chunk are 512 bytes apart in the layout, which
 // would put them all in one LDS bank.  With TILE the scale bytes are gathered in LDS and the
@@ -225,24 +261,22 @@ __device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr,
 // parameters) each byte is stored directly.
 
 constexpr int kStagedWaves = 8;
-constexpr int kStagedThreads = kStagedWaves * kWave;
-constexpr int kRowsPerWave = 128 / kStagedWaves;
 
 template <int CPL, bool Y, bool TILE>
-__global__ __launch_bounds__(kStagedThreads) void rms_adaln_staged(RmsArgs a, const int32_t* __restrict__ frame_idx) {
+__global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs a, const int32_t* __restrict__ frame_idx) {
+  constexpr int WAVES = kStagedWaves;
+  constexpr int kThreads = WAVES * kWave;
+  constexpr int kRowsPerWave = 128 / WAVES;
   constexpr int kChunks = CPL * kWave;          // chunks per row (k / 8)
   constexpr int kTileWords = kChunks * 4;        // 128 rows x k/16 bytes, in uint4
   constexpr int kTileLdsWords = kTileWords / 32 * 33;   // with one padding uint4 per 32
   constexpr int kK = kChunks * 8;
   extern __shared__ float4 lds4[];
   float* inv_tab = reinterpret_cast<float*>(lds4);
-  float4* wA = lds4 + 32;                 // 128 floats = 32 float4
-  float4* wB = wA + kChunks;
-  float4* oA = wB + kChunks;
-  float4* oB = oA + kChunks;
-  float4* hA = oB + kChunks;
-  float4* hB = hA + kChunks;
-  uint4* tile_sc = reinterpret_cast<uint4*>(hB + kChunks);
+  float2* wp = reinterpret_cast<float2*>(lds4 + 32);   // after 128 floats = 32 float4
+  float2* op = wp + 4 * kChunks;
+  float2* hp = op + 4 * kChunks;
+  uint4* tile_sc = reinterpret_cast<uint4*>(hp + 4 * kChunks);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -250,32 +284,33 @@ __global__ __launch_bounds__(kStagedThreads) void rms_adaln_staged(RmsArgs a, co
   const int64_t m = a.m;
   const int64_t ntiles = a.padded >> 7;
   if ((int64_t)blockIdx.x >= ntiles) return;            // idle workgroup (uniform)
-  // Byte offsets of this lane's chunk 0 in wA, oA and hA.  Each array pair (A, B) and its
-  // 64-lane steps then lie within the 16-bit immediate offset of one ds_read_b128 base;
-  // hiding the three bases from the optimiser keeps it from materialising one address per
-  // array and chunk (the arrays together span more than the immediate range).
-  constexpr uint32_t kArray = kChunks * 16;
-  uint32_t pw = 512 + 16 * lane, po = pw + 2 * kArray, ph = pw + 4 * kArray;
+  // Byte offsets of this lane's chunk 0 in the weight, 1 + scale and shift planes.  The
+  // four planes of one parameter and their 64-lane steps then lie within the 16-bit
+  // immediate offset of one ds_read_b64 base; hiding the three bases from the optimiser
+  // keeps it from materialising one address per plane and chunk (the planes together span
+  // more than the immediate range).  Each read is 8 bytes per lane, consecutive across
+  // the wavefront: ds_read_b64 runs at twice the LDS bandwidth of ds_read_b128 on gfx950.
+  constexpr uint32_t kPlane = kChunks * 8;
+  uint32_t pw = 512 + 8 * lane, po = pw + 4 * kPlane, ph = pw + 8 * kPlane;
   asm volatile("" : "+v"(pw), "+v"(po), "+v"(ph));
 
-  // the first row of this wavefront is in flight while the parameters are staged
-  // (loads are unconditional: a row past the end re-reads row m - 1, which is never used)
-  uint4 nxt[CPL];
+  // The first row of this wavefront is in flight while the parameters are staged (loads
+  // are unconditional: a row past the end re-reads row m - 1, which is never used).
+  uint4 xr[CPL];
   {
     const int64_t r0 = ((int64_t)blockIdx.x << 7) + wave;
-    load_row<CPL>(nxt, x + (r0 < m ? r0 : m - 1) * kChunks, lane);
+    load_row<CPL>(xr, x + (r0 < m ? r0 : m - 1) * kChunks, lane);
   }
 
   const float gsf = global_scale(a.global_amax);
   fill_inverse_table(inv_tab, gsf, tid);
-  for (int c = tid; c < kChunks; c += kStagedThreads) {
+  for (int c = tid; c < kChunks; c += kThreads) {
     float f[8];
     unpack8(*reinterpret_cast<const NVFP4_GLOBAL uint4*>(global_ptr(a.w) + 8 * c), f);
-    wA[c] = make_float4(f[0], f[1], f[2], f[3]);
-    wB[c] = make_float4(f[4], f[5], f[6], f[7]);
+    store_planes(wp, kChunks, c, f);
   }
   if (TILE)
-    for (int i = tid; i < kTileLdsWords; i += kStagedThreads) tile_sc[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < kTileLdsWords; i += kThreads) tile_sc[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   int64_t staged = -1;
@@ -283,7 +318,7 @@ __global__ __launch_bounds__(kStagedThreads) void rms_adaln_staged(RmsArgs a, co
     const int64_t base = tile << 7;
     const int64_t next_first = ((tile + gridDim.x) << 7) + wave;   // this wave's row in the next tile
     for (int i = 0; i < kRowsPerWave; ++i) {
-      const int64_t g = base + kStagedWaves * i;
+      const int64_t g = base + WAVES * i;
       // restage the modulation row when the group's first row needs another frame (uniform)
       int64_t want = staged;
       if (g < m) {
@@ -292,13 +327,11 @@ __global__ __launch_bounds__(kStagedThreads) void rms_adaln_staged(RmsArgs a, co
       }
       if (want != staged) {
         __syncthreads();
-        for (int c = tid; c < kChunks; c += kStagedThreads) {
+        for (int c = tid; c < kChunks; c += kThreads) {
           float o8[8], h8[8];
           load_frame_chunk(a, want, c, o8, h8);
-          oA[c] = make_float4(o8[0], o8[1], o8[2], o8[3]);
-          oB[c] = make_float4(o8[4], o8[5], o8[6], o8[7]);
-          hA[c] = make_float4(h8[0], h8[1], h8[2], h8[3]);
-          hB[c] = make_float4(h8[4], h8[5], h8[6], h8[7]);
+          store_planes(op, kChunks, c, o8);
+          store_planes(hp, kChunks, c, h8);
         }
         __syncthreads();
         staged = want;
@@ -308,18 +341,20 @@ __global__ __launch_bounds__(kStagedThreads) void rms_adaln_staged(RmsArgs a, co
         if (!TILE) zero_row_scales(a.scales, r, kK, lane);   // TILE: already zero in LDS
         continue;
       }
-      // the row arrives (loaded one row earlier): unpack it once, take the statistic
+      // this wavefront's next row (prefetched right after the statistic)
+      int64_t rn = (i + 1 < kRowsPerWave) ? r + WAVES : next_first;
+      rn = rn < m ? rn : m - 1;
+      // the row arrived during the previous row's output pass: unpack it once, take the
+      // statistic, then prefetch the next row into the packed registers
       float xf[CPL][8];
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) unpack8(nxt[j], xf[j]);
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < CPL; ++j)
+      for (int j = 0; j < CPL; ++j) {
+        unpack8(xr[j], xf[j]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(xf[j][e], xf[j][e], acc[e]);
-      // prefetch this wavefront's next row
-      const int64_t rn = (i + 1 < kRowsPerWave) ? r + kStagedWaves : next_first;
-      load_row<CPL>(nxt, x + (rn < m ? rn : m - 1) * kChunks, lane);
+      }
+      load_row<CPL>(xr, x + rn * kChunks, lane);
       const float sum = lane_sum_butterfly(((acc[0] + acc[1]) + (acc[2] + acc[3])) +
                                            ((acc[4] + acc[5]) + (acc[6] + acc[7])));
       const float rstd = 1.0f / sqrtf(sum / (float)kK + a.eps);
@@ -333,26 +368,47 @@ __global__ __launch_bounds__(kStagedThreads) void rms_adaln_staged(RmsArgs a, co
       if (TILE) o.scales_lds = reinterpret_cast<uint8_t*>(tile_sc) + (row_scale_base(r, kK) & 511) +
                                (lane >> 3) * 528 + ((lane >> 1) & 3);
       if (t != staged) {
-        emit_row_unstaged(a.x, a.shift, a.scale, a.frame_stride, o, kK, r, t, wA, wB, rstd, gsf, inv_tab,
+        emit_row_unstaged(a.x, a.shift, a.scale, a.frame_stride, o, kK, r, t, wp, rstd, gsf, inv_tab,
                           TILE);
         continue;
       }
+      // Output pass, software-pipelined over the lane's chunks: the parameters of chunk j + 1
+      // are read from LDS while chunk j is modulated, and chunk j's inverse scale (an LDS
+      // table lookup) is consumed only after chunk j + 1 has been modulated, so neither LDS
+      // round trip sits on the critical path of a chunk.
+      float2 pc[12], pn[12];
+      load_params(lds4, pw, po, ph, kPlane, 0, pc);
+      float yp[8];
+      uint32_t sp = 0;
+      float invp = 0.0f;
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
+        if (j + 1 < CPL) load_params(lds4, pw, po, ph, kPlane, j + 1, pn);
         float w8[8], o8[8], h8[8], y[8];
-        split8(lds_f4(lds4, pw, 1024 * j), lds_f4(lds4, pw, kArray + 1024 * j), w8);
-        split8(lds_f4(lds4, po, 1024 * j), lds_f4(lds4, po, kArray + 1024 * j), o8);
-        split8(lds_f4(lds4, ph, 1024 * j), lds_f4(lds4, ph, kArray + 1024 * j), h8);
+        split8(pc[0], pc[1], pc[2], pc[3], w8);
+        split8(pc[4], pc[5], pc[6], pc[7], o8);
+        split8(pc[8], pc[9], pc[10], pc[11], h8);
         modulate8(xf[j], w8, o8, h8, rstd, y);
-        emit_chunk<Y, TILE>(o, j, y, gsf, inv_tab);
+        const uint32_t s = block_scale_code(y, gsf);
+        const float inv = inv_tab[s];
+        if (j > 0) emit_encoded<Y, TILE>(o, j - 1, yp, invp, sp);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) yp[e] = y[e];
+        sp = s;
+        invp = inv;
+        if (j + 1 < CPL) {
+#pragma unroll
+          for (int q = 0; q < 12; ++q) pc[q] = pn[q];
+        }
       }
+      emit_encoded<Y, TILE>(o, CPL - 1, yp, invp, sp);
     }
     if (TILE) {
       // the tile's scale block is complete: copy it out and zero it for the next tile (each
       // thread clears exactly the words it copied, so no barrier is needed in between)
       __syncthreads();
       NVFP4_GLOBAL uint4* dst = reinterpret_cast<NVFP4_GLOBAL uint4*>(global_ptr(a.scales) + tile * (kK >> 6) * 512);
-      for (int i = tid; i < kTileWords; i += kStagedThreads) {
+      for (int i = tid; i < kTileWords; i += kThreads) {
         dst[i] = tile_sc[i + (i >> 5)];
         tile_sc[i + (i >> 5)] = make_uint4(0, 0, 0, 0);
       }
@@ -420,7 +476,7 @@ hipError_t launch_staged(const RmsArgs& a, const DeviceInfo& dev, hipStream_t st
   const size_t lds = staged_lds_bytes(a.k, tile);
   const int64_t ntiles = a.padded >> 7;
   const int64_t grid = ntiles < dev.cu_count ? ntiles : dev.cu_count;
-  const dim3 g((uint32_t)grid), b(kStagedThreads);
+  const dim3 g((uint32_t)grid), b(kStagedWaves * kWave);
   if (tile) {
     if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, true, true>), g, b, lds, stream, a, a.frame_idx);
     else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, true>), g, b, lds, stream, a, a.frame_idx);
