@@ -1,12 +1,24 @@
 // quantize.hip -- standalone NVFP4 quantize of a bf16 tensor (the attention-output
 // quantize of TensorRT-LLM PR #21483; FastVideo API page, quantize).
 //
-// Bandwidth-bound: 2 bytes in, 0.5625 bytes out per element.  The tensor is cut into
-// tiles of 128 rows x 1024 columns (the last column tile may be narrower).  One
-// 256-thread workgroup per tile: each wavefront takes 32 of the rows, kRowBatch rows at a
-// time so 2 x kRowBatch 1 KiB loads per wavefront are in flight.  The tile's scale bytes
-// (16 groups of 4 blocks x 128 rows = 8 KiB, contiguous in the swizzled layout) are
-// gathered in LDS and written out with 16-byte stores; rows m..pad(m)-1 stay zero.
+// Bandwidth-bound: 2 bytes in, 0.5625 bytes out per element, a few VALU operations per
+// element.  The launch is shaped for HBM streaming rather than for reuse:
+//
+// * One wavefront per row, non-persistent.  A wavefront issues the 16-byte loads of a whole
+//   row piece (up to 1024 chunks = 8192 columns, 16 per lane) at once, quantizes it and
+//   exits; workgroups are dispatched in row order, so the rows being read at any moment
+//   form one compact window of the tensor and finished wavefronts are replaced at once.
+//
+// * A workgroup of four wavefronts owns the four rows r, r + 32, r + 64, r + 96 of a 128-row
+//   tile (r = tile * 128 + rr, rr < 32).  In the 128x4 swizzled scale layout those rows'
+//   scale bytes of four consecutive blocks form one contiguous 16-byte unit (row-group
+//   major, then block), so the workgroup gathers the units of each row piece in LDS and
+//   writes each with one 16-byte store; padding rows (>= m) contribute zero bytes.
+//
+// * The eight workgroups rr = 8p .. 8p + 7 of a tile fill the same 128-byte lines of the
+//   scale buffer.  Block indices are arranged so that those eight are consecutive on one
+//   XCD (workgroups are dealt round-robin over the 8 XCDs), so each line is completed in
+//   one L2 before it is written back.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -14,85 +26,139 @@ namespace nvfp4act {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWavesPerWg = kThreads / kWave;
-constexpr int kTileCols = 1024;                    // 128 chunks: 2 per lane per row
-constexpr int kChunkSlots = kTileCols / 8 / kWave;  // 2
-constexpr int kRowBatch = 4;                       // rows per wavefront in flight
-constexpr int kScaleBytes = kTileCols / 64 * 512;  // 8 KiB
+constexpr int kWaves = 4;                  // rows per workgroup (r + 32 i)
+constexpr int kThreads = kWaves * kWave;
+constexpr int kPieceSlots = 16;            // chunks per lane per row piece (8192 columns)
 
+// Row group of workgroup b: unit group u = b / 64 * 8 + b % 8 (tile u / 4, rr block u % 4),
+// rr = 8 (u % 4) + (b / 8) % 8.  For a fixed u the eight values of (b / 8) % 8 share b % 8.
+struct RowGroup {
+  int64_t tile;
+  int rr;
+};
+
+__device__ __forceinline__ RowGroup row_group(int64_t b) {
+  const int64_t u = (b >> 6) * 8 + (b & 7);
+  RowGroup g;
+  g.tile = u >> 2;
+  g.rr = (int)((u & 3) * 8 + ((b >> 3) & 7));
+  return g;
+}
+
+// The 16-byte loads of SLOTS chunk slots (lane + 64 j, j < SLOTS) of a row from chunk c0.
+template <int SLOTS>
+__device__ __forceinline__ void load_piece(const NVFP4_GLOBAL uint4* xr, int64_t c0, int64_t chunks, int lane,
+                                           uint4* v) {
+#pragma unroll
+  for (int j = 0; j < SLOTS; ++j) {
+    const int64_t c = c0 + lane + kWave * j;
+    v[j] = (c < chunks) ? load_stream(reinterpret_cast<const uint4*>(xr + c)) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Quantize the loaded piece and gather its scale bytes in the workgroup's LDS units of this
+// piece (unit (c - c0) / 8, byte wave * 4 + block % 4).
+template <int SLOTS>
+__device__ __forceinline__ void quantize_piece(const uint4* v, NVFP4_GLOBAL uint32_t* cr, int64_t c0, int64_t chunks,
+                                               int lane, int wave, float gsf, const float* inv_tab, uint8_t* units) {
+#pragma unroll
+  for (int j = 0; j < SLOTS; ++j) {
+    const int64_t c = c0 + lane + kWave * j;
+    float y[8] = {bf16_lo(v[j].x), bf16_hi(v[j].x), bf16_lo(v[j].y), bf16_hi(v[j].y),
+                  bf16_lo(v[j].z), bf16_hi(v[j].z), bf16_lo(v[j].w), bf16_hi(v[j].w)};
+    const uint32_t s = block_scale_code(y, gsf);
+    const uint32_t q = encode_chunk(y, inv_tab[s]);
+    if (c < chunks) {
+      cr[c] = q;
+      units[((c - c0) >> 3) * 16 + wave * 4 + ((c >> 1) & 3)] = (uint8_t)s;
+    }
+  }
+}
+
+template <int SLOTS>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint4* __restrict__ x, int64_t m, int64_t k,
                                                             float global_amax, uint32_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales, int64_t col_tiles) {
+                                                            uint8_t* __restrict__ scales) {
+  constexpr int kPieceChunks = kWave * SLOTS;       // chunks per row piece
+  constexpr int kPieceUnits = kPieceChunks / 8;     // 16-byte units per row-group piece
   __shared__ float inv_tab[128];
-  __shared__ uint4 tile_sc[kScaleBytes / 16];
+  __shared__ uint4 units[kPieceUnits];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const RowGroup g = row_group(blockIdx.x);
+  const int64_t ntiles = (m + 127) >> 7;
+  if (g.tile >= ntiles) return;                                     // idle workgroup (uniform)
+  const int64_t chunks = k >> 3;
+  const int64_t groups = k >> 6;                                    // 16-byte units per row group
+  const int64_t r = (g.tile << 7) + g.rr + 32 * wave;
+  const NVFP4_GLOBAL uint4* xr = global_ptr(x) + r * chunks;
+  NVFP4_GLOBAL uint32_t* cr = global_ptr(codes) + r * chunks;
+  // unit q of this row group sits at ((tile * k / 64) + q) * 512 + rr * 16
+  NVFP4_GLOBAL uint8_t* dst = global_ptr(scales) + (g.tile * groups) * 512 + g.rr * 16;
+
+  // the first piece is in flight while the inverse-scale table is built
+  uint4 v[SLOTS];
+  if (r < m) load_piece<SLOTS>(xr, 0, chunks, lane, v);
   const float gsf = global_scale(global_amax);
   fill_inverse_table(inv_tab, gsf, tid);
-  for (int i = tid; i < kScaleBytes / 16; i += kThreads) tile_sc[i] = make_uint4(0, 0, 0, 0);
+  for (int i = tid; i < kPieceUnits; i += kThreads) units[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  const int64_t tile_row = blockIdx.x / col_tiles;
-  const int64_t col_tile = blockIdx.x % col_tiles;
-  const int64_t c0 = col_tile * (kTileCols / 8);                 // first chunk of the tile
-  const int64_t row_chunks = k >> 3;
-  const int64_t tchunks = (row_chunks - c0 < kTileCols / 8) ? row_chunks - c0 : kTileCols / 8;
-  const int64_t r0 = tile_row << 7;
-  const int64_t rows = (m - r0 < 128) ? (m - r0 > 0 ? m - r0 : 0) : 128;   // real rows of the tile
-  uint8_t* sc_lane = reinterpret_cast<uint8_t*>(tile_sc) + scale_lane_offset(lane);
-
-  for (int64_t rb = wave * kRowBatch; rb < rows; rb += kWavesPerWg * kRowBatch) {
-    uint4 v[kRowBatch][kChunkSlots];
-#pragma unroll
-    for (int i = 0; i < kRowBatch; ++i) {
-      const int64_t rr = rb + i;
-#pragma unroll
-      for (int j = 0; j < kChunkSlots; ++j) {
-        const int64_t c = j * kWave + lane;
-        if (rr < rows && c < tchunks)
-          v[i][j] = load_stream(reinterpret_cast<const uint4*>(global_ptr(x) + (r0 + rr) * row_chunks + c0 + c));
-        else
-          v[i][j] = make_uint4(0, 0, 0, 0);
-      }
+  for (int64_t c0 = 0; c0 < chunks; c0 += kPieceChunks) {
+    if (r < m) {
+      if (c0 > 0) load_piece<SLOTS>(xr, c0, chunks, lane, v);
+      quantize_piece<SLOTS>(v, cr, c0, chunks, lane, wave, gsf, inv_tab, reinterpret_cast<uint8_t*>(units));
     }
-#pragma unroll
-    for (int i = 0; i < kRowBatch; ++i) {
-      const int64_t rr = rb + i;
-      const int row_part = (int)((rr & 31) * 16 + ((rr >> 5) & 3) * 4);
-#pragma unroll
-      for (int j = 0; j < kChunkSlots; ++j) {
-        const int64_t c = j * kWave + lane;
-        float y[8] = {bf16_lo(v[i][j].x), bf16_hi(v[i][j].x), bf16_lo(v[i][j].y), bf16_hi(v[i][j].y),
-                      bf16_lo(v[i][j].z), bf16_hi(v[i][j].z), bf16_lo(v[i][j].w), bf16_hi(v[i][j].w)};
-        uint32_t s;
-        const uint32_t q = quantize_chunk(y, gsf, inv_tab, &s);
-        if (rr < rows && c < tchunks) {
-          global_ptr(codes)[(r0 + rr) * row_chunks + c0 + c] = q;
-          sc_lane[row_part + 4096 * j] = (uint8_t)s;
-        }
-      }
+    __syncthreads();
+    // the piece's units (zero bytes for rows >= m); each thread clears what it copied
+    const int64_t q0 = c0 >> 3;
+    for (int i = tid; i < kPieceUnits && q0 + i < groups; i += kThreads) {
+      *reinterpret_cast<NVFP4_GLOBAL uint4*>(dst + (q0 + i) * 512) = units[i];
+      units[i] = make_uint4(0, 0, 0, 0);
     }
+    if (c0 + kPieceChunks < chunks) __syncthreads();
   }
-  __syncthreads();
-  // the tile's scale slice: (tchunks / 8) groups of 512 bytes, contiguous in the layout
-  NVFP4_GLOBAL uint4* dst = reinterpret_cast<NVFP4_GLOBAL uint4*>(
-      global_ptr(scales) + (tile_row * (k >> 6) + c0 / 8) * 512);
-  const int words = (int)(tchunks / 8) * 32;
-  for (int i = tid; i < words; i += kThreads) dst[i] = tile_sc[i];
+}
+
+template <int SLOTS>
+hipError_t launch_slots(const uint4* x, int64_t m, int64_t k, float global_amax, uint32_t* codes, uint8_t* scales,
+                        hipStream_t stream) {
+  const int64_t ntiles = (m + 127) / 128;
+  const int64_t unit_groups = ntiles * 4;
+  const int64_t blocks = (unit_groups + 7) / 8 * 64;
+  hipLaunchKernelGGL((quantize_kernel<SLOTS>), dim3((uint32_t)blocks), dim3(kThreads), 0, stream, x, m, k,
+                     global_amax, codes, scales);
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const void* x, int64_t m, int64_t k, float global_amax, void* codes,
                            void* scales, hipStream_t stream) {
-  const int64_t tile_rows = (m + 127) / 128;
-  const int64_t col_tiles = (k + kTileCols - 1) / kTileCols;
-  hipLaunchKernelGGL(quantize_kernel, dim3((uint32_t)(tile_rows * col_tiles)), dim3(kThreads), 0, stream,
-                     static_cast<const uint4*>(x), m, k, global_amax, static_cast<uint32_t*>(codes),
-                     static_cast<uint8_t*>(scales), col_tiles);
-  return hipGetLastError();
+  const uint4* xv = static_cast<const uint4*>(x);
+  uint32_t* cv = static_cast<uint32_t*>(codes);
+  uint8_t* sv = static_cast<uint8_t*>(scales);
+  // chunk slots per lane: the whole row when it has at most 1024 chunks, else pieces of 16
+  const int64_t slots = (k / 8 + kWave - 1) / kWave;
+  switch (slots < kPieceSlots ? slots : kPieceSlots) {
+    case 1: return launch_slots<1>(xv, m, k, global_amax, cv, sv, stream);
+    case 2: return launch_slots<2>(xv, m, k, global_amax, cv, sv, stream);
+    case 3: return launch_slots<3>(xv, m, k, global_amax, cv, sv, stream);
+    case 4: return launch_slots<4>(xv, m, k, global_amax, cv, sv, stream);
+    case 5: return launch_slots<5>(xv, m, k, global_amax, cv, sv, stream);
+    case 6: return launch_slots<6>(xv, m, k, global_amax, cv, sv, stream);
+    case 7: return launch_slots<7>(xv, m, k, global_amax, cv, sv, stream);
+    case 8: return launch_slots<8>(xv, m, k, global_amax, cv, sv, stream);
+    case 9: return launch_slots<9>(xv, m, k, global_amax, cv, sv, stream);
+    case 10: return launch_slots<10>(xv, m, k, global_amax, cv, sv, stream);
+    case 11: return launch_slots<11>(xv, m, k, global_amax, cv, sv, stream);
+    case 12: return launch_slots<12>(xv, m, k, global_amax, cv, sv, stream);
+    case 13: return launch_slots<13>(xv, m, k, global_amax, cv, sv, stream);
+    case 14: return launch_slots<14>(xv, m, k, global_amax, cv, sv, stream);
+    case 15: return launch_slots<15>(xv, m, k, global_amax, cv, sv, stream);
+    default: return launch_slots<16>(xv, m, k, global_amax, cv, sv, stream);
+  }
 }
 
 }  // namespace nvfp4act
