@@ -66,6 +66,12 @@ def _load():
             "orc_scale_offset": (I64, [I64, I64, I64]),
             "orc_padded_rows": (I64, [I64]),
             "orc_global_scale": (F, [F]),
+            "orc_dynamic_global_scale": (F, [F]),
+            "orc_max_abs_bf16": (F, [P, I64]),
+            "orc_nvfp4_quantize_gsf": (None, [P, I64, I64, F, P, P]),
+            "orc_rms_adaln_rows_gsf": (None, [P, I64, I64, P, P, P, P, I64, I64, P, F, F,
+                                              P, P, P, P, P, P]),
+            "orc_swiglu_rows_gsf": (None, [P, P, I64, I64, I64, P, P, F, P, P, P, P]),
             "orc_rms_rstd": (F, [P, I64, F]),
             "orc_quantize_rows": (None, [P, I64, I64, F, P, P]),
             "orc_nvfp4_quantize": (None, [P, I64, I64, F, P, P]),
@@ -151,6 +157,17 @@ def global_scale(global_amax: float) -> float:
     return _load().orc_global_scale(float(global_amax))
 
 
+def dynamic_global_scale(amax: float) -> float:
+    """Global scale of a per-call amax: 2688 / amax when positive and finite, else 0."""
+    return _load().orc_dynamic_global_scale(float(amax))
+
+
+def max_abs(u16) -> float:
+    """max |x| over bf16 patterns, as fp32 (exact)."""
+    a = _c(u16, np.uint16)
+    return _load().orc_max_abs_bf16(_ptr(a), a.size)
+
+
 def rms_rstd(x_row_u16, eps: float) -> float:
     a = _c(x_row_u16, np.uint16)
     return _load().orc_rms_rstd(_ptr(a), a.size, float(eps))
@@ -170,22 +187,37 @@ def quantize_rows(y_u16, global_amax: float):
     return codes, sb
 
 
-def nvfp4_quantize(x_u16, global_amax: float):
-    """Standalone quantize: codes [m, k/2] and swizzled scales [pad(m), k/16]."""
+def nvfp4_quantize(x_u16, global_amax: float, gsf: float | None = None):
+    """Standalone quantize: codes [m, k/2] and swizzled scales [pad(m), k/16].
+
+    With gsf given, that global scale is used as is (global_amax is ignored)."""
     x = _c(x_u16, np.uint16)
     m, k = x.shape
     codes = np.empty((m, k // 2), np.uint8)
     scales = np.empty((padded_rows(m), k // 16), np.uint8)
-    _load().orc_nvfp4_quantize(_ptr(x), m, k, float(global_amax), _ptr(codes), _ptr(scales))
+    if gsf is None:
+        _load().orc_nvfp4_quantize(_ptr(x), m, k, float(global_amax), _ptr(codes), _ptr(scales))
+    else:
+        _load().orc_nvfp4_quantize_gsf(_ptr(x), m, k, float(gsf), _ptr(codes), _ptr(scales))
     return codes, scales
 
 
+def nvfp4_quantize_dynamic(x_u16):
+    """Standalone quantize under the tensor's own amax (per-call scale, the FlashRT
+    dynamic activation scale): returns (codes, scales, amax)."""
+    amax = max_abs(x_u16)
+    codes, scales = nvfp4_quantize(x_u16, 0.0, gsf=dynamic_global_scale(amax))
+    return codes, scales, amax
+
+
 def rms_adaln_rows(x_u16, w_u16, table_u16, frame_idx, eps: float, global_amax: float,
-                   row_ids=None, want_y: bool = False, scales_rows: int | None = None):
+                   row_ids=None, want_y: bool = False, scales_rows: int | None = None,
+                   gsf: float | None = None):
     """RMSNorm + adaLN -> NVFP4 for rows of x.
 
     table_u16: [T, 2, k] bf16 (shift, scale).  frame_idx: per-row frame.
     row_ids: the rows' indices in the full tensor (default 0..n-1).
+    gsf: use this global scale as is (global_amax is then ignored).
     Returns dict(codes [n,k/2], scale_bytes [n,k/16], rstd [n], y [n,k] or None,
     status, scales: swizzled [scales_rows, k/16] when scales_rows is given).
     """
@@ -206,11 +238,23 @@ def rms_adaln_rows(x_u16, w_u16, table_u16, frame_idx, eps: float, global_amax: 
     status = np.zeros(1, np.uint32)
     shift_ptr = tab.ctypes.data                    # table row t: shift at t*2k elements
     scale_ptr = tab.ctypes.data + k * tab.itemsize  # ... and scale k elements further
-    _load().orc_rms_adaln_rows(_ptr(x), n, k, _ptr(rid), _ptr(w), shift_ptr, scale_ptr, 2 * k,
-                               t_frames, _ptr(idx), float(eps),
-                               float(global_amax), _ptr(codes), _ptr(sb), _ptr(scales), _ptr(rstd),
-                               _ptr(y), _ptr(status))
+    fn = _load().orc_rms_adaln_rows if gsf is None else _load().orc_rms_adaln_rows_gsf
+    fn(_ptr(x), n, k, _ptr(rid), _ptr(w), shift_ptr, scale_ptr, 2 * k, t_frames, _ptr(idx), float(eps),
+       float(global_amax if gsf is None else gsf), _ptr(codes), _ptr(sb), _ptr(scales), _ptr(rstd),
+       _ptr(y), _ptr(status))
     return dict(codes=codes, scale_bytes=sb, rstd=rstd, y=y, status=int(status[0]), scales=scales)
+
+
+def rms_adaln_dynamic(x_u16, w_u16, table_u16, frame_idx, eps: float, want_y: bool = False,
+                      scales_rows: int | None = None):
+    """RMSNorm + adaLN -> NVFP4 under the amax of the tensor's own y (two passes: y, then
+    the quantizer with dynamic_global_scale(max|y|)).  The result dict gains 'amax'."""
+    first = rms_adaln_rows(x_u16, w_u16, table_u16, frame_idx, eps, 1.0, want_y=True)
+    amax = max_abs(first["y"])
+    out = rms_adaln_rows(x_u16, w_u16, table_u16, frame_idx, eps, 0.0, want_y=want_y,
+                         scales_rows=scales_rows, gsf=dynamic_global_scale(amax))
+    out["amax"] = amax
+    return out
 
 
 _silu_cache = None
@@ -229,10 +273,11 @@ def silu_table() -> np.ndarray:
 
 
 def swiglu_rows(up_u16, gate_u16, global_amax: float, row_ids=None, want_y: bool = False,
-                scales_rows: int | None = None):
+                scales_rows: int | None = None, gsf: float | None = None):
     """SwiGLU -> NVFP4: y = bf16(S[gate] * up), then the block quantizer.
 
     up_u16 / gate_u16: [n, f] bf16 (views into a packed [n, 2f] are fine).
+    gsf: use this global scale as is (global_amax is then ignored).
     """
     up = _c(up_u16, np.uint16)
     gate = _c(gate_u16, np.uint16)
@@ -245,9 +290,21 @@ def swiglu_rows(up_u16, gate_u16, global_amax: float, row_ids=None, want_y: bool
     scales = None
     if scales_rows is not None:
         scales = np.zeros((scales_rows, f // 16), np.uint8)
-    _load().orc_swiglu_rows(_ptr(up), _ptr(gate), f, n, f, _ptr(rid), _ptr(table),
-                            float(global_amax), _ptr(codes), _ptr(sb), _ptr(scales), _ptr(y))
+    fn = _load().orc_swiglu_rows if gsf is None else _load().orc_swiglu_rows_gsf
+    fn(_ptr(up), _ptr(gate), f, n, f, _ptr(rid), _ptr(table), float(global_amax if gsf is None else gsf),
+       _ptr(codes), _ptr(sb), _ptr(scales), _ptr(y))
     return dict(codes=codes, scale_bytes=sb, y=y, scales=scales)
+
+
+def swiglu_dynamic(up_u16, gate_u16, want_y: bool = False, scales_rows: int | None = None):
+    """SwiGLU -> NVFP4 under the amax of the tensor's own y (two passes).  The result dict
+    gains 'amax'."""
+    first = swiglu_rows(up_u16, gate_u16, 1.0, want_y=True)
+    amax = max_abs(first["y"])
+    out = swiglu_rows(up_u16, gate_u16, 0.0, want_y=want_y, scales_rows=scales_rows,
+                      gsf=dynamic_global_scale(amax))
+    out["amax"] = amax
+    return out
 
 
 # --------------------------------------------------------------------------

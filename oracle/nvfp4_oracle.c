@@ -174,6 +174,19 @@ static const uint32_t RCP6_BITS = 0x3E2AAAABu;   /* fp32 nearest to 1/6 */
 
 static float global_scale(float global_amax) { return 2688.0f / global_amax; }
 
+/* Global scale of a per-call (dynamic) amax, measured on the tensor itself
+   ([FlashRT] "dynamic per-call activation" scale, device-side amax then
+   quantize; [H3-API] NVFP4DecoderLinear act_scale="dynamic", per-call
+   abs-max).  The pages give the scale only for a positive amax.  Reading: the
+   same 2688 / amax when that is positive and finite; otherwise (an all-zero
+   tensor, or an amax so small that 2688 / amax overflows) the scale is 0, so
+   every block scale is E4M3 0 and every element code is a signed zero. */
+static float dynamic_global_scale(float amax) {
+    if (!(amax > 0.0f)) return 0.0f;
+    float g = 2688.0f / amax;
+    return isfinite(g) ? g : 0.0f;
+}
+
 /* Quantize one row of bf16 values y[0..k) ([PROBE] quant_probe):
    for every 16-element block, amax = max |y|; sf = gsf * (amax * (1/6));
    s = E4M3(sf); inv = s ? gsf / dec(s) : 0; code_i = E2M1(y_i * inv).
@@ -277,6 +290,23 @@ EXPORT float orc_global_scale(float global_amax) {
     return g;
 }
 
+EXPORT float orc_dynamic_global_scale(float amax) {
+    unsigned int s = enter_ieee();
+    float g = dynamic_global_scale(amax);
+    leave_ieee(s);
+    return g;
+}
+
+/* max |x| over n bf16 values, as fp32 (exact: a maximum of exact values). */
+EXPORT float orc_max_abs_bf16(const uint16_t* x, int64_t n) {
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(bf16_to_f32(x[i]));
+        if (a > m) m = a;
+    }
+    return m;
+}
+
 EXPORT float orc_rms_rstd(const uint16_t* x, int64_t k, float eps) {
     unsigned int s = enter_ieee();
     float r = rms_rstd(x, k, eps);
@@ -302,10 +332,9 @@ EXPORT void orc_quantize_rows(const uint16_t* y, int64_t n, int64_t k, float glo
 /* Standalone quantize of x [m, k] ([H3-API] quantize; [TRT] attention-output
    quantize).  scales is the swizzled [pad(m), k/16] buffer; padding rows are
    written as zero. */
-EXPORT void orc_nvfp4_quantize(const uint16_t* x, int64_t m, int64_t k, float global_amax,
-                               uint8_t* codes, uint8_t* scales) {
+EXPORT void orc_nvfp4_quantize_gsf(const uint16_t* x, int64_t m, int64_t k, float gsf,
+                                   uint8_t* codes, uint8_t* scales) {
     unsigned int s = enter_ieee();
-    float gsf = global_scale(global_amax);
     memset(scales, 0, (size_t)(padded_rows(m) * (k / 16)));
     float* row = (float*)malloc(sizeof(float) * (size_t)k);
     uint8_t* sb = (uint8_t*)malloc((size_t)(k / 16));
@@ -317,6 +346,14 @@ EXPORT void orc_nvfp4_quantize(const uint16_t* x, int64_t m, int64_t k, float gl
     free(sb);
     free(row);
     leave_ieee(s);
+}
+
+EXPORT void orc_nvfp4_quantize(const uint16_t* x, int64_t m, int64_t k, float global_amax,
+                               uint8_t* codes, uint8_t* scales) {
+    unsigned int s = enter_ieee();
+    float gsf = global_scale(global_amax);
+    leave_ieee(s);
+    orc_nvfp4_quantize_gsf(x, m, k, gsf, codes, scales);
 }
 
 /* RMSNorm + adaLN modulation of one row ([TRT] AdaLN RMSNorm + modulation;
@@ -349,13 +386,12 @@ static void rms_adaln_row(const uint16_t* x, const uint16_t* w, const uint16_t* 
      codes [n, k/2]; scale_bytes [n, k/16] plain order (or NULL);
      scales: swizzled buffer addressed by row_ids (or NULL);
      rstd [n]; y [n, k] bf16 patterns. */
-EXPORT void orc_rms_adaln_rows(const uint16_t* x, int64_t n, int64_t k, const int64_t* row_ids,
-                               const uint16_t* w, const uint16_t* shift, const uint16_t* scale,
-                               int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx,
-                               float eps, float global_amax, uint8_t* codes, uint8_t* scale_bytes,
-                               uint8_t* scales, float* rstd_out, uint16_t* y_out, uint32_t* status) {
+EXPORT void orc_rms_adaln_rows_gsf(const uint16_t* x, int64_t n, int64_t k, const int64_t* row_ids,
+                                   const uint16_t* w, const uint16_t* shift, const uint16_t* scale,
+                                   int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx,
+                                   float eps, float gsf, uint8_t* codes, uint8_t* scale_bytes,
+                                   uint8_t* scales, float* rstd_out, uint16_t* y_out, uint32_t* status) {
     unsigned int s = enter_ieee();
-    float gsf = global_scale(global_amax);
     float* y = (float*)malloc(sizeof(float) * (size_t)k);
     uint8_t* sb = (uint8_t*)malloc((size_t)(k / 16));
     for (int64_t i = 0; i < n; ++i) {
@@ -382,6 +418,19 @@ EXPORT void orc_rms_adaln_rows(const uint16_t* x, int64_t n, int64_t k, const in
     free(sb);
     free(y);
     leave_ieee(s);
+}
+
+/* The same with the global scale of a static amax (2688 / global_amax). */
+EXPORT void orc_rms_adaln_rows(const uint16_t* x, int64_t n, int64_t k, const int64_t* row_ids,
+                               const uint16_t* w, const uint16_t* shift, const uint16_t* scale,
+                               int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx,
+                               float eps, float global_amax, uint8_t* codes, uint8_t* scale_bytes,
+                               uint8_t* scales, float* rstd_out, uint16_t* y_out, uint32_t* status) {
+    unsigned int s = enter_ieee();
+    float gsf = global_scale(global_amax);
+    leave_ieee(s);
+    orc_rms_adaln_rows_gsf(x, n, k, row_ids, w, shift, scale, frame_stride, num_frames, frame_idx, eps, gsf,
+                           codes, scale_bytes, scales, rstd_out, y_out, status);
 }
 
 /* ------------------------------------------------------------------------- */
@@ -455,12 +504,11 @@ EXPORT int orc_silu_table(uint16_t* table) {
    up / gate rows are ld elements apart (row i at up + i*ld, gate + i*ld);
    f output columns.  table: the 65536-entry SiLU table from orc_silu_table.
    row_ids / scales / scale_bytes / y_out as in orc_rms_adaln_rows. */
-EXPORT void orc_swiglu_rows(const uint16_t* up, const uint16_t* gate, int64_t ld, int64_t n,
-                            int64_t f, const int64_t* row_ids, const uint16_t* table,
-                            float global_amax, uint8_t* codes, uint8_t* scale_bytes,
-                            uint8_t* scales, uint16_t* y_out) {
+EXPORT void orc_swiglu_rows_gsf(const uint16_t* up, const uint16_t* gate, int64_t ld, int64_t n,
+                                int64_t f, const int64_t* row_ids, const uint16_t* table,
+                                float gsf, uint8_t* codes, uint8_t* scale_bytes,
+                                uint8_t* scales, uint16_t* y_out) {
     unsigned int s = enter_ieee();
-    float gsf = global_scale(global_amax);
     float* y = (float*)malloc(sizeof(float) * (size_t)f);
     uint8_t* sb = (uint8_t*)malloc((size_t)(f / 16));
     for (int64_t i = 0; i < n; ++i) {
@@ -478,4 +526,15 @@ EXPORT void orc_swiglu_rows(const uint16_t* up, const uint16_t* gate, int64_t ld
     free(sb);
     free(y);
     leave_ieee(s);
+}
+
+/* The same with the global scale of a static amax (2688 / global_amax). */
+EXPORT void orc_swiglu_rows(const uint16_t* up, const uint16_t* gate, int64_t ld, int64_t n,
+                            int64_t f, const int64_t* row_ids, const uint16_t* table,
+                            float global_amax, uint8_t* codes, uint8_t* scale_bytes,
+                            uint8_t* scales, uint16_t* y_out) {
+    unsigned int s = enter_ieee();
+    float gsf = global_scale(global_amax);
+    leave_ieee(s);
+    orc_swiglu_rows_gsf(up, gate, ld, n, f, row_ids, table, gsf, codes, scale_bytes, scales, y_out);
 }

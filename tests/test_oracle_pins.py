@@ -429,3 +429,89 @@ def test_tensor_quantize_matches_rows_and_layout():
     mask = np.ones(scales.size, bool)
     mask[offs.ravel()] = False
     assert not scales.ravel()[mask].any()
+
+
+# --------------------------------------------------------------------------
+# per-call (dynamic) global amax
+# --------------------------------------------------------------------------
+
+def test_dynamic_global_scale_special_cases():
+    f32 = np.float32
+    fmax = float(np.finfo(np.float32).max)
+    # positive amax with a finite quotient: the static rule 2688 / amax (IEEE fp32)
+    for a in [2688.0, 1.0, 63.25, 1.0e-35, fmax]:
+        want = float(f32(2688.0) / f32(a))
+        assert oracle.dynamic_global_scale(a) == want
+    # zero, negative zero, a quotient that overflows, non-finite amax: scale 0
+    assert np.isinf(f32(2688.0) / f32(1e-38))
+    for a in [0.0, -0.0, 1e-38, float(2.0 ** -133), float("inf"), float("nan")]:
+        assert oracle.dynamic_global_scale(a) == 0.0
+
+
+def test_max_abs_vs_numpy():
+    g = np.random.Generator(np.random.PCG64(77))
+    x = oracle.bf16_round((g.standard_normal(5000) * 3).astype(np.float32))
+    x[17] = 0x8000                       # -0
+    x[18] = 0x0001                       # smallest positive subnormal
+    x[19] = 0xC2F7                       # -123.5
+    want = float(np.abs(oracle.bf16_to_f32(x)).max())
+    assert oracle.max_abs(x) == want == 123.5
+    assert oracle.max_abs(np.array([0x8000, 0x0000], np.uint16)) == 0.0
+
+
+def test_dynamic_quantize_is_static_quantize_at_the_measured_amax():
+    g = np.random.Generator(np.random.PCG64(78))
+    x = oracle.bf16_round((g.standard_normal((300, 192)) * np.linspace(0.1, 5, 192)).astype(np.float32))
+    codes, scales, amax = oracle.nvfp4_quantize_dynamic(x)
+    assert amax == float(np.abs(oracle.bf16_to_f32(x)).max())
+    c2, s2 = oracle.nvfp4_quantize(x, amax)
+    assert np.array_equal(codes, c2) and np.array_equal(scales, s2)
+
+
+def test_dynamic_quantize_block_holding_the_max_gets_the_top_scale():
+    # gsf * (amax * fp32(1/6)) rounds to 448 for the block holding the global maximum, so
+    # its scale code is 0x7E and the maximal element encodes as magnitude 6 (code 7)
+    g = np.random.Generator(np.random.PCG64(79))
+    for trial in range(20):
+        x = oracle.bf16_round(g.standard_normal((8, 64)).astype(np.float32) * np.float32(10.0 ** g.uniform(-30, 30)))
+        codes, scales, amax = oracle.nvfp4_quantize_dynamic(x)
+        xf = oracle.bf16_to_f32(x)
+        r, c = np.unravel_index(int(np.argmax(np.abs(xf))), xf.shape)
+        b = c // 16
+        assert scales.reshape(-1)[oracle.scale_offset(r, b, 64)] == 0x7E
+        nib = (codes[r, c // 2] >> (4 * (c % 2))) & 0xF
+        assert nib & 0x7 == 7 and (nib >> 3) == (1 if xf[r, c] < 0 else 0)
+
+
+@pytest.mark.parametrize("pattern", [0x0000, 0x8000, 0x0001, 0x8005])
+def test_dynamic_quantize_all_zero_or_subnormal_tensor(pattern):
+    # an all-(+/-)zero tensor, and one whose amax is so small that 2688 / amax overflows:
+    # scale 0, so every code is the sign of the value and every scale byte is 0
+    x = np.full((130, 64), pattern, np.uint16)
+    x[::3, ::5] = 0x0000
+    codes, scales, amax = oracle.nvfp4_quantize_dynamic(x)
+    assert oracle.dynamic_global_scale(amax) == 0.0
+    sign = (x >> 15).astype(np.uint8) * 8
+    assert np.array_equal(codes, sign[:, 0::2] | (sign[:, 1::2] << 4))
+    assert not scales.any()
+
+
+def test_dynamic_rms_adaln_and_swiglu_are_static_at_their_own_amax():
+    g = np.random.Generator(np.random.PCG64(80))
+    m, k, t = 70, 1024, 3
+    x = oracle.bf16_round(g.standard_normal((m, k)).astype(np.float32))
+    w = oracle.bf16_round((1 + 0.1 * g.standard_normal(k)).astype(np.float32))
+    tab = oracle.bf16_round((0.1 * g.standard_normal((t, 2, k))).astype(np.float32))
+    idx = (np.arange(m) * t // m).astype(np.int32)
+    dyn = oracle.rms_adaln_dynamic(x, w, tab, idx, 1e-6, want_y=True, scales_rows=oracle.padded_rows(m))
+    assert dyn["amax"] == float(np.abs(oracle.bf16_to_f32(dyn["y"])).max())
+    st = oracle.rms_adaln_rows(x, w, tab, idx, 1e-6, dyn["amax"], scales_rows=oracle.padded_rows(m))
+    assert np.array_equal(dyn["codes"], st["codes"]) and np.array_equal(dyn["scales"], st["scales"])
+    assert (dyn["scale_bytes"] == 0x7E).any()
+
+    proj = oracle.bf16_round(g.standard_normal((m, 2 * 256)).astype(np.float32))
+    dyn = oracle.swiglu_dynamic(proj[:, :256], proj[:, 256:], want_y=True, scales_rows=oracle.padded_rows(m))
+    assert dyn["amax"] == float(np.abs(oracle.bf16_to_f32(dyn["y"])).max())
+    st = oracle.swiglu_rows(proj[:, :256], proj[:, 256:], dyn["amax"], scales_rows=oracle.padded_rows(m))
+    assert np.array_equal(dyn["codes"], st["codes"]) and np.array_equal(dyn["scales"], st["scales"])
+    assert (dyn["scale_bytes"] == 0x7E).any()
