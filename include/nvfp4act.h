@@ -155,6 +155,38 @@ int rms_adaln_nvfp4(const void* x, const void* weight, const void* shift, const 
 int swiglu_nvfp4(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f,
                  float global_amax, void* codes, void* scales, void* y_out, void* stream);
 
+/* Per-call (dynamic) global amax
+   ------------------------------
+   The *_dynamic forms take the global amax from the tensor itself instead of
+   a static calibration (FlashRT PR #142: NVFP4 W4A4 with a dynamic per-call
+   activation scale, a device-side amax pass then the quantize, no host sync;
+   FastVideo API page, NVFP4DecoderLinear act_scale="dynamic", per-call
+   abs-max).  Each call enqueues three kernels on `stream`: *amax_out = 0; an
+   amax pass that folds max |y| over all rows into *amax_out (y = the producer's
+   pre-quantization activation; rows with an out-of-range frame index count as
+   y = 0); the producer with the global scale computed on the device:
+     gsf = 2688 / *amax_out   if that is positive and finite,
+     gsf = 0                  otherwise (an all-zero tensor, or an amax so
+                              small that 2688 / amax overflows): every block
+                              scale is 0 and every code a signed zero.
+   The maximum is exact and order-free, so results do not depend on the launch.
+   amax_out is one float in device memory (4-byte aligned, required unless
+   m == 0; not written when m == 0).  The other arguments, outputs and status
+   codes are those of the static form; the producer's work is done twice (once
+   for the amax, once to quantize).  Calls that share one amax_out and overlap
+   on the device race on it. */
+int nvfp4_quantize_dynamic(const void* x, int64_t m, int64_t k, float* amax_out,
+                           void* codes, void* scales, void* stream);
+
+int rms_adaln_nvfp4_dynamic(const void* x, const void* weight, const void* shift, const void* scale,
+                            int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx,
+                            float eps, int64_t m, int64_t k, float* amax_out,
+                            void* codes, void* scales, float* rstd_out, void* y_out,
+                            uint32_t* status_word, void* stream);
+
+int swiglu_nvfp4_dynamic(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f,
+                         float* amax_out, void* codes, void* scales, void* y_out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

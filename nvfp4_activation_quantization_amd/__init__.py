@@ -10,7 +10,10 @@ Entry points (see ``include/nvfp4act.h`` for the exact contract):
   nvfp4_quantize(x, global_amax)                          standalone quantize
   rms_adaln_nvfp4(x, weight, table, frame_idx, eps, global_amax)
   swiglu_nvfp4(projection, global_amax)                   value-first [m, 2f]
-each returning ``(codes, scales)``: codes ``[m, k/2]`` uint8, scales
+each returning ``(codes, scales)``; and the per-call (dynamic) amax forms
+  nvfp4_quantize_dynamic(x), rms_adaln_nvfp4_dynamic(x, weight, table, frame_idx, eps),
+  swiglu_nvfp4_dynamic(projection)
+returning ``(codes, scales, amax)`` with ``amax`` a one-element float32 device tensor, codes ``[m, k/2]`` uint8, scales
 ``[pad(m), k/16]`` uint8 in the 128x4 swizzle (buffer shapes as the FastVideo
 API page's ``new_quantized``).
 """
@@ -42,6 +45,9 @@ _SIGS = {
     "nvfp4_quantize": (_I, [_P, _I64, _I64, _F, _P, _P, _P]),
     "rms_adaln_nvfp4": (_I, [_P, _P, _P, _P, _I64, _I64, _P, _F, _I64, _I64, _F, _P, _P, _P, _P, _P, _P]),
     "swiglu_nvfp4": (_I, [_P, _P, _I64, _I64, _I64, _F, _P, _P, _P, _P]),
+    "nvfp4_quantize_dynamic": (_I, [_P, _I64, _I64, _P, _P, _P, _P]),
+    "rms_adaln_nvfp4_dynamic": (_I, [_P, _P, _P, _P, _I64, _I64, _P, _F, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "swiglu_nvfp4_dynamic": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -127,6 +133,29 @@ def nvfp4_quantize(x: torch.Tensor, global_amax: float, codes=None, scales=None,
     return codes, scales
 
 
+def _amax_ptr(amax_out, device):
+    if amax_out is None:
+        amax_out = torch.empty(1, dtype=torch.float32, device=device)
+    if amax_out.dtype != torch.float32 or amax_out.numel() < 1 or not amax_out.is_cuda:
+        raise ValueError("amax_out must be a float32 device tensor with at least one element")
+    return amax_out, amax_out.data_ptr()
+
+
+def nvfp4_quantize_dynamic(x: torch.Tensor, amax_out=None, codes=None, scales=None, stream=None):
+    """Standalone NVFP4 quantize under the tensor's own amax (computed on the device)."""
+    m, k = x.shape
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if codes is None or scales is None:
+        codes, scales = new_quantized(m, k, x.device)
+    amax_out, ap = _amax_ptr(amax_out, x.device)
+    _check(_lib.nvfp4_quantize_dynamic(_bf16_ptr(x, "x"), m, k, ap,
+                                       _out_ptr(codes, torch.uint8, (m, k // 2), "codes"),
+                                       _out_ptr(scales, torch.uint8, (padded_rows(m), k // 16), "scales"),
+                                       _stream(stream, x.device)))
+    return codes, scales, amax_out
+
+
 def rms_adaln_nvfp4(x: torch.Tensor, weight: torch.Tensor, table: torch.Tensor, frame_idx: torch.Tensor,
                     eps: float, global_amax: float, codes=None, scales=None, rstd_out=None, y_out=None,
                     status_word=None, stream=None):
@@ -162,6 +191,38 @@ def rms_adaln_nvfp4(x: torch.Tensor, weight: torch.Tensor, table: torch.Tensor, 
     return codes, scales
 
 
+def rms_adaln_nvfp4_dynamic(x: torch.Tensor, weight: torch.Tensor, table: torch.Tensor, frame_idx: torch.Tensor,
+                            eps: float, amax_out=None, codes=None, scales=None, rstd_out=None, y_out=None,
+                            status_word=None, stream=None):
+    """Fused RMSNorm + adaLN -> NVFP4 under the amax of this call's own y (computed on the
+    device by an amax pass).  Arguments as rms_adaln_nvfp4 without global_amax."""
+    m, k = x.shape
+    if not x.is_contiguous() or not table.is_contiguous() or not weight.is_contiguous():
+        raise ValueError("x, weight and table must be contiguous")
+    if table.dim() != 3 or table.shape[1] != 2 or table.shape[2] != k:
+        raise ValueError("table must be [T, 2, k]")
+    if frame_idx.dtype != torch.int32 or not frame_idx.is_contiguous() or frame_idx.numel() != m:
+        raise ValueError("frame_idx must be a contiguous int32 tensor of m elements")
+    if codes is None or scales is None:
+        codes, scales = new_quantized(m, k, x.device)
+    amax_out, ap = _amax_ptr(amax_out, x.device)
+    tab = _bf16_ptr(table, "table")
+    sw = 0
+    if status_word is not None:
+        if status_word.dtype not in (torch.int32, torch.uint32) or not status_word.is_cuda:
+            raise ValueError("status_word must be a 32-bit device tensor")
+        sw = status_word.data_ptr()
+    _check(_lib.rms_adaln_nvfp4_dynamic(
+        _bf16_ptr(x, "x"), _bf16_ptr(weight, "weight"), tab, tab + 2 * k, 2 * k, table.shape[0],
+        frame_idx.data_ptr(), float(eps), m, k, ap,
+        _out_ptr(codes, torch.uint8, (m, k // 2), "codes"),
+        _out_ptr(scales, torch.uint8, (padded_rows(m), k // 16), "scales"),
+        _out_ptr(rstd_out, torch.float32, (m,), "rstd_out"),
+        _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, k), "y_out") if y_out is not None else 0,
+        sw, _stream(stream, x.device)))
+    return codes, scales, amax_out
+
+
 def swiglu_nvfp4(projection: torch.Tensor, global_amax: float, codes=None, scales=None, y_out=None,
                  gate: torch.Tensor | None = None, stream=None):
     """SwiGLU -> NVFP4.
@@ -195,3 +256,35 @@ def swiglu_nvfp4(projection: torch.Tensor, global_amax: float, codes=None, scale
                              if y_out is not None else 0,
                              _stream(stream, projection.device)))
     return codes, scales
+
+
+def swiglu_nvfp4_dynamic(projection: torch.Tensor, amax_out=None, codes=None, scales=None, y_out=None,
+                         gate: torch.Tensor | None = None, stream=None):
+    """SwiGLU -> NVFP4 under the amax of this call's own y (computed on the device).
+    Arguments as swiglu_nvfp4 without global_amax."""
+    if gate is None:
+        m, two_f = projection.shape
+        f = two_f // 2
+        if not projection.is_contiguous():
+            raise ValueError("projection must be contiguous")
+        up_ptr = _bf16_ptr(projection, "projection")
+        gate_ptr = up_ptr + 2 * f
+        ld = two_f
+    else:
+        m, f = projection.shape
+        if gate.shape != projection.shape or projection.stride(1) != 1 or gate.stride(1) != 1 \
+                or projection.stride(0) != gate.stride(0):
+            raise ValueError("up and gate must be [m, f] views with unit column stride and equal row stride")
+        up_ptr = _bf16_ptr(projection, "up")
+        gate_ptr = _bf16_ptr(gate, "gate")
+        ld = projection.stride(0)
+    if codes is None or scales is None:
+        codes, scales = new_quantized(m, f, projection.device)
+    amax_out, ap = _amax_ptr(amax_out, projection.device)
+    _check(_lib.swiglu_nvfp4_dynamic(up_ptr, gate_ptr, ld, m, f, ap,
+                                     _out_ptr(codes, torch.uint8, (m, f // 2), "codes"),
+                                     _out_ptr(scales, torch.uint8, (padded_rows(m), f // 16), "scales"),
+                                     _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, f), "y_out")
+                                     if y_out is not None else 0,
+                                     _stream(stream, projection.device)))
+    return codes, scales, amax_out

@@ -130,67 +130,157 @@ int nvfp4act_init(void) {
   return ensure_silu_table(dev);
 }
 
-int nvfp4_quantize(const void* x, int64_t m, int64_t k, float global_amax, void* codes, void* scales,
-                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// The checks and launches shared by the static (amax_dev == nullptr) and per-call
+// (amax_dev: the device float receiving the call's amax) forms of each entry point.
+int quantize_call(const void* x, int64_t m, int64_t k, float global_amax, float* amax_dev, void* codes,
+                  void* scales, void* stream) {
   if (m < 0 || k <= 0 || k % 64 != 0) return NVFP4ACT_ERR_SHAPE;
   if (m == 0) return NVFP4ACT_OK;
   if (!x || !codes || !scales) return NVFP4ACT_ERR_NULL;
   if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return NVFP4ACT_ERR_ALIGN;
-  int st = check_amax(global_amax);
-  if (st != NVFP4ACT_OK) return st;
+  if (!amax_dev) {
+    int st = check_amax(global_amax);
+    if (st != NVFP4ACT_OK) return st;
+  }
   const DeviceInfo* info = nullptr;
-  st = current_device(&info, nullptr);
+  int st = current_device(&info, nullptr);
   if (st != NVFP4ACT_OK) return st;
-  hipError_t e = nvfp4act::launch_quantize(x, m, k, global_amax, codes, scales,
-                                           static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (amax_dev) {
+    e = nvfp4act::launch_zero_amax(amax_dev, s);
+    if (e == hipSuccess) e = nvfp4act::launch_amax_x(x, m, k, amax_dev, *info, s);
+  }
+  if (e == hipSuccess) e = nvfp4act::launch_quantize(x, m, k, global_amax, amax_dev, codes, scales, s);
   return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
 }
 
-int rms_adaln_nvfp4(const void* x, const void* weight, const void* shift, const void* scale,
-                    int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx, float eps,
-                    int64_t m, int64_t k, float global_amax, void* codes, void* scales, float* rstd_out,
-                    void* y_out, uint32_t* status_word, void* stream) {
+int rms_adaln_call(const void* x, const void* weight, const void* shift, const void* scale, int64_t frame_stride,
+                   int64_t num_frames, const int32_t* frame_idx, float eps, int64_t m, int64_t k,
+                   float global_amax, float* amax_dev, void* codes, void* scales, float* rstd_out, void* y_out,
+                   uint32_t* status_word, void* stream) {
   if (m < 0 || k <= 0 || k % 512 != 0 || num_frames < 1 || frame_stride < k) return NVFP4ACT_ERR_SHAPE;
   if (m == 0) return NVFP4ACT_OK;
   if (!x || !weight || !shift || !scale || !frame_idx || !codes || !scales) return NVFP4ACT_ERR_NULL;
   if (!aligned16(x) || !aligned16(weight) || !aligned16(shift) || !aligned16(scale) ||
       !aligned16(codes) || !aligned16(scales) || (frame_stride * 2) % 16 != 0 ||
-      (rstd_out && (reinterpret_cast<uintptr_t>(rstd_out) & 3u)) || (y_out && !aligned16(y_out)) ||
-      (reinterpret_cast<uintptr_t>(frame_idx) & 3u) ||
-      (status_word && (reinterpret_cast<uintptr_t>(status_word) & 3u)))
+      (rstd_out && !aligned4(rstd_out)) || (y_out && !aligned16(y_out)) || !aligned4(frame_idx) ||
+      (status_word && !aligned4(status_word)))
     return NVFP4ACT_ERR_ALIGN;
-  int st = check_amax(global_amax);
-  if (st != NVFP4ACT_OK) return st;
+  if (!amax_dev) {
+    int st = check_amax(global_amax);
+    if (st != NVFP4ACT_OK) return st;
+  }
   if (!std::isfinite(eps) || eps < 0.0f) return NVFP4ACT_ERR_VALUE;
   const DeviceInfo* info = nullptr;
-  st = current_device(&info, nullptr);
+  int st = current_device(&info, nullptr);
   if (st != NVFP4ACT_OK) return st;
-  hipError_t e = nvfp4act::launch_rms_adaln(x, weight, shift, scale, frame_stride, num_frames,
-                                            frame_idx, eps, m, k, global_amax, codes, scales,
-                                            rstd_out, y_out, status_word, *info,
-                                            static_cast<hipStream_t>(stream));
+  nvfp4act::RmsLaunch p;
+  p.x = x;
+  p.weight = weight;
+  p.shift = shift;
+  p.scale = scale;
+  p.frame_stride = frame_stride;
+  p.num_frames = num_frames;
+  p.frame_idx = frame_idx;
+  p.eps = eps;
+  p.m = m;
+  p.k = k;
+  p.global_amax = global_amax;
+  p.amax_dev = amax_dev;
+  p.codes = codes;
+  p.scales = scales;
+  p.rstd_out = rstd_out;
+  p.y_out = y_out;
+  p.status_word = status_word;
+  hipError_t e = nvfp4act::launch_rms_adaln(p, *info, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
 }
 
-int swiglu_nvfp4(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f, float global_amax,
-                 void* codes, void* scales, void* y_out, void* stream) {
+int swiglu_call(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f, float global_amax,
+                float* amax_dev, void* codes, void* scales, void* y_out, void* stream) {
   if (m < 0 || f <= 0 || f % 64 != 0 || ld < f) return NVFP4ACT_ERR_SHAPE;
   if (m == 0) return NVFP4ACT_OK;
   if (!up || !gate || !codes || !scales) return NVFP4ACT_ERR_NULL;
   if (!aligned16(up) || !aligned16(gate) || !aligned16(codes) || !aligned16(scales) ||
       (ld * 2) % 16 != 0 || (y_out && !aligned16(y_out)))
     return NVFP4ACT_ERR_ALIGN;
-  int st = check_amax(global_amax);
-  if (st != NVFP4ACT_OK) return st;
+  if (!amax_dev) {
+    int st = check_amax(global_amax);
+    if (st != NVFP4ACT_OK) return st;
+  }
   const DeviceInfo* info = nullptr;
   int dev = -1;
-  st = current_device(&info, &dev);
+  int st = current_device(&info, &dev);
   if (st != NVFP4ACT_OK) return st;
   st = ensure_silu_table(dev);
   if (st != NVFP4ACT_OK) return st;
-  hipError_t e = nvfp4act::launch_swiglu(up, gate, ld, m, f, global_amax, codes, scales, y_out, *info,
+  hipError_t e = nvfp4act::launch_swiglu(up, gate, ld, m, f, global_amax, amax_dev, codes, scales, y_out, *info,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
+}
+
+// The per-call forms need the amax destination: one 4-byte aligned float (m == 0 aside).
+int check_amax_out(int64_t m, const float* amax_out) {
+  if (m == 0) return NVFP4ACT_OK;
+  if (!amax_out) return NVFP4ACT_ERR_NULL;
+  if (!aligned4(amax_out)) return NVFP4ACT_ERR_ALIGN;
+  return NVFP4ACT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_quantize(const void* x, int64_t m, int64_t k, float global_amax, void* codes, void* scales,
+                   void* stream) {
+  return quantize_call(x, m, k, global_amax, nullptr, codes, scales, stream);
+}
+
+int nvfp4_quantize_dynamic(const void* x, int64_t m, int64_t k, float* amax_out, void* codes, void* scales,
+                           void* stream) {
+  if (m < 0 || k <= 0 || k % 64 != 0) return NVFP4ACT_ERR_SHAPE;
+  int st = check_amax_out(m, amax_out);
+  if (st != NVFP4ACT_OK) return st;
+  return quantize_call(x, m, k, 0.0f, amax_out, codes, scales, stream);
+}
+
+int rms_adaln_nvfp4(const void* x, const void* weight, const void* shift, const void* scale,
+                    int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx, float eps,
+                    int64_t m, int64_t k, float global_amax, void* codes, void* scales, float* rstd_out,
+                    void* y_out, uint32_t* status_word, void* stream) {
+  return rms_adaln_call(x, weight, shift, scale, frame_stride, num_frames, frame_idx, eps, m, k, global_amax,
+                        nullptr, codes, scales, rstd_out, y_out, status_word, stream);
+}
+
+int rms_adaln_nvfp4_dynamic(const void* x, const void* weight, const void* shift, const void* scale,
+                            int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx, float eps,
+                            int64_t m, int64_t k, float* amax_out, void* codes, void* scales, float* rstd_out,
+                            void* y_out, uint32_t* status_word, void* stream) {
+  if (m < 0 || k <= 0 || k % 512 != 0 || num_frames < 1 || frame_stride < k) return NVFP4ACT_ERR_SHAPE;
+  int st = check_amax_out(m, amax_out);
+  if (st != NVFP4ACT_OK) return st;
+  return rms_adaln_call(x, weight, shift, scale, frame_stride, num_frames, frame_idx, eps, m, k, 0.0f, amax_out,
+                        codes, scales, rstd_out, y_out, status_word, stream);
+}
+
+int swiglu_nvfp4(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f, float global_amax,
+                 void* codes, void* scales, void* y_out, void* stream) {
+  return swiglu_call(up, gate, ld, m, f, global_amax, nullptr, codes, scales, y_out, stream);
+}
+
+int swiglu_nvfp4_dynamic(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f, float* amax_out,
+                         void* codes, void* scales, void* y_out, void* stream) {
+  if (m < 0 || f <= 0 || f % 64 != 0 || ld < f) return NVFP4ACT_ERR_SHAPE;
+  int st = check_amax_out(m, amax_out);
+  if (st != NVFP4ACT_OK) return st;
+  return swiglu_call(up, gate, ld, m, f, 0.0f, amax_out, codes, scales, y_out, stream);
 }
 
 }  // extern "C"

@@ -124,6 +124,21 @@ __device__ __forceinline__ float max_abs2(float t, float b, float c) {
 // gsf = 2688 / global_amax, IEEE fp32 (every lane computes the same value).
 __device__ __forceinline__ float global_scale(float global_amax) { return 2688.0f / global_amax; }
 
+// Global scale of a per-call amax measured on the tensor (FlashRT dynamic per-call
+// activation scale; FastVideo API page, NVFP4DecoderLinear act_scale="dynamic"): 2688 / a
+// when that is positive and finite, else 0 (every block scale 0, every code a signed zero).
+__device__ __forceinline__ float dynamic_global_scale(float a) {
+  if (!(a > 0.0f)) return 0.0f;
+  const float g = 2688.0f / a;
+  return __builtin_isfinite(g) ? g : 0.0f;
+}
+
+// The global scale of a call: from the static amax, or, when amax_dev is not null, from
+// the amax a preceding pass left in device memory.
+__device__ __forceinline__ float call_global_scale(float global_amax, const float* amax_dev) {
+  return amax_dev ? dynamic_global_scale(*global_ptr(amax_dev)) : global_scale(global_amax);
+}
+
 // Fill inv[0..127] with gsf / dec(s) (0 for s == 0); needs a barrier before use.
 __device__ __forceinline__ void fill_inverse_table(float* inv, float gsf, int tid) {
   if (tid < 128) inv[tid] = (tid == 0) ? 0.0f : gsf / e4m3_value((uint32_t)tid);
@@ -192,6 +207,35 @@ __device__ __forceinline__ void zero_row_scales(uint8_t* scales, int64_t r, int6
   NVFP4_GLOBAL uint8_t* base = global_ptr(scales) + row_scale_base(r, k);
   for (int64_t q = lane; q < (k >> 6); q += kWave)
     *reinterpret_cast<NVFP4_GLOBAL uint32_t*>(base + q * 512) = 0u;
+}
+
+// ---- amax reduction --------------------------------------------------------------------
+
+// max(|a|, |b|, ..) of the eight values of a chunk folded into t (t >= 0).
+__device__ __forceinline__ float fold_abs8(float t, const float* y) {
+  t = max_abs2(t, y[0], y[1]);
+  t = max_abs2(t, y[2], y[3]);
+  t = max_abs2(t, y[4], y[5]);
+  return max_abs2(t, y[6], y[7]);
+}
+
+// Workgroup maximum of the non-negative values v, folded into *dst with one device-scope
+// atomic max per workgroup (the maximum is exact and order-free, so the result does not
+// depend on which workgroup arrives first).  red: `waves` floats of LDS.  Every thread of
+// the workgroup must call it.
+__device__ __forceinline__ void workgroup_max_to(float* dst, float v, float* red, int waves) {
+  uint32_t u = __float_as_uint(v);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) u = __builtin_elementwise_max(u, (uint32_t)__shfl_xor((int)u, d));
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  if (lane == 0) red[wave] = __uint_as_float(u);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    for (int w = 0; w < waves; ++w) m = __builtin_elementwise_max(m, __float_as_uint(red[w]));
+    __hip_atomic_fetch_max(reinterpret_cast<NVFP4_GLOBAL uint32_t*>(global_ptr(dst)), m, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---- streaming loads ------------------------------------------------------------------

@@ -12,17 +12,42 @@ struct DeviceInfo {
   int cu_count;
 };
 
-hipError_t launch_quantize(const void* x, int64_t m, int64_t k, float global_amax, void* codes,
-                           void* scales, hipStream_t stream);
+// amax_dev: null for a static global_amax, else the device float an amax pass wrote (the
+// global scale is then computed on the device from it).
+hipError_t launch_quantize(const void* x, int64_t m, int64_t k, float global_amax, const float* amax_dev,
+                           void* codes, void* scales, hipStream_t stream);
 
-hipError_t launch_rms_adaln(const void* x, const void* weight, const void* shift, const void* scale,
-                            int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx,
-                            float eps, int64_t m, int64_t k, float global_amax, void* codes,
-                            void* scales, float* rstd_out, void* y_out, uint32_t* status_word,
-                            const DeviceInfo& dev, hipStream_t stream);
+// *amax = 0, then max |x| over the m x k tensor folded into it.
+hipError_t launch_zero_amax(float* amax, hipStream_t stream);
+hipError_t launch_amax_x(const void* x, int64_t m, int64_t k, float* amax, const DeviceInfo& dev,
+                         hipStream_t stream);
 
+// The arguments of one rms_adaln_nvfp4 call (see include/nvfp4act.h).  amax_dev: null for
+// the static global_amax; else the device float that receives max |y| of this call (an
+// amax pass runs first and the quantizer takes its global scale from it).
+struct RmsLaunch {
+  const void* x;
+  const void* weight;
+  const void* shift;
+  const void* scale;
+  int64_t frame_stride, num_frames;
+  const int32_t* frame_idx;
+  float eps;
+  int64_t m, k;
+  float global_amax;
+  float* amax_dev;
+  void* codes;
+  void* scales;
+  float* rstd_out;
+  void* y_out;
+  uint32_t* status_word;
+};
+
+hipError_t launch_rms_adaln(const RmsLaunch& p, const DeviceInfo& dev, hipStream_t stream);
+
+// amax_dev: as for RmsLaunch (null: static global_amax; else the per-call amax of y).
 hipError_t launch_swiglu(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f,
-                         float global_amax, void* codes, void* scales, void* y_out,
+                         float global_amax, float* amax_dev, void* codes, void* scales, void* y_out,
                          const DeviceInfo& dev, hipStream_t stream);
 
 // Per-device, once: allow the LDS sizes the kernels use.

@@ -77,7 +77,8 @@ __device__ __forceinline__ void quantize_piece(const uint4* v, NVFP4_GLOBAL uint
 
 template <int SLOTS>
 __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint4* __restrict__ x, int64_t m, int64_t k,
-                                                            float global_amax, uint32_t* __restrict__ codes,
+                                                            float global_amax, const float* amax_dev,
+                                                            uint32_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
   constexpr int kPieceChunks = kWave * SLOTS;       // chunks per row piece
   constexpr int kPieceUnits = kPieceChunks / 8;     // 16-byte units per row-group piece
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint4* __restr
   // the first piece is in flight while the inverse-scale table is built
   uint4 v[SLOTS];
   if (r < m) load_piece<SLOTS>(xr, 0, chunks, lane, v);
-  const float gsf = global_scale(global_amax);
+  const float gsf = call_global_scale(global_amax, amax_dev);
   fill_inverse_table(inv_tab, gsf, tid);
   for (int i = tid; i < kPieceUnits; i += kThreads) units[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
@@ -122,42 +123,92 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint4* __restr
 }
 
 template <int SLOTS>
-hipError_t launch_slots(const uint4* x, int64_t m, int64_t k, float global_amax, uint32_t* codes, uint8_t* scales,
-                        hipStream_t stream) {
+hipError_t launch_slots(const uint4* x, int64_t m, int64_t k, float global_amax, const float* amax_dev,
+                        uint32_t* codes, uint8_t* scales, hipStream_t stream) {
   const int64_t ntiles = (m + 127) / 128;
   const int64_t unit_groups = ntiles * 4;
   const int64_t blocks = (unit_groups + 7) / 8 * 64;
   hipLaunchKernelGGL((quantize_kernel<SLOTS>), dim3((uint32_t)blocks), dim3(kThreads), 0, stream, x, m, k,
-                     global_amax, codes, scales);
+                     global_amax, amax_dev, codes, scales);
   return hipGetLastError();
+}
+
+// ---- the amax pass of the per-call scale: max |x| over the tensor ----------------------
+//
+// A read-only stream over all m * k / 8 chunks (16-byte loads, kAmaxUnroll per thread in
+// flight), a few workgroups per CU striding over the tensor; each workgroup folds its
+// maximum into *amax with one atomic.
+constexpr int kAmaxThreads = 512;
+constexpr int kAmaxUnroll = 8;
+
+__global__ __launch_bounds__(kAmaxThreads) void amax_x_kernel(const uint4* __restrict__ x, int64_t chunks,
+                                                              float* amax) {
+  __shared__ float red[kAmaxThreads / kWave];
+  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+  float t = 0.0f;
+  for (int64_t c = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; c < chunks; c += stride * kAmaxUnroll) {
+    uint4 v[kAmaxUnroll];
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u)
+      v[u] = (c + stride * u < chunks) ? load_stream(x + c + stride * u) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < kAmaxUnroll; ++u) {
+      const float y[8] = {bf16_lo(v[u].x), bf16_hi(v[u].x), bf16_lo(v[u].y), bf16_hi(v[u].y),
+                          bf16_lo(v[u].z), bf16_hi(v[u].z), bf16_lo(v[u].w), bf16_hi(v[u].w)};
+      t = fold_abs8(t, y);
+    }
+  }
+  workgroup_max_to(amax, t, red, kAmaxThreads / kWave);
+}
+
+// *amax = 0 (the start of an amax pass), as a kernel so that the call stays capturable.
+__global__ void zero_amax_kernel(float* amax) {
+  if (threadIdx.x == 0) *global_ptr(amax) = 0.0f;
 }
 
 }  // namespace
 
-hipError_t launch_quantize(const void* x, int64_t m, int64_t k, float global_amax, void* codes,
-                           void* scales, hipStream_t stream) {
+hipError_t launch_zero_amax(float* amax, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_amax_kernel, dim3(1), dim3(64), 0, stream, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_amax_x(const void* x, int64_t m, int64_t k, float* amax, const DeviceInfo& dev,
+                         hipStream_t stream) {
+  const int64_t chunks = m * (k / 8);
+  const int64_t per_block = (int64_t)kAmaxThreads * kAmaxUnroll;
+  int64_t blocks = (chunks + per_block - 1) / per_block;
+  const int64_t cap = (int64_t)dev.cu_count * 2;
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL(amax_x_kernel, dim3((uint32_t)blocks), dim3(kAmaxThreads), 0, stream,
+                     static_cast<const uint4*>(x), chunks, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const void* x, int64_t m, int64_t k, float global_amax, const float* amax_dev,
+                           void* codes, void* scales, hipStream_t stream) {
   const uint4* xv = static_cast<const uint4*>(x);
   uint32_t* cv = static_cast<uint32_t*>(codes);
   uint8_t* sv = static_cast<uint8_t*>(scales);
   // chunk slots per lane: the whole row when it has at most 1024 chunks, else pieces of 16
   const int64_t slots = (k / 8 + kWave - 1) / kWave;
   switch (slots < kPieceSlots ? slots : kPieceSlots) {
-    case 1: return launch_slots<1>(xv, m, k, global_amax, cv, sv, stream);
-    case 2: return launch_slots<2>(xv, m, k, global_amax, cv, sv, stream);
-    case 3: return launch_slots<3>(xv, m, k, global_amax, cv, sv, stream);
-    case 4: return launch_slots<4>(xv, m, k, global_amax, cv, sv, stream);
-    case 5: return launch_slots<5>(xv, m, k, global_amax, cv, sv, stream);
-    case 6: return launch_slots<6>(xv, m, k, global_amax, cv, sv, stream);
-    case 7: return launch_slots<7>(xv, m, k, global_amax, cv, sv, stream);
-    case 8: return launch_slots<8>(xv, m, k, global_amax, cv, sv, stream);
-    case 9: return launch_slots<9>(xv, m, k, global_amax, cv, sv, stream);
-    case 10: return launch_slots<10>(xv, m, k, global_amax, cv, sv, stream);
-    case 11: return launch_slots<11>(xv, m, k, global_amax, cv, sv, stream);
-    case 12: return launch_slots<12>(xv, m, k, global_amax, cv, sv, stream);
-    case 13: return launch_slots<13>(xv, m, k, global_amax, cv, sv, stream);
-    case 14: return launch_slots<14>(xv, m, k, global_amax, cv, sv, stream);
-    case 15: return launch_slots<15>(xv, m, k, global_amax, cv, sv, stream);
-    default: return launch_slots<16>(xv, m, k, global_amax, cv, sv, stream);
+    case 1: return launch_slots<1>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 2: return launch_slots<2>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 3: return launch_slots<3>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 4: return launch_slots<4>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 5: return launch_slots<5>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 6: return launch_slots<6>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 7: return launch_slots<7>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 8: return launch_slots<8>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 9: return launch_slots<9>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 10: return launch_slots<10>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 11: return launch_slots<11>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 12: return launch_slots<12>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 13: return launch_slots<13>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 14: return launch_slots<14>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    case 15: return launch_slots<15>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
+    default: return launch_slots<16>(xv, m, k, global_amax, amax_dev, cv, sv, stream);
   }
 }
 

@@ -41,6 +41,8 @@ struct RmsArgs {
   float* rstd_out;
   uint4* y_out;
   uint32_t* status;
+  const float* amax_dev;   // per-call scale: the amax pass's result (null: static global_amax)
+  float* amax_out;         // the amax pass: where max |y| is folded
 };
 
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
@@ -182,13 +184,15 @@ __device__ __forceinline__ void load_frame_chunk(const RmsArgs& a, int64_t t, in
 
 // A row whose frame is not the staged one: re-read x (an L2 hit in practice) and the
 // frame's modulation row from global memory, one chunk at a time.  Out of line and with
-// plain arguments, so the kernel's hot loop is not shaped by this rare path.
-__device__ __noinline__ void emit_row_unstaged(const uint4* x, const uint16_t* shift, const uint16_t* scale,
-                                               int64_t frame_stride, RowOut o, int64_t k, int64_t r, int64_t t,
-                                               const float2* wp, float rstd, float gsf,
-                                               const float* inv_tab, bool tile) {
+// plain arguments, so the kernel's hot loop is not shaped by this rare path.  In the amax
+// pass (amax_only) nothing is stored and the lane's max |y| is returned (else 0).
+__device__ __noinline__ float emit_row_unstaged(const uint4* x, const uint16_t* shift, const uint16_t* scale,
+                                                int64_t frame_stride, RowOut o, int64_t k, int64_t r, int64_t t,
+                                                const float2* wp, float rstd, float gsf,
+                                                const float* inv_tab, bool tile, bool amax_only) {
   const int lane = threadIdx.x & (kWave - 1);
   const NVFP4_GLOBAL uint4* xr = global_ptr(x) + r * (k >> 3);
+  float lane_amax = 0.0f;
 #pragma unroll 1
   for (int j = 0; j < (int)(k >> 9); ++j) {
     const int64_t c = lane + (int64_t)kWave * j;
@@ -198,8 +202,10 @@ __device__ __noinline__ void emit_row_unstaged(const uint4* x, const uint16_t* s
     split8(wp[c], wp[chunks + c], wp[2 * chunks + c], wp[3 * chunks + c], w8);
     load_frame_chunk(shift, scale, frame_stride, t, c, o8, h8);
     modulate8(x8, w8, o8, h8, rstd, y);
-    store_chunk(o, j, y, gsf, inv_tab, tile);
+    if (amax_only) lane_amax = fold_abs8(lane_amax, y);
+    else store_chunk(o, j, y, gsf, inv_tab, tile);
   }
+  return lane_amax;
 }
 
 // The float2 at byte offset base + off of the dynamic LDS block.
@@ -262,8 +268,13 @@ __device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr,
 
 constexpr int kStagedWaves = 8;
 
-template <int CPL, bool Y, bool TILE>
+// AMAX: the amax pass of a per-call scale -- the same rows and chain, no quantizer and no
+// stores; each workgroup folds its max |y| into a.amax_out (rows with an out-of-range frame
+// have y = 0 and contribute nothing).
+template <int CPL, bool Y, bool TILE, bool AMAX>
 __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs a, const int32_t* __restrict__ frame_idx) {
+  static_assert(!(AMAX && (TILE || Y)), "the amax pass writes no outputs");
+  __shared__ float amax_red[kStagedWaves];
   constexpr int WAVES = kStagedWaves;
   constexpr int kThreads = WAVES * kWave;
   constexpr int kRowsPerWave = 128 / WAVES;
@@ -302,7 +313,8 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
     load_row<CPL>(xr, x + (r0 < m ? r0 : m - 1) * kChunks, lane);
   }
 
-  const float gsf = global_scale(a.global_amax);
+  const float gsf = call_global_scale(a.global_amax, a.amax_dev);
+  float lane_amax = 0.0f;
   fill_inverse_table(inv_tab, gsf, tid);
   for (int c = tid; c < kChunks; c += kThreads) {
     float f[8];
@@ -338,7 +350,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
       }
       const int64_t r = g + wave;
       if (r >= m) {                        // a padding row (and so is every later row)
-        if (!TILE) zero_row_scales(a.scales, r, kK, lane);   // TILE: already zero in LDS
+        if (!TILE && !AMAX) zero_row_scales(a.scales, r, kK, lane);   // TILE: already zero in LDS
         continue;
       }
       // this wavefront's next row (prefetched right after the statistic)
@@ -358,18 +370,19 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
       const float sum = lane_sum_butterfly(((acc[0] + acc[1]) + (acc[2] + acc[3])) +
                                            ((acc[4] + acc[5]) + (acc[6] + acc[7])));
       const float rstd = 1.0f / sqrtf(sum / (float)kK + a.eps);
-      if (lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
+      if (!AMAX && lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
       const int64_t t = frame_idx[r];
       if (t < 0 || t >= a.num_frames) {
-        zero_row(a, r, lane, !TILE);
+        if (!AMAX) zero_row(a, r, lane, !TILE);
         continue;
       }
       RowOut o = row_out(a, r, lane);
       if (TILE) o.scales_lds = reinterpret_cast<uint8_t*>(tile_sc) + (row_scale_base(r, kK) & 511) +
                                (lane >> 3) * 528 + ((lane >> 1) & 3);
       if (t != staged) {
-        emit_row_unstaged(a.x, a.shift, a.scale, a.frame_stride, o, kK, r, t, wp, rstd, gsf, inv_tab,
-                          TILE);
+        const float u = emit_row_unstaged(a.x, a.shift, a.scale, a.frame_stride, o, kK, r, t, wp, rstd, gsf,
+                                          inv_tab, TILE, AMAX);
+        lane_amax = __builtin_fmaxf(lane_amax, u);
         continue;
       }
       // Output pass, software-pipelined over the lane's chunks: the parameters of chunk j + 1
@@ -389,6 +402,14 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
         split8(pc[4], pc[5], pc[6], pc[7], o8);
         split8(pc[8], pc[9], pc[10], pc[11], h8);
         modulate8(xf[j], w8, o8, h8, rstd, y);
+        if (AMAX) {
+          lane_amax = fold_abs8(lane_amax, y);
+          if (j + 1 < CPL) {
+#pragma unroll
+            for (int q = 0; q < 12; ++q) pc[q] = pn[q];
+          }
+          continue;
+        }
         const uint32_t s = block_scale_code(y, gsf);
         const float inv = inv_tab[s];
         if (j > 0) emit_encoded<Y, TILE>(o, j - 1, yp, invp, sp);
@@ -401,7 +422,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
           for (int q = 0; q < 12; ++q) pc[q] = pn[q];
         }
       }
-      emit_encoded<Y, TILE>(o, CPL - 1, yp, invp, sp);
+      if (!AMAX) emit_encoded<Y, TILE>(o, CPL - 1, yp, invp, sp);
     }
     if (TILE) {
       // the tile's scale block is complete: copy it out and zero it for the next tile (each
@@ -415,24 +436,19 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
       __syncthreads();
     }
   }
+  if (AMAX) workgroup_max_to(a.amax_out, lane_amax, amax_red, kStagedWaves);
 }
 
 // ---- the general kernel (any k % 512 == 0): parameters from global memory, two passes ----
 
-__global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
-  __shared__ float inv_tab[128];
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+// Row r of the general kernel; returns the lane's max |y| in the amax pass (else 0).
+template <bool AMAX>
+__device__ __forceinline__ float general_row(const RmsArgs& a, int64_t r, int lane, float gsf, const float* inv_tab) {
   const int64_t chunks = a.k >> 3;
-  const float gsf = global_scale(a.global_amax);
-  fill_inverse_table(inv_tab, gsf, tid);
-  __syncthreads();
-  const int64_t r = (int64_t)blockIdx.x * 4 + wave;
-  if (r >= a.padded) return;
+  if (r >= a.padded) return 0.0f;
   if (r >= a.m) {
-    zero_row_scales(a.scales, r, a.k, lane);
-    return;
+    if (!AMAX) zero_row_scales(a.scales, r, a.k, lane);
+    return 0.0f;
   }
   const NVFP4_GLOBAL uint4* xr = global_ptr(a.x) + r * chunks;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -445,13 +461,14 @@ __global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
   const float s = lane_sum_butterfly(((acc[0] + acc[1]) + (acc[2] + acc[3])) +
                                      ((acc[4] + acc[5]) + (acc[6] + acc[7])));
   const float rstd = 1.0f / sqrtf(s / (float)a.k + a.eps);
-  if (lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
+  if (!AMAX && lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
   const int64_t t = global_ptr(a.frame_idx)[r];
   if (t < 0 || t >= a.num_frames) {
-    zero_row(a, r, lane, true);
-    return;
+    if (!AMAX) zero_row(a, r, lane, true);
+    return 0.0f;
   }
   const RowOut o = row_out(a, r, lane);
+  float lane_amax = 0.0f;
   for (int j = 0; j < (int)(chunks >> 6); ++j) {
     const int64_t c = lane + (int64_t)kWave * j;
     float x8[8], w8[8], o8[8], h8[8], y[8];
@@ -459,47 +476,94 @@ __global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
     unpack8(*reinterpret_cast<const NVFP4_GLOBAL uint4*>(global_ptr(a.w) + 8 * c), w8);
     load_frame_chunk(a, t, c, o8, h8);
     modulate8(x8, w8, o8, h8, rstd, y);
-    store_chunk(o, j, y, gsf, inv_tab, false);
+    if (AMAX) lane_amax = fold_abs8(lane_amax, y);
+    else store_chunk(o, j, y, gsf, inv_tab, false);
   }
+  return lane_amax;
+}
+
+template <bool AMAX>
+__global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
+  __shared__ float inv_tab[128];
+  __shared__ float amax_red[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const float gsf = call_global_scale(a.global_amax, a.amax_dev);
+  fill_inverse_table(inv_tab, gsf, tid);
+  __syncthreads();
+  const float lane_amax = general_row<AMAX>(a, (int64_t)blockIdx.x * 4 + wave, lane, gsf, inv_tab);
+  if (AMAX) workgroup_max_to(a.amax_out, lane_amax, amax_red, 4);
 }
 
 // The tile's scale block (128 rows x k/16 bytes) is staged in LDS when it fits beside the
 // parameters (k <= 7680).
-constexpr size_t kLdsLimit = 160 * 1024;
+// Dynamic LDS cap: the 160 KiB of a CU less a little for the kernels' static arrays.
+constexpr size_t kLdsLimit = 160 * 1024 - 256;
 inline size_t staged_lds_bytes(int64_t k, bool tile) {
   return 512 + 12 * (size_t)k + (tile ? 8 * (size_t)k / 32 * 33 : 0);
 }
 
 template <int CPL>
-hipError_t launch_staged(const RmsArgs& a, const DeviceInfo& dev, hipStream_t stream) {
-  const bool tile = staged_lds_bytes(a.k, true) <= kLdsLimit;
+hipError_t launch_staged(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev, hipStream_t stream) {
+  const bool tile = !amax_pass && staged_lds_bytes(a.k, true) <= kLdsLimit;
   const size_t lds = staged_lds_bytes(a.k, tile);
   const int64_t ntiles = a.padded >> 7;
   const int64_t grid = ntiles < dev.cu_count ? ntiles : dev.cu_count;
   const dim3 g((uint32_t)grid), b(kStagedWaves * kWave);
-  if (tile) {
-    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, true, true>), g, b, lds, stream, a, a.frame_idx);
-    else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, true>), g, b, lds, stream, a, a.frame_idx);
+  if (amax_pass) {
+    hipLaunchKernelGGL((rms_adaln_staged<CPL, false, false, true>), g, b, lds, stream, a, a.frame_idx);
+  } else if (tile) {
+    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, true, true, false>), g, b, lds, stream, a, a.frame_idx);
+    else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, true, false>), g, b, lds, stream, a, a.frame_idx);
   } else {
-    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, true, false>), g, b, lds, stream, a, a.frame_idx);
-    else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, false>), g, b, lds, stream, a, a.frame_idx);
+    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, true, false, false>), g, b, lds, stream, a, a.frame_idx);
+    else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, false, false>), g, b, lds, stream, a, a.frame_idx);
   }
   return hipGetLastError();
 }
 
-template <int CPL, bool Y, bool TILE>
+template <int CPL, bool Y, bool TILE, bool AMAX>
 hipError_t allow_lds_one() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&rms_adaln_staged<CPL, Y, TILE>),
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&rms_adaln_staged<CPL, Y, TILE, AMAX>),
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsLimit);
 }
 
 template <int CPL>
 hipError_t allow_lds() {
-  hipError_t e = allow_lds_one<CPL, false, false>();
-  if (e == hipSuccess) e = allow_lds_one<CPL, true, false>();
-  if (e == hipSuccess) e = allow_lds_one<CPL, false, true>();
-  if (e == hipSuccess) e = allow_lds_one<CPL, true, true>();
+  hipError_t e = allow_lds_one<CPL, false, false, false>();
+  if (e == hipSuccess) e = allow_lds_one<CPL, true, false, false>();
+  if (e == hipSuccess) e = allow_lds_one<CPL, false, true, false>();
+  if (e == hipSuccess) e = allow_lds_one<CPL, true, true, false>();
+  if (e == hipSuccess) e = allow_lds_one<CPL, false, false, true>();
   return e;
+}
+
+// One launch of the producer (amax_pass: the amax pass of a per-call scale instead).
+hipError_t launch_rms(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev, hipStream_t stream) {
+  switch (a.k / 512) {
+    case 1: return launch_staged<1>(a, amax_pass, dev, stream);
+    case 2: return launch_staged<2>(a, amax_pass, dev, stream);
+    case 3: return launch_staged<3>(a, amax_pass, dev, stream);
+    case 4: return launch_staged<4>(a, amax_pass, dev, stream);
+    case 5: return launch_staged<5>(a, amax_pass, dev, stream);
+    case 6: return launch_staged<6>(a, amax_pass, dev, stream);
+    case 7: return launch_staged<7>(a, amax_pass, dev, stream);
+    case 8: return launch_staged<8>(a, amax_pass, dev, stream);
+    case 9: return launch_staged<9>(a, amax_pass, dev, stream);
+    case 10: return launch_staged<10>(a, amax_pass, dev, stream);
+    case 11: return launch_staged<11>(a, amax_pass, dev, stream);
+    case 12: return launch_staged<12>(a, amax_pass, dev, stream);
+    case 13: return launch_staged<13>(a, amax_pass, dev, stream);
+    case 14: return launch_staged<14>(a, amax_pass, dev, stream);
+    case 15: return launch_staged<15>(a, amax_pass, dev, stream);
+    case 16: return launch_staged<16>(a, amax_pass, dev, stream);
+    default: break;
+  }
+  const int64_t blocks = (a.padded + 3) / 4;
+  if (amax_pass) hipLaunchKernelGGL(rms_adaln_general<true>, dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(rms_adaln_general<false>, dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -516,51 +580,37 @@ hipError_t prepare_rms_adaln() {
   return hipSuccess;
 }
 
-hipError_t launch_rms_adaln(const void* x, const void* weight, const void* shift, const void* scale,
-                            int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx,
-                            float eps, int64_t m, int64_t k, float global_amax, void* codes,
-                            void* scales, float* rstd_out, void* y_out, uint32_t* status_word,
-                            const DeviceInfo& dev, hipStream_t stream) {
+hipError_t launch_rms_adaln(const RmsLaunch& p, const DeviceInfo& dev, hipStream_t stream) {
   RmsArgs a;
-  a.x = static_cast<const uint4*>(x);
-  a.w = static_cast<const uint16_t*>(weight);
-  a.shift = static_cast<const uint16_t*>(shift);
-  a.scale = static_cast<const uint16_t*>(scale);
-  a.frame_stride = frame_stride;
-  a.num_frames = num_frames;
-  a.frame_idx = frame_idx;
-  a.eps = eps;
-  a.m = m;
-  a.k = k;
-  a.padded = (m + 127) / 128 * 128;
-  a.global_amax = global_amax;
-  a.codes = static_cast<uint32_t*>(codes);
-  a.scales = static_cast<uint8_t*>(scales);
-  a.rstd_out = rstd_out;
-  a.y_out = static_cast<uint4*>(y_out);
-  a.status = status_word;
-  switch (k / 512) {
-    case 1: return launch_staged<1>(a, dev, stream);
-    case 2: return launch_staged<2>(a, dev, stream);
-    case 3: return launch_staged<3>(a, dev, stream);
-    case 4: return launch_staged<4>(a, dev, stream);
-    case 5: return launch_staged<5>(a, dev, stream);
-    case 6: return launch_staged<6>(a, dev, stream);
-    case 7: return launch_staged<7>(a, dev, stream);
-    case 8: return launch_staged<8>(a, dev, stream);
-    case 9: return launch_staged<9>(a, dev, stream);
-    case 10: return launch_staged<10>(a, dev, stream);
-    case 11: return launch_staged<11>(a, dev, stream);
-    case 12: return launch_staged<12>(a, dev, stream);
-    case 13: return launch_staged<13>(a, dev, stream);
-    case 14: return launch_staged<14>(a, dev, stream);
-    case 15: return launch_staged<15>(a, dev, stream);
-    case 16: return launch_staged<16>(a, dev, stream);
-    default: break;
+  a.x = static_cast<const uint4*>(p.x);
+  a.w = static_cast<const uint16_t*>(p.weight);
+  a.shift = static_cast<const uint16_t*>(p.shift);
+  a.scale = static_cast<const uint16_t*>(p.scale);
+  a.frame_stride = p.frame_stride;
+  a.num_frames = p.num_frames;
+  a.frame_idx = p.frame_idx;
+  a.eps = p.eps;
+  a.m = p.m;
+  a.k = p.k;
+  a.padded = (p.m + 127) / 128 * 128;
+  a.global_amax = p.global_amax;
+  a.codes = static_cast<uint32_t*>(p.codes);
+  a.scales = static_cast<uint8_t*>(p.scales);
+  a.rstd_out = p.rstd_out;
+  a.y_out = static_cast<uint4*>(p.y_out);
+  a.status = p.status_word;
+  a.amax_dev = p.amax_dev;
+  a.amax_out = nullptr;
+  if (p.amax_dev) {
+    // per-call scale: zero the amax, fold max |y| into it, then quantize with it
+    RmsArgs pass = a;
+    pass.amax_dev = nullptr;
+    pass.amax_out = p.amax_dev;
+    hipError_t e = launch_zero_amax(pass.amax_out, stream);
+    if (e == hipSuccess) e = launch_rms(pass, true, dev, stream);
+    if (e != hipSuccess) return e;
   }
-  const int64_t blocks = (a.padded + 3) / 4;
-  hipLaunchKernelGGL(rms_adaln_general, dim3((uint32_t)blocks), dim3(256), 0, stream, a);
-  return hipGetLastError();
+  return launch_rms(a, false, dev, stream);
 }
 
 }  // namespace nvfp4act

@@ -74,12 +74,14 @@ __global__ void silu_table_kernel() {
 }
 
 // One 128-row x kTileCols tile: each wavefront takes rows wave, wave + 16, ... (8 rows),
-// kRowBatch at a time; scale bytes go to the tile's LDS block.
+// kRowBatch at a time; scale bytes go to the tile's LDS block.  AMAX (the amax pass of a
+// per-call scale): nothing is quantized or stored; max |y| is folded into *lane_amax.
+template <bool AMAX>
 __device__ __forceinline__ void swiglu_tile(const uint4* up, const uint4* gate, int64_t ld8, int64_t m,
                                             int64_t row_chunks, uint32_t* codes, uint4* y_out,
                                             int64_t tile_row, int64_t c0, int64_t tchunks, int lane, int wave,
                                             const uint16_t* table, float gsf, const float* inv_tab,
-                                            uint8_t* sc_lane) {
+                                            uint8_t* sc_lane, float* lane_amax) {
   const int64_t r0 = tile_row << 7;
   const int64_t rows = (m - r0 < 128) ? (m - r0 > 0 ? m - r0 : 0) : 128;
   const int64_t c = c0 + lane;
@@ -110,6 +112,11 @@ __device__ __forceinline__ void swiglu_tile(const uint4* up, const uint4* gate, 
         y[2 * q] = round_bf16(s0 * bf16_lo(uw[q]));
         y[2 * q + 1] = round_bf16(s1 * bf16_hi(uw[q]));
       }
+      if (AMAX) {
+        // lanes past the real rows or columns loaded zeros, whose y is 0
+        *lane_amax = fold_abs8(*lane_amax, y);
+        continue;
+      }
       uint32_t s;
       const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
       if (rr < rows && lane_ok) {
@@ -125,12 +132,15 @@ __device__ __forceinline__ void swiglu_tile(const uint4* up, const uint4* gate, 
   }
 }
 
+template <bool AMAX>
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restrict__ up,
                                                           const uint4* __restrict__ gate, int64_t ld8,
                                                           int64_t m, int64_t f, float global_amax,
+                                                          const float* amax_dev, float* amax_out,
                                                           uint32_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales, uint4* y_out,
                                                           int64_t col_tiles, int64_t ntiles) {
+  __shared__ float amax_red[kWaves];
   extern __shared__ uint4 lds4[];
   uint16_t* table = reinterpret_cast<uint16_t*>(lds4);
   float* inv_tab = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lds4) + kTableBytes);
@@ -140,7 +150,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restric
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   if ((int64_t)blockIdx.x >= ntiles) return;              // idle workgroup (uniform)
 
-  const float gsf = global_scale(global_amax);
+  const float gsf = call_global_scale(global_amax, amax_dev);
+  float lane_amax = 0.0f;
   fill_inverse_table(inv_tab, gsf, tid);
   const uint4* src = reinterpret_cast<const uint4*>(g_silu_table);
   for (int i = tid; i < (int)(kTableBytes / 16); i += kThreads) lds4[i] = src[i];
@@ -153,8 +164,9 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restric
     const int64_t tile_row = t / col_tiles, col_tile = t % col_tiles;
     const int64_t c0 = col_tile * (kTileCols / 8);
     const int64_t tchunks = (row_chunks - c0 < kTileCols / 8) ? row_chunks - c0 : kTileCols / 8;
-    swiglu_tile(up, gate, ld8, m, row_chunks, codes, y_out, tile_row, c0, tchunks, lane, wave, table, gsf,
-                inv_tab, sc_lane);
+    swiglu_tile<AMAX>(up, gate, ld8, m, row_chunks, codes, y_out, tile_row, c0, tchunks, lane, wave, table, gsf,
+                      inv_tab, sc_lane, &lane_amax);
+    if (AMAX) continue;
     __syncthreads();
     // copy the tile's scale slice out and zero it for the next tile (each thread clears
     // exactly the words it copied)
@@ -167,6 +179,7 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restric
     }
     __syncthreads();
   }
+  if (AMAX) workgroup_max_to(amax_out, lane_amax, amax_red, kWaves);
 }
 
 }  // namespace
@@ -184,21 +197,37 @@ hipError_t build_silu_table(unsigned int* ambiguous) {
 }
 
 hipError_t prepare_swiglu() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&swiglu_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kTableBytes + 512 + kScaleBytes));
+  const int lds = (int)(kTableBytes + 512 + kScaleBytes);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&swiglu_kernel<false>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&swiglu_kernel<true>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  return e;
 }
 
 hipError_t launch_swiglu(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f,
-                         float global_amax, void* codes, void* scales, void* y_out,
+                         float global_amax, float* amax_dev, void* codes, void* scales, void* y_out,
                          const DeviceInfo& dev, hipStream_t stream) {
   const int64_t tile_rows = (m + 127) / 128;
   const int64_t col_tiles = (f + kTileCols - 1) / kTileCols;
   const int64_t ntiles = tile_rows * col_tiles;
   const int64_t grid = ntiles < dev.cu_count ? ntiles : dev.cu_count;
-  hipLaunchKernelGGL(swiglu_kernel, dim3((uint32_t)grid), dim3(kThreads), kTableBytes + 512 + kScaleBytes, stream,
-                     static_cast<const uint4*>(up), static_cast<const uint4*>(gate), ld / 8, m, f, global_amax,
-                     static_cast<uint32_t*>(codes), static_cast<uint8_t*>(scales), static_cast<uint4*>(y_out),
-                     col_tiles, ntiles);
+  const size_t lds = kTableBytes + 512 + kScaleBytes;
+  const uint4* u = static_cast<const uint4*>(up);
+  const uint4* g = static_cast<const uint4*>(gate);
+  if (amax_dev) {
+    // per-call scale: zero the amax, fold max |y| into it, then quantize with it
+    hipError_t e = launch_zero_amax(amax_dev, stream);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(swiglu_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), lds, stream, u, g, ld / 8, m, f,
+                       global_amax, nullptr, amax_dev, nullptr, nullptr, nullptr, col_tiles, ntiles);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(swiglu_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), lds, stream, u, g, ld / 8, m, f,
+                     global_amax, amax_dev, nullptr, static_cast<uint32_t*>(codes), static_cast<uint8_t*>(scales),
+                     static_cast<uint4*>(y_out), col_tiles, ntiles);
   return hipGetLastError();
 }
 

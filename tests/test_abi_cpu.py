@@ -103,3 +103,37 @@ def test_binding_raises_on_status():
     with pytest.raises(nq.NVFP4Error) as e:
         nq._check(2)
     assert e.value.status == 2 and "bad shape" in str(e.value)
+
+
+def test_dynamic_forms_status_codes():
+    f = ctypes.c_float
+    # quantize: the amax destination is required (m > 0) and 4-byte aligned; shapes first
+    assert lib.nvfp4_quantize_dynamic(A, 4, 64, None, A, A, None) == 1
+    assert lib.nvfp4_quantize_dynamic(A, 4, 64, A + 2, A, A, None) == 3
+    assert lib.nvfp4_quantize_dynamic(A, 4, 48, A, A, A, None) == 2
+    assert lib.nvfp4_quantize_dynamic(A, -1, 64, A, A, A, None) == 2
+    assert lib.nvfp4_quantize_dynamic(None, 4, 64, A, A, A, None) == 1
+    assert lib.nvfp4_quantize_dynamic(A, 4, 64, A, U, A, None) == 3
+    assert lib.nvfp4_quantize_dynamic(None, 0, 64, None, None, None, None) == 0
+    # rms_adaln: same shape rules as the static form, plus the amax destination
+    args = [A, A, A, A, 1024, 2, A, f(1e-6), 4, 512, A, A, A, None, None, None, None]
+    bad_amax = list(args)
+    bad_amax[10] = None
+    assert lib.rms_adaln_nvfp4_dynamic(*bad_amax) == 1
+    bad_amax[10] = A + 2
+    assert lib.rms_adaln_nvfp4_dynamic(*bad_amax) == 3
+    bad_k = list(args)
+    bad_k[9] = 256
+    assert lib.rms_adaln_nvfp4_dynamic(*bad_k) == 2
+    bad_eps = list(args)
+    bad_eps[7] = f(-1.0)
+    assert lib.rms_adaln_nvfp4_dynamic(*bad_eps) == 4
+    empty = list(args)
+    empty[8] = 0
+    empty[10] = None
+    assert lib.rms_adaln_nvfp4_dynamic(*empty) == 0
+    # swiglu
+    assert lib.swiglu_nvfp4_dynamic(A, A, 128, 4, 64, None, A, A, None, None) == 1
+    assert lib.swiglu_nvfp4_dynamic(A, A, 128, 4, 64, A + 2, A, A, None, None) == 3
+    assert lib.swiglu_nvfp4_dynamic(A, A, 32, 4, 64, A, A, A, None, None) == 2
+    assert lib.swiglu_nvfp4_dynamic(A, A, 128, 0, 64, None, None, None, None, None) == 0

@@ -31,14 +31,16 @@ def split_rows(n: int, parts: int):
     return [(i, min(n, i + step)) for i in range(0, n, step)]
 
 
-def oracle_rms_adaln(x, w, table, idx, eps, amax, row_ids=None, want_y=True):
-    """oracle.rms_adaln_rows over row blocks in parallel threads; concatenated results."""
+def oracle_rms_adaln(x, w, table, idx, eps, amax, row_ids=None, want_y=True, gsf=None):
+    """oracle.rms_adaln_rows over row blocks in parallel threads; concatenated results
+    (gsf: a global scale used as is instead of the one of amax)."""
     n = x.shape[0]
     rid = np.arange(n, dtype=np.int64) if row_ids is None else np.asarray(row_ids, np.int64)
 
     def part(se):
         s, e = se
-        return oracle.rms_adaln_rows(x[s:e], w, table, idx[s:e], eps, amax, row_ids=rid[s:e], want_y=want_y)
+        return oracle.rms_adaln_rows(x[s:e], w, table, idx[s:e], eps, amax, row_ids=rid[s:e], want_y=want_y,
+                                     gsf=gsf)
 
     with ThreadPoolExecutor(threads()) as ex:
         res = list(ex.map(part, split_rows(n, 4 * threads())))
@@ -60,13 +62,13 @@ def oracle_quantize_rows(y, amax):
     return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])
 
 
-def oracle_swiglu(up, gate, amax, want_y=True):
+def oracle_swiglu(up, gate, amax, want_y=True, gsf=None):
     n = up.shape[0]
     oracle.silu_table()  # build once before the threads start
 
     def part(se):
         s, e = se
-        return oracle.swiglu_rows(up[s:e], gate[s:e], amax, want_y=want_y)
+        return oracle.swiglu_rows(up[s:e], gate[s:e], amax, want_y=want_y, gsf=gsf)
 
     with ThreadPoolExecutor(threads()) as ex:
         res = list(ex.map(part, split_rows(n, 4 * threads())))
