@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="rms_adaln_63240x7168")
+    p.add_argument("--dynamic", action="store_true",
+                   help="time the per-call (dynamic) amax form: amax pass + quantize pass")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=32768, help="rows of the oracle sample")
     return p.parse_args()
@@ -104,15 +106,27 @@ def main():
     torch.cuda.set_device(0)
     inp = make_inputs(wl, torch, amax)
     codes, scales = nq.new_quantized(wl.m, wl.k, "cuda:0")
+    amax_dev = torch.zeros(1, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
 
-    if wl.kind == "rms_adaln":
+    if wl.kind == "rms_adaln" and a.dynamic:
+        def step():
+            nq.rms_adaln_nvfp4_dynamic(inp["x"], inp["weight"], inp["table"], inp["frame_idx"], wl.eps,
+                                       amax_out=amax_dev, codes=codes, scales=scales, stream=stream)
+    elif wl.kind == "rms_adaln":
         def step():
             nq.rms_adaln_nvfp4(inp["x"], inp["weight"], inp["table"], inp["frame_idx"], wl.eps, amax,
                                codes=codes, scales=scales, stream=stream)
+    elif wl.kind == "quantize" and a.dynamic:
+        def step():
+            nq.nvfp4_quantize_dynamic(inp["x"], amax_out=amax_dev, codes=codes, scales=scales, stream=stream)
     elif wl.kind == "quantize":
         def step():
             nq.nvfp4_quantize(inp["x"], amax, codes=codes, scales=scales, stream=stream)
+    elif a.dynamic:
+        def step():
+            nq.swiglu_nvfp4_dynamic(inp["x"], amax_out=amax_dev, codes=codes, scales=scales, stream=stream)
+        nq.init()
     else:
         def step():
             nq.swiglu_nvfp4(inp["x"], amax, codes=codes, scales=scales, stream=stream)
@@ -149,7 +163,8 @@ def main():
     kernel_ms = float(np.mean(per_launch_ms))
     ms_per_step = region_ms / a.steps
 
-    alg_bytes = wl.algorithmic_bytes()
+    # the per-call form reads the input twice (the amax pass, then the quantize pass)
+    alg_bytes = wl.algorithmic_bytes() + (2 * wl.m * wl.in_cols if a.dynamic else 0)
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
 
@@ -168,10 +183,11 @@ def main():
     copy_gbps = 2 * x.numel() * x.element_size() / (copy_ms * 1e-3) / 1e9
     del dst
 
-    traffic = measured_traffic(wl.name)
+    traffic = None if a.dynamic else measured_traffic(wl.name)
 
     out = {
-        "metric": METRIC if wl.name == "rms_adaln_63240x7168" else "NVFP4 producer HBM GB/s (%s)" % wl.name,
+        "metric": (METRIC if wl.name == "rms_adaln_63240x7168" and not a.dynamic
+                   else "NVFP4 producer HBM GB/s (%s%s)" % (wl.name, ", per-call amax" if a.dynamic else "")),
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -185,7 +201,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "rows": wl.m, "hidden": wl.k,
                    "frames": wl.frames if wl.kind == "rms_adaln" else None,
-                   "algorithmic_bytes_per_step": alg_bytes, "global_amax": amax},
+                   "algorithmic_bytes_per_step": alg_bytes,
+                   "global_amax": "per-call (device amax pass)" if a.dynamic else amax},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
