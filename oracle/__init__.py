@@ -72,6 +72,8 @@ def _load():
             "orc_rms_adaln_rows_gsf": (None, [P, I64, I64, P, P, P, P, I64, I64, P, F, F,
                                               P, P, P, P, P, P]),
             "orc_swiglu_rows_gsf": (None, [P, P, I64, I64, I64, P, P, F, P, P, P, P]),
+            "orc_swiglu_packed_rows_gsf": (None, [P, P, ctypes.c_int, I64, I64, I64, P, P, F,
+                                                  P, P, P, P]),
             "orc_rms_rstd": (F, [P, I64, F]),
             "orc_quantize_rows": (None, [P, I64, I64, F, P, P]),
             "orc_nvfp4_quantize": (None, [P, I64, I64, F, P, P]),
@@ -303,6 +305,44 @@ def swiglu_dynamic(up_u16, gate_u16, want_y: bool = False, scales_rows: int | No
     amax = max_abs(first["y"])
     out = swiglu_rows(up_u16, gate_u16, 0.0, want_y=want_y, scales_rows=scales_rows,
                       gsf=dynamic_global_scale(amax))
+    out["amax"] = amax
+    return out
+
+
+def swiglu_packed_rows(proj_u16, bias_u16, interleaved: bool, global_amax: float, row_ids=None,
+                       want_y: bool = False, scales_rows: int | None = None, gsf: float | None = None):
+    """SwiGLU -> NVFP4 of a packed projection [n, 2f] with an optional bf16 bias [2f].
+
+    interleaved False: value columns [0, f), gate columns [f, 2f); True: value at column
+    2j and gate at 2j + 1.  bias (None: no bias) follows the projection's column order and
+    is added as a bf16 tensor add before SiLU and the product.
+    gsf: use this global scale as is (global_amax is then ignored).
+    """
+    proj = _c(proj_u16, np.uint16)
+    n, two_f = proj.shape
+    f = two_f // 2
+    bias = None if bias_u16 is None else _c(bias_u16, np.uint16).reshape(-1)
+    if bias is not None and bias.size != two_f:
+        raise ValueError("bias must hold 2f entries")
+    rid = None if row_ids is None else _c(row_ids, np.int64)
+    codes = np.empty((n, f // 2), np.uint8)
+    sb = np.empty((n, f // 16), np.uint8)
+    y = np.empty((n, f), np.uint16) if want_y else None
+    scales = None if scales_rows is None else np.zeros((scales_rows, f // 16), np.uint8)
+    g = float(global_scale(global_amax) if gsf is None else gsf)
+    _load().orc_swiglu_packed_rows_gsf(_ptr(proj), _ptr(bias), int(bool(interleaved)), two_f, n, f, _ptr(rid),
+                                       _ptr(silu_table()), g, _ptr(codes), _ptr(sb), _ptr(scales), _ptr(y))
+    return dict(codes=codes, scale_bytes=sb, y=y, scales=scales)
+
+
+def swiglu_packed_dynamic(proj_u16, bias_u16, interleaved: bool, want_y: bool = False,
+                          scales_rows: int | None = None):
+    """swiglu_packed_rows under the amax of the tensor's own y (two passes).  The result
+    dict gains 'amax'."""
+    first = swiglu_packed_rows(proj_u16, bias_u16, interleaved, 1.0, want_y=True)
+    amax = max_abs(first["y"])
+    out = swiglu_packed_rows(proj_u16, bias_u16, interleaved, 0.0, want_y=want_y, scales_rows=scales_rows,
+                             gsf=dynamic_global_scale(amax))
     out["amax"] = amax
     return out
 

@@ -538,3 +538,47 @@ EXPORT void orc_swiglu_rows(const uint16_t* up, const uint16_t* gate, int64_t ld
     leave_ieee(s);
     orc_swiglu_rows_gsf(up, gate, ld, n, f, row_ids, table, gsf, codes, scale_bytes, scales, y_out);
 }
+
+/* SwiGLU -> NVFP4 of a packed projection with an optional bias ([H3-API]
+   swiglu_quantize: o [M, 2F] holds the value half first and arrives without
+   its bias;
+   [branch compare] quant_probe: the paired layout with the value of output
+   column j at projection column 2j and its gate at 2j + 1).  Row i of the
+   projection starts at proj + i*ld.  For output column j:
+     interleaved == 0:  value column j,      gate column F + j
+     interleaved == 1:  value column 2j,     gate column 2j + 1
+   bias (NULL: none) is one bf16 row of 2F entries in the projection's own
+   column order.  The bias add is a bf16 tensor add: each of value and gate
+   becomes bf16(o + bias) at its column (as residual_norm_quantize's bf16(o +
+   bias) on the same page), and then y = bf16(S[gate] * value), the block
+   quantizer and the layout as in orc_swiglu_rows_gsf. */
+EXPORT void orc_swiglu_packed_rows_gsf(const uint16_t* proj, const uint16_t* bias, int interleaved,
+                                       int64_t ld, int64_t n, int64_t f, const int64_t* row_ids,
+                                       const uint16_t* table, float gsf, uint8_t* codes,
+                                       uint8_t* scale_bytes, uint8_t* scales, uint16_t* y_out) {
+    unsigned int s = enter_ieee();
+    float* y = (float*)malloc(sizeof(float) * (size_t)f);
+    uint8_t* sb = (uint8_t*)malloc((size_t)(f / 16));
+    for (int64_t i = 0; i < n; ++i) {
+        int64_t r = row_ids ? row_ids[i] : i;
+        const uint16_t* row = proj + i * ld;
+        for (int64_t j = 0; j < f; ++j) {
+            int64_t vc = interleaved ? 2 * j : j;          /* value column */
+            int64_t gc = interleaved ? 2 * j + 1 : f + j;  /* gate column  */
+            uint16_t v = row[vc], g = row[gc];
+            if (bias) {
+                v = bf16_round(bf16_to_f32(v) + bf16_to_f32(bias[vc]));
+                g = bf16_round(bf16_to_f32(g) + bf16_to_f32(bias[gc]));
+            }
+            y[j] = rb(bf16_to_f32(table[g]) * bf16_to_f32(v));
+        }
+        quantize_row(y, f, gsf, codes + i * (f / 2), sb);
+        if (scale_bytes) memcpy(scale_bytes + i * (f / 16), sb, (size_t)(f / 16));
+        if (scales) place_scales(sb, r, f, scales);
+        if (y_out)
+            for (int64_t j = 0; j < f; ++j) y_out[i * f + j] = bf16_round(y[j]);
+    }
+    free(sb);
+    free(y);
+    leave_ieee(s);
+}

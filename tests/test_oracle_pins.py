@@ -414,6 +414,100 @@ def test_swiglu_product_rounding_vs_torch():
 
 
 # --------------------------------------------------------------------------
+# SwiGLU of a packed projection with a bias (value-first and paired columns)
+# --------------------------------------------------------------------------
+
+def _f32_list(vals):
+    return np.array([-0.0 if v == "-0" else float(v) for v in vals], np.float32)
+
+
+def _pack_columns(value, gate, interleaved):
+    """[n, f] value and gate halves -> one [n, 2f] projection in the given column order."""
+    n, f = value.shape
+    out = np.empty((n, 2 * f), value.dtype)
+    if interleaved:
+        out[:, 0::2], out[:, 1::2] = value, gate
+    else:
+        out[:, :f], out[:, f:] = value, gate
+    return out
+
+
+def _torch_bf16_add(a_u16, b_u16):
+    """bf16 + bf16 by torch on the CPU (fp32 sum, nearest-even to bf16)."""
+    a = torch.from_numpy(a_u16.view(np.int16).copy()).view(torch.bfloat16)
+    b = torch.from_numpy(b_u16.view(np.int16).copy()).view(torch.bfloat16)
+    return (a + b).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_swiglu_packed_hand_worked_blocks(interleaved):
+    d = json.load(open(os.path.join(GOLDEN, "swiglu_packed_blocks.json")))
+    f, cols = d["f"], d["columns"]
+    half = {}
+    for key in ("value", "value_bias", "gate", "gate_bias"):
+        row = np.zeros((1, f), np.float32)
+        row[0, :cols] = _f32_list(d[key])
+        half[key] = oracle.bf16_round(row)
+    proj = _pack_columns(half["value"], half["gate"], interleaved)
+    bias = _pack_columns(half["value_bias"], half["gate_bias"], interleaved).reshape(-1)
+    res = oracle.swiglu_packed_rows(proj, bias, interleaved, d["global_amax"], want_y=True)
+    want = bytes.fromhex(d["codes_hex"]) + bytes(f // 2 - len(d["codes_hex"]) // 2)
+    assert res["codes"][0].tobytes() == want
+    assert list(res["scale_bytes"][0]) == d["scale_codes"]
+
+
+def _random_projection(seed, n, f):
+    g = np.random.Generator(np.random.PCG64(seed))
+    proj = oracle.bf16_round(g.standard_normal((n, 2 * f)).astype(np.float32))
+    # bias values of the same scale, so that most sums need rounding and some tie
+    bias = oracle.bf16_round((0.5 * g.standard_normal(2 * f)).astype(np.float32))
+    return proj, bias
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_swiglu_packed_without_bias_is_the_two_pointer_form(interleaved):
+    n, f = 6, 192
+    proj_vf, _ = _random_projection(31, n, f)
+    value, gate = proj_vf[:, :f], proj_vf[:, f:]
+    proj = _pack_columns(value, gate, interleaved)
+    got = oracle.swiglu_packed_rows(proj, None, interleaved, 7.5, want_y=True, scales_rows=128)
+    ref = oracle.swiglu_rows(value, gate, 7.5, want_y=True, scales_rows=128)
+    for key in ("codes", "scale_bytes", "y", "scales"):
+        assert np.array_equal(got[key], ref[key]), key
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_swiglu_packed_bias_is_a_bf16_add_before_silu(interleaved):
+    n, f = 6, 256
+    proj_vf, bias_vf = _random_projection(32, n, f)
+    value, gate = proj_vf[:, :f], proj_vf[:, f:]
+    bv, bg = bias_vf[:f], bias_vf[f:]
+    proj = _pack_columns(value, gate, interleaved)
+    bias = _pack_columns(bv[None], bg[None], interleaved).reshape(-1)
+    got = oracle.swiglu_packed_rows(proj, bias, interleaved, 9.0, want_y=True)
+    ref = oracle.swiglu_rows(_torch_bf16_add(value, np.broadcast_to(bv, value.shape)),
+                             _torch_bf16_add(gate, np.broadcast_to(bg, gate.shape)), 9.0, want_y=True)
+    for key in ("codes", "scale_bytes", "y"):
+        assert np.array_equal(got[key], ref[key]), key
+    # the bias changes the result (a dropped bias would pass the test above only by accident)
+    plain = oracle.swiglu_packed_rows(proj, None, interleaved, 9.0, want_y=True)
+    assert not np.array_equal(plain["y"], got["y"])
+
+
+@pytest.mark.parametrize("interleaved", [False, True])
+def test_swiglu_packed_negative_zero_bias_is_no_bias(interleaved):
+    n, f = 4, 128
+    proj, _ = _random_projection(33, n, f)
+    proj[0, :8] = 0x0000          # x + (-0) = x also for both zeros
+    proj[0, 8:16] = 0x8000
+    bias = np.full(2 * f, 0x8000, np.uint16)
+    got = oracle.swiglu_packed_rows(proj, bias, interleaved, 5.0, want_y=True)
+    ref = oracle.swiglu_packed_rows(proj, None, interleaved, 5.0, want_y=True)
+    for key in ("codes", "scale_bytes", "y"):
+        assert np.array_equal(got[key], ref[key]), key
+
+
+# --------------------------------------------------------------------------
 # whole-tensor quantize equals per-row quantize placed by the layout
 # --------------------------------------------------------------------------
 
@@ -494,6 +588,17 @@ def test_dynamic_quantize_all_zero_or_subnormal_tensor(pattern):
     sign = (x >> 15).astype(np.uint8) * 8
     assert np.array_equal(codes, sign[:, 0::2] | (sign[:, 1::2] << 4))
     assert not scales.any()
+
+
+def test_dynamic_swiglu_packed_is_static_at_its_own_amax():
+    proj, bias = _random_projection(34, 5, 128)
+    for interleaved in (False, True):
+        dyn = oracle.swiglu_packed_dynamic(proj, bias, interleaved, want_y=True, scales_rows=128)
+        y = oracle.swiglu_packed_rows(proj, bias, interleaved, 1.0, want_y=True)["y"]
+        assert dyn["amax"] == float(np.abs(oracle.bf16_to_f32(y)).max())
+        ref = oracle.swiglu_packed_rows(proj, bias, interleaved, dyn["amax"], want_y=True, scales_rows=128)
+        for key in ("codes", "scales", "y"):
+            assert np.array_equal(dyn[key], ref[key]), key
 
 
 def test_dynamic_rms_adaln_and_swiglu_are_static_at_their_own_amax():
