@@ -85,6 +85,8 @@ def make_inputs(wl, torch, amax):
                     frame_idx=torch.from_numpy(wl.frame_idx()).to(dev))
     else:
         args = dict(x=up(wl.x()))
+        if wl.kind == "swiglu" and wl.bias_std > 0:
+            args["bias"] = up(wl.bias())
     return args
 
 
@@ -123,6 +125,16 @@ def main():
     elif wl.kind == "quantize":
         def step():
             nq.nvfp4_quantize(inp["x"], amax, codes=codes, scales=scales, stream=stream)
+    elif (wl.bias_std > 0 or wl.interleaved) and a.dynamic:
+        def step():
+            nq.swiglu_packed_nvfp4_dynamic(inp["x"], bias=inp.get("bias"), interleaved=wl.interleaved,
+                                           amax_out=amax_dev, codes=codes, scales=scales, stream=stream)
+        nq.init()
+    elif wl.bias_std > 0 or wl.interleaved:
+        def step():
+            nq.swiglu_packed_nvfp4(inp["x"], amax, bias=inp.get("bias"), interleaved=wl.interleaved, codes=codes,
+                                   scales=scales, stream=stream)
+        nq.init()
     elif a.dynamic:
         def step():
             nq.swiglu_nvfp4_dynamic(inp["x"], amax_out=amax_dev, codes=codes, scales=scales, stream=stream)
@@ -238,6 +250,13 @@ def cpu_baseline(wl, amax, rows, np):
         def part(se):
             s, e = se
             oracle.quantize_rows(x[s:e], amax)
+    elif wl.bias_std > 0 or wl.interleaved:
+        oracle.silu_table()
+        bias = wl.bias()
+
+        def part(se):
+            s, e = se
+            oracle.swiglu_packed_rows(x[s:e], bias, wl.interleaved, amax)
     else:
         oracle.silu_table()
 

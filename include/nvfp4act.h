@@ -5,6 +5,8 @@
  * Three producers, each fused with the same NVFP4 block quantizer:
  *   rms_adaln_nvfp4  RMSNorm (fp32 statistic) + adaLN modulation -> NVFP4
  *   swiglu_nvfp4     SiLU(gate) * up                              -> NVFP4
+ *                    (swiglu_packed_nvfp4: packed projection, bias before
+ *                    SiLU, value-first or paired columns)
  *   nvfp4_quantize   identity (attention-output quantize)         -> NVFP4
  *
  * Sources: TensorRT-LLM PR #21483 "Fuse the MiniMax-H3 NVFP4 activation
@@ -39,9 +41,9 @@
  *   current device).  bf16 data is passed as raw 16-bit patterns.
  * - Every compute call is asynchronous on `stream` (a hipStream_t passed as
  *   void*, NULL = the default stream), allocates nothing and never waits for
- *   the device.  The one exception is the first swiglu_nvfp4 call on a device
- *   (or an explicit nvfp4act_init), which builds the device's SiLU table once
- *   and waits for it.
+ *   the device.  The one exception is the first SwiGLU call (any swiglu_*
+ *   entry point) on a device (or an explicit nvfp4act_init), which builds the
+ *   device's SiLU table once and waits for it.
  * - Ownership: the caller allocates and frees every buffer.  Inputs must stay
  *   valid and unmodified, and outputs untouched, until the stream work is done.
  *   The library writes only codes, scales and the non-NULL side outputs.
@@ -87,9 +89,9 @@ const char* nvfp4act_status_string(int status);
 int nvfp4act_last_hip_error(void);
 
 /* Build the per-device constant tables on the current device (the SiLU table
-   of swiglu_nvfp4) and wait for them.  Idempotent; optional (swiglu_nvfp4
-   calls it on first use).  Call it before capturing swiglu_nvfp4 into a HIP
-   graph.  Returns a status. */
+   of the swiglu_* calls) and wait for them.  Idempotent; optional (the
+   swiglu_* calls run it on first use).  Call it before capturing a swiglu_*
+   call into a HIP graph.  Returns a status. */
 int nvfp4act_init(void);
 
 /* Standalone NVFP4 quantize of a bf16 tensor (the attention-output quantize).
@@ -155,6 +157,28 @@ int rms_adaln_nvfp4(const void* x, const void* weight, const void* shift, const 
 int swiglu_nvfp4(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f,
                  float global_amax, void* codes, void* scales, void* y_out, void* stream);
 
+/* SwiGLU -> NVFP4 of a packed [m, 2f] projection with an optional bias added
+   before SiLU (FastVideo API page, swiglu_quantize: the projection arrives
+   value half first and without its bias; FastVideo branch compare,
+   minimax_h3_swiglu_quant.cuh, quant_probe: the paired layout).  For output
+   column j of row i (row i of the projection at proj + i*ld elements):
+     interleaved = 0   value at column j,    gate at column f + j
+     interleaved = 1   value at column 2j,   gate at column 2j + 1
+   With a bias, value and gate first become bf16(value + bias[vc]) and
+   bf16(gate + bias[gc]) (fp32 sum, round to nearest even), vc and gc being the
+   columns just named; then y = bf16(S[gate] * value) and the quantizer.
+     proj         bf16, 16-byte aligned
+     bias         nullable; 2f bf16 values in the projection's column order
+                  (one projection row), 16-byte aligned
+     interleaved  0 or 1 (otherwise status 2)
+     ld           row stride in elements (>= 2f; ld*2 a multiple of 16)
+     m, f, global_amax, codes, scales, y_out  as for swiglu_nvfp4
+   A biased value or gate that overflows bf16 is outside the contract, like a
+   non-finite input.  Returns a status. */
+int swiglu_packed_nvfp4(const void* proj, const void* bias, int interleaved, int64_t ld, int64_t m,
+                        int64_t f, float global_amax, void* codes, void* scales, void* y_out,
+                        void* stream);
+
 /* Per-call (dynamic) global amax
    ------------------------------
    The *_dynamic forms take the global amax from the tensor itself instead of
@@ -186,6 +210,10 @@ int rms_adaln_nvfp4_dynamic(const void* x, const void* weight, const void* shift
 
 int swiglu_nvfp4_dynamic(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f,
                          float* amax_out, void* codes, void* scales, void* y_out, void* stream);
+
+int swiglu_packed_nvfp4_dynamic(const void* proj, const void* bias, int interleaved, int64_t ld,
+                                int64_t m, int64_t f, float* amax_out, void* codes, void* scales,
+                                void* y_out, void* stream);
 
 #ifdef __cplusplus
 }

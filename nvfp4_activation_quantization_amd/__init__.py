@@ -10,9 +10,12 @@ Entry points (see ``include/nvfp4act.h`` for the exact contract):
   nvfp4_quantize(x, global_amax)                          standalone quantize
   rms_adaln_nvfp4(x, weight, table, frame_idx, eps, global_amax)
   swiglu_nvfp4(projection, global_amax)                   value-first [m, 2f]
+  swiglu_packed_nvfp4(projection, global_amax, bias, interleaved)
+                                                          bias before SiLU; value-first
+                                                          or paired columns
 each returning ``(codes, scales)``; and the per-call (dynamic) amax forms
   nvfp4_quantize_dynamic(x), rms_adaln_nvfp4_dynamic(x, weight, table, frame_idx, eps),
-  swiglu_nvfp4_dynamic(projection)
+  swiglu_nvfp4_dynamic(projection), swiglu_packed_nvfp4_dynamic(projection, bias, interleaved)
 returning ``(codes, scales, amax)`` with ``amax`` a one-element float32 device tensor, codes ``[m, k/2]`` uint8, scales
 ``[pad(m), k/16]`` uint8 in the 128x4 swizzle (buffer shapes as the FastVideo
 API page's ``new_quantized``).
@@ -48,6 +51,8 @@ _SIGS = {
     "nvfp4_quantize_dynamic": (_I, [_P, _I64, _I64, _P, _P, _P, _P]),
     "rms_adaln_nvfp4_dynamic": (_I, [_P, _P, _P, _P, _I64, _I64, _P, _F, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "swiglu_nvfp4_dynamic": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "swiglu_packed_nvfp4": (_I, [_P, _P, _I, _I64, _I64, _I64, _F, _P, _P, _P, _P]),
+    "swiglu_packed_nvfp4_dynamic": (_I, [_P, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -287,4 +292,52 @@ def swiglu_nvfp4_dynamic(projection: torch.Tensor, amax_out=None, codes=None, sc
                                      _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, f), "y_out")
                                      if y_out is not None else 0,
                                      _stream(stream, projection.device)))
+    return codes, scales, amax_out
+
+
+def _packed_args(projection, bias):
+    if projection.dim() != 2 or projection.stride(1) != 1:
+        raise ValueError("projection must be a [m, 2f] view with unit column stride")
+    m, two_f = projection.shape
+    f = two_f // 2
+    if bias is not None and (bias.numel() != two_f or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous tensor of 2f = %d values" % two_f)
+    pp = _bf16_ptr(projection, "projection")
+    bp = _bf16_ptr(bias, "bias") if bias is not None else 0
+    return m, f, pp, bp, projection.stride(0)
+
+
+def swiglu_packed_nvfp4(projection: torch.Tensor, global_amax: float, bias: torch.Tensor | None = None,
+                        interleaved: bool = False, codes=None, scales=None, y_out=None, stream=None):
+    """SwiGLU -> NVFP4 of a packed [m, 2f] projection, with an optional bias of 2f values
+    (in the projection's column order) added as bf16 before SiLU.  interleaved=False:
+    value columns first, then gate columns; True: value of column j at 2j, gate at 2j+1.
+    The projection may be a row-strided view (unit column stride)."""
+    m, f, pp, bp, ld = _packed_args(projection, bias)
+    if codes is None or scales is None:
+        codes, scales = new_quantized(m, f, projection.device)
+    _check(_lib.swiglu_packed_nvfp4(pp, bp, int(bool(interleaved)), ld, m, f, float(global_amax),
+                                    _out_ptr(codes, torch.uint8, (m, f // 2), "codes"),
+                                    _out_ptr(scales, torch.uint8, (padded_rows(m), f // 16), "scales"),
+                                    _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, f), "y_out")
+                                    if y_out is not None else 0,
+                                    _stream(stream, projection.device)))
+    return codes, scales
+
+
+def swiglu_packed_nvfp4_dynamic(projection: torch.Tensor, bias: torch.Tensor | None = None,
+                                interleaved: bool = False, amax_out=None, codes=None, scales=None, y_out=None,
+                                stream=None):
+    """swiglu_packed_nvfp4 under the amax of this call's own y (computed on the device).
+    Returns (codes, scales, amax_out)."""
+    m, f, pp, bp, ld = _packed_args(projection, bias)
+    if codes is None or scales is None:
+        codes, scales = new_quantized(m, f, projection.device)
+    amax_out, ap = _amax_ptr(amax_out, projection.device)
+    _check(_lib.swiglu_packed_nvfp4_dynamic(pp, bp, int(bool(interleaved)), ld, m, f, ap,
+                                            _out_ptr(codes, torch.uint8, (m, f // 2), "codes"),
+                                            _out_ptr(scales, torch.uint8, (padded_rows(m), f // 16), "scales"),
+                                            _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, f),
+                                                     "y_out") if y_out is not None else 0,
+                                            _stream(stream, projection.device)))
     return codes, scales, amax_out

@@ -203,16 +203,9 @@ int rms_adaln_call(const void* x, const void* weight, const void* shift, const v
   return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
 }
 
-int swiglu_call(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f, float global_amax,
-                float* amax_dev, void* codes, void* scales, void* y_out, void* stream) {
-  if (m < 0 || f <= 0 || f % 64 != 0 || ld < f) return NVFP4ACT_ERR_SHAPE;
-  if (m == 0) return NVFP4ACT_OK;
-  if (!up || !gate || !codes || !scales) return NVFP4ACT_ERR_NULL;
-  if (!aligned16(up) || !aligned16(gate) || !aligned16(codes) || !aligned16(scales) ||
-      (ld * 2) % 16 != 0 || (y_out && !aligned16(y_out)))
-    return NVFP4ACT_ERR_ALIGN;
-  if (!amax_dev) {
-    int st = check_amax(global_amax);
+int swiglu_launch(const nvfp4act::SwigluLaunch& p, void* stream) {
+  if (!p.amax_dev) {
+    int st = check_amax(p.global_amax);
     if (st != NVFP4ACT_OK) return st;
   }
   const DeviceInfo* info = nullptr;
@@ -221,9 +214,62 @@ int swiglu_call(const void* up, const void* gate, int64_t ld, int64_t m, int64_t
   if (st != NVFP4ACT_OK) return st;
   st = ensure_silu_table(dev);
   if (st != NVFP4ACT_OK) return st;
-  hipError_t e = nvfp4act::launch_swiglu(up, gate, ld, m, f, global_amax, amax_dev, codes, scales, y_out, *info,
-                                         static_cast<hipStream_t>(stream));
+  hipError_t e = nvfp4act::launch_swiglu(p, *info, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
+}
+
+int swiglu_call(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f, float global_amax,
+                float* amax_dev, void* codes, void* scales, void* y_out, void* stream) {
+  if (m < 0 || f <= 0 || f % 64 != 0 || ld < f) return NVFP4ACT_ERR_SHAPE;
+  if (m == 0) return NVFP4ACT_OK;
+  if (!up || !gate || !codes || !scales) return NVFP4ACT_ERR_NULL;
+  if (!aligned16(up) || !aligned16(gate) || !aligned16(codes) || !aligned16(scales) ||
+      (ld * 2) % 16 != 0 || (y_out && !aligned16(y_out)))
+    return NVFP4ACT_ERR_ALIGN;
+  nvfp4act::SwigluLaunch p{};
+  p.up = up;
+  p.gate = gate;
+  p.paired = false;
+  p.ld = ld;
+  p.m = m;
+  p.f = f;
+  p.global_amax = global_amax;
+  p.amax_dev = amax_dev;
+  p.codes = codes;
+  p.scales = scales;
+  p.y_out = y_out;
+  return swiglu_launch(p, stream);
+}
+
+bool packed_shape_ok(int interleaved, int64_t ld, int64_t m, int64_t f) {
+  return m >= 0 && f > 0 && f % 64 == 0 && ld >= 2 * f && (interleaved == 0 || interleaved == 1);
+}
+
+int swiglu_packed_call(const void* proj, const void* bias, int interleaved, int64_t ld, int64_t m, int64_t f,
+                       float global_amax, float* amax_dev, void* codes, void* scales, void* y_out, void* stream) {
+  if (!packed_shape_ok(interleaved, ld, m, f)) return NVFP4ACT_ERR_SHAPE;
+  if (m == 0) return NVFP4ACT_OK;
+  if (!proj || !codes || !scales) return NVFP4ACT_ERR_NULL;
+  if (!aligned16(proj) || !aligned16(codes) || !aligned16(scales) || (ld * 2) % 16 != 0 ||
+      (bias && !aligned16(bias)) || (y_out && !aligned16(y_out)))
+    return NVFP4ACT_ERR_ALIGN;
+  const uint16_t* o = static_cast<const uint16_t*>(proj);
+  const uint16_t* b = static_cast<const uint16_t*>(bias);
+  nvfp4act::SwigluLaunch p{};
+  p.up = proj;
+  p.paired = interleaved == 1;
+  p.gate = p.paired ? nullptr : o + f;                 // value-first: gate half f columns on
+  p.bias_up = bias;
+  p.bias_gate = (b && !p.paired) ? b + f : nullptr;
+  p.ld = ld;
+  p.m = m;
+  p.f = f;
+  p.global_amax = global_amax;
+  p.amax_dev = amax_dev;
+  p.codes = codes;
+  p.scales = scales;
+  p.y_out = y_out;
+  return swiglu_launch(p, stream);
 }
 
 // The per-call forms need the amax destination: one 4-byte aligned float (m == 0 aside).
@@ -281,6 +327,19 @@ int swiglu_nvfp4_dynamic(const void* up, const void* gate, int64_t ld, int64_t m
   int st = check_amax_out(m, amax_out);
   if (st != NVFP4ACT_OK) return st;
   return swiglu_call(up, gate, ld, m, f, 0.0f, amax_out, codes, scales, y_out, stream);
+}
+
+int swiglu_packed_nvfp4(const void* proj, const void* bias, int interleaved, int64_t ld, int64_t m, int64_t f,
+                        float global_amax, void* codes, void* scales, void* y_out, void* stream) {
+  return swiglu_packed_call(proj, bias, interleaved, ld, m, f, global_amax, nullptr, codes, scales, y_out, stream);
+}
+
+int swiglu_packed_nvfp4_dynamic(const void* proj, const void* bias, int interleaved, int64_t ld, int64_t m,
+                                int64_t f, float* amax_out, void* codes, void* scales, void* y_out, void* stream) {
+  if (!packed_shape_ok(interleaved, ld, m, f)) return NVFP4ACT_ERR_SHAPE;
+  int st = check_amax_out(m, amax_out);
+  if (st != NVFP4ACT_OK) return st;
+  return swiglu_packed_call(proj, bias, interleaved, ld, m, f, 0.0f, amax_out, codes, scales, y_out, stream);
 }
 
 }  // extern "C"

@@ -45,10 +45,27 @@ struct RmsLaunch {
 
 hipError_t launch_rms_adaln(const RmsLaunch& p, const DeviceInfo& dev, hipStream_t stream);
 
-// amax_dev: as for RmsLaunch (null: static global_amax; else the per-call amax of y).
-hipError_t launch_swiglu(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f,
-                         float global_amax, float* amax_dev, void* codes, void* scales, void* y_out,
-                         const DeviceInfo& dev, hipStream_t stream);
+// The arguments of one SwiGLU call.  Value-first or two-pointer form (paired == false):
+// row r of the values at up + r*ld and of the gates at gate + r*ld (bf16 elements);
+// bias_up / bias_gate: null, or the f-entry bf16 biases of the value and gate columns.
+// Paired form: row r of the projection at up + r*ld, the value of output column j at 2j and
+// its gate at 2j + 1; gate and bias_gate unused; bias_up: null or one 2f-entry paired bias
+// row.  amax_dev: as for RmsLaunch (null: static global_amax; else the per-call amax of y).
+struct SwigluLaunch {
+  const void* up;
+  const void* gate;
+  const void* bias_up;
+  const void* bias_gate;
+  bool paired;
+  int64_t ld, m, f;
+  float global_amax;
+  float* amax_dev;
+  void* codes;
+  void* scales;
+  void* y_out;
+};
+
+hipError_t launch_swiglu(const SwigluLaunch& p, const DeviceInfo& dev, hipStream_t stream);
 
 // Per-device, once: allow the LDS sizes the kernels use.
 hipError_t prepare_rms_adaln();

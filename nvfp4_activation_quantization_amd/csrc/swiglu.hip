@@ -1,7 +1,10 @@
 // swiglu.hip -- SwiGLU producer -> NVFP4 (FastVideo API page, swiglu_quantize over a
 // value-first [M, 2F] projection; TensorRT-LLM PR #21483, SiLU-and-mul producer):
 //   y = bf16(S[gate] * up),  S[g] = bf16(g * sigmoid(g)) correctly rounded
-// followed by the NVFP4 block quantizer.
+// followed by the NVFP4 block quantizer.  Two forms of the same kernel widen it:
+// a bias added to value and gate before SiLU (swiglu_quantize's bias, as a bf16 add:
+// up = bf16(up + bias_up), gate = bf16(gate + bias_gate)), and the paired column layout of
+// the FastVideo branch compare's quant_probe (value of column j at 2j, gate at 2j + 1).
 //
 // S is a 65,536-entry bf16 table indexed by the gate's bit pattern, built once per
 // device in fp64 by silu_table_kernel.  Each workgroup (one per CU, persistent over a
@@ -73,27 +76,70 @@ __global__ void silu_table_kernel() {
   g_silu_table[g] = (uint16_t)out;
 }
 
+// The kernel arguments.  Two-pointer / value-first form: value row r at up + r*ld8 and gate
+// row r at gate + r*ld8 (uint4 units).  Paired form: row r of the projection at up + r*ld8,
+// output chunk c (8 columns) in its uint4s 2c and 2c+1, each 32-bit word holding one column's
+// value (low half) and gate (high half); gate is unused.  bias_up / bias_gate: the bf16 bias
+// of the value and gate columns (value-first), or bias_up alone as one paired row.
+struct SwArgs {
+  const uint4* up;
+  const uint4* gate;
+  const uint4* bias_up;
+  const uint4* bias_gate;
+  int64_t ld8, m, f;
+  float global_amax;
+  const float* amax_dev;
+  float* amax_out;
+  uint32_t* codes;
+  uint8_t* scales;
+  uint4* y_out;
+  int64_t col_tiles, ntiles;
+};
+
+__device__ __forceinline__ uint32_t words_at(const uint4& v, int q) {
+  return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+}
+
+// bf16(a + b) for the two bf16 values of a word each (the bias add).
+__device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b) {
+  return pack_bf16x2(bf16_lo(a) + bf16_lo(b), bf16_hi(a) + bf16_hi(b));
+}
+
 // One 128-row x kTileCols tile: each wavefront takes rows wave, wave + 16, ... (8 rows),
 // kRowBatch at a time; scale bytes go to the tile's LDS block.  AMAX (the amax pass of a
 // per-call scale): nothing is quantized or stored; max |y| is folded into *lane_amax.
-template <bool AMAX>
-__device__ __forceinline__ void swiglu_tile(const uint4* up, const uint4* gate, int64_t ld8, int64_t m,
-                                            int64_t row_chunks, uint32_t* codes, uint4* y_out,
-                                            int64_t tile_row, int64_t c0, int64_t tchunks, int lane, int wave,
-                                            const uint16_t* table, float gsf, const float* inv_tab,
-                                            uint8_t* sc_lane, float* lane_amax) {
+template <bool AMAX, bool PAIRED, bool BIAS>
+__device__ __forceinline__ void swiglu_tile(const SwArgs& a, int64_t row_chunks, int64_t tile_row, int64_t c0,
+                                            int64_t tchunks, int lane, int wave, const uint16_t* table, float gsf,
+                                            const float* inv_tab, uint8_t* sc_lane, float* lane_amax) {
   const int64_t r0 = tile_row << 7;
-  const int64_t rows = (m - r0 < 128) ? (m - r0 > 0 ? m - r0 : 0) : 128;
+  const int64_t rows = (a.m - r0 < 128) ? (a.m - r0 > 0 ? a.m - r0 : 0) : 128;
   const int64_t c = c0 + lane;
   const bool lane_ok = lane < tchunks;
+  // this lane's 16 bias values: (value, gate) of its 8 columns, laid out like one row's loads
+  uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
+  if (BIAS && lane_ok) {
+    if (PAIRED) {
+      b0 = global_ptr(a.bias_up)[2 * c];
+      b1 = global_ptr(a.bias_up)[2 * c + 1];
+    } else {
+      b0 = global_ptr(a.bias_up)[c];
+      b1 = global_ptr(a.bias_gate)[c];
+    }
+  }
   for (int64_t rb = wave * kRowBatch; rb < rows; rb += kWaves * kRowBatch) {
     uint4 u[kRowBatch], g[kRowBatch];
 #pragma unroll
     for (int i = 0; i < kRowBatch; ++i) {
       const int64_t r = r0 + rb + i;
       if (rb + i < rows && lane_ok) {
-        u[i] = load_stream(reinterpret_cast<const uint4*>(global_ptr(up) + r * ld8 + c));
-        g[i] = load_stream(reinterpret_cast<const uint4*>(global_ptr(gate) + r * ld8 + c));
+        if (PAIRED) {
+          u[i] = load_stream(a.up + r * a.ld8 + 2 * c);
+          g[i] = load_stream(a.up + r * a.ld8 + 2 * c + 1);
+        } else {
+          u[i] = load_stream(a.up + r * a.ld8 + c);
+          g[i] = load_stream(a.gate + r * a.ld8 + c);
+        }
       } else {
         u[i] = make_uint4(0, 0, 0, 0);
         g[i] = make_uint4(0, 0, 0, 0);
@@ -102,29 +148,42 @@ __device__ __forceinline__ void swiglu_tile(const uint4* up, const uint4* gate, 
 #pragma unroll
     for (int i = 0; i < kRowBatch; ++i) {
       const int64_t rr = rb + i;
-      const uint32_t gw[4] = {g[i].x, g[i].y, g[i].z, g[i].w};
-      const uint32_t uw[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
       float y[8];
+      if (PAIRED) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float s0 = __uint_as_float((uint32_t)table[gw[q] & 0xFFFFu] << 16);
-        const float s1 = __uint_as_float((uint32_t)table[gw[q] >> 16] << 16);
-        y[2 * q] = round_bf16(s0 * bf16_lo(uw[q]));
-        y[2 * q + 1] = round_bf16(s1 * bf16_hi(uw[q]));
+        for (int e = 0; e < 8; ++e) {
+          uint32_t w = words_at(e < 4 ? u[i] : g[i], e & 3);
+          if (BIAS) w = add_bf16x2(w, words_at(e < 4 ? b0 : b1, e & 3));
+          const float s = __uint_as_float((uint32_t)table[w >> 16] << 16);
+          y[e] = round_bf16(s * bf16_lo(w));
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t uw = words_at(u[i], q), gw = words_at(g[i], q);
+          if (BIAS) {
+            uw = add_bf16x2(uw, words_at(b0, q));
+            gw = add_bf16x2(gw, words_at(b1, q));
+          }
+          const float s0 = __uint_as_float((uint32_t)table[gw & 0xFFFFu] << 16);
+          const float s1 = __uint_as_float((uint32_t)table[gw >> 16] << 16);
+          y[2 * q] = round_bf16(s0 * bf16_lo(uw));
+          y[2 * q + 1] = round_bf16(s1 * bf16_hi(uw));
+        }
       }
       if (AMAX) {
-        // lanes past the real rows or columns loaded zeros, whose y is 0
-        *lane_amax = fold_abs8(*lane_amax, y);
+        // rows past the tensor loaded zeros, but a bias would make their y nonzero
+        if (rr < rows && lane_ok) *lane_amax = fold_abs8(*lane_amax, y);
         continue;
       }
       uint32_t s;
       const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
       if (rr < rows && lane_ok) {
         const int64_t r = r0 + rr;
-        global_ptr(codes)[r * row_chunks + c] = code;
+        global_ptr(a.codes)[r * row_chunks + c] = code;
         sc_lane[(rr & 31) * 16 + ((rr >> 5) & 3) * 4] = (uint8_t)s;
-        if (y_out)
-          global_ptr(y_out)[r * row_chunks + c] =
+        if (a.y_out)
+          global_ptr(a.y_out)[r * row_chunks + c] =
               make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
                          pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
       }
@@ -132,14 +191,8 @@ __device__ __forceinline__ void swiglu_tile(const uint4* up, const uint4* gate, 
   }
 }
 
-template <bool AMAX>
-__global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restrict__ up,
-                                                          const uint4* __restrict__ gate, int64_t ld8,
-                                                          int64_t m, int64_t f, float global_amax,
-                                                          const float* amax_dev, float* amax_out,
-                                                          uint32_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales, uint4* y_out,
-                                                          int64_t col_tiles, int64_t ntiles) {
+template <bool AMAX, bool PAIRED, bool BIAS>
+__global__ __launch_bounds__(kThreads) void swiglu_kernel(const SwArgs a) {
   __shared__ float amax_red[kWaves];
   extern __shared__ uint4 lds4[];
   uint16_t* table = reinterpret_cast<uint16_t*>(lds4);
@@ -148,9 +201,9 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restric
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  if ((int64_t)blockIdx.x >= ntiles) return;              // idle workgroup (uniform)
+  if ((int64_t)blockIdx.x >= a.ntiles) return;            // idle workgroup (uniform)
 
-  const float gsf = call_global_scale(global_amax, amax_dev);
+  const float gsf = call_global_scale(a.global_amax, a.amax_dev);
   float lane_amax = 0.0f;
   fill_inverse_table(inv_tab, gsf, tid);
   const uint4* src = reinterpret_cast<const uint4*>(g_silu_table);
@@ -158,20 +211,20 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restric
   for (int i = tid; i < kScaleBytes / 16; i += kThreads) tile_sc[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  const int64_t row_chunks = f >> 3;
+  const int64_t row_chunks = a.f >> 3;
   uint8_t* sc_lane = reinterpret_cast<uint8_t*>(tile_sc) + scale_lane_offset(lane);
-  for (int64_t t = blockIdx.x; t < ntiles; t += gridDim.x) {
-    const int64_t tile_row = t / col_tiles, col_tile = t % col_tiles;
+  for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
+    const int64_t tile_row = t / a.col_tiles, col_tile = t % a.col_tiles;
     const int64_t c0 = col_tile * (kTileCols / 8);
     const int64_t tchunks = (row_chunks - c0 < kTileCols / 8) ? row_chunks - c0 : kTileCols / 8;
-    swiglu_tile<AMAX>(up, gate, ld8, m, row_chunks, codes, y_out, tile_row, c0, tchunks, lane, wave, table, gsf,
-                      inv_tab, sc_lane, &lane_amax);
+    swiglu_tile<AMAX, PAIRED, BIAS>(a, row_chunks, tile_row, c0, tchunks, lane, wave, table, gsf, inv_tab,
+                                    sc_lane, &lane_amax);
     if (AMAX) continue;
     __syncthreads();
     // copy the tile's scale slice out and zero it for the next tile (each thread clears
     // exactly the words it copied)
     NVFP4_GLOBAL uint4* dst = reinterpret_cast<NVFP4_GLOBAL uint4*>(
-        global_ptr(scales) + (tile_row * (f >> 6) + c0 / 8) * 512);
+        global_ptr(a.scales) + (tile_row * (a.f >> 6) + c0 / 8) * 512);
     const int words = (int)(tchunks / 8) * 32;
     for (int i = tid; i < words; i += kThreads) {
       dst[i] = tile_sc[i];
@@ -179,7 +232,38 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const uint4* __restric
     }
     __syncthreads();
   }
-  if (AMAX) workgroup_max_to(amax_out, lane_amax, amax_red, kWaves);
+  if (AMAX) workgroup_max_to(a.amax_out, lane_amax, amax_red, kWaves);
+}
+
+constexpr size_t kSwigluLds = kTableBytes + 512 + kScaleBytes;
+
+template <bool AMAX, bool PAIRED, bool BIAS>
+hipError_t allow_lds() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&swiglu_kernel<AMAX, PAIRED, BIAS>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSwigluLds);
+}
+
+template <bool PAIRED, bool BIAS>
+hipError_t launch_form(SwArgs a, int64_t grid, hipStream_t stream) {
+  if (a.amax_out) {
+    // per-call scale: zero the amax, fold max |y| into it, then quantize with it
+    hipError_t e = launch_zero_amax(a.amax_out, stream);
+    if (e != hipSuccess) return e;
+    SwArgs p = a;
+    p.amax_dev = nullptr;
+    p.codes = nullptr;
+    p.scales = nullptr;
+    p.y_out = nullptr;
+    hipLaunchKernelGGL((swiglu_kernel<true, PAIRED, BIAS>), dim3((uint32_t)grid), dim3(kThreads), kSwigluLds,
+                       stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    a.amax_dev = a.amax_out;
+    a.amax_out = nullptr;
+  }
+  hipLaunchKernelGGL((swiglu_kernel<false, PAIRED, BIAS>), dim3((uint32_t)grid), dim3(kThreads), kSwigluLds,
+                     stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -197,38 +281,41 @@ hipError_t build_silu_table(unsigned int* ambiguous) {
 }
 
 hipError_t prepare_swiglu() {
-  const int lds = (int)(kTableBytes + 512 + kScaleBytes);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&swiglu_kernel<false>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&swiglu_kernel<true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipError_t e = allow_lds<false, false, false>();
+  if (e == hipSuccess) e = allow_lds<true, false, false>();
+  if (e == hipSuccess) e = allow_lds<false, false, true>();
+  if (e == hipSuccess) e = allow_lds<true, false, true>();
+  if (e == hipSuccess) e = allow_lds<false, true, false>();
+  if (e == hipSuccess) e = allow_lds<true, true, false>();
+  if (e == hipSuccess) e = allow_lds<false, true, true>();
+  if (e == hipSuccess) e = allow_lds<true, true, true>();
   return e;
 }
 
-hipError_t launch_swiglu(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f,
-                         float global_amax, float* amax_dev, void* codes, void* scales, void* y_out,
-                         const DeviceInfo& dev, hipStream_t stream) {
-  const int64_t tile_rows = (m + 127) / 128;
-  const int64_t col_tiles = (f + kTileCols - 1) / kTileCols;
+hipError_t launch_swiglu(const SwigluLaunch& p, const DeviceInfo& dev, hipStream_t stream) {
+  const int64_t tile_rows = (p.m + 127) / 128;
+  const int64_t col_tiles = (p.f + kTileCols - 1) / kTileCols;
   const int64_t ntiles = tile_rows * col_tiles;
   const int64_t grid = ntiles < dev.cu_count ? ntiles : dev.cu_count;
-  const size_t lds = kTableBytes + 512 + kScaleBytes;
-  const uint4* u = static_cast<const uint4*>(up);
-  const uint4* g = static_cast<const uint4*>(gate);
-  if (amax_dev) {
-    // per-call scale: zero the amax, fold max |y| into it, then quantize with it
-    hipError_t e = launch_zero_amax(amax_dev, stream);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(swiglu_kernel<true>, dim3((uint32_t)grid), dim3(kThreads), lds, stream, u, g, ld / 8, m, f,
-                       global_amax, nullptr, amax_dev, nullptr, nullptr, nullptr, col_tiles, ntiles);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL(swiglu_kernel<false>, dim3((uint32_t)grid), dim3(kThreads), lds, stream, u, g, ld / 8, m, f,
-                     global_amax, amax_dev, nullptr, static_cast<uint32_t*>(codes), static_cast<uint8_t*>(scales),
-                     static_cast<uint4*>(y_out), col_tiles, ntiles);
-  return hipGetLastError();
+  SwArgs a;
+  a.up = static_cast<const uint4*>(p.up);
+  a.gate = static_cast<const uint4*>(p.gate);
+  a.bias_up = static_cast<const uint4*>(p.bias_up);
+  a.bias_gate = static_cast<const uint4*>(p.bias_gate);
+  a.ld8 = p.ld / 8;
+  a.m = p.m;
+  a.f = p.f;
+  a.global_amax = p.global_amax;
+  a.amax_dev = nullptr;
+  a.amax_out = p.amax_dev;
+  a.codes = static_cast<uint32_t*>(p.codes);
+  a.scales = static_cast<uint8_t*>(p.scales);
+  a.y_out = static_cast<uint4*>(p.y_out);
+  a.col_tiles = col_tiles;
+  a.ntiles = ntiles;
+  const bool bias = p.bias_up != nullptr;
+  if (p.paired) return bias ? launch_form<true, true>(a, grid, stream) : launch_form<true, false>(a, grid, stream);
+  return bias ? launch_form<false, true>(a, grid, stream) : launch_form<false, false>(a, grid, stream);
 }
 
 }  // namespace nvfp4act

@@ -11,6 +11,8 @@ TensorRT-LLM fusions apply only to static NVFP4 scales).  For each workload:
   rms_adaln_63240x7168   max |y| of the oracle on 8,192 calibration rows,
   rms_adaln_300000x7168    frame index (r * T) // 8192
   swiglu_16384x19456     max |y| of the oracle on 2,048 calibration rows
+  swiglu_bias_16384x19456, swiglu_paired_16384x19456
+                         the same, with the workload's bias and column layout
 
 Run:  python tests/golden/make_calibration.py
 """
@@ -43,6 +45,10 @@ def calibrate(w: workloads.Workload) -> dict:
     elif w.kind == "quantize":
         amax = amax_of_bf16(w.calibration_x())
         how = "max|x| over %d calibration rows" % w.cal_rows
+    elif w.kind == "swiglu" and (w.bias_std > 0 or w.interleaved):
+        res = oracle.swiglu_packed_rows(w.calibration_x(), w.bias(), w.interleaved, 1.0, want_y=True)
+        amax = amax_of_bf16(res["y"])
+        how = "max|y| of the oracle over %d calibration rows" % w.cal_rows
     elif w.kind == "swiglu":
         o = w.calibration_x()
         res = oracle.swiglu_rows(o[:, :w.k], o[:, w.k:], 1.0, want_y=True)

@@ -91,11 +91,39 @@ def test_swiglu_status_codes():
     assert sw(m=0) == 0
 
 
+def swp(dynamic=False, **kw):
+    a = dict(proj=A, bias=A, il=0, ld=128, m=4, f=64, amax=1.0, amax_out=A, codes=A, scales=A, y=None)
+    a.update(kw)
+    if dynamic:
+        return lib.swiglu_packed_nvfp4_dynamic(a["proj"], a["bias"], a["il"], a["ld"], a["m"], a["f"],
+                                               a["amax_out"], a["codes"], a["scales"], a["y"], None)
+    return lib.swiglu_packed_nvfp4(a["proj"], a["bias"], a["il"], a["ld"], a["m"], a["f"], a["amax"],
+                                   a["codes"], a["scales"], a["y"], None)
+
+
+@pytest.mark.parametrize("dynamic", [False, True])
+def test_swiglu_packed_status_codes(dynamic):
+    for key in ("proj", "codes", "scales"):
+        assert swp(dynamic, **{key: None}) == 1, key
+    # the row must hold both halves: ld >= 2f; only layouts 0 and 1 exist
+    assert swp(dynamic, ld=127) == 2 and swp(dynamic, ld=64) == 2 and swp(dynamic, f=48) == 2
+    assert swp(dynamic, m=-1) == 2 and swp(dynamic, il=2) == 2 and swp(dynamic, il=-1) == 2
+    assert swp(dynamic, proj=U) == 3 and swp(dynamic, bias=U) == 3 and swp(dynamic, ld=132) == 3
+    assert swp(dynamic, y=U) == 3
+    assert swp(dynamic, m=0) == 0 and swp(dynamic, m=0, il=1, bias=None) == 0
+    if dynamic:
+        assert swp(True, amax_out=None) == 1 and swp(True, amax_out=A + 2) == 3
+        assert swp(True, m=0, amax_out=None) == 0
+    else:
+        assert swp(amax=float("inf")) == 4 and swp(amax=0.0) == 4
+
+
 def test_valid_call_without_a_gpu_reports_no_device():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible: a valid call would launch on fake pointers")
     assert q() == 5 and rms() == 5 and sw() == 5
+    assert swp() == 5 and swp(bias=None, il=1) == 5 and swp(True) == 5
     assert lib.nvfp4act_init() == 5
 
 

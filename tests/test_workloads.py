@@ -59,3 +59,14 @@ def test_calibration_file_reproduces_for_the_tiny_workload():
     res = oracle.rms_adaln_rows(w.x(), w.weight(), w.table(), w.frame_idx(), w.eps, 1.0, want_y=True)
     amax = float(np.max(np.abs(oracle.bf16_to_f32(res["y"]))))
     assert amax == data[w.name]["global_amax"] == workloads.calibration_amax(w.name)
+
+
+def test_packed_swiglu_workloads():
+    for name, paired in [("swiglu_bias_16384x19456", False), ("swiglu_paired_16384x19456", True)]:
+        w = workloads.get(name)
+        assert w.interleaved == paired and w.in_cols == 2 * w.k
+        b = w.bias()
+        assert b.shape == (2 * w.k,) and b.dtype == np.uint16 and np.array_equal(b, w.bias())
+        assert 0.2 < float(np.std(oracle.bf16_to_f32(b))) < 0.3
+        assert w.algorithmic_bytes() == 1_454_374_912 and w.param_bytes() == 4 * w.k
+    assert workloads.get("swiglu_16384x19456").bias() is None

@@ -77,6 +77,22 @@ def oracle_swiglu(up, gate, amax, want_y=True, gsf=None):
     return out
 
 
+def oracle_swiglu_packed(proj, bias, interleaved, amax, want_y=True, gsf=None):
+    """oracle.swiglu_packed_rows over row blocks in parallel threads."""
+    n = proj.shape[0]
+    oracle.silu_table()
+
+    def part(se):
+        s, e = se
+        return oracle.swiglu_packed_rows(proj[s:e], bias, interleaved, amax, want_y=want_y, gsf=gsf)
+
+    with ThreadPoolExecutor(threads()) as ex:
+        res = list(ex.map(part, split_rows(n, 4 * threads())))
+    out = {key: np.concatenate([r[key] for r in res]) for key in ("codes", "scale_bytes")}
+    out["y"] = np.concatenate([r["y"] for r in res]) if want_y else None
+    return out
+
+
 def scales_from_rows(scale_bytes: np.ndarray, m: int, k: int, rows=None) -> np.ndarray:
     """Place plain-order scale bytes of rows into a zeroed swizzled [pad(m), k/16] buffer."""
     buf = np.zeros(oracle.padded_rows(m) * (k // 16), np.uint8)

@@ -16,10 +16,13 @@ a 34x60 latent grid per frame over 31 frames = 63,240 tokens from
   rms_adaln_63240x7168     RMSNorm+adaLN at the H3 block shape (31 frames)
   swiglu_16384x19456       SwiGLU producer over a value-first [M, 2F] projection
   rms_adaln_300000x7168    RMSNorm+adaLN over 2.15e9 elements (147 frames)
+  swiglu_bias_16384x19456  the same projection shape, value-first, with a bf16 bias
+                           of 2F values (std 0.25) added before SiLU
+  swiglu_paired_16384x19456  the same with value/gate columns paired (2j, 2j + 1)
 
 Seeds: numpy ``PCG64``; the seed of role ``role`` in workload number ``i``
-(1..5 in the order above) is ``1000*i + role`` with roles 1 x, 2 weight,
-3 modulation table, 4 calibration rows, 5 outlier pick, 6 per-head std.
+(1..7 in the order above) is ``1000*i + role`` with roles 1 x, 2 weight (or
+bias), 3 modulation table, 4 calibration rows, 5 outlier pick, 6 per-head std.
 Large tensors are drawn in 4096-row chunks, chunk ``c`` from
 ``SeedSequence(1000*i + role).spawn(n_chunks)[c]``, so any chunk can be
 regenerated alone and chunks can be drawn in parallel threads.
@@ -63,6 +66,8 @@ class Workload:
     eps: float = 1e-6
     outliers: str = ""        # "iid1pct_x20" | "cols36_x30" | ""
     cal_rows: int = 0         # calibration rows for the static amax (0: from the data itself)
+    bias_std: float = 0.0     # swiglu: std of the 2F-entry bias (0: no bias)
+    interleaved: bool = False  # swiglu: value/gate columns paired instead of value-first
     extra: dict = field(default_factory=dict)
 
     # ---- sizes -------------------------------------------------------------
@@ -82,6 +87,8 @@ class Workload:
     def param_bytes(self) -> int:
         if self.kind == "rms_adaln":
             return 2 * self.k + 2 * self.frames * 2 * self.k + 4 * self.m
+        if self.kind == "swiglu" and self.bias_std > 0:
+            return 2 * 2 * self.k
         return 0
 
     # ---- generation ----------------------------------------------------------
@@ -157,6 +164,12 @@ class Workload:
     def weight(self) -> np.ndarray:
         return to_bf16(1.0 + 0.1 * rng(self.number, ROLE_W).standard_normal(self.k, dtype=np.float32))
 
+    def bias(self) -> np.ndarray | None:
+        """swiglu: the [2k] bf16 bias in the projection's column order, or None."""
+        if self.bias_std <= 0:
+            return None
+        return to_bf16(self.bias_std * rng(self.number, ROLE_W).standard_normal(2 * self.k, dtype=np.float32))
+
     def table(self) -> np.ndarray:
         """[frames, 2, k] bf16: row t holds (shift, scale) of frame t."""
         t = 0.1 * rng(self.number, ROLE_TABLE).standard_normal((self.frames, 2, self.k),
@@ -189,6 +202,9 @@ WORKLOADS = {
         Workload("swiglu_16384x19456", 4, "swiglu", 16384, 19456, cal_rows=2048),
         Workload("rms_adaln_300000x7168", 5, "rms_adaln", 300000, 7168, frames=147,
                  rows_per_frame=2041, outliers="cols36_x30", cal_rows=8192),
+        Workload("swiglu_bias_16384x19456", 6, "swiglu", 16384, 19456, cal_rows=2048, bias_std=0.25),
+        Workload("swiglu_paired_16384x19456", 7, "swiglu", 16384, 19456, cal_rows=2048, bias_std=0.25,
+                 interleaved=True),
     ]
 }
 
