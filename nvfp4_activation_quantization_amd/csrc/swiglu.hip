@@ -134,8 +134,11 @@ __device__ __forceinline__ void swiglu_tile(const SwArgs& a, int64_t row_chunks,
       const int64_t r = r0 + rb + i;
       if (rb + i < rows && lane_ok) {
         if (PAIRED) {
-          u[i] = load_stream(a.up + r * a.ld8 + 2 * c);
-          g[i] = load_stream(a.up + r * a.ld8 + 2 * c + 1);
+          // 32 contiguous bytes per lane: each of the two loads covers half of every
+          // 128-byte line of the wave's 2 KiB, so the second must find the line still in
+          // the L1 cache -- plain loads, not the streaming (nontemporal) ones
+          u[i] = global_ptr(a.up)[r * a.ld8 + 2 * c];
+          g[i] = global_ptr(a.up)[r * a.ld8 + 2 * c + 1];
         } else {
           u[i] = load_stream(a.up + r * a.ld8 + c);
           g[i] = load_stream(a.gate + r * a.ld8 + c);

@@ -75,6 +75,9 @@ def _load():
             "orc_swiglu_packed_rows_gsf": (None, [P, P, ctypes.c_int, I64, I64, I64, P, P, F,
                                                   P, P, P, P]),
             "orc_rms_rstd": (F, [P, I64, F]),
+            "orc_rms_sum_f32": (F, [P, I64]),
+            "orc_rms_rstd_f32": (F, [P, I64, F]),
+            "orc_residual_rms_rows_gsf": (None, [P, P, P, P, P, F, I64, I64, P, F, P, P, P, P, P]),
             "orc_quantize_rows": (None, [P, I64, I64, F, P, P]),
             "orc_nvfp4_quantize": (None, [P, I64, I64, F, P, P]),
             "orc_rms_adaln_rows": (None, [P, I64, I64, P, P, P, P, I64, I64, P, F, F,
@@ -255,6 +258,61 @@ def rms_adaln_dynamic(x_u16, w_u16, table_u16, frame_idx, eps: float, want_y: bo
     amax = max_abs(first["y"])
     out = rms_adaln_rows(x_u16, w_u16, table_u16, frame_idx, eps, 0.0, want_y=want_y,
                          scales_rows=scales_rows, gsf=dynamic_global_scale(amax))
+    out["amax"] = amax
+    return out
+
+
+def rms_sum_f32(h_row) -> float:
+    """The fixed-tree sum of h^2 over one fp32 row (k % 256 == 0)."""
+    h = _c(h_row, np.float32).reshape(-1)
+    return _load().orc_rms_sum_f32(_ptr(h), h.size)
+
+
+def rms_rstd_f32(h_row, eps: float) -> float:
+    h = _c(h_row, np.float32).reshape(-1)
+    return _load().orc_rms_rstd_f32(_ptr(h), h.size, float(eps))
+
+
+def residual_rms_rows(h_f32, o_u16, bias_u16, scale_f32, gamma_f32, eps: float, global_amax: float,
+                      row_ids=None, want_y: bool = False, scales_rows: int | None = None,
+                      gsf: float | None = None):
+    """fp32 residual stream + RMSNorm (fp32 gamma) -> NVFP4 over rows.
+
+    h_f32 [n, k] is not modified: the updated stream is returned as 'h'.  o_u16 [n, k]
+    bf16 or None (no residual add); bias_u16 [k] bf16 or None; scale_f32, gamma_f32 [k].
+    gsf: use this global scale as is (global_amax is then ignored).
+    Returns dict(codes, scale_bytes, y, scales, rstd, h).
+    """
+    h = np.array(h_f32, dtype=np.float32, copy=True, order="C")
+    n, k = h.shape
+    o = None if o_u16 is None else _c(o_u16, np.uint16)
+    bias = None if bias_u16 is None else _c(bias_u16, np.uint16).reshape(-1)
+    scale = None if scale_f32 is None else _c(scale_f32, np.float32).reshape(-1)
+    gamma = _c(gamma_f32, np.float32).reshape(-1)
+    if o is not None and (o.shape != (n, k) or scale is None or scale.size != k):
+        raise ValueError("o must be [n, k] and scale [k] when a residual is given")
+    if gamma.size != k or (bias is not None and bias.size != k):
+        raise ValueError("gamma and bias hold k values")
+    rid = None if row_ids is None else _c(row_ids, np.int64)
+    codes = np.empty((n, k // 2), np.uint8)
+    sb = np.empty((n, k // 16), np.uint8)
+    rstd = np.empty(n, np.float32)
+    y = np.empty((n, k), np.uint16) if want_y else None
+    scales = None if scales_rows is None else np.zeros((scales_rows, k // 16), np.uint8)
+    g = float(global_scale(global_amax) if gsf is None else gsf)
+    _load().orc_residual_rms_rows_gsf(_ptr(h), _ptr(o), _ptr(bias), _ptr(scale), _ptr(gamma), float(eps), n, k,
+                                      _ptr(rid), g, _ptr(codes), _ptr(sb), _ptr(scales), _ptr(rstd), _ptr(y))
+    return dict(codes=codes, scale_bytes=sb, y=y, scales=scales, rstd=rstd, h=h)
+
+
+def residual_rms_dynamic(h_f32, o_u16, bias_u16, scale_f32, gamma_f32, eps: float, want_y: bool = False,
+                         scales_rows: int | None = None):
+    """residual_rms_rows under the amax of the call's own y (two passes over the same
+    input h).  The result dict gains 'amax'."""
+    first = residual_rms_rows(h_f32, o_u16, bias_u16, scale_f32, gamma_f32, eps, 1.0, want_y=True)
+    amax = max_abs(first["y"])
+    out = residual_rms_rows(h_f32, o_u16, bias_u16, scale_f32, gamma_f32, eps, 0.0, want_y=want_y,
+                            scales_rows=scales_rows, gsf=dynamic_global_scale(amax))
     out["amax"] = amax
     return out
 

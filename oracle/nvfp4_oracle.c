@@ -26,6 +26,9 @@
  *   [INT64]   FastVideo commit log, branch vae-parallel-decode: the int64
  *             indexing fix at 2^31 elements and the frame-index bounds
  *             contract of the modulation wrappers.
+ *   [H3-API residual_norm_quantize]  the fp32 residual stream: in-place
+ *             h += bf16(o + bias) * scale, then NVFP4 of bf16(rms_norm(h,
+ *             gamma, eps)) with fp32 gamma; hidden size a multiple of 512.
  *
  * Readings taken where the pages are silent (each is listed in the design doc):
  *   - global scale gsf = 2688 / global_amax (448 * 6), IEEE fp32 division;
@@ -33,7 +36,10 @@
  *   - inverse scale = gsf / dec(s) (IEEE), and 0 when the scale code is 0;
  *   - RMSNorm statistic: the fixed reduction tree of rms_rstd() below;
  *   - RMSNorm output is rounded to bf16 before the weight multiply;
- *   - SiLU is tabulated as the correctly rounded bf16 of g*sigmoid(g).
+ *   - SiLU is tabulated as the correctly rounded bf16 of g*sigmoid(g);
+ *   - fp32 residual stream: the quad tree of rms_sum_f32() below; the product
+ *     t * scale is rounded before the add (no fused multiply-add); the norm
+ *     is (h * rstd) * gamma in fp32, rounded to bf16 once.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math (SSE float, no x87
  * for the fp32 chain).  Every entry point clears FTZ/DAZ and selects
@@ -431,6 +437,104 @@ EXPORT void orc_rms_adaln_rows(const uint16_t* x, int64_t n, int64_t k, const in
     leave_ieee(s);
     orc_rms_adaln_rows_gsf(x, n, k, row_ids, w, shift, scale, frame_stride, num_frames, frame_idx, eps, gsf,
                            codes, scale_bytes, scales, rstd_out, y_out, status);
+}
+
+/* ------------------------------------------------------------------------- */
+/* fp32 residual stream + RMSNorm -> NVFP4                                   */
+/* ------------------------------------------------------------------------- */
+
+/* Sum of h^2 over an fp32 row in a fixed tree (the fp32 counterpart of
+   rms_rstd's; [H3-API] module summary: the statistic follows a fixed
+   reduction order with 4-wide vectors and sequential fused multiply-adds per
+   thread, whose order this tree fixes for 64 lanes).  Requires k % 256 == 0.
+   The row is cut into quads of 4 consecutive elements; lane L in [0, 64) owns
+   quads L, L + 64, L + 128, ... and keeps four accumulators a_e (e = position
+   in the quad) starting at +0, updated for its quads in ascending order with
+   a_e = fma(v, v, a_e).  Its lane value is (a0 + a1) + (a2 + a3).  The 64
+   lane values are combined by the same butterfly as rms_rstd's. */
+static float rms_sum_f32(const float* h, int64_t k) {
+    float lane[64];
+    const int64_t quads = k / 4;
+    for (int L = 0; L < 64; ++L) {
+        float a[4] = {0, 0, 0, 0};
+        for (int64_t q = L; q < quads; q += 64)
+            for (int e = 0; e < 4; ++e) a[e] = fmaf(h[4 * q + e], h[4 * q + e], a[e]);
+        lane[L] = (a[0] + a[1]) + (a[2] + a[3]);
+    }
+    for (int s = 1; s < 64; s *= 2) {
+        float next[64];
+        for (int L = 0; L < 64; ++L) next[L] = lane[L] + lane[L ^ s];
+        memcpy(lane, next, sizeof lane);
+    }
+    return lane[0];
+}
+
+EXPORT float orc_rms_sum_f32(const float* h, int64_t k) {
+    unsigned int s = enter_ieee();
+    float r = rms_sum_f32(h, k);
+    leave_ieee(s);
+    return r;
+}
+
+/* rstd of an fp32 row: 1 / sqrt(sum / k + eps), IEEE fp32. */
+static float rms_rstd_f32(const float* h, int64_t k, float eps) {
+    float ms = rms_sum_f32(h, k) / (float)k;
+    return 1.0f / sqrtf(ms + eps);
+}
+
+EXPORT float orc_rms_rstd_f32(const float* h, int64_t k, float eps) {
+    unsigned int s = enter_ieee();
+    float r = rms_rstd_f32(h, k, eps);
+    leave_ieee(s);
+    return r;
+}
+
+/* Residual add into an fp32 stream, then RMSNorm with an fp32 weight, then
+   the NVFP4 quantizer, over rows ([H3-API] residual_norm_quantize).
+   h: [n, k] fp32 rows, updated in place when o is given.  For element d of a
+   row, with o given:
+     t    = bf16(o[d] + bias[d])        (t = o[d] when bias is NULL)
+     h[d] = h[d] + fp32(t * scale[d])   (the product rounded, then the add)
+   and in every case, on the (updated) row:
+     rstd = 1 / sqrt(sum(h^2) / k + eps)   (rms_sum_f32's tree)
+     y[d] = bf16((h[d] * rstd) * gamma[d])
+   then the block quantizer.  o: [n, k] bf16 or NULL (no residual: h is only
+   read); bias: [k] bf16 or NULL; scale, gamma: [k] fp32.  row_ids, codes,
+   scale_bytes, scales, rstd_out, y_out as in orc_rms_adaln_rows_gsf. */
+EXPORT void orc_residual_rms_rows_gsf(float* h, const uint16_t* o, const uint16_t* bias,
+                                      const float* scale, const float* gamma, float eps, int64_t n,
+                                      int64_t k, const int64_t* row_ids, float gsf, uint8_t* codes,
+                                      uint8_t* scale_bytes, uint8_t* scales, float* rstd_out,
+                                      uint16_t* y_out) {
+    unsigned int s = enter_ieee();
+    float* y = (float*)malloc(sizeof(float) * (size_t)k);
+    uint8_t* sb = (uint8_t*)malloc((size_t)(k / 16));
+    for (int64_t i = 0; i < n; ++i) {
+        float* hr = h + i * k;
+        int64_t r = row_ids ? row_ids[i] : i;
+        if (o) {
+            for (int64_t d = 0; d < k; ++d) {
+                uint16_t t = o[i * k + d];
+                if (bias) t = bf16_round(bf16_to_f32(t) + bf16_to_f32(bias[d]));
+                float prod = bf16_to_f32(t) * scale[d];
+                hr[d] = hr[d] + prod;
+            }
+        }
+        float rstd = rms_rstd_f32(hr, k, eps);
+        if (rstd_out) rstd_out[i] = rstd;
+        for (int64_t d = 0; d < k; ++d) {
+            float nrm = hr[d] * rstd;
+            y[d] = rb(nrm * gamma[d]);
+        }
+        quantize_row(y, k, gsf, codes + i * (k / 2), sb);
+        if (scale_bytes) memcpy(scale_bytes + i * (k / 16), sb, (size_t)(k / 16));
+        if (scales) place_scales(sb, r, k, scales);
+        if (y_out)
+            for (int64_t d = 0; d < k; ++d) y_out[i * k + d] = bf16_round(y[d]);
+    }
+    free(sb);
+    free(y);
+    leave_ieee(s);
 }
 
 /* ------------------------------------------------------------------------- */

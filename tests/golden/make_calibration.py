@@ -13,6 +13,8 @@ TensorRT-LLM fusions apply only to static NVFP4 scales).  For each workload:
   swiglu_16384x19456     max |y| of the oracle on 2,048 calibration rows
   swiglu_bias_16384x19456, swiglu_paired_16384x19456
                          the same, with the workload's bias and column layout
+  residual_rms_63240x7168  max |y| of the oracle (residual add, then RMSNorm) over
+                         8,192 calibration rows of h and o
 
 Run:  python tests/golden/make_calibration.py
 """
@@ -45,6 +47,11 @@ def calibrate(w: workloads.Workload) -> dict:
     elif w.kind == "quantize":
         amax = amax_of_bf16(w.calibration_x())
         how = "max|x| over %d calibration rows" % w.cal_rows
+    elif w.kind == "residual_rms":
+        res = oracle.residual_rms_rows(w.calibration_h(), w.calibration_o(), w.bias(), w.residual_scale(),
+                                       w.gamma(), w.eps, 1.0, want_y=True)
+        amax = amax_of_bf16(res["y"])
+        how = "max|y| of the oracle over %d calibration rows" % w.cal_rows
     elif w.kind == "swiglu" and (w.bias_std > 0 or w.interleaved):
         res = oracle.swiglu_packed_rows(w.calibration_x(), w.bias(), w.interleaved, 1.0, want_y=True)
         amax = amax_of_bf16(res["y"])

@@ -378,6 +378,123 @@ def test_frame_index_out_of_range_zeroes_the_row_and_sets_status():
 
 
 # --------------------------------------------------------------------------
+# fp32 residual stream + RMSNorm with an fp32 weight
+# --------------------------------------------------------------------------
+
+def test_rms_sum_f32_equal_values_row_is_exact():
+    for k, c in [(512, 1.0), (7168, 0.5), (2048, 3.0), (7168, 1.25)]:
+        # every partial sum is a multiple of c^2 below 2^24 ulps: exact in any order
+        assert oracle.rms_sum_f32(np.full(k, c, np.float32)) == np.float32(k * c * c)
+    assert oracle.rms_rstd_f32(np.zeros(1024, np.float32), 0.25) == np.float32(2.0)
+
+
+def test_rms_sum_f32_tree_order_is_the_documented_one():
+    """k = 512: lane L owns quads L and L + 64, i.e. elements 4L..4L+3 and 256+4L..256+4L+3.
+    2^24 + 1 rounds back to 2^24 in fp32 (tie to even) while 2^24 + 2 is exact, so the
+    grouping of the additions is visible in the sum."""
+    k = 512
+
+    def row(**ones):
+        h = np.zeros(k, np.float32)
+        h[0] = 4096.0                       # lane 0, quad 0, element 0: 4096^2 = 2^24
+        for idx in ones["at"]:
+            h[idx] = 1.0
+        return h
+
+    big, big2 = np.float32(2.0 ** 24), np.float32(2.0 ** 24 + 2)
+    # lanes 1 and 3 (butterfly distance 1 pairs 0+1 and 2+3, so each 1 meets 2^24 alone)
+    assert oracle.rms_sum_f32(row(at=[4, 12])) == big
+    # lanes 2 and 3: 1 + 1 = 2 at distance 1, then 2^24 + 2 at distance 2
+    assert oracle.rms_sum_f32(row(at=[8, 12])) == big2
+    # one lane, the same element position in its two quads: one accumulator, so
+    # fma(1, 1, 2^24) = 2^24; then the other element's accumulator adds 1 -> 2^24
+    assert oracle.rms_sum_f32(row(at=[256, 1])) == big
+    # both ones in another element position of lane 0: a1 = 2, then (2^24 + 2) exact
+    assert oracle.rms_sum_f32(row(at=[1, 257])) == big2
+    # ones in elements 2 and 3 of lane 0: the lane folds (a0 + a1) + (a2 + a3), so 1 + 1
+    # first; a left-to-right fold would lose both ones against 2^24
+    assert oracle.rms_sum_f32(row(at=[2, 3])) == big2
+
+
+def test_rms_sum_f32_uses_fused_multiply_add():
+    """Element 0 of lane 0 takes 2^-12 (quad 0) then 1 + 2^-12 (quad 64): with a fused
+    multiply-add the accumulator is 2^-24 + (1 + 2^-11 + 2^-24) = 1 + 2^-11 + 2^-23
+    exactly; rounding the square first would give 1 + 2^-11 (the 2^-24 tie goes to even)."""
+    h = np.zeros(512, np.float32)
+    h[0], h[256] = 2.0 ** -12, 1.0 + 2.0 ** -12
+    assert oracle.rms_sum_f32(h) == np.float32(1.0 + 2.0 ** -11 + 2.0 ** -23)
+
+
+def test_rms_rstd_f32_close_to_fp64():
+    g = np.random.Generator(np.random.PCG64(41))
+    for k in [512, 2048, 7168]:
+        h = (g.standard_normal(k) * 3).astype(np.float32)
+        ref = 1.0 / np.sqrt(np.mean(h.astype(np.float64) ** 2) + 1e-6)
+        assert abs(oracle.rms_rstd_f32(h, 1e-6) / ref - 1) < 1e-6
+
+
+def _residual_case(seed, n=4, k=1024):
+    g = np.random.Generator(np.random.PCG64(seed))
+    h = (g.standard_normal((n, k)) * 2).astype(np.float32)
+    o = oracle.bf16_round(g.standard_normal((n, k)).astype(np.float32))
+    bias = oracle.bf16_round((0.5 * g.standard_normal(k)).astype(np.float32))
+    scale = (0.3 * g.standard_normal(k)).astype(np.float32)
+    gamma = (1 + 0.1 * g.standard_normal(k)).astype(np.float32)
+    return h, o, bias, scale, gamma
+
+
+def _t16(a_u16):
+    return torch.from_numpy(a_u16.view(np.int16).copy()).view(torch.bfloat16)
+
+
+def test_residual_update_matches_torch_eager_ops():
+    h, o, bias, scale, gamma = _residual_case(42)
+    for b in (bias, None):
+        res = oracle.residual_rms_rows(h, o, b, scale, gamma, 1e-6, 8.0)
+        t = _t16(o) + _t16(b) if b is not None else _t16(o)      # bf16 tensor add
+        want = torch.from_numpy(h) + t.float() * torch.from_numpy(scale)
+        assert np.array_equal(res["h"].view(np.uint32), want.numpy().view(np.uint32))
+
+
+def test_residual_norm_output_matches_torch_eager_ops():
+    h, o, bias, scale, gamma = _residual_case(43)
+    res = oracle.residual_rms_rows(h, o, bias, scale, gamma, 1e-6, 8.0, want_y=True)
+    hn = torch.from_numpy(res["h"])
+    rstd = torch.from_numpy(res["rstd"])[:, None]
+    want = ((hn * rstd) * torch.from_numpy(gamma)).to(torch.bfloat16)
+    assert np.array_equal(res["y"], want.view(torch.int16).numpy().view(np.uint16))
+    # rstd is the fixed-tree statistic of the updated rows
+    for i in range(h.shape[0]):
+        assert res["rstd"][i] == oracle.rms_rstd_f32(res["h"][i], 1e-6)
+    # without a residual the stream is only read
+    plain = oracle.residual_rms_rows(h, None, None, None, gamma, 1e-6, 8.0)
+    assert np.array_equal(plain["h"], h)
+    assert plain["rstd"][0] == oracle.rms_rstd_f32(h[0], 1e-6)
+
+
+def test_residual_norm_hand_worked_block():
+    """h' = 1.5 + bf16(0.25 + 0.25) * 1 = 2 everywhere (k = 512), eps = 0: sum = 2048 exactly,
+    rstd = 1 / sqrt(4) = 0.5 and y = bf16(1 * gamma).  gamma's first block holds the first
+    block of hand_worked_blocks.json, whose codes and scale code follow at gsf = 1."""
+    blk = json.load(open(os.path.join(GOLDEN, "hand_worked_blocks.json")))["blocks"][0]
+    k = 512
+    gamma = np.ones(k, np.float32)
+    gamma[:16] = _block_values(blk["values"])
+    h = np.full((1, k), 1.5, np.float32)
+    o = oracle.bf16_round(np.full((1, k), 0.25, np.float32))
+    bias = oracle.bf16_round(np.full(k, 0.25, np.float32))
+    res = oracle.residual_rms_rows(h, o, bias, np.ones(k, np.float32), gamma, 0.0, blk["global_amax"])
+    assert np.all(res["h"] == 2.0) and res["rstd"][0] == 0.5
+    assert res["scale_bytes"][0, 0] == blk["scale_code"]
+    assert res["codes"][0, :8].tobytes().hex() == blk["packed_hex"]
+    # every other block is all ones: amax 1 -> the E4M3 code of 1/6 = 1.333.. * 2^-3, which
+    # rounds to 1.375 * 2^-3 = 0.171875 (exponent field 4, mantissa 3: 0x23), and
+    # 1 * (1 / 0.171875) = 5.818.. lies above 5 -> code 7 (6)
+    assert np.all(res["scale_bytes"][0, 1:] == 0x23)
+    assert np.all(res["codes"][0, 8:] == 0x77)
+
+
+# --------------------------------------------------------------------------
 # SiLU table and the SwiGLU producer
 # --------------------------------------------------------------------------
 
@@ -599,6 +716,16 @@ def test_dynamic_swiglu_packed_is_static_at_its_own_amax():
         ref = oracle.swiglu_packed_rows(proj, bias, interleaved, dyn["amax"], want_y=True, scales_rows=128)
         for key in ("codes", "scales", "y"):
             assert np.array_equal(dyn[key], ref[key]), key
+
+
+def test_dynamic_residual_rms_is_static_at_its_own_amax():
+    h, o, bias, scale, gamma = _residual_case(44, n=5, k=512)
+    dyn = oracle.residual_rms_dynamic(h, o, bias, scale, gamma, 1e-6, want_y=True, scales_rows=128)
+    y = oracle.residual_rms_rows(h, o, bias, scale, gamma, 1e-6, 1.0, want_y=True)["y"]
+    assert dyn["amax"] == float(np.abs(oracle.bf16_to_f32(y)).max())
+    ref = oracle.residual_rms_rows(h, o, bias, scale, gamma, 1e-6, dyn["amax"], want_y=True, scales_rows=128)
+    for key in ("codes", "scales", "y", "h", "rstd"):
+        assert np.array_equal(dyn[key], ref[key]), key
 
 
 def test_dynamic_rms_adaln_and_swiglu_are_static_at_their_own_amax():

@@ -70,3 +70,17 @@ def test_packed_swiglu_workloads():
         assert 0.2 < float(np.std(oracle.bf16_to_f32(b))) < 0.3
         assert w.algorithmic_bytes() == 1_454_374_912 and w.param_bytes() == 4 * w.k
     assert workloads.get("swiglu_16384x19456").bias() is None
+
+
+def test_residual_rms_workload():
+    w = workloads.get("residual_rms_63240x7168")
+    assert w.algorithmic_bytes() == 10 * w.m * w.k + w.m * w.k // 2 + w.padded_rows * w.k // 16
+    assert w.bias().shape == (w.k,) and w.residual_scale().dtype == np.float32 and w.gamma().shape == (w.k,)
+    rows = np.array([0, 4095, 4096, 63239])
+    h = w._rows_bf16(workloads.ROLE_X, w.m, chunks=[0, 1, 15], fp32=True)
+    assert h.dtype == np.float32 and h.shape == (4096 * 2 + (w.m - 15 * 4096), w.k)
+    cols = w.outlier_columns()
+    assert np.std(h[:, cols]) > 20 and np.std(np.delete(h[:64], cols, axis=1)) < 1.1
+    o = w.calibration_o()
+    assert o.dtype == np.uint16 and o.shape == (w.cal_rows, w.k)
+    del rows

@@ -19,10 +19,16 @@ a 34x60 latent grid per frame over 31 frames = 63,240 tokens from
   swiglu_bias_16384x19456  the same projection shape, value-first, with a bf16 bias
                            of 2F values (std 0.25) added before SiLU
   swiglu_paired_16384x19456  the same with value/gate columns paired (2j, 2j + 1)
+  residual_rms_63240x7168  fp32 residual stream h (the H3 block shape, N(0,1) with the
+                           36 outlier columns x30 of rms_adaln_63240x7168), a bf16 branch
+                           output o ~ N(0,1), bf16 bias (std 0.25), fp32 per-channel
+                           scale (std 0.2) and fp32 RMSNorm weight 1 + 0.1 N(0,1)
 
 Seeds: numpy ``PCG64``; the seed of role ``role`` in workload number ``i``
-(1..7 in the order above) is ``1000*i + role`` with roles 1 x, 2 weight (or
-bias), 3 modulation table, 4 calibration rows, 5 outlier pick, 6 per-head std.
+(1..8 in the order above) is ``1000*i + role`` with roles 1 x (or h), 2 weight
+(or bias), 3 modulation table (or residual scale), 4 calibration rows, 5
+outlier pick, 6 per-head std, 8 the residual branch o, 9 its calibration rows,
+10 the fp32 RMSNorm weight.
 Large tensors are drawn in 4096-row chunks, chunk ``c`` from
 ``SeedSequence(1000*i + role).spawn(n_chunks)[c]``, so any chunk can be
 regenerated alone and chunks can be drawn in parallel threads.
@@ -37,6 +43,7 @@ import numpy as np
 
 CHUNK_ROWS = 4096
 ROLE_X, ROLE_W, ROLE_TABLE, ROLE_CAL, ROLE_OUTLIER, ROLE_HEADSTD = 1, 2, 3, 4, 5, 6
+ROLE_O, ROLE_CAL_O, ROLE_GAMMA = 8, 9, 10
 
 
 def to_bf16(a: np.ndarray) -> np.ndarray:
@@ -58,7 +65,7 @@ def _threads() -> int:
 class Workload:
     name: str
     number: int               # 1..5, selects the seeds
-    kind: str                 # "rms_adaln" | "quantize" | "swiglu"
+    kind: str                 # "rms_adaln" | "quantize" | "swiglu" | "residual_rms"
     m: int                    # rows (tokens)
     k: int                    # output columns (hidden, or F for swiglu)
     frames: int = 0           # modulation table rows (rms_adaln)
@@ -81,14 +88,20 @@ class Workload:
 
     def algorithmic_bytes(self) -> int:
         """HBM bytes one pass must move: bf16 inputs once, packed codes once,
-        scale bytes over the padded rows (parameters not counted)."""
-        return (2 * self.m * self.in_cols + self.m * self.k // 2 + self.padded_rows * self.k // 16)
+        scale bytes over the padded rows (parameters not counted).  residual_rms: the
+        fp32 stream read and written back, the bf16 branch read."""
+        out = self.m * self.k // 2 + self.padded_rows * self.k // 16
+        if self.kind == "residual_rms":
+            return (4 + 2 + 4) * self.m * self.k + out
+        return 2 * self.m * self.in_cols + out
 
     def param_bytes(self) -> int:
         if self.kind == "rms_adaln":
             return 2 * self.k + 2 * self.frames * 2 * self.k + 4 * self.m
         if self.kind == "swiglu" and self.bias_std > 0:
             return 2 * 2 * self.k
+        if self.kind == "residual_rms":
+            return (2 + 4 + 4) * self.k
         return 0
 
     # ---- generation ----------------------------------------------------------
@@ -122,14 +135,18 @@ class Workload:
         heads = self.k // 128
         return (0.5 * rng(self.number, ROLE_HEADSTD).uniform(0.2, 2.0, heads)).astype(np.float32)
 
-    def _rows_bf16(self, role: int, rows: int, chunks=None, out: np.ndarray | None = None):
-        cols = self.outlier_columns()
-        hs = self.head_std()
+    def _rows_bf16(self, role: int, rows: int, chunks=None, out: np.ndarray | None = None, fp32: bool = False,
+                   plain: bool = False):
+        """Rows drawn in chunks; bf16 patterns, or the fp32 draws themselves with fp32.
+        plain: N(0,1) without the workload's outlier or per-head recipe."""
+        cols = None if plain else self.outlier_columns()
+        hs = None if plain else self.head_std()
         idx = range(self.n_chunks(rows)) if chunks is None else chunks
         idx = list(idx)
 
         def one(c):
-            return c, to_bf16(self._chunk_f32(role, rows, c, cols, hs))
+            a = self._chunk_f32(role, rows, c, cols, hs)
+            return c, (a if fp32 else to_bf16(a))
 
         parts = {}
         with ThreadPoolExecutor(_threads()) as ex:
@@ -148,6 +165,34 @@ class Workload:
             out = np.empty((self.m, self.in_cols), np.uint16)
         return self._rows_bf16(ROLE_X, self.m, out=out)
 
+    # ---- residual_rms inputs -------------------------------------------------
+    def h(self, out: np.ndarray | None = None) -> np.ndarray:
+        """residual_rms: the fp32 residual stream [m, k]."""
+        if out is None:
+            out = np.empty((self.m, self.k), np.float32)
+        return self._rows_bf16(ROLE_X, self.m, out=out, fp32=True)
+
+    def o(self, out: np.ndarray | None = None) -> np.ndarray:
+        """residual_rms: the bf16 branch output [m, k], N(0,1)."""
+        if out is None:
+            out = np.empty((self.m, self.k), np.uint16)
+        return self._rows_bf16(ROLE_O, self.m, out=out, plain=True)
+
+    def calibration_h(self) -> np.ndarray:
+        return self._rows_bf16(ROLE_CAL, self.cal_rows, fp32=True)
+
+    def calibration_o(self) -> np.ndarray:
+        return self._rows_bf16(ROLE_CAL_O, self.cal_rows, plain=True)
+
+    def residual_scale(self) -> np.ndarray:
+        """residual_rms: the fp32 per-channel scale [k] of the branch."""
+        return (0.2 * rng(self.number, ROLE_TABLE).standard_normal(self.k, dtype=np.float32)).astype(np.float32)
+
+    def gamma(self) -> np.ndarray:
+        """residual_rms: the fp32 RMSNorm weight [k]."""
+        return (1.0 + 0.1 * rng(self.number, ROLE_GAMMA).standard_normal(self.k, dtype=np.float32)).astype(
+            np.float32)
+
     def x_rows(self, rows) -> np.ndarray:
         """Rows of the input regenerated from their chunks alone."""
         rows = np.asarray(rows, np.int64)
@@ -165,10 +210,12 @@ class Workload:
         return to_bf16(1.0 + 0.1 * rng(self.number, ROLE_W).standard_normal(self.k, dtype=np.float32))
 
     def bias(self) -> np.ndarray | None:
-        """swiglu: the [2k] bf16 bias in the projection's column order, or None."""
+        """swiglu: the [2k] bf16 bias in the projection's column order; residual_rms: the
+        [k] bf16 bias of the branch; None without a bias."""
         if self.bias_std <= 0:
             return None
-        return to_bf16(self.bias_std * rng(self.number, ROLE_W).standard_normal(2 * self.k, dtype=np.float32))
+        n = self.k if self.kind == "residual_rms" else 2 * self.k
+        return to_bf16(self.bias_std * rng(self.number, ROLE_W).standard_normal(n, dtype=np.float32))
 
     def table(self) -> np.ndarray:
         """[frames, 2, k] bf16: row t holds (shift, scale) of frame t."""
@@ -205,6 +252,8 @@ WORKLOADS = {
         Workload("swiglu_bias_16384x19456", 6, "swiglu", 16384, 19456, cal_rows=2048, bias_std=0.25),
         Workload("swiglu_paired_16384x19456", 7, "swiglu", 16384, 19456, cal_rows=2048, bias_std=0.25,
                  interleaved=True),
+        Workload("residual_rms_63240x7168", 8, "residual_rms", 63240, 7168, outliers="cols36_x30",
+                 cal_rows=8192, bias_std=0.25),
     ]
 }
 
