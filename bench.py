@@ -83,6 +83,11 @@ def make_inputs(wl, torch, amax):
         x = up(wl.x())
         args = dict(x=x, weight=up(wl.weight()), table=up(wl.table()),
                     frame_idx=torch.from_numpy(wl.frame_idx()).to(dev))
+    elif wl.kind == "residual_rms":
+        def f32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
+        args = dict(x=f32(wl.h()), o=up(wl.o()), bias=up(wl.bias()), scale=f32(wl.residual_scale()),
+                    gamma=f32(wl.gamma()))
     else:
         args = dict(x=up(wl.x()))
         if wl.kind == "swiglu" and wl.bias_std > 0:
@@ -111,7 +116,18 @@ def main():
     amax_dev = torch.zeros(1, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
 
-    if wl.kind == "rms_adaln" and a.dynamic:
+    if wl.kind == "residual_rms":
+        # the stream is updated in place every step (the same work each time)
+        residual = (inp["o"], inp["bias"], inp["scale"])
+        if a.dynamic:
+            def step():
+                nq.residual_rms_nvfp4_dynamic(inp["x"], inp["gamma"], wl.eps, residual=residual, amax_out=amax_dev,
+                                              codes=codes, scales=scales, stream=stream)
+        else:
+            def step():
+                nq.residual_rms_nvfp4(inp["x"], inp["gamma"], wl.eps, amax, residual=residual, codes=codes,
+                                      scales=scales, stream=stream)
+    elif wl.kind == "rms_adaln" and a.dynamic:
         def step():
             nq.rms_adaln_nvfp4_dynamic(inp["x"], inp["weight"], inp["table"], inp["frame_idx"], wl.eps,
                                        amax_out=amax_dev, codes=codes, scales=scales, stream=stream)
@@ -176,7 +192,8 @@ def main():
     ms_per_step = region_ms / a.steps
 
     # the per-call form reads the input twice (the amax pass, then the quantize pass)
-    alg_bytes = wl.algorithmic_bytes() + (2 * wl.m * wl.in_cols if a.dynamic else 0)
+    reread = (4 + 2) * wl.m * wl.k if wl.kind == "residual_rms" else 2 * wl.m * wl.in_cols
+    alg_bytes = wl.algorithmic_bytes() + (reread if a.dynamic else 0)
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
 
@@ -239,8 +256,15 @@ def cpu_baseline(wl, amax, rows, np):
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     rows = min(rows, wl.m)
     sel = np.arange(rows)
-    x = wl.x_rows(sel)
-    if wl.kind == "rms_adaln":
+    x = wl.x_rows(sel) if wl.kind != "residual_rms" else None
+    if wl.kind == "residual_rms":
+        x, o = wl.h_rows(sel), wl.o_rows(sel)
+        bias, scale, gamma = wl.bias(), wl.residual_scale(), wl.gamma()
+
+        def part(se):
+            s, e = se
+            oracle.residual_rms_rows(x[s:e], o[s:e], bias, scale, gamma, wl.eps, amax)
+    elif wl.kind == "rms_adaln":
         w, table, idx = wl.weight(), wl.table(), wl.frame_idx(sel)
 
         def part(se):

@@ -8,6 +8,9 @@
  *                    (swiglu_packed_nvfp4: packed projection, bias before
  *                    SiLU, value-first or paired columns)
  *   nvfp4_quantize   identity (attention-output quantize)         -> NVFP4
+ * and a fourth that folds a residual add into the norm:
+ *   residual_rms_nvfp4  h += bf16(o + bias) * scale (fp32, in place);
+ *                       RMSNorm with an fp32 weight               -> NVFP4
  *
  * Sources: TensorRT-LLM PR #21483 "Fuse the MiniMax-H3 NVFP4 activation
  * quantize into the AdaLN, SwiGLU and attention-output producers" (Summary);
@@ -179,6 +182,37 @@ int swiglu_packed_nvfp4(const void* proj, const void* bias, int interleaved, int
                         int64_t f, float global_amax, void* codes, void* scales, void* y_out,
                         void* stream);
 
+/* fp32 residual stream + RMSNorm (fp32 weight) -> NVFP4 (FastVideo API page,
+   residual_norm_quantize: a block's branch output is added to the fp32
+   residual stream in place, and the next norm's quantized activation is
+   produced in the same pass).  Per row, element d:
+     t    = bf16(o[d] + bias[d])            (t = o[d] without a bias)
+     h[d] = h[d] + t * scale[d]             fp32, the product rounded before the
+                                            add; written back into h
+     rstd = 1 / sqrt(sum(h^2) / k + eps)    fp32, fixed reduction tree:
+            4 accumulators per lane over the 4-element quads L, L+64, ...
+            (fused multiply-add), folded as (a0 + a1) + (a2 + a3), then the
+            butterfly of rms_adaln_nvfp4 over the 64 lanes
+     y[d] = bf16((h[d] * rstd) * gamma[d])
+   then the NVFP4 quantizer above.
+     h         [m, k] fp32, row-major, contiguous, 16-byte aligned; updated in
+               place when o is given, only read otherwise
+     o         [m, k] bf16 (contiguous, 16-byte aligned), nullable: no residual
+     bias      [k] bf16, nullable (ignored without o)
+     scale     [k] fp32, required with o (ignored without)
+     gamma     [k] fp32 RMSNorm weight
+     eps       >= 0 and finite
+     m, k      m >= 0; k a positive multiple of 512, at most 8192 (a row is
+               held in registers)
+     global_amax, codes, scales  as for nvfp4_quantize
+     rstd_out  [m] fp32, nullable
+     y_out     [m, k] bf16, nullable: the pre-quantization activation
+   Every pointer argument is 16-byte aligned (rstd_out 4-byte).  Returns a
+   status. */
+int residual_rms_nvfp4(float* h, const void* o, const void* bias, const float* scale,
+                       const float* gamma, float eps, int64_t m, int64_t k, float global_amax,
+                       void* codes, void* scales, float* rstd_out, void* y_out, void* stream);
+
 /* Per-call (dynamic) global amax
    ------------------------------
    The *_dynamic forms take the global amax from the tensor itself instead of
@@ -214,6 +248,13 @@ int swiglu_nvfp4_dynamic(const void* up, const void* gate, int64_t ld, int64_t m
 int swiglu_packed_nvfp4_dynamic(const void* proj, const void* bias, int interleaved, int64_t ld,
                                 int64_t m, int64_t f, float* amax_out, void* codes, void* scales,
                                 void* y_out, void* stream);
+
+/* The amax pass reads h and o without writing anything; the second pass
+   updates h as the static form does. */
+int residual_rms_nvfp4_dynamic(float* h, const void* o, const void* bias, const float* scale,
+                               const float* gamma, float eps, int64_t m, int64_t k,
+                               float* amax_out, void* codes, void* scales, float* rstd_out,
+                               void* y_out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -15,7 +15,11 @@ Entry points (see ``include/nvfp4act.h`` for the exact contract):
                                                           or paired columns
 each returning ``(codes, scales)``; and the per-call (dynamic) amax forms
   nvfp4_quantize_dynamic(x), rms_adaln_nvfp4_dynamic(x, weight, table, frame_idx, eps),
-  swiglu_nvfp4_dynamic(projection), swiglu_packed_nvfp4_dynamic(projection, bias, interleaved)
+  residual_rms_nvfp4(h, gamma, eps, global_amax, residual=(o, bias, scale))
+                                                          fp32 residual stream (in place) +
+                                                          RMSNorm with an fp32 weight
+  swiglu_nvfp4_dynamic(projection), swiglu_packed_nvfp4_dynamic(projection, bias, interleaved),
+  residual_rms_nvfp4_dynamic(h, gamma, eps, residual)
 returning ``(codes, scales, amax)`` with ``amax`` a one-element float32 device tensor, codes ``[m, k/2]`` uint8, scales
 ``[pad(m), k/16]`` uint8 in the 128x4 swizzle (buffer shapes as the FastVideo
 API page's ``new_quantized``).
@@ -53,6 +57,8 @@ _SIGS = {
     "swiglu_nvfp4_dynamic": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "swiglu_packed_nvfp4": (_I, [_P, _P, _I, _I64, _I64, _I64, _F, _P, _P, _P, _P]),
     "swiglu_packed_nvfp4_dynamic": (_I, [_P, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "residual_rms_nvfp4": (_I, [_P, _P, _P, _P, _P, _F, _I64, _I64, _F, _P, _P, _P, _P, _P]),
+    "residual_rms_nvfp4_dynamic": (_I, [_P, _P, _P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -340,4 +346,65 @@ def swiglu_packed_nvfp4_dynamic(projection: torch.Tensor, bias: torch.Tensor | N
                                             _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, f),
                                                      "y_out") if y_out is not None else 0,
                                             _stream(stream, projection.device)))
+    return codes, scales, amax_out
+
+
+def _f32_ptr(t, n, name):
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or t.numel() != n:
+        raise ValueError("%s must be a contiguous float32 device tensor of %d values" % (name, n))
+    return t.data_ptr()
+
+
+def _residual_args(h, gamma, residual):
+    if h.dim() != 2 or h.dtype != torch.float32 or not h.is_cuda or not h.is_contiguous():
+        raise ValueError("h must be a contiguous float32 [m, k] device tensor")
+    m, k = h.shape
+    gp = _f32_ptr(gamma, k, "gamma")
+    op = bp = sp = 0
+    if residual is not None:
+        o, bias, scale = residual
+        if tuple(o.shape) != (m, k) or not o.is_contiguous():
+            raise ValueError("o must be a contiguous [m, k] tensor")
+        op = _bf16_ptr(o, "o")
+        if bias is not None:
+            if bias.numel() != k or not bias.is_contiguous():
+                raise ValueError("bias must be a contiguous tensor of k values")
+            bp = _bf16_ptr(bias, "bias")
+        sp = _f32_ptr(scale, k, "scale")
+    return m, k, gp, op, bp, sp
+
+
+def residual_rms_nvfp4(h: torch.Tensor, gamma: torch.Tensor, eps: float, global_amax: float, residual=None,
+                       codes=None, scales=None, rstd_out=None, y_out=None, stream=None):
+    """In place h += bf16(o + bias) * scale (residual = (o, bias or None, scale), or None for
+    no residual add), then NVFP4 of bf16(rms_norm(h, gamma, eps)) with the fp32 weight gamma.
+    h: contiguous float32 [m, k]."""
+    m, k, gp, op, bp, sp = _residual_args(h, gamma, residual)
+    if codes is None or scales is None:
+        codes, scales = new_quantized(m, k, h.device)
+    _check(_lib.residual_rms_nvfp4(h.data_ptr(), op, bp, sp, gp, float(eps), m, k, float(global_amax),
+                                   _out_ptr(codes, torch.uint8, (m, k // 2), "codes"),
+                                   _out_ptr(scales, torch.uint8, (padded_rows(m), k // 16), "scales"),
+                                   _out_ptr(rstd_out, torch.float32, (m,), "rstd_out"),
+                                   _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, k), "y_out")
+                                   if y_out is not None else 0,
+                                   _stream(stream, h.device)))
+    return codes, scales
+
+
+def residual_rms_nvfp4_dynamic(h: torch.Tensor, gamma: torch.Tensor, eps: float, residual=None, amax_out=None,
+                               codes=None, scales=None, rstd_out=None, y_out=None, stream=None):
+    """residual_rms_nvfp4 under the amax of this call's own y (computed on the device).
+    Returns (codes, scales, amax_out)."""
+    m, k, gp, op, bp, sp = _residual_args(h, gamma, residual)
+    if codes is None or scales is None:
+        codes, scales = new_quantized(m, k, h.device)
+    amax_out, ap = _amax_ptr(amax_out, h.device)
+    _check(_lib.residual_rms_nvfp4_dynamic(h.data_ptr(), op, bp, sp, gp, float(eps), m, k, ap,
+                                           _out_ptr(codes, torch.uint8, (m, k // 2), "codes"),
+                                           _out_ptr(scales, torch.uint8, (padded_rows(m), k // 16), "scales"),
+                                           _out_ptr(rstd_out, torch.float32, (m,), "rstd_out"),
+                                           _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, k),
+                                                    "y_out") if y_out is not None else 0,
+                                           _stream(stream, h.device)))
     return codes, scales, amax_out

@@ -272,6 +272,43 @@ int swiglu_packed_call(const void* proj, const void* bias, int interleaved, int6
   return swiglu_launch(p, stream);
 }
 
+int residual_rms_call(float* h, const void* o, const void* bias, const float* scale, const float* gamma, float eps,
+                      int64_t m, int64_t k, float global_amax, float* amax_dev, void* codes, void* scales,
+                      float* rstd_out, void* y_out, void* stream) {
+  if (m < 0 || k <= 0 || k % 512 != 0 || k > nvfp4act::kMaxResidualK) return NVFP4ACT_ERR_SHAPE;
+  if (m == 0) return NVFP4ACT_OK;
+  if (!h || !gamma || !codes || !scales || (o && !scale)) return NVFP4ACT_ERR_NULL;
+  if (!aligned16(h) || !aligned16(gamma) || !aligned16(codes) || !aligned16(scales) || (o && !aligned16(o)) ||
+      (o && !aligned16(scale)) || (o && bias && !aligned16(bias)) || (y_out && !aligned16(y_out)) ||
+      (rstd_out && !aligned4(rstd_out)))
+    return NVFP4ACT_ERR_ALIGN;
+  if (!std::isfinite(eps) || eps < 0.0f) return NVFP4ACT_ERR_VALUE;
+  if (!amax_dev) {
+    int st = check_amax(global_amax);
+    if (st != NVFP4ACT_OK) return st;
+  }
+  const DeviceInfo* info = nullptr;
+  int st = current_device(&info, nullptr);
+  if (st != NVFP4ACT_OK) return st;
+  nvfp4act::ResidualLaunch p{};
+  p.h = h;
+  p.o = o;
+  p.bias = o ? bias : nullptr;
+  p.scale = o ? scale : nullptr;
+  p.gamma = gamma;
+  p.eps = eps;
+  p.m = m;
+  p.k = k;
+  p.global_amax = global_amax;
+  p.amax_dev = amax_dev;
+  p.codes = codes;
+  p.scales = scales;
+  p.rstd_out = rstd_out;
+  p.y_out = y_out;
+  hipError_t e = nvfp4act::launch_residual_rms(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
+}
+
 // The per-call forms need the amax destination: one 4-byte aligned float (m == 0 aside).
 int check_amax_out(int64_t m, const float* amax_out) {
   if (m == 0) return NVFP4ACT_OK;
@@ -340,6 +377,23 @@ int swiglu_packed_nvfp4_dynamic(const void* proj, const void* bias, int interlea
   int st = check_amax_out(m, amax_out);
   if (st != NVFP4ACT_OK) return st;
   return swiglu_packed_call(proj, bias, interleaved, ld, m, f, 0.0f, amax_out, codes, scales, y_out, stream);
+}
+
+int residual_rms_nvfp4(float* h, const void* o, const void* bias, const float* scale, const float* gamma, float eps,
+                      int64_t m, int64_t k, float global_amax, void* codes, void* scales, float* rstd_out,
+                      void* y_out, void* stream) {
+  return residual_rms_call(h, o, bias, scale, gamma, eps, m, k, global_amax, nullptr, codes, scales, rstd_out, y_out,
+                           stream);
+}
+
+int residual_rms_nvfp4_dynamic(float* h, const void* o, const void* bias, const float* scale, const float* gamma,
+                              float eps, int64_t m, int64_t k, float* amax_out, void* codes, void* scales,
+                              float* rstd_out, void* y_out, void* stream) {
+  if (m < 0 || k <= 0 || k % 512 != 0 || k > nvfp4act::kMaxResidualK) return NVFP4ACT_ERR_SHAPE;
+  int st = check_amax_out(m, amax_out);
+  if (st != NVFP4ACT_OK) return st;
+  return residual_rms_call(h, o, bias, scale, gamma, eps, m, k, 0.0f, amax_out, codes, scales, rstd_out, y_out,
+                           stream);
 }
 
 }  // extern "C"

@@ -209,6 +209,34 @@ __device__ __forceinline__ void zero_row_scales(uint8_t* scales, int64_t r, int6
     *reinterpret_cast<NVFP4_GLOBAL uint32_t*>(base + q * 512) = 0u;
 }
 
+// ---- cross-lane sum ---------------------------------------------------------------------
+
+// Butterfly sum over the 64 lanes: for s = 1, 2, 4, 8, 16, 32 every lane replaces v by
+// v + v[lane ^ s] (IEEE fp32 adds; both lanes of a pair compute the same sum, so every
+// lane ends with the same value).  The partner values come from DPP and the gfx950 row
+// swaps rather than LDS permutes: s = 1, 2 are quad permutations; s = 4 is row_shl:4 on
+// the even 4-lane banks of each 16-lane row and row_shr:4 on the odd ones; s = 8 is
+// row_ror:8; s = 16 and 32 use v_permlane16_swap / v_permlane32_swap, whose two results
+// are the lane's value and its partner's.
+__device__ __forceinline__ float lane_sum_butterfly(float v) {
+  uint32_t u = __float_as_uint(v);
+  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0xB1, 0xF, 0xF, false));
+  u = __float_as_uint(v);
+  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x4E, 0xF, 0xF, false));
+  u = __float_as_uint(v);
+  int t = __builtin_amdgcn_update_dpp((int)u, (int)u, 0x104, 0xF, 0x5, false);   // banks 0, 2: lane + 4
+  t = __builtin_amdgcn_update_dpp(t, (int)u, 0x114, 0xF, 0xA, false);            // banks 1, 3: lane - 4
+  v = v + __uint_as_float((uint32_t)t);
+  u = __float_as_uint(v);
+  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x128, 0xF, 0xF, false));
+  u = __float_as_uint(v);
+  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  u = __float_as_uint(v);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+}
+
 // ---- amax reduction --------------------------------------------------------------------
 
 // max(|a|, |b|, ..) of the eight values of a chunk folded into t (t >= 0).
@@ -248,53 +276,53 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// ---- workgroup -> work-unit mapping ---------------------------------------------------
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// Workgroups are dispatched round-robin over the 8 XCDs, each with its own L2.  Two maps
-// keep the scale bytes of a 128-row tile (whose 128-byte lines collect bytes from 32
-// different rows) inside one L2 while they are written:
-constexpr int kXcds = 8;
-
-// Non-persistent grids: launch 8 * per workgroups; the workgroups of one XCD take
-// consecutive work units.  A bijection of [0, 8*per); units >= the real count are idle.
-__device__ __forceinline__ int64_t xcd_unit(int64_t per) {
-  int64_t bid = blockIdx.x;
-  return (bid % kXcds) * per + bid / kXcds;
+// 16- and 2-byte stores that are not expected to be re-read soon (non-temporal hint).
+__device__ __forceinline__ void store_stream(uint4* p, const uint4& v) {
+  const u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<NVFP4_GLOBAL u32x4*>(global_ptr(p)));
 }
 
-// Persistent grids of 8 * W workgroups (one per CU) with `waves` rows per step each:
-// XCD x owns rows [x * rows_per_xcd, (x+1) * rows_per_xcd); at step s its W workgroups
-// process the W * waves consecutive rows starting at x * rows_per_xcd + s * W * waves
-// together, so every tile of the step is finished within the step.
-struct XcdSteps {
-  int64_t first;      // first row of this workgroup's slot in step 0
-  int64_t end;        // end of this XCD's rows (clamped to the padded row count)
-  int64_t step;       // rows per step of the whole XCD
+__device__ __forceinline__ void store_stream(uint16_t* p, uint16_t v) {
+  __builtin_nontemporal_store(v, global_ptr(p));
+}
+
+__device__ __forceinline__ uint2 load_stream(const uint2* p) {
+  u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const NVFP4_GLOBAL u32x2*>(global_ptr(p)));
+  return make_uint2(v.x, v.y);
+}
+
+// ---- workgroup -> row-group mapping ----------------------------------------------------
+
+// A workgroup of four wavefronts owns the rows r, r + 32, r + 64, r + 96 of a 128-row tile
+// (r = tile * 128 + rr, rr < 32): in the 128x4 swizzled scale layout those rows' scale bytes
+// of four consecutive blocks form one contiguous 16-byte unit, which the workgroup can
+// gather in LDS and write whole.  The eight workgroups rr = 8p .. 8p + 7 of a tile fill the
+// same 128-byte lines of the scale buffer; workgroups are dealt round-robin over the 8 XCDs
+// (each with its own L2), so block indices are arranged to put those eight consecutively
+// on one XCD, and each line is completed in one L2 before it is written back.
+//
+// Row group of workgroup b: unit group u = b / 64 * 8 + b % 8 (tile u / 4, rr block u % 4),
+// rr = 8 (u % 4) + (b / 8) % 8.  For a fixed u the eight values of (b / 8) % 8 share b % 8.
+struct RowGroup {
+  int64_t tile;
+  int rr;
 };
 
-__device__ __forceinline__ XcdSteps xcd_steps(int64_t rows_per_xcd, int64_t padded, int waves) {
-  const int64_t bid = blockIdx.x;
-  const int64_t w_count = gridDim.x / kXcds;
-  const int64_t xcd = bid % kXcds, w = bid / kXcds;
-  XcdSteps s;
-  const int64_t begin = xcd * rows_per_xcd;
-  s.end = (begin + rows_per_xcd < padded) ? begin + rows_per_xcd : padded;
-  s.step = w_count * waves;
-  s.first = begin + w * waves;
-  return s;
+__device__ __forceinline__ RowGroup row_group(int64_t b) {
+  const int64_t u = (b >> 6) * 8 + (b & 7);
+  RowGroup g;
+  g.tile = u >> 2;
+  g.rr = (int)((u & 3) * 8 + ((b >> 3) & 7));
+  return g;
 }
 
-// Host side: workgroups per XCD and rows per XCD for a persistent launch.
-inline void plan_xcd_steps(int64_t padded, int cu_count, int waves, int64_t* wgs_per_xcd,
-                           int64_t* rows_per_xcd) {
-  const int64_t per_xcd = (padded + kXcds - 1) / kXcds;
-  int64_t w = cu_count / kXcds;
-  if (w < 1) w = 1;
-  const int64_t need = (per_xcd + waves - 1) / waves;
-  if (need < w) w = need;
-  const int64_t step = w * waves;
-  *wgs_per_xcd = w;
-  *rows_per_xcd = (per_xcd + step - 1) / step * step;
+// Workgroups to launch for m rows: whole groups of 64 covering the tiles' 4 row groups each
+// (the surplus workgroups find a tile past the end and return).
+inline int64_t row_group_blocks(int64_t m) {
+  const int64_t unit_groups = (m + 127) / 128 * 4;
+  return (unit_groups + 7) / 8 * 64;
 }
 
 }  // namespace nvfp4act

@@ -67,6 +67,28 @@ struct SwigluLaunch {
 
 hipError_t launch_swiglu(const SwigluLaunch& p, const DeviceInfo& dev, hipStream_t stream);
 
+// The arguments of one residual_rms_nvfp4 call (see include/nvfp4act.h).  o null: no branch
+// (h is only read); bias null: no bias.  amax_dev: as for RmsLaunch.
+constexpr int64_t kMaxResidualK = 8192;   // the row is held in registers
+
+struct ResidualLaunch {
+  float* h;
+  const void* o;
+  const void* bias;
+  const float* scale;
+  const float* gamma;
+  float eps;
+  int64_t m, k;
+  float global_amax;
+  float* amax_dev;
+  void* codes;
+  void* scales;
+  float* rstd_out;
+  void* y_out;
+};
+
+hipError_t launch_residual_rms(const ResidualLaunch& p, hipStream_t stream);
+
 // Per-device, once: allow the LDS sizes the kernels use.
 hipError_t prepare_rms_adaln();
 hipError_t prepare_swiglu();

@@ -30,21 +30,6 @@ constexpr int kWaves = 4;                  // rows per workgroup (r + 32 i)
 constexpr int kThreads = kWaves * kWave;
 constexpr int kPieceSlots = 16;            // chunks per lane per row piece (8192 columns)
 
-// Row group of workgroup b: unit group u = b / 64 * 8 + b % 8 (tile u / 4, rr block u % 4),
-// rr = 8 (u % 4) + (b / 8) % 8.  For a fixed u the eight values of (b / 8) % 8 share b % 8.
-struct RowGroup {
-  int64_t tile;
-  int rr;
-};
-
-__device__ __forceinline__ RowGroup row_group(int64_t b) {
-  const int64_t u = (b >> 6) * 8 + (b & 7);
-  RowGroup g;
-  g.tile = u >> 2;
-  g.rr = (int)((u & 3) * 8 + ((b >> 3) & 7));
-  return g;
-}
-
 // The 16-byte loads of SLOTS chunk slots (lane + 64 j, j < SLOTS) of a row from chunk c0.
 template <int SLOTS>
 __device__ __forceinline__ void load_piece(const NVFP4_GLOBAL uint4* xr, int64_t c0, int64_t chunks, int lane,
@@ -125,9 +110,7 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(const uint4* __restr
 template <int SLOTS>
 hipError_t launch_slots(const uint4* x, int64_t m, int64_t k, float global_amax, const float* amax_dev,
                         uint32_t* codes, uint8_t* scales, hipStream_t stream) {
-  const int64_t ntiles = (m + 127) / 128;
-  const int64_t unit_groups = ntiles * 4;
-  const int64_t blocks = (unit_groups + 7) / 8 * 64;
+  const int64_t blocks = row_group_blocks(m);
   hipLaunchKernelGGL((quantize_kernel<SLOTS>), dim3((uint32_t)blocks), dim3(kThreads), 0, stream, x, m, k,
                      global_amax, amax_dev, codes, scales);
   return hipGetLastError();

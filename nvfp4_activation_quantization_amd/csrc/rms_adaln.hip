@@ -64,32 +64,6 @@ __device__ __forceinline__ void store_planes(float2* planes, int chunks, int c, 
   planes[3 * chunks + c] = make_float2(f[6], f[7]);
 }
 
-// Butterfly sum over the 64 lanes: for s = 1, 2, 4, 8, 16, 32 every lane replaces v by
-// v + v[lane ^ s] (IEEE fp32 adds; both lanes of a pair compute the same sum, so every
-// lane ends with the same value).  The partner values come from DPP and the gfx950 row
-// swaps rather than LDS permutes: s = 1, 2 are quad permutations; s = 4 is row_shl:4 on
-// the even 4-lane banks of each 16-lane row and row_shr:4 on the odd ones; s = 8 is
-// row_ror:8; s = 16 and 32 use v_permlane16_swap / v_permlane32_swap, whose two results
-// are the lane's value and its partner's.
-__device__ __forceinline__ float lane_sum_butterfly(float v) {
-  uint32_t u = __float_as_uint(v);
-  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0xB1, 0xF, 0xF, false));
-  u = __float_as_uint(v);
-  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x4E, 0xF, 0xF, false));
-  u = __float_as_uint(v);
-  int t = __builtin_amdgcn_update_dpp((int)u, (int)u, 0x104, 0xF, 0x5, false);   // banks 0, 2: lane + 4
-  t = __builtin_amdgcn_update_dpp(t, (int)u, 0x114, 0xF, 0xA, false);            // banks 1, 3: lane - 4
-  v = v + __uint_as_float((uint32_t)t);
-  u = __float_as_uint(v);
-  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x128, 0xF, 0xF, false));
-  u = __float_as_uint(v);
-  const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
-  u = __float_as_uint(v);
-  const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
-}
-
 // y = bf16(bf16(bf16(bf16(x * rstd) * w) * opl) + shift) for the 8 elements of a chunk;
 // every rounding yields the fp32 encoding of the bf16 result directly (round_bf16).
 __device__ __forceinline__ void modulate8(const float* x8, const float* w8, const float* o8,

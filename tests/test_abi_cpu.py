@@ -118,12 +118,53 @@ def test_swiglu_packed_status_codes(dynamic):
         assert swp(amax=float("inf")) == 4 and swp(amax=0.0) == 4
 
 
+def rr(dynamic=False, **kw):
+    a = dict(h=A, o=A, bias=A, scale=A, gamma=A, eps=1e-6, m=4, k=512, amax=1.0, amax_out=A, codes=A, scales=A,
+             rstd=None, y=None)
+    a.update(kw)
+    f = ctypes.c_float(a["eps"])
+    if dynamic:
+        return lib.residual_rms_nvfp4_dynamic(a["h"], a["o"], a["bias"], a["scale"], a["gamma"], f, a["m"], a["k"],
+                                              a["amax_out"], a["codes"], a["scales"], a["rstd"], a["y"], None)
+    return lib.residual_rms_nvfp4(a["h"], a["o"], a["bias"], a["scale"], a["gamma"], f, a["m"], a["k"], a["amax"],
+                                  a["codes"], a["scales"], a["rstd"], a["y"], None)
+
+
+@pytest.mark.parametrize("dynamic", [False, True])
+def test_residual_rms_status_codes(dynamic):
+    for key in ("h", "gamma", "codes", "scales", "scale"):
+        assert rr(dynamic, **{key: None}) == 1, key
+    # without a branch, scale (and bias) are not needed
+    if not torch_has_gpu():
+        assert rr(dynamic, o=None, scale=None, bias=None) == 5
+    # k: a positive multiple of 512, at most 8192
+    for k in (0, 256, 768, 8704, -512):
+        assert rr(dynamic, k=k) == 2, k
+    assert rr(dynamic, m=-1) == 2
+    for key in ("h", "o", "bias", "scale", "gamma", "codes", "scales", "y"):
+        assert rr(dynamic, **{key: U}) == 3, key
+    assert rr(dynamic, rstd=A + 2) == 3
+    assert rr(dynamic, eps=-1.0) == 4 and rr(dynamic, eps=float("nan")) == 4
+    assert rr(dynamic, m=0) == 0
+    if dynamic:
+        assert rr(True, amax_out=None) == 1 and rr(True, amax_out=A + 2) == 3
+        assert rr(True, m=0, amax_out=None) == 0
+    else:
+        assert rr(amax=float("inf")) == 4 and rr(amax=-1.0) == 4
+
+
+def torch_has_gpu():
+    import torch
+    return torch.cuda.is_available()
+
+
 def test_valid_call_without_a_gpu_reports_no_device():
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is visible: a valid call would launch on fake pointers")
     assert q() == 5 and rms() == 5 and sw() == 5
     assert swp() == 5 and swp(bias=None, il=1) == 5 and swp(True) == 5
+    assert rr() == 5 and rr(bias=None) == 5 and rr(True) == 5
     assert lib.nvfp4act_init() == 5
 
 

@@ -178,6 +178,12 @@ class Workload:
             out = np.empty((self.m, self.k), np.uint16)
         return self._rows_bf16(ROLE_O, self.m, out=out, plain=True)
 
+    def h_rows(self, rows) -> np.ndarray:
+        return self.x_rows(rows, ROLE_X, fp32=True)
+
+    def o_rows(self, rows) -> np.ndarray:
+        return self.x_rows(rows, ROLE_O, plain=True)
+
     def calibration_h(self) -> np.ndarray:
         return self._rows_bf16(ROLE_CAL, self.cal_rows, fp32=True)
 
@@ -193,11 +199,11 @@ class Workload:
         return (1.0 + 0.1 * rng(self.number, ROLE_GAMMA).standard_normal(self.k, dtype=np.float32)).astype(
             np.float32)
 
-    def x_rows(self, rows) -> np.ndarray:
-        """Rows of the input regenerated from their chunks alone."""
+    def x_rows(self, rows, role: int = ROLE_X, fp32: bool = False, plain: bool = False) -> np.ndarray:
+        """Rows of the input (or of another role's rows) regenerated from their chunks alone."""
         rows = np.asarray(rows, np.int64)
         chunks = sorted(set((rows // CHUNK_ROWS).tolist()))
-        blocks = self._rows_bf16(ROLE_X, self.m, chunks=chunks)
+        blocks = self._rows_bf16(role, self.m, chunks=chunks, fp32=fp32, plain=plain)
         pos = {c: i for i, c in enumerate(chunks)}
         starts = np.cumsum([0] + [min(CHUNK_ROWS, self.m - c * CHUNK_ROWS) for c in chunks])
         sel = [starts[pos[int(r // CHUNK_ROWS)]] + int(r % CHUNK_ROWS) for r in rows]
