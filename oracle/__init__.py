@@ -78,6 +78,8 @@ def _load():
             "orc_rms_sum_f32": (F, [P, I64]),
             "orc_rms_rstd_f32": (F, [P, I64, F]),
             "orc_residual_rms_rows_gsf": (None, [P, P, P, P, P, F, I64, I64, P, F, P, P, P, P, P]),
+            "orc_residual_rms_adaln_rows_gsf": (None, [P, P, P, P, I64, P, P, P, I64, I64, P, F, I64, I64, P, F,
+                                                       P, P, P, P, P, P]),
             "orc_quantize_rows": (None, [P, I64, I64, F, P, P]),
             "orc_nvfp4_quantize": (None, [P, I64, I64, F, P, P]),
             "orc_rms_adaln_rows": (None, [P, I64, I64, P, P, P, P, I64, I64, P, F, F,
@@ -313,6 +315,57 @@ def residual_rms_dynamic(h_f32, o_u16, bias_u16, scale_f32, gamma_f32, eps: floa
     amax = max_abs(first["y"])
     out = residual_rms_rows(h_f32, o_u16, bias_u16, scale_f32, gamma_f32, eps, 0.0, want_y=want_y,
                             scales_rows=scales_rows, gsf=dynamic_global_scale(amax))
+    out["amax"] = amax
+    return out
+
+
+def residual_rms_adaln_rows(h_f32, o_u16, bias_u16, gate_table_u16, w_u16, table_u16, frame_idx, eps: float,
+                            global_amax: float, row_ids=None, want_y: bool = False,
+                            scales_rows: int | None = None, gsf: float | None = None):
+    """Gated residual add into an fp32 stream, then RMSNorm + adaLN -> NVFP4 over rows.
+
+    h_f32 [n, k] is not modified (the updated stream is returned as 'h').  o_u16 [n, k] bf16
+    or None; bias_u16 [k] or None; gate_table_u16 [T, k] (the folding block's gates);
+    w_u16 [k]; table_u16 [T, 2, k] (the next block's shift, scale); frame_idx [n].
+    Returns dict(codes, scale_bytes, y, scales, rstd, h, status).
+    """
+    h = np.array(h_f32, dtype=np.float32, copy=True, order="C")
+    n, k = h.shape
+    o = None if o_u16 is None else _c(o_u16, np.uint16)
+    bias = None if bias_u16 is None else _c(bias_u16, np.uint16).reshape(-1)
+    gate = _c(gate_table_u16, np.uint16)
+    w = _c(w_u16, np.uint16).reshape(-1)
+    tab = _c(table_u16, np.uint16)
+    T = tab.shape[0]
+    if gate.shape != (T, k) or tab.shape != (T, 2, k) or w.size != k:
+        raise ValueError("gate table [T, k], table [T, 2, k] and w [k] expected")
+    if o is not None and o.shape != (n, k):
+        raise ValueError("o must be [n, k]")
+    idx = _c(frame_idx, np.int32).reshape(-1)
+    rid = None if row_ids is None else _c(row_ids, np.int64)
+    codes = np.empty((n, k // 2), np.uint8)
+    sb = np.empty((n, k // 16), np.uint8)
+    rstd = np.empty(n, np.float32)
+    y = np.empty((n, k), np.uint16) if want_y else None
+    scales = None if scales_rows is None else np.zeros((scales_rows, k // 16), np.uint8)
+    status = np.zeros(1, np.uint32)
+    g = float(global_scale(global_amax) if gsf is None else gsf)
+    shift_ptr = tab.ctypes.data
+    scale_ptr = tab.ctypes.data + k * tab.itemsize
+    _load().orc_residual_rms_adaln_rows_gsf(_ptr(h), _ptr(o), _ptr(bias), _ptr(gate), k, _ptr(w), shift_ptr,
+                                            scale_ptr, 2 * k, T, _ptr(idx), float(eps), n, k, _ptr(rid), g,
+                                            _ptr(codes), _ptr(sb), _ptr(scales), _ptr(rstd), _ptr(y), _ptr(status))
+    return dict(codes=codes, scale_bytes=sb, y=y, scales=scales, rstd=rstd, h=h, status=int(status[0]))
+
+
+def residual_rms_adaln_dynamic(h_f32, o_u16, bias_u16, gate_table_u16, w_u16, table_u16, frame_idx, eps: float,
+                               want_y: bool = False, scales_rows: int | None = None):
+    """residual_rms_adaln_rows under the amax of the call's own y.  Adds 'amax'."""
+    first = residual_rms_adaln_rows(h_f32, o_u16, bias_u16, gate_table_u16, w_u16, table_u16, frame_idx, eps, 1.0,
+                                    want_y=True)
+    amax = max_abs(first["y"])
+    out = residual_rms_adaln_rows(h_f32, o_u16, bias_u16, gate_table_u16, w_u16, table_u16, frame_idx, eps, 0.0,
+                                  want_y=want_y, scales_rows=scales_rows, gsf=dynamic_global_scale(amax))
     out["amax"] = amax
     return out
 

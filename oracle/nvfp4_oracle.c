@@ -537,6 +537,82 @@ EXPORT void orc_residual_rms_rows_gsf(float* h, const uint16_t* o, const uint16_
     leave_ieee(s);
 }
 
+/* The residual add of a DiT block's gated MLP branch folded into the next
+   block's RMSNorm + adaLN producer ([TRT] Summary: the MLP residual add is
+   folded into the next block's norm; the folding block reads the gate from its
+   own AdaLN table while shift and scale come from the next block's table),
+   over an fp32 residual stream as in orc_residual_rms_rows_gsf.  Row i with
+   t = frame_idx[i] in [0, num_frames), element d:
+     u    = bf16(o[d] + bias[d])            (u = o[d] when bias is NULL)
+     h[d] = h[d] + u * gate_t[d]            fp32: the product rounded, then the add
+   with gate_t the row t of the block's own table (gate + t*gate_stride, bf16);
+   then on the updated row, with the statistic of rms_sum_f32's tree:
+     rstd = 1 / sqrt(sum(h^2) / k + eps)
+     n    = bf16(h * rstd)
+     nw   = bf16(n * w)
+     opl  = bf16(1 + scale_t)
+     mm   = bf16(nw * opl)
+     y    = bf16(mm + shift_t)
+   (shift_t, scale_t: row t of the next block's table, at shift + t*frame_stride,
+   scale + t*frame_stride) and the block quantizer.  A row whose index lies
+   outside [0, num_frames) is left unchanged in h, gets all-zero codes and
+   scale bytes and a zero y row, its rstd is that of the unchanged row, and bit
+   0 of *status is set ([INT64] bounds contract).  o may be NULL (no residual
+   add); bias may be NULL.  Outputs as in orc_rms_adaln_rows_gsf. */
+EXPORT void orc_residual_rms_adaln_rows_gsf(float* h, const uint16_t* o, const uint16_t* bias,
+                                            const uint16_t* gate, int64_t gate_stride, const uint16_t* w,
+                                            const uint16_t* shift, const uint16_t* scale,
+                                            int64_t frame_stride, int64_t num_frames,
+                                            const int32_t* frame_idx, float eps, int64_t n, int64_t k,
+                                            const int64_t* row_ids, float gsf, uint8_t* codes,
+                                            uint8_t* scale_bytes, uint8_t* scales, float* rstd_out,
+                                            uint16_t* y_out, uint32_t* status) {
+    unsigned int s = enter_ieee();
+    float* y = (float*)malloc(sizeof(float) * (size_t)k);
+    uint8_t* sb = (uint8_t*)malloc((size_t)(k / 16));
+    for (int64_t i = 0; i < n; ++i) {
+        float* hr = h + i * k;
+        int64_t r = row_ids ? row_ids[i] : i;
+        int32_t t = frame_idx[i];
+        int ok = t >= 0 && (int64_t)t < num_frames;
+        if (ok && o) {
+            const uint16_t* gt = gate + (int64_t)t * gate_stride;
+            for (int64_t d = 0; d < k; ++d) {
+                uint16_t u = o[i * k + d];
+                if (bias) u = bf16_round(bf16_to_f32(u) + bf16_to_f32(bias[d]));
+                float prod = bf16_to_f32(u) * bf16_to_f32(gt[d]);
+                hr[d] = hr[d] + prod;
+            }
+        }
+        float rstd = rms_rstd_f32(hr, k, eps);
+        if (rstd_out) rstd_out[i] = rstd;
+        if (!ok) {
+            memset(codes + i * (k / 2), 0, (size_t)(k / 2));
+            memset(sb, 0, (size_t)(k / 16));
+            for (int64_t d = 0; d < k; ++d) y[d] = 0.0f;
+            if (status) *status |= 1u;
+        } else {
+            const uint16_t* sh = shift + (int64_t)t * frame_stride;
+            const uint16_t* sc = scale + (int64_t)t * frame_stride;
+            for (int64_t d = 0; d < k; ++d) {
+                float nn = rb(hr[d] * rstd);
+                float nw = rb(nn * bf16_to_f32(w[d]));
+                float opl = rb(1.0f + bf16_to_f32(sc[d]));
+                float mm = rb(nw * opl);
+                y[d] = rb(mm + bf16_to_f32(sh[d]));
+            }
+            quantize_row(y, k, gsf, codes + i * (k / 2), sb);
+        }
+        if (scale_bytes) memcpy(scale_bytes + i * (k / 16), sb, (size_t)(k / 16));
+        if (scales) place_scales(sb, r, k, scales);
+        if (y_out)
+            for (int64_t d = 0; d < k; ++d) y_out[i * k + d] = bf16_round(y[d]);
+    }
+    free(sb);
+    free(y);
+    leave_ieee(s);
+}
+
 /* ------------------------------------------------------------------------- */
 /* SiLU table and the SwiGLU producer                                        */
 /* ------------------------------------------------------------------------- */

@@ -15,6 +15,8 @@ TensorRT-LLM fusions apply only to static NVFP4 scales).  For each workload:
                          the same, with the workload's bias and column layout
   residual_rms_63240x7168  max |y| of the oracle (residual add, then RMSNorm) over
                          8,192 calibration rows of h and o
+  residual_adaln_63240x7168  the same for the gated residual + RMSNorm + adaLN, frame
+                         (r * 31) // 8192
 
 Run:  python tests/golden/make_calibration.py
 """
@@ -47,6 +49,12 @@ def calibrate(w: workloads.Workload) -> dict:
     elif w.kind == "quantize":
         amax = amax_of_bf16(w.calibration_x())
         how = "max|x| over %d calibration rows" % w.cal_rows
+    elif w.kind == "residual_adaln":
+        res = oracle.residual_rms_adaln_rows(w.calibration_h(), w.calibration_o(), w.bias(), w.gate_table(),
+                                             w.weight(), w.table(), w.calibration_frame_idx(), w.eps, 1.0,
+                                             want_y=True)
+        amax = amax_of_bf16(res["y"])
+        how = "max|y| of the oracle over %d calibration rows" % w.cal_rows
     elif w.kind == "residual_rms":
         res = oracle.residual_rms_rows(w.calibration_h(), w.calibration_o(), w.bias(), w.residual_scale(),
                                        w.gamma(), w.eps, 1.0, want_y=True)

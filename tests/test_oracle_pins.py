@@ -494,6 +494,69 @@ def test_residual_norm_hand_worked_block():
     assert np.all(res["codes"][0, 8:] == 0x77)
 
 
+def _adaln_fold_case(seed, n=6, k=1024, frames=3):
+    g = np.random.Generator(np.random.PCG64(seed))
+    h = (g.standard_normal((n, k)) * 2).astype(np.float32)
+    o = oracle.bf16_round(g.standard_normal((n, k)).astype(np.float32))
+    bias = oracle.bf16_round((0.5 * g.standard_normal(k)).astype(np.float32))
+    gate = oracle.bf16_round((0.3 * g.standard_normal((frames, k))).astype(np.float32))
+    w = oracle.bf16_round((1 + 0.1 * g.standard_normal(k)).astype(np.float32))
+    tab = oracle.bf16_round((0.1 * g.standard_normal((frames, 2, k))).astype(np.float32))
+    idx = (np.arange(n) * frames // n).astype(np.int32)[::-1].copy()
+    return h, o, bias, gate, w, tab, idx
+
+
+def test_gated_residual_update_is_the_stream_update_with_the_frame_gate():
+    h, o, bias, gate, w, tab, idx = _adaln_fold_case(51)
+    res = oracle.residual_rms_adaln_rows(h, o, bias, gate, w, tab, idx, 1e-6, 8.0)
+    for i, t in enumerate(idx):
+        ref = oracle.residual_rms_rows(h[i:i + 1], o[i:i + 1], bias, oracle.bf16_to_f32(gate[t]),
+                                       np.ones(h.shape[1], np.float32), 1e-6, 8.0)
+        assert np.array_equal(res["h"][i].view(np.uint32), ref["h"][0].view(np.uint32))
+        assert res["rstd"][i] == ref["rstd"][0]
+    # and against torch's eager ops directly (bf16 tensor add, fp32 product and add)
+    gt = _t16(gate[idx]).float()
+    want = torch.from_numpy(h) + (_t16(o) + _t16(bias)).float() * gt
+    assert np.array_equal(res["h"].view(np.uint32), want.numpy().view(np.uint32))
+
+
+def test_gated_residual_adaln_chain_matches_torch_eager_ops():
+    h, o, bias, gate, w, tab, idx = _adaln_fold_case(52)
+    res = oracle.residual_rms_adaln_rows(h, o, None, gate, w, tab, idx, 1e-6, 8.0, want_y=True)
+    B = torch.bfloat16
+    hn = torch.from_numpy(res["h"])
+    rstd = torch.from_numpy(res["rstd"])[:, None]
+    shift = _t16(tab[idx, 0]).float()
+    scale = _t16(tab[idx, 1]).float()
+    n_ = (hn * rstd).to(B).float()
+    nw = (n_ * _t16(w).float()).to(B).float()
+    opl = (1.0 + scale).to(B).float()
+    mm = (nw * opl).to(B).float()
+    y = (mm + shift).to(B)
+    assert np.array_equal(res["y"], y.view(torch.int16).numpy().view(np.uint16))
+    # the gate comes from the first table, shift and scale from the second: exchanging
+    # the gate table with the scale rows changes the result
+    other = oracle.residual_rms_adaln_rows(h, o, None, np.ascontiguousarray(tab[:, 1]), w,
+                                           np.stack([tab[:, 0], gate], axis=1), idx, 1e-6, 8.0, want_y=True)
+    assert not np.array_equal(other["y"], res["y"])
+
+
+def test_gated_residual_out_of_range_frame_leaves_the_row():
+    h, o, bias, gate, w, tab, idx = _adaln_fold_case(53)
+    idx[[1, 4]] = [3, -1]
+    res = oracle.residual_rms_adaln_rows(h, o, bias, gate, w, tab, idx, 1e-6, 8.0, want_y=True)
+    assert res["status"] == 1
+    for i in (1, 4):
+        assert np.array_equal(res["h"][i], h[i])
+        assert res["rstd"][i] == oracle.rms_rstd_f32(h[i], 1e-6)
+        assert not res["codes"][i].any() and not res["scale_bytes"][i].any() and not res["y"][i].any()
+    ok = [0, 2, 3, 5]
+    part = oracle.residual_rms_adaln_rows(h[ok], o[ok], bias, gate, w, tab, idx[ok], 1e-6, 8.0, want_y=True)
+    assert part["status"] == 0
+    for key in ("codes", "scale_bytes", "y", "h", "rstd"):
+        assert np.array_equal(part[key], res[key][ok]), key
+
+
 # --------------------------------------------------------------------------
 # SiLU table and the SwiGLU producer
 # --------------------------------------------------------------------------
@@ -724,6 +787,16 @@ def test_dynamic_residual_rms_is_static_at_its_own_amax():
     y = oracle.residual_rms_rows(h, o, bias, scale, gamma, 1e-6, 1.0, want_y=True)["y"]
     assert dyn["amax"] == float(np.abs(oracle.bf16_to_f32(y)).max())
     ref = oracle.residual_rms_rows(h, o, bias, scale, gamma, 1e-6, dyn["amax"], want_y=True, scales_rows=128)
+    for key in ("codes", "scales", "y", "h", "rstd"):
+        assert np.array_equal(dyn[key], ref[key]), key
+
+
+def test_dynamic_gated_residual_adaln_is_static_at_its_own_amax():
+    h, o, bias, gate, w, tab, idx = _adaln_fold_case(54, n=5, k=512)
+    dyn = oracle.residual_rms_adaln_dynamic(h, o, bias, gate, w, tab, idx, 1e-6, want_y=True, scales_rows=128)
+    ref = oracle.residual_rms_adaln_rows(h, o, bias, gate, w, tab, idx, 1e-6, dyn["amax"], want_y=True,
+                                         scales_rows=128)
+    assert dyn["amax"] == float(np.abs(oracle.bf16_to_f32(ref["y"])).max())
     for key in ("codes", "scales", "y", "h", "rstd"):
         assert np.array_equal(dyn[key], ref[key]), key
 

@@ -23,12 +23,17 @@ a 34x60 latent grid per frame over 31 frames = 63,240 tokens from
                            36 outlier columns x30 of rms_adaln_63240x7168), a bf16 branch
                            output o ~ N(0,1), bf16 bias (std 0.25), fp32 per-channel
                            scale (std 0.2) and fp32 RMSNorm weight 1 + 0.1 N(0,1)
+  residual_adaln_63240x7168  the same stream and branch, gated by a per-frame bf16 gate
+                           table (31 x 7168, std 0.2) of the folding block, then RMSNorm
+                           (bf16 weight) + adaLN with the next block's (shift, scale) table
+                           (31 frames, frame = token // 2040, as rms_adaln_63240x7168)
 
 Seeds: numpy ``PCG64``; the seed of role ``role`` in workload number ``i``
-(1..8 in the order above) is ``1000*i + role`` with roles 1 x (or h), 2 weight
+(1..9 in the order above) is ``1000*i + role`` with roles 1 x (or h), 2 weight
 (or bias), 3 modulation table (or residual scale), 4 calibration rows, 5
 outlier pick, 6 per-head std, 8 the residual branch o, 9 its calibration rows,
-10 the fp32 RMSNorm weight.
+10 the fp32 RMSNorm weight, 11 the gate table, 12 the bias where a weight is
+drawn too.
 Large tensors are drawn in 4096-row chunks, chunk ``c`` from
 ``SeedSequence(1000*i + role).spawn(n_chunks)[c]``, so any chunk can be
 regenerated alone and chunks can be drawn in parallel threads.
@@ -43,7 +48,7 @@ import numpy as np
 
 CHUNK_ROWS = 4096
 ROLE_X, ROLE_W, ROLE_TABLE, ROLE_CAL, ROLE_OUTLIER, ROLE_HEADSTD = 1, 2, 3, 4, 5, 6
-ROLE_O, ROLE_CAL_O, ROLE_GAMMA = 8, 9, 10
+ROLE_O, ROLE_CAL_O, ROLE_GAMMA, ROLE_GATE, ROLE_BIAS = 8, 9, 10, 11, 12
 
 
 def to_bf16(a: np.ndarray) -> np.ndarray:
@@ -65,7 +70,7 @@ def _threads() -> int:
 class Workload:
     name: str
     number: int               # 1..5, selects the seeds
-    kind: str                 # "rms_adaln" | "quantize" | "swiglu" | "residual_rms"
+    kind: str                 # "rms_adaln" | "quantize" | "swiglu" | "residual_rms" | "residual_adaln"
     m: int                    # rows (tokens)
     k: int                    # output columns (hidden, or F for swiglu)
     frames: int = 0           # modulation table rows (rms_adaln)
@@ -91,7 +96,7 @@ class Workload:
         scale bytes over the padded rows (parameters not counted).  residual_rms: the
         fp32 stream read and written back, the bf16 branch read."""
         out = self.m * self.k // 2 + self.padded_rows * self.k // 16
-        if self.kind == "residual_rms":
+        if self.kind in ("residual_rms", "residual_adaln"):
             return (4 + 2 + 4) * self.m * self.k + out
         return 2 * self.m * self.in_cols + out
 
@@ -102,6 +107,8 @@ class Workload:
             return 2 * 2 * self.k
         if self.kind == "residual_rms":
             return (2 + 4 + 4) * self.k
+        if self.kind == "residual_adaln":
+            return 2 * self.k + 2 * self.frames * self.k + 2 * self.k + 2 * self.frames * 2 * self.k + 4 * self.m
         return 0
 
     # ---- generation ----------------------------------------------------------
@@ -220,8 +227,16 @@ class Workload:
         [k] bf16 bias of the branch; None without a bias."""
         if self.bias_std <= 0:
             return None
+        if self.kind == "residual_adaln":
+            g = rng(self.number, ROLE_BIAS)
+            return to_bf16(self.bias_std * g.standard_normal(self.k, dtype=np.float32))
         n = self.k if self.kind == "residual_rms" else 2 * self.k
         return to_bf16(self.bias_std * rng(self.number, ROLE_W).standard_normal(n, dtype=np.float32))
+
+    def gate_table(self) -> np.ndarray:
+        """residual_adaln: the folding block's [frames, k] bf16 gate rows (std 0.2)."""
+        g = rng(self.number, ROLE_GATE)
+        return to_bf16(0.2 * g.standard_normal((self.frames, self.k), dtype=np.float32))
 
     def table(self) -> np.ndarray:
         """[frames, 2, k] bf16: row t holds (shift, scale) of frame t."""
@@ -260,6 +275,8 @@ WORKLOADS = {
                  interleaved=True),
         Workload("residual_rms_63240x7168", 8, "residual_rms", 63240, 7168, outliers="cols36_x30",
                  cal_rows=8192, bias_std=0.25),
+        Workload("residual_adaln_63240x7168", 9, "residual_adaln", 63240, 7168, frames=31,
+                 rows_per_frame=2040, outliers="cols36_x30", cal_rows=8192, bias_std=0.25),
     ]
 }
 
