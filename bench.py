@@ -88,6 +88,9 @@ def make_inputs(wl, torch, amax):
             return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
         args = dict(x=f32(wl.h()), o=up(wl.o()), bias=up(wl.bias()), scale=f32(wl.residual_scale()),
                     gamma=f32(wl.gamma()))
+    elif wl.kind == "residual_adaln":
+        args = dict(x=torch.from_numpy(wl.h()).to(dev), o=up(wl.o()), bias=up(wl.bias()), gate=up(wl.gate_table()),
+                    weight=up(wl.weight()), table=up(wl.table()), frame_idx=torch.from_numpy(wl.frame_idx()).to(dev))
     else:
         args = dict(x=up(wl.x()))
         if wl.kind == "swiglu" and wl.bias_std > 0:
@@ -116,7 +119,19 @@ def main():
     amax_dev = torch.zeros(1, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
 
-    if wl.kind == "residual_rms":
+    if wl.kind == "residual_adaln":
+        # the stream is updated in place every step (the same work each time)
+        residual = (inp["o"], inp["bias"], inp["gate"])
+        fold_args = (inp["x"], inp["weight"], inp["table"], inp["frame_idx"], wl.eps)
+        if a.dynamic:
+            def step():
+                nq.residual_rms_adaln_nvfp4_dynamic(*fold_args, residual=residual, amax_out=amax_dev, codes=codes,
+                                                    scales=scales, stream=stream)
+        else:
+            def step():
+                nq.residual_rms_adaln_nvfp4(*fold_args, amax, residual=residual, codes=codes, scales=scales,
+                                            stream=stream)
+    elif wl.kind == "residual_rms":
         # the stream is updated in place every step (the same work each time)
         residual = (inp["o"], inp["bias"], inp["scale"])
         if a.dynamic:
@@ -192,7 +207,7 @@ def main():
     ms_per_step = region_ms / a.steps
 
     # the per-call form reads the input twice (the amax pass, then the quantize pass)
-    reread = (4 + 2) * wl.m * wl.k if wl.kind == "residual_rms" else 2 * wl.m * wl.in_cols
+    reread = (4 + 2) * wl.m * wl.k if wl.kind.startswith("residual") else 2 * wl.m * wl.in_cols
     alg_bytes = wl.algorithmic_bytes() + (reread if a.dynamic else 0)
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
@@ -229,7 +244,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "rows": wl.m, "hidden": wl.k,
-                   "frames": wl.frames if wl.kind == "rms_adaln" else None,
+                   "frames": wl.frames if wl.frames else None,
                    "algorithmic_bytes_per_step": alg_bytes,
                    "global_amax": "per-call (device amax pass)" if a.dynamic else amax},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -256,8 +271,16 @@ def cpu_baseline(wl, amax, rows, np):
     threads = max(1, min(16, len(os.sched_getaffinity(0))))
     rows = min(rows, wl.m)
     sel = np.arange(rows)
-    x = wl.x_rows(sel) if wl.kind != "residual_rms" else None
-    if wl.kind == "residual_rms":
+    x = wl.x_rows(sel) if not wl.kind.startswith("residual") else None
+    if wl.kind == "residual_adaln":
+        x, o = wl.h_rows(sel), wl.o_rows(sel)
+        fold = (wl.bias(), wl.gate_table(), wl.weight(), wl.table())
+        idx = wl.frame_idx(sel)
+
+        def part(se):
+            s, e = se
+            oracle.residual_rms_adaln_rows(x[s:e], o[s:e], *fold, idx[s:e], wl.eps, amax)
+    elif wl.kind == "residual_rms":
         x, o = wl.h_rows(sel), wl.o_rows(sel)
         bias, scale, gamma = wl.bias(), wl.residual_scale(), wl.gamma()
 

@@ -11,6 +11,8 @@
  * and a fourth that folds a residual add into the norm:
  *   residual_rms_nvfp4  h += bf16(o + bias) * scale (fp32, in place);
  *                       RMSNorm with an fp32 weight               -> NVFP4
+ *   residual_rms_adaln_nvfp4  h += bf16(o + bias) * gate[t] (fp32, in place);
+ *                       RMSNorm + adaLN of the next block         -> NVFP4
  *
  * Sources: TensorRT-LLM PR #21483 "Fuse the MiniMax-H3 NVFP4 activation
  * quantize into the AdaLN, SwiGLU and attention-output producers" (Summary);
@@ -213,6 +215,41 @@ int residual_rms_nvfp4(float* h, const void* o, const void* bias, const float* s
                        const float* gamma, float eps, int64_t m, int64_t k, float global_amax,
                        void* codes, void* scales, float* rstd_out, void* y_out, void* stream);
 
+/* The gated MLP residual of a DiT block folded into the next block's RMSNorm +
+   adaLN producer, over an fp32 residual stream (TensorRT-LLM PR #21483,
+   Summary: the MLP residual add is folded into the next block's norm, and the
+   folding block reads the gate from its own AdaLN table while shift and scale
+   come from the next block's; FastVideo API page, residual_norm_quantize: the
+   fp32 stream updated in place).  Per row r with t = frame_idx[r], element d:
+     u    = bf16(o[d] + bias[d])               (u = o[d] without a bias)
+     h[d] = h[d] + u * gate_t[d]               fp32, the product rounded, then
+                                               the add; written back into h
+     rstd = the fp32 statistic of residual_rms_nvfp4 over the updated row
+     y    = bf16(bf16(bf16(bf16(h*rstd) * w) * bf16(1 + scale_t)) + shift_t)
+   then the NVFP4 quantizer above.
+     h            [m, k] fp32 (as for residual_rms_nvfp4)
+     o, bias      the branch and its bias, as for residual_rms_nvfp4 (o
+                  nullable: no residual add)
+     gate         the folding block's gate rows: row t at gate + t*gate_stride
+                  bf16 elements (required with o)
+     gate_stride  >= k, gate_stride*2 a multiple of 16 (checked only with o)
+     weight       [k] bf16 RMSNorm weight
+     shift, scale the next block's modulation rows, laid out as for
+                  rms_adaln_nvfp4 (frame_stride, num_frames)
+     frame_idx    [m] int32, in [0, num_frames).  A row outside that range keeps
+                  its h (no residual add), is written as zero codes, zero scale
+                  bytes and a zero y_out row, and sets bit 0 of *status_word;
+                  its rstd_out is the statistic of the unchanged row
+     eps, m, k, global_amax, codes, scales, rstd_out, y_out  as for
+                  residual_rms_nvfp4; status_word as for rms_adaln_nvfp4
+   Returns a status. */
+int residual_rms_adaln_nvfp4(float* h, const void* o, const void* bias, const void* gate,
+                             int64_t gate_stride, const void* weight, const void* shift,
+                             const void* scale, int64_t frame_stride, int64_t num_frames,
+                             const int32_t* frame_idx, float eps, int64_t m, int64_t k,
+                             float global_amax, void* codes, void* scales, float* rstd_out,
+                             void* y_out, uint32_t* status_word, void* stream);
+
 /* Per-call (dynamic) global amax
    ------------------------------
    The *_dynamic forms take the global amax from the tensor itself instead of
@@ -255,6 +292,13 @@ int residual_rms_nvfp4_dynamic(float* h, const void* o, const void* bias, const 
                                const float* gamma, float eps, int64_t m, int64_t k,
                                float* amax_out, void* codes, void* scales, float* rstd_out,
                                void* y_out, void* stream);
+
+int residual_rms_adaln_nvfp4_dynamic(float* h, const void* o, const void* bias, const void* gate,
+                                     int64_t gate_stride, const void* weight, const void* shift,
+                                     const void* scale, int64_t frame_stride, int64_t num_frames,
+                                     const int32_t* frame_idx, float eps, int64_t m, int64_t k,
+                                     float* amax_out, void* codes, void* scales, float* rstd_out,
+                                     void* y_out, uint32_t* status_word, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,8 +18,13 @@ each returning ``(codes, scales)``; and the per-call (dynamic) amax forms
   residual_rms_nvfp4(h, gamma, eps, global_amax, residual=(o, bias, scale))
                                                           fp32 residual stream (in place) +
                                                           RMSNorm with an fp32 weight
+  residual_rms_adaln_nvfp4(h, weight, table, frame_idx, eps, global_amax,
+                           residual=(o, bias, gate_table))
+                                                          gated residual (own table) + RMSNorm
+                                                          + adaLN (next block's table)
   swiglu_nvfp4_dynamic(projection), swiglu_packed_nvfp4_dynamic(projection, bias, interleaved),
-  residual_rms_nvfp4_dynamic(h, gamma, eps, residual)
+  residual_rms_nvfp4_dynamic(h, gamma, eps, residual),
+  residual_rms_adaln_nvfp4_dynamic(h, weight, table, frame_idx, eps, residual)
 returning ``(codes, scales, amax)`` with ``amax`` a one-element float32 device tensor, codes ``[m, k/2]`` uint8, scales
 ``[pad(m), k/16]`` uint8 in the 128x4 swizzle (buffer shapes as the FastVideo
 API page's ``new_quantized``).
@@ -59,6 +64,10 @@ _SIGS = {
     "swiglu_packed_nvfp4_dynamic": (_I, [_P, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "residual_rms_nvfp4": (_I, [_P, _P, _P, _P, _P, _F, _I64, _I64, _F, _P, _P, _P, _P, _P]),
     "residual_rms_nvfp4_dynamic": (_I, [_P, _P, _P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "residual_rms_adaln_nvfp4": (_I, [_P, _P, _P, _P, _I64, _P, _P, _P, _I64, _I64, _P, _F, _I64, _I64, _F,
+                                      _P, _P, _P, _P, _P, _P]),
+    "residual_rms_adaln_nvfp4_dynamic": (_I, [_P, _P, _P, _P, _I64, _P, _P, _P, _I64, _I64, _P, _F, _I64, _I64,
+                                              _P, _P, _P, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -407,4 +416,79 @@ def residual_rms_nvfp4_dynamic(h: torch.Tensor, gamma: torch.Tensor, eps: float,
                                            _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, k),
                                                     "y_out") if y_out is not None else 0,
                                            _stream(stream, h.device)))
+    return codes, scales, amax_out
+
+
+def _fold_args(h, weight, table, frame_idx, residual):
+    if h.dim() != 2 or h.dtype != torch.float32 or not h.is_cuda or not h.is_contiguous():
+        raise ValueError("h must be a contiguous float32 [m, k] device tensor")
+    m, k = h.shape
+    if table.dim() != 3 or table.shape[1] != 2 or table.shape[2] != k or not table.is_contiguous():
+        raise ValueError("table must be a contiguous [T, 2, k] tensor of (shift, scale) rows")
+    if weight.numel() != k or not weight.is_contiguous():
+        raise ValueError("weight must be a contiguous tensor of k values")
+    if frame_idx.dtype != torch.int32 or frame_idx.numel() != m or not frame_idx.is_cuda:
+        raise ValueError("frame_idx must be an int32 device tensor of m values")
+    tp = _bf16_ptr(table, "table")
+    args = dict(m=m, k=k, w=_bf16_ptr(weight, "weight"), shift=tp, scale=tp + 2 * k, frame_stride=2 * k,
+                frames=table.shape[0], idx=frame_idx.data_ptr(), o=0, bias=0, gate=0, gate_stride=k)
+    if residual is not None:
+        o, bias, gate = residual
+        if tuple(o.shape) != (m, k) or not o.is_contiguous():
+            raise ValueError("o must be a contiguous [m, k] tensor")
+        if gate.dim() != 2 or gate.shape[1] != k or gate.stride(1) != 1:
+            raise ValueError("gate must be a [T, k] table with unit column stride")
+        args["o"] = _bf16_ptr(o, "o")
+        if bias is not None:
+            if bias.numel() != k or not bias.is_contiguous():
+                raise ValueError("bias must be a contiguous tensor of k values")
+            args["bias"] = _bf16_ptr(bias, "bias")
+        args["gate"] = _bf16_ptr(gate, "gate")
+        args["gate_stride"] = gate.stride(0)
+    return args
+
+
+def residual_rms_adaln_nvfp4(h: torch.Tensor, weight: torch.Tensor, table: torch.Tensor, frame_idx: torch.Tensor,
+                             eps: float, global_amax: float, residual=None, codes=None, scales=None, rstd_out=None,
+                             y_out=None, status_word=None, stream=None):
+    """In place h += bf16(o + bias) * gate[frame_idx[r]] (residual = (o, bias or None, gate table [T, k]), the
+    folding block's gates), then RMSNorm + adaLN with the next block's (shift, scale) table [T, 2, k] -> NVFP4.
+    h: contiguous float32 [m, k]."""
+    a = _fold_args(h, weight, table, frame_idx, residual)
+    m, k = a["m"], a["k"]
+    if codes is None or scales is None:
+        codes, scales = new_quantized(m, k, h.device)
+    _check(_lib.residual_rms_adaln_nvfp4(h.data_ptr(), a["o"], a["bias"], a["gate"], a["gate_stride"], a["w"],
+                                         a["shift"], a["scale"], a["frame_stride"], a["frames"], a["idx"],
+                                         float(eps), m, k, float(global_amax),
+                                         _out_ptr(codes, torch.uint8, (m, k // 2), "codes"),
+                                         _out_ptr(scales, torch.uint8, (padded_rows(m), k // 16), "scales"),
+                                         _out_ptr(rstd_out, torch.float32, (m,), "rstd_out"),
+                                         _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, k), "y_out")
+                                         if y_out is not None else 0,
+                                         status_word.data_ptr() if status_word is not None else 0,
+                                         _stream(stream, h.device)))
+    return codes, scales
+
+
+def residual_rms_adaln_nvfp4_dynamic(h: torch.Tensor, weight: torch.Tensor, table: torch.Tensor,
+                                     frame_idx: torch.Tensor, eps: float, residual=None, amax_out=None, codes=None,
+                                     scales=None, rstd_out=None, y_out=None, status_word=None, stream=None):
+    """residual_rms_adaln_nvfp4 under the amax of this call's own y (computed on the device).
+    Returns (codes, scales, amax_out)."""
+    a = _fold_args(h, weight, table, frame_idx, residual)
+    m, k = a["m"], a["k"]
+    if codes is None or scales is None:
+        codes, scales = new_quantized(m, k, h.device)
+    amax_out, ap = _amax_ptr(amax_out, h.device)
+    _check(_lib.residual_rms_adaln_nvfp4_dynamic(h.data_ptr(), a["o"], a["bias"], a["gate"], a["gate_stride"],
+                                                 a["w"], a["shift"], a["scale"], a["frame_stride"], a["frames"],
+                                                 a["idx"], float(eps), m, k, ap,
+                                                 _out_ptr(codes, torch.uint8, (m, k // 2), "codes"),
+                                                 _out_ptr(scales, torch.uint8, (padded_rows(m), k // 16), "scales"),
+                                                 _out_ptr(rstd_out, torch.float32, (m,), "rstd_out"),
+                                                 _out_ptr(y_out, y_out.dtype if y_out is not None else None, (m, k),
+                                                          "y_out") if y_out is not None else 0,
+                                                 status_word.data_ptr() if status_word is not None else 0,
+                                                 _stream(stream, h.device)))
     return codes, scales, amax_out

@@ -21,7 +21,6 @@ HIPCC_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-mcode-object-version=5",
     # IEEE fp32: no contraction of a*b+c into FMA (the kernels call fmaf where the
     # specification has a fused multiply-add), correctly rounded divide and sqrt, denormals
@@ -43,22 +42,41 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libnvfp4act.so)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into libnvfp4act.so (always rebuilds)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd):
     proc = subprocess.run(cmd, capture_output=True, text=True)
     # hipcc's host pass does not know the packed-fp32 feature and says so: harmless
     noise = "not a recognized feature for this target"
     err = "\n".join(l for l in proc.stderr.splitlines() if noise not in l)
-    if proc.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
-    if err.strip() and verbose:
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+    return proc.returncode, err
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source into libnvfp4act.so (always rebuilds).  The sources are
+    compiled to objects in parallel, then linked."""
+    from concurrent.futures import ThreadPoolExecutor
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(PKG, "_obj_%s_%s.o" % (os.path.splitext(s)[0], tag)) for s in SOURCES]
+    cmds = [[hipcc(), *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj] for src, obj in zip(SOURCES, objs)]
+    if verbose:
+        for c in cmds:
+            print(" ".join(c), flush=True)
+    try:
+        with ThreadPoolExecutor(len(cmds)) as ex:
+            results = list(ex.map(_run, cmds))
+        for (rc, err), src in zip(results, SOURCES):
+            if rc != 0:
+                raise RuntimeError("hipcc failed on %s:\n%s" % (src, err))
+            if err.strip() and verbose:
+                print(err, file=sys.stderr)
+        tmp = LIB + ".tmp" + tag
+        rc, err = _run([hipcc(), *HIPCC_FLAGS, "-shared", *objs, "-o", tmp])
+        if rc != 0:
+            raise RuntimeError("hipcc link failed:\n" + err)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

@@ -58,6 +58,7 @@ int current_device(const DeviceInfo** info, int* device_out) {
     st.info.cu_count = prop.multiProcessorCount;
     hipError_t e = nvfp4act::prepare_rms_adaln();
     if (e == hipSuccess) e = nvfp4act::prepare_swiglu();
+    if (e == hipSuccess) e = nvfp4act::prepare_residual_rms();
     if (e != hipSuccess) {
       st.probed = false;
       return fail_hip(e);
@@ -309,6 +310,75 @@ int residual_rms_call(float* h, const void* o, const void* bias, const float* sc
   return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
 }
 
+// The adaLN form: the gate table multiplies the branch; RMSNorm weight and the next block's
+// (shift, scale) rows replace gamma.
+struct FoldTables {
+  const void* gate;
+  int64_t gate_stride;
+  const void* weight;
+  const void* shift;
+  const void* scale;
+  int64_t frame_stride, num_frames;
+  const int32_t* frame_idx;
+  uint32_t* status_word;
+};
+
+int residual_adaln_shape(int64_t m, int64_t k, const void* o, const FoldTables& f) {
+  if (m < 0 || k <= 0 || k % 512 != 0 || k > nvfp4act::kMaxResidualK || f.num_frames < 1 || f.frame_stride < k ||
+      (o && f.gate_stride < k))
+    return NVFP4ACT_ERR_SHAPE;
+  return NVFP4ACT_OK;
+}
+
+int residual_adaln_call(float* h, const void* o, const void* bias, const FoldTables& f, float eps, int64_t m,
+                        int64_t k, float global_amax, float* amax_dev, void* codes, void* scales, float* rstd_out,
+                        void* y_out, void* stream) {
+  int st = residual_adaln_shape(m, k, o, f);
+  if (st != NVFP4ACT_OK) return st;
+  if (m == 0) return NVFP4ACT_OK;
+  if (!h || !f.weight || !f.shift || !f.scale || !f.frame_idx || !codes || !scales || (o && !f.gate))
+    return NVFP4ACT_ERR_NULL;
+  if (!aligned16(h) || !aligned16(f.weight) || !aligned16(f.shift) || !aligned16(f.scale) || !aligned16(codes) ||
+      !aligned16(scales) || (o && !aligned16(o)) || (o && !aligned16(f.gate)) || (o && bias && !aligned16(bias)) ||
+      (y_out && !aligned16(y_out)) || (rstd_out && !aligned4(rstd_out)) || !aligned4(f.frame_idx) ||
+      (f.status_word && !aligned4(f.status_word)) || (f.frame_stride * 2) % 16 != 0 ||
+      (o && (f.gate_stride * 2) % 16 != 0))
+    return NVFP4ACT_ERR_ALIGN;
+  if (!std::isfinite(eps) || eps < 0.0f) return NVFP4ACT_ERR_VALUE;
+  if (!amax_dev) {
+    st = check_amax(global_amax);
+    if (st != NVFP4ACT_OK) return st;
+  }
+  const DeviceInfo* info = nullptr;
+  st = current_device(&info, nullptr);
+  if (st != NVFP4ACT_OK) return st;
+  nvfp4act::ResidualLaunch p{};
+  p.h = h;
+  p.o = o;
+  p.bias = o ? bias : nullptr;
+  p.eps = eps;
+  p.m = m;
+  p.k = k;
+  p.global_amax = global_amax;
+  p.amax_dev = amax_dev;
+  p.codes = codes;
+  p.scales = scales;
+  p.rstd_out = rstd_out;
+  p.y_out = y_out;
+  p.mod = true;
+  p.gate = o ? f.gate : nullptr;
+  p.gate_stride = f.gate_stride;
+  p.weight = f.weight;
+  p.shift = f.shift;
+  p.mod_scale = f.scale;
+  p.frame_stride = f.frame_stride;
+  p.num_frames = f.num_frames;
+  p.frame_idx = f.frame_idx;
+  p.status_word = f.status_word;
+  hipError_t e = nvfp4act::launch_residual_rms(p, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
+}
+
 // The per-call forms need the amax destination: one 4-byte aligned float (m == 0 aside).
 int check_amax_out(int64_t m, const float* amax_out) {
   if (m == 0) return NVFP4ACT_OK;
@@ -394,6 +464,28 @@ int residual_rms_nvfp4_dynamic(float* h, const void* o, const void* bias, const 
   if (st != NVFP4ACT_OK) return st;
   return residual_rms_call(h, o, bias, scale, gamma, eps, m, k, 0.0f, amax_out, codes, scales, rstd_out, y_out,
                            stream);
+}
+
+int residual_rms_adaln_nvfp4(float* h, const void* o, const void* bias, const void* gate, int64_t gate_stride,
+                             const void* weight, const void* shift, const void* scale, int64_t frame_stride,
+                             int64_t num_frames, const int32_t* frame_idx, float eps, int64_t m, int64_t k,
+                             float global_amax, void* codes, void* scales, float* rstd_out, void* y_out,
+                             uint32_t* status_word, void* stream) {
+  const FoldTables f{gate, gate_stride, weight, shift, scale, frame_stride, num_frames, frame_idx, status_word};
+  return residual_adaln_call(h, o, bias, f, eps, m, k, global_amax, nullptr, codes, scales, rstd_out, y_out, stream);
+}
+
+int residual_rms_adaln_nvfp4_dynamic(float* h, const void* o, const void* bias, const void* gate,
+                                     int64_t gate_stride, const void* weight, const void* shift, const void* scale,
+                                     int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx, float eps,
+                                     int64_t m, int64_t k, float* amax_out, void* codes, void* scales,
+                                     float* rstd_out, void* y_out, uint32_t* status_word, void* stream) {
+  const FoldTables f{gate, gate_stride, weight, shift, scale, frame_stride, num_frames, frame_idx, status_word};
+  int st = residual_adaln_shape(m, k, o, f);
+  if (st != NVFP4ACT_OK) return st;
+  st = check_amax_out(m, amax_out);
+  if (st != NVFP4ACT_OK) return st;
+  return residual_adaln_call(h, o, bias, f, eps, m, k, 0.0f, amax_out, codes, scales, rstd_out, y_out, stream);
 }
 
 }  // extern "C"

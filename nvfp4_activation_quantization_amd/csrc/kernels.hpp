@@ -67,8 +67,10 @@ struct SwigluLaunch {
 
 hipError_t launch_swiglu(const SwigluLaunch& p, const DeviceInfo& dev, hipStream_t stream);
 
-// The arguments of one residual_rms_nvfp4 call (see include/nvfp4act.h).  o null: no branch
-// (h is only read); bias null: no bias.  amax_dev: as for RmsLaunch.
+// The arguments of one residual_rms_nvfp4 or residual_rms_adaln_nvfp4 call (see
+// include/nvfp4act.h).  o null: no branch (h is only read); bias null: no bias.  mod: the
+// adaLN form (gate rows multiply the branch; weight, shift, mod_scale and the frame index
+// replace gamma; scale unused); strides in elements.  amax_dev: as for RmsLaunch.
 constexpr int64_t kMaxResidualK = 8192;   // the row is held in registers
 
 struct ResidualLaunch {
@@ -85,6 +87,15 @@ struct ResidualLaunch {
   void* scales;
   float* rstd_out;
   void* y_out;
+  bool mod;
+  const void* gate;
+  int64_t gate_stride;
+  const void* weight;
+  const void* shift;
+  const void* mod_scale;
+  int64_t frame_stride, num_frames;
+  const int32_t* frame_idx;
+  uint32_t* status_word;
 };
 
 hipError_t launch_residual_rms(const ResidualLaunch& p, hipStream_t stream);
@@ -92,6 +103,7 @@ hipError_t launch_residual_rms(const ResidualLaunch& p, hipStream_t stream);
 // Per-device, once: allow the LDS sizes the kernels use.
 hipError_t prepare_rms_adaln();
 hipError_t prepare_swiglu();
+hipError_t prepare_residual_rms();
 
 // Build the SiLU table of the current device and wait for it; *ambiguous receives the
 // number of entries whose rounding fp64 could not decide (0 expected).

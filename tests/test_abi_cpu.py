@@ -153,6 +153,40 @@ def test_residual_rms_status_codes(dynamic):
         assert rr(amax=float("inf")) == 4 and rr(amax=-1.0) == 4
 
 
+def fold(dynamic=False, **kw):
+    a = dict(h=A, o=A, bias=A, gate=A, gate_stride=512, w=A, shift=A, scale=A, frame_stride=1024, frames=2, idx=A,
+             eps=1e-6, m=4, k=512, amax=1.0, amax_out=A, codes=A, scales=A, rstd=None, y=None, status=None)
+    a.update(kw)
+    f = ctypes.c_float(a["eps"])
+    head = (a["h"], a["o"], a["bias"], a["gate"], a["gate_stride"], a["w"], a["shift"], a["scale"],
+            a["frame_stride"], a["frames"], a["idx"], f, a["m"], a["k"])
+    tail = (a["codes"], a["scales"], a["rstd"], a["y"], a["status"], None)
+    if dynamic:
+        return lib.residual_rms_adaln_nvfp4_dynamic(*head, a["amax_out"], *tail)
+    return lib.residual_rms_adaln_nvfp4(*head, a["amax"], *tail)
+
+
+@pytest.mark.parametrize("dynamic", [False, True])
+def test_residual_rms_adaln_status_codes(dynamic):
+    for key in ("h", "w", "shift", "scale", "idx", "codes", "scales", "gate"):
+        assert fold(dynamic, **{key: None}) == 1, key
+    for kw in (dict(k=768), dict(k=8704), dict(m=-1), dict(frames=0), dict(frame_stride=256),
+               dict(gate_stride=256)):
+        assert fold(dynamic, **kw) == 2, kw
+    # the gate table is not needed without a branch
+    assert fold(dynamic, o=None, gate=None, gate_stride=0, m=0) == 0
+    for key in ("h", "o", "bias", "gate", "w", "shift", "scale", "codes", "scales", "y"):
+        assert fold(dynamic, **{key: U}) == 3, key
+    assert fold(dynamic, idx=A + 2) == 3 and fold(dynamic, status=A + 1) == 3 and fold(dynamic, rstd=A + 2) == 3
+    assert fold(dynamic, frame_stride=1028) == 3 and fold(dynamic, gate_stride=516) == 3
+    assert fold(dynamic, eps=-1.0) == 4
+    assert fold(dynamic, m=0) == 0
+    if dynamic:
+        assert fold(True, amax_out=None) == 1 and fold(True, amax_out=A + 2) == 3
+    else:
+        assert fold(amax=0.0) == 4
+
+
 def torch_has_gpu():
     import torch
     return torch.cuda.is_available()
@@ -165,6 +199,7 @@ def test_valid_call_without_a_gpu_reports_no_device():
     assert q() == 5 and rms() == 5 and sw() == 5
     assert swp() == 5 and swp(bias=None, il=1) == 5 and swp(True) == 5
     assert rr() == 5 and rr(bias=None) == 5 and rr(True) == 5
+    assert fold() == 5 and fold(o=None, gate=None) == 5 and fold(True) == 5
     assert lib.nvfp4act_init() == 5
 
 

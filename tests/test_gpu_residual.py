@@ -10,7 +10,8 @@ import pytest
 
 import oracle
 import workloads
-from util import first_mismatch, gather_scales, oracle_residual_rms, scales_from_rows, to_device, to_host
+from util import (first_mismatch, gather_scales, oracle_residual_adaln, oracle_residual_rms, scales_from_rows,
+                  to_device, to_host)
 
 pytestmark = pytest.mark.gpu
 
@@ -149,6 +150,90 @@ def test_dynamic(nq, m, k, form):
 
 
 # --------------------------------------------------------------------------------------
+# the gated residual folded into the next block's RMSNorm + adaLN
+# --------------------------------------------------------------------------------------
+
+def fold_case(m, k, seed, form="bias", frames=3):
+    h, o, bias, _, _ = case(m, k, seed, form)
+    g = np.random.Generator(np.random.PCG64(seed + 1))
+    gate = oracle.bf16_round((0.3 * g.standard_normal((frames, k))).astype(np.float32))
+    w = oracle.bf16_round((1 + 0.1 * g.standard_normal(k)).astype(np.float32))
+    table = oracle.bf16_round((0.1 * g.standard_normal((frames, 2, k))).astype(np.float32))
+    idx = g.integers(0, frames, m).astype(np.int32)
+    return h, o, bias, gate, w, table, idx
+
+
+def gpu_fold(nq, h, o, bias, gate, w, table, idx, eps, amax, y=True, dynamic=False):
+    m, k = h.shape
+    hd = dev_f32(h)
+    residual = None if o is None else (to_device(o), None if bias is None else to_device(bias), to_device(gate))
+    rstd = torch.empty(m, dtype=torch.float32, device="cuda:0")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda:0")
+    yd = torch.empty((m, k), dtype=torch.int16, device="cuda:0") if y else None
+    args = (hd, to_device(w), to_device(table), torch.from_numpy(idx).to("cuda:0"), eps)
+    if dynamic:
+        codes, scales, amax_t = nq.residual_rms_adaln_nvfp4_dynamic(*args, residual=residual, rstd_out=rstd,
+                                                                     y_out=yd, status_word=status)
+    else:
+        codes, scales = nq.residual_rms_adaln_nvfp4(*args, amax, residual=residual, rstd_out=rstd, y_out=yd,
+                                                    status_word=status)
+    torch.cuda.synchronize()
+    out = dict(codes=to_host(codes), scales=to_host(scales), y=to_host(yd) if y else None,
+               rstd=rstd.cpu().numpy(), h=hd.cpu().numpy(), status=int(status.cpu().numpy()[0]))
+    if dynamic:
+        out["amax"] = float(amax_t.cpu().numpy()[0])
+    return out
+
+
+def check_fold(got, want, m, k):
+    assert_equal(u32(got["h"]), u32(want["h"]), "h")
+    assert_equal(u32(got["rstd"]), u32(want["rstd"]), "rstd")
+    if got["y"] is not None:
+        assert_equal(got["y"], want["y"], "y_out")
+    assert_equal(got["codes"], want["codes"], "codes")
+    assert got["status"] == want["status"]
+
+
+@pytest.mark.parametrize("form", ["bias", "nobias", "none"])
+@pytest.mark.parametrize("m,k", [(1, 512), (127, 1024), (129, 2048), (64, 3584), (300, 7168), (257, 8192)])
+def test_fold_shapes(nq, m, k, form):
+    print("residual_rms_adaln", m, k, form, flush=True)
+    h, o, bias, gate, w, table, idx = fold_case(m, k, 17 * m + k + len(form), form)
+    for amax in [12.0, 2688.0]:
+        got = gpu_fold(nq, h, o, bias, gate, w, table, idx, 1e-6, amax)
+        want = oracle_residual_adaln(h, o, bias, gate, w, table, idx, 1e-6, amax)
+        check_fold(got, want, m, k)
+        assert_equal(got["scales"], scales_from_rows(want["scale_bytes"], m, k), "scales")
+
+
+def test_fold_out_of_range_frames(nq):
+    m, k = 300, 2048
+    h, o, bias, gate, w, table, idx = fold_case(m, k, 5)
+    idx[[0, 33, 64, 299]] = [3, -1, 1 << 30, -(1 << 31)]
+    got = gpu_fold(nq, h, o, bias, gate, w, table, idx, 1e-6, 10.0)
+    want = oracle_residual_adaln(h, o, bias, gate, w, table, idx, 1e-6, 10.0)
+    assert want["status"] == 1
+    check_fold(got, want, m, k)
+    assert_equal(got["scales"], scales_from_rows(want["scale_bytes"], m, k), "scales")
+    for r in (0, 33, 64, 299):
+        assert_equal(u32(got["h"][r]), u32(h[r]), "h row %d kept" % r)
+
+
+@pytest.mark.parametrize("form", ["bias", "none"])
+@pytest.mark.parametrize("m,k", [(1, 512), (129, 2048), (300, 7168)])
+def test_fold_dynamic(nq, m, k, form):
+    print("residual_rms_adaln_dynamic", m, k, form, flush=True)
+    h, o, bias, gate, w, table, idx = fold_case(m, k, 3 * m + k, form)
+    idx[m // 2] = 7                                         # one row out of range: y = 0
+    got = gpu_fold(nq, h, o, bias, gate, w, table, idx, 1e-6, None, dynamic=True)
+    want = oracle.residual_rms_adaln_dynamic(h, o, bias, gate, w, table, idx, 1e-6, want_y=True,
+                                             scales_rows=oracle.padded_rows(m))
+    assert u32(got["amax"]) == u32(want["amax"])
+    check_fold(got, want, m, k)
+    assert_equal(got["scales"], want["scales"], "scales")
+
+
+# --------------------------------------------------------------------------------------
 # full size, the launch configuration the benchmark times
 # --------------------------------------------------------------------------------------
 
@@ -161,3 +246,16 @@ def test_full_residual_rms_63240x7168(nq):
     got = gpu_residual(nq, h, o, bias, scale, gamma, wl.eps, amax, y=False)
     print("oracle", flush=True)
     check(got, h, o, bias, scale, gamma, wl.eps, amax)
+
+
+def test_full_residual_adaln_63240x7168(nq):
+    wl = workloads.get("residual_adaln_63240x7168")
+    amax = workloads.calibration_amax(wl.name)
+    print("generating", wl.name, flush=True)
+    h, o = wl.h(), wl.o()
+    args = (wl.bias(), wl.gate_table(), wl.weight(), wl.table(), wl.frame_idx())
+    got = gpu_fold(nq, h, o, *args, wl.eps, amax, y=False)
+    print("oracle", flush=True)
+    want = oracle_residual_adaln(h, o, *args, wl.eps, amax, want_y=False)
+    check_fold(got, want, wl.m, wl.k)
+    assert_equal(got["scales"], scales_from_rows(want["scale_bytes"], wl.m, wl.k), "scales")

@@ -110,6 +110,23 @@ def oracle_residual_rms(h, o, bias, scale, gamma, eps, amax, want_y=True, gsf=No
     return out
 
 
+def oracle_residual_adaln(h, o, bias, gate, w, table, idx, eps, amax, want_y=True, gsf=None):
+    """oracle.residual_rms_adaln_rows over row blocks in parallel threads."""
+    n = h.shape[0]
+
+    def part(se):
+        s, e = se
+        return oracle.residual_rms_adaln_rows(h[s:e], None if o is None else o[s:e], bias, gate, w, table,
+                                              idx[s:e], eps, amax, want_y=want_y, gsf=gsf)
+
+    with ThreadPoolExecutor(threads()) as ex:
+        res = list(ex.map(part, split_rows(n, 4 * threads())))
+    out = {key: np.concatenate([r[key] for r in res]) for key in ("codes", "scale_bytes", "rstd", "h")}
+    out["y"] = np.concatenate([r["y"] for r in res]) if want_y else None
+    out["status"] = int(np.bitwise_or.reduce([r["status"] for r in res]))
+    return out
+
+
 def scales_from_rows(scale_bytes: np.ndarray, m: int, k: int, rows=None) -> np.ndarray:
     """Place plain-order scale bytes of rows into a zeroed swizzled [pad(m), k/16] buffer."""
     buf = np.zeros(oracle.padded_rows(m) * (k // 16), np.uint8)
