@@ -85,6 +85,11 @@ def _load():
             "orc_rms_adaln_rows": (None, [P, I64, I64, P, P, P, P, I64, I64, P, F, F,
                                           P, P, P, P, P, P]),
             "orc_silu_table": (ctypes.c_int, [P]),
+            "orc_silu_table_f16": (ctypes.c_int, [P]),
+            "orc_f16_round": (None, [P, P, I64]),
+            "orc_rms_rstd_f16row": (F, [P, I64, F]),
+            "orc_rms_sum_f16row": (F, [P, I64]),
+            "orc_rms_silu_rows_gsf": (None, [P, P, F, I64, I64, P, F, P, P, P, P]),
             "orc_swiglu_rows": (None, [P, P, I64, I64, I64, P, P, F, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
@@ -455,6 +460,139 @@ def swiglu_packed_dynamic(proj_u16, bias_u16, interleaved: bool, want_y: bool = 
     out = swiglu_packed_rows(proj_u16, bias_u16, interleaved, 0.0, want_y=want_y, scales_rows=scales_rows,
                              gsf=dynamic_global_scale(amax))
     out["amax"] = amax
+    return out
+
+
+# --------------------------------------------------------------------------
+# fp16: codec, SiLU table, channels-last RMSNorm + SiLU -> NVFP4
+# --------------------------------------------------------------------------
+
+def f16_round(f32) -> np.ndarray:
+    """fp32 -> fp16 bit patterns, round to nearest even (NaN -> 0x7E00)."""
+    a = _c(f32, np.float32)
+    out = np.empty(a.shape, np.uint16)
+    _load().orc_f16_round(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def f16_to_f32(u16) -> np.ndarray:
+    return np.asarray(u16, np.uint16).view(np.float16).astype(np.float32)
+
+
+_silu16_cache = None
+
+
+def silu_table_f16() -> np.ndarray:
+    """The 65536-entry fp16 SiLU table (C, long double, single rounding)."""
+    global _silu16_cache
+    if _silu16_cache is None:
+        t = np.empty(65536, np.uint16)
+        amb = _load().orc_silu_table_f16(_ptr(t))
+        if amb:
+            raise RuntimeError("oracle fp16 SiLU table: %d entries undecidable in long double" % amb)
+        _silu16_cache = t
+    return _silu16_cache
+
+
+def rms_sum_f16row(x_row_u16) -> float:
+    """The fixed-tree sum of x^2 over one fp16 row (c % 16 == 0, c <= 512)."""
+    x = _c(x_row_u16, np.uint16).reshape(-1)
+    return _load().orc_rms_sum_f16row(_ptr(x), x.size)
+
+
+def rms_rstd_f16row(x_row_u16, eps: float) -> float:
+    x = _c(x_row_u16, np.uint16).reshape(-1)
+    return _load().orc_rms_rstd_f16row(_ptr(x), x.size, float(eps))
+
+
+def rms_silu_rows(x_u16, gamma_u16, eps: float, global_amax: float, want_y: bool = False,
+                  gsf: float | None = None):
+    """Channels-last RMSNorm (fp32 statistic, fp16 affine) + SiLU -> NVFP4 over rows.
+
+    x_u16 [n, c] fp16 patterns (c % 16 == 0, c <= 512); gamma_u16 [c] fp16.
+    Returns dict(codes [n, c/2], scale_bytes [n, c/16] (the plain scale layout of this
+    producer), rstd [n], y [n, c] fp16 or None).
+    """
+    x = _c(x_u16, np.uint16)
+    n, c = x.shape
+    if c % 16 or c > 512:
+        raise ValueError("c must be a multiple of 16, at most 512")
+    gamma = _c(gamma_u16, np.uint16).reshape(-1)
+    codes = np.empty((n, c // 2), np.uint8)
+    sb = np.empty((n, c // 16), np.uint8)
+    rstd = np.empty(n, np.float32)
+    y = np.empty((n, c), np.uint16) if want_y else None
+    g = float(global_scale(global_amax) if gsf is None else gsf)
+    _load().orc_rms_silu_rows_gsf(_ptr(x), _ptr(gamma), float(eps), n, c, _ptr(silu_table_f16()), g, _ptr(codes),
+                                  _ptr(sb), _ptr(rstd), _ptr(y))
+    return dict(codes=codes, scale_bytes=sb, rstd=rstd, y=y)
+
+
+def max_abs_f16(u16) -> float:
+    """max |x| over fp16 patterns (no NaN), as fp32 (exact)."""
+    return float(np.abs(f16_to_f32(u16)).max()) if np.asarray(u16).size else 0.0
+
+
+def rms_silu_dynamic(x_u16, gamma_u16, eps: float, want_y: bool = False):
+    """rms_silu_rows under the amax of the call's own y.  Adds 'amax'."""
+    first = rms_silu_rows(x_u16, gamma_u16, eps, 1.0, want_y=True)
+    amax = max_abs_f16(first["y"])
+    out = rms_silu_rows(x_u16, gamma_u16, eps, 0.0, want_y=want_y, gsf=dynamic_global_scale(amax))
+    out["amax"] = amax
+    return out
+
+
+def _round_fraction_to_f16(q: Fraction) -> int:
+    """Exact rational -> nearest fp16 bit pattern, ties to even."""
+    sign = 0x8000 if q < 0 else 0
+    a = -q if q < 0 else q
+    if a == 0:
+        return sign
+    if a >= 65520:
+        return sign | 0x7C00
+    E = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** E > a:
+        E -= 1
+    elif Fraction(2) ** (E + 1) <= a:
+        E += 1
+    qexp = -24 if E < -14 else E - 10
+    n = a / (Fraction(2) ** qexp)
+    fl = n.numerator // n.denominator
+    frac = n - fl
+    if abs(frac - Fraction(1, 2)) < Fraction(1, 10 ** 45):
+        raise ArithmeticError("SiLU value too close to an fp16 midpoint for 60-digit evaluation")
+    if frac > Fraction(1, 2) or (frac == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    value = float(Fraction(fl) * Fraction(2) ** qexp)   # exact: <= 11 significant bits
+    return sign | int(np.array([value], np.float16).view(np.uint16)[0])
+
+
+def silu_exact_f16() -> np.ndarray:
+    """fp16 SiLU table from Python's decimal module (60 digits), independent of the C
+    table.  g <= -25 gives |g| e^g < 2^-25 (half the smallest fp16 subnormal): -0;
+    g >= 20 differs from g by a relative e^-20, below half an fp16 ulp: g."""
+    import decimal
+    ctx = decimal.Context(prec=60)
+    out = np.empty(65536, np.uint16)
+    vals = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+    for g in range(65536):
+        e = (g >> 10) & 0x1F
+        if e == 0x1F:
+            out[g] = 0x7E00 if (g & 0x3FF) else (0x8000 if g & 0x8000 else 0x7C00)
+            continue
+        x = float(vals[g])
+        if x <= -25.0:
+            out[g] = 0x8000
+            continue
+        if x >= 20.0:
+            out[g] = g
+            continue
+        if x == 0.0:
+            out[g] = g
+            continue
+        dx = decimal.Decimal(x)
+        s = ctx.divide(dx, ctx.add(decimal.Decimal(1), ctx.exp(ctx.minus(dx))))
+        out[g] = _round_fraction_to_f16(Fraction(s))
     return out
 
 

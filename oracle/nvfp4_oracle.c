@@ -26,6 +26,10 @@
  *   [INT64]   FastVideo commit log, branch vae-parallel-decode: the int64
  *             indexing fix at 2^31 elements and the frame-index bounds
  *             contract of the modulation wrappers.
+ *   [FlashRT] FlashRT PR #142 (MiniMax-Remover): fp16_quant_nvfp4_ndhwc, the
+ *             fused RMS_norm + SiLU + NVFP4 quantize of channels-last VAE
+ *             activations, per-16-channel UE4M3 scales; the RMSNorm+RoPE
+ *             kernel's fp32 statistics with an fp16 affine.
  *   [H3-API residual_norm_quantize]  the fp32 residual stream: in-place
  *             h += bf16(o + bias) * scale, then NVFP4 of bf16(rms_norm(h,
  *             gamma, eps)) with fp32 gamma; hidden size a multiple of 512.
@@ -93,6 +97,51 @@ static float bf16_to_f32(uint16_t h) { return f32_from_bits((uint32_t)h << 16); 
 
 /* fp32 -> bf16 -> fp32: the value after one kept bf16 rounding */
 static float rb(float f) { return bf16_to_f32(bf16_round(f)); }
+
+/* ------------------------------------------------------------------------- */
+/* fp16 (IEEE binary16: 5 exponent bits, bias 15, 10 mantissa bits)          */
+/* ------------------------------------------------------------------------- */
+
+/* Exact value of an fp16 pattern as fp32 (every fp16 value is an fp32 value). */
+static float f16_to_f32(uint16_t h) {
+    uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+    if (e == 0x1Fu) return f32_from_bits(sign | 0x7F800000u | (m << 13));   /* inf, NaN */
+    double v = (e == 0) ? ldexp((double)m, -24) : ldexp(1.0 + (double)m / 1024.0, (int)e - 15);
+    float f = (float)v;                       /* exact */
+    return (sign ? -f : f);
+}
+
+/* The fp16 value nearest to f, ties to the even pattern; magnitudes from the
+   midpoint 65520 up round to infinity; subnormals kept (quantum 2^-24);
+   NaN -> 0x7E00.  Works on the exact fp32 value in double precision. */
+static uint16_t f16_round(float f) {
+    if (isnan(f)) return 0x7E00u;
+    uint16_t sign = signbit(f) ? 0x8000u : 0;
+    double a = fabs((double)f);
+    if (a == 0.0) return sign;
+    if (a >= 65520.0) return (uint16_t)(sign | 0x7C00u);
+    int e2;
+    frexp(a, &e2);                            /* a = fr * 2^e2, fr in [0.5, 1) */
+    int E = e2 - 1;                           /* 2^E <= a < 2^(E+1) */
+    int qexp = (E < -14) ? -24 : E - 10;      /* fp16 quantum exponent */
+    double n = ldexp(a, -qexp);               /* exact */
+    double fl = floor(n), frac = n - fl;
+    if (frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) == 1.0)) fl += 1.0;
+    if (fl == 0.0) return sign;               /* below half the smallest subnormal */
+    double v = ldexp(fl, qexp);               /* the rounded magnitude (< 65520: finite) */
+    /* encode */
+    int ev;
+    frexp(v, &ev);
+    int Ev = ev - 1;
+    uint16_t bits;
+    if (Ev < -14) bits = (uint16_t)ldexp(v, 24);                       /* subnormal (or 2^-14) */
+    else bits = (uint16_t)(((Ev + 15) << 10) | ((uint32_t)(ldexp(v, -Ev) * 1024.0) - 1024u));
+    return (uint16_t)(sign | bits);
+}
+
+/* fp32 -> fp16 -> fp32: the value after one kept fp16 rounding */
+static float rh(float f) { return f16_to_f32(f16_round(f)); }
 
 /* ------------------------------------------------------------------------- */
 /* E4M3 (OCP FN: bias 7, 3 mantissa bits, max finite 448 = code 0x7E)       */
@@ -614,6 +663,92 @@ EXPORT void orc_residual_rms_adaln_rows_gsf(float* h, const uint16_t* o, const u
 }
 
 /* ------------------------------------------------------------------------- */
+/* channels-last RMSNorm + SiLU -> NVFP4 (fp16)                              */
+/* ------------------------------------------------------------------------- */
+
+/* RMS statistic of one channels-last row of c fp16 values (c % 16 == 0,
+   c <= 512), the fixed tree of rms_rstd with one 8-element chunk per lane
+   over S slots, S = the smallest power of two >= c/8: slot L < c/8 holds the
+   lane value ((q0+q1)+(q2+q3))+((q4+q5)+(q6+q7)) of chunk L (q_e = x_e^2,
+   exact in fp32), the other slots hold +0, and a butterfly over the S slots
+   at distances 1, 2, ..., S/2 combines them into the sum (rms_sum_f16row);
+   rstd = 1 / sqrt(sum / c + eps). */
+static float rms_sum_f16row(const uint16_t* x, int64_t c) {
+    float slot[64];
+    int chunks = (int)(c / 8), S = 1;
+    while (S < chunks) S *= 2;
+    for (int L = 0; L < S; ++L) {
+        if (L >= chunks) { slot[L] = 0.0f; continue; }
+        float q[8];
+        for (int e = 0; e < 8; ++e) {
+            float v = f16_to_f32(x[8 * L + e]);
+            q[e] = v * v;
+        }
+        slot[L] = ((q[0] + q[1]) + (q[2] + q[3])) + ((q[4] + q[5]) + (q[6] + q[7]));
+    }
+    for (int d = 1; d < S; d *= 2) {
+        float next[64];
+        for (int L = 0; L < S; ++L) next[L] = slot[L] + slot[L ^ d];
+        memcpy(slot, next, sizeof(float) * (size_t)S);
+    }
+    return slot[0];
+}
+
+static float rms_rstd_f16row(const uint16_t* x, int64_t c, float eps) {
+    return 1.0f / sqrtf(rms_sum_f16row(x, c) / (float)c + eps);
+}
+
+EXPORT float orc_rms_sum_f16row(const uint16_t* x, int64_t c) {
+    unsigned int s = enter_ieee();
+    float r = rms_sum_f16row(x, c);
+    leave_ieee(s);
+    return r;
+}
+
+EXPORT float orc_rms_rstd_f16row(const uint16_t* x, int64_t c, float eps) {
+    unsigned int s = enter_ieee();
+    float r = rms_rstd_f16row(x, c, eps);
+    leave_ieee(s);
+    return r;
+}
+
+/* RMSNorm (fp32 statistic, fp16 affine) + SiLU -> NVFP4 over channels-last
+   rows ([FlashRT] fp16_quant_nvfp4_ndhwc, the fused RMS_norm + SiLU + NVFP4
+   variant; the RMSNorm+RoPE kernel's "fp32 stats + fp16 affine").  Row i of
+   x [n, c] fp16 (one voxel's channels):
+     rstd = rms_rstd_f16row(row)
+     nn   = fp16(x * rstd)
+     a    = fp16(nn * gamma)               gamma: [c] fp16
+     y    = S16[a]                         S16: the fp16 SiLU table
+   then the block quantizer over the c channels.  Scale bytes are written in
+   plain row order, [n, c/16] (channels-last operand, no GEMM swizzle).
+   rstd_out [n], y_out [n, c] fp16, scale_bytes: nullable. */
+EXPORT void orc_rms_silu_rows_gsf(const uint16_t* x, const uint16_t* gamma, float eps, int64_t n,
+                                  int64_t c, const uint16_t* table, float gsf, uint8_t* codes,
+                                  uint8_t* scale_bytes, float* rstd_out, uint16_t* y_out) {
+    unsigned int s = enter_ieee();
+    float* y = (float*)malloc(sizeof(float) * (size_t)c);
+    uint8_t* sb = (uint8_t*)malloc((size_t)(c / 16));
+    for (int64_t i = 0; i < n; ++i) {
+        const uint16_t* xr = x + i * c;
+        float rstd = rms_rstd_f16row(xr, c, eps);
+        if (rstd_out) rstd_out[i] = rstd;
+        for (int64_t d = 0; d < c; ++d) {
+            float nn = rh(f16_to_f32(xr[d]) * rstd);
+            uint16_t a = f16_round(nn * f16_to_f32(gamma[d]));
+            y[d] = f16_to_f32(table[a]);
+        }
+        quantize_row(y, c, gsf, codes + i * (c / 2), sb);
+        if (scale_bytes) memcpy(scale_bytes + i * (c / 16), sb, (size_t)(c / 16));
+        if (y_out)
+            for (int64_t d = 0; d < c; ++d) y_out[i * c + d] = f16_round(y[d]);
+    }
+    free(sb);
+    free(y);
+    leave_ieee(s);
+}
+
+/* ------------------------------------------------------------------------- */
 /* SiLU table and the SwiGLU producer                                        */
 /* ------------------------------------------------------------------------- */
 
@@ -677,6 +812,68 @@ EXPORT int orc_silu_table(uint16_t* table) {
     }
     leave_ieee(s);
     return ambiguous;
+}
+
+/* Round the real hi + lo to the nearest fp16, ties to even (as ld_to_bf16,
+   with fp16's quantum: 2^(E-10) for 2^E <= |v| < 2^(E+1), E >= -14, and the
+   subnormal quantum 2^-24; from 65520 up: infinity). */
+static uint16_t ld_to_f16(long double hi, long double lo, int* ambiguous) {
+    uint16_t sign = signbit(hi) ? 0x8000u : 0;
+    long double a = fabsl(hi);
+    if (a == 0.0L) return sign;
+    if (a >= 65520.0L) return (uint16_t)(sign | 0x7C00u);   /* no value sits near 65520 */
+    int e2;
+    frexpl(a, &e2);
+    int E = e2 - 1;
+    int qexp = (E < -14) ? -24 : E - 10;
+    long double n = ldexpl(a, -qexp);
+    long double fl = floorl(n);
+    long double frac = n - fl;
+    int up;
+    if (frac == 0.5L && lo != 0.0L) {
+        up = (signbit(lo) == signbit(hi));
+    } else {
+        if (fabsl(frac - 0.5L) < 0x1p-40L) (*ambiguous)++;
+        up = frac > 0.5L || (frac == 0.5L && fmodl(fl, 2.0L) == 1.0L);
+    }
+    long double r = up ? fl + 1.0L : fl;
+    return (uint16_t)(sign | f16_round((float)ldexpl(r, qexp)));   /* exact: <= 11 bits */
+}
+
+/* S16[g] = fp16(g * sigmoid(g)) for every fp16 pattern g, as orc_silu_table
+   does for bf16 (long double, one rounding; |g| < 2^-30 through the tanh
+   form).  -inf -> -0, +inf -> +inf, NaN -> 0x7E00.  Returns the number of
+   entries too close to a midpoint to decide (expected 0). */
+EXPORT int orc_silu_table_f16(uint16_t* table) {
+    unsigned int s = enter_ieee();
+    int ambiguous = 0;
+    for (uint32_t g = 0; g < 65536u; ++g) {
+        uint32_t exp_field = (g >> 10) & 0x1Fu;
+        uint32_t mant = g & 0x3FFu;
+        if (exp_field == 0x1Fu) {
+            if (mant != 0) table[g] = 0x7E00u;
+            else table[g] = (g & 0x8000u) ? 0x8000u : 0x7C00u;
+            continue;
+        }
+        long double x = (long double)f16_to_f32((uint16_t)g);
+        long double hi, lo;
+        if (fabsl(x) < 0x1p-30L) {
+            hi = x / 2.0L;
+            lo = hi * tanhl(hi);
+        } else {
+            hi = x / (1.0L + expl(-x));
+            lo = 0.0L;
+        }
+        table[g] = ld_to_f16(hi, lo, &ambiguous);
+    }
+    leave_ieee(s);
+    return ambiguous;
+}
+
+EXPORT void orc_f16_round(const float* in, uint16_t* out, int64_t n) {
+    unsigned int s = enter_ieee();
+    for (int64_t i = 0; i < n; ++i) out[i] = f16_round(in[i]);
+    leave_ieee(s);
 }
 
 /* SwiGLU -> NVFP4 over rows ([H3-API] swiglu_quantize; [TRT] SiLU-and-mul

@@ -17,6 +17,7 @@ TensorRT-LLM fusions apply only to static NVFP4 scales).  For each workload:
                          8,192 calibration rows of h and o
   residual_adaln_63240x7168  the same for the gated residual + RMSNorm + adaLN, frame
                          (r * 31) // 8192
+  rms_silu_16x120x216x192  max |y| of the oracle over 32,768 calibration voxel rows
 
 Run:  python tests/golden/make_calibration.py
 """
@@ -49,6 +50,10 @@ def calibrate(w: workloads.Workload) -> dict:
     elif w.kind == "quantize":
         amax = amax_of_bf16(w.calibration_x())
         how = "max|x| over %d calibration rows" % w.cal_rows
+    elif w.kind == "rms_silu":
+        res = oracle.rms_silu_rows(w.calibration_x(), w.weight(), w.eps, 1.0, want_y=True)
+        amax = oracle.max_abs_f16(res["y"])
+        how = "max|y| of the oracle over %d calibration rows" % w.cal_rows
     elif w.kind == "residual_adaln":
         res = oracle.residual_rms_adaln_rows(w.calibration_h(), w.calibration_o(), w.bias(), w.gate_table(),
                                              w.weight(), w.table(), w.calibration_frame_idx(), w.eps, 1.0,

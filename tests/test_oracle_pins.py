@@ -558,6 +558,135 @@ def test_gated_residual_out_of_range_frame_leaves_the_row():
 
 
 # --------------------------------------------------------------------------
+# fp16 codec, fp16 SiLU table, channels-last RMSNorm + SiLU -> NVFP4
+# --------------------------------------------------------------------------
+
+def _f16_chunk(start, step):
+    u = np.arange(step, dtype=np.uint32) + np.uint32(start)
+    f = u.view(np.float32)
+    ours = oracle.f16_round(f)
+    ref = torch.from_numpy(f).to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    diff = np.nonzero(ours != ref)[0]
+    nan_count = int(np.count_nonzero(((u & 0x7F800000) == 0x7F800000) & ((u & 0x7FFFFF) != 0)))
+    return (bool(np.all(np.isnan(f[diff]))) and bool(np.all(ours[diff] == 0x7E00)),
+            len(diff) <= nan_count, start)
+
+
+def test_f16_round_all_fp32_inputs_match_torch():
+    from concurrent.futures import ThreadPoolExecutor
+    step = 1 << 26
+    with ThreadPoolExecutor(8) as ex:
+        for only_nan, count_ok, start in ex.map(lambda s: _f16_chunk(s, step), range(0, 1 << 32, step)):
+            assert only_nan and count_ok, hex(start)
+
+
+def test_f16_decode_is_numpy_float16():
+    u = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((u >> 10) & 0x1F) != 0x1F
+    # every finite pattern decodes and re-encodes to itself
+    assert np.array_equal(oracle.f16_round(oracle.f16_to_f32(u[finite])), u[finite])
+
+
+def test_silu_table_f16_equals_exact_decimal_derivation():
+    assert np.array_equal(oracle.silu_table_f16(), oracle.silu_exact_f16())
+
+
+def test_silu_table_f16_special_values():
+    t = oracle.silu_table_f16()
+    assert t[0x0000] == 0x0000 and t[0x8000] == 0x8000 and t[0x7C00] == 0x7C00 and t[0xFC00] == 0x8000
+    # silu(1) = 0.7310585..: fp16 0x39D9 = 0.73095703125 (next 0x39DA = 0.7314453125);
+    # silu(-20) = -4.12e-8 rounds to the smallest subnormal -2^-24 (0x8001), silu(-25) to -0
+    assert t[0x3C00] == 0x39D9
+    assert t[0xCD00] == 0x8001 and t[0xCE40] == 0x8000
+
+
+def _rms_silu_case(seed, n=6, c=192):
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = oracle.f16_round((g.standard_normal((n, c)) * 2).astype(np.float32))
+    gamma = oracle.f16_round((1 + 0.3 * g.standard_normal(c)).astype(np.float32))
+    return x, gamma
+
+
+def test_rms_f16row_statistic():
+    for c in (96, 192, 384):
+        for v in (1.0, 0.5, 3.0):
+            x = oracle.f16_round(np.full(c, v, np.float32))
+            assert oracle.rms_rstd_f16row(x, 1e-6) == np.float32(1.0) / np.sqrt(np.float32(v * v) + np.float32(1e-6))
+        g = np.random.Generator(np.random.PCG64(c))
+        x = oracle.f16_round((g.standard_normal(c) * 3).astype(np.float32))
+        xf = oracle.f16_to_f32(x).astype(np.float64)
+        ref = 1.0 / np.sqrt(np.mean(xf * xf) + 1e-6)
+        assert abs(oracle.rms_rstd_f16row(x, 1e-6) / ref - 1) < 1e-6
+
+
+def test_rms_f16row_tree_over_padded_slots():
+    """c = 96: 12 chunks in 16 slots.  Chunk 0 holds 4096 (4096^2 = 2^24) and two other
+    chunks 1.0 each: 2^24 + 1 rounds back to 2^24 in fp32, 1 + 1 = 2 and 2^24 + 2 are exact,
+    so the pairing of the butterfly shows in the sum (as in the bf16 row statistic)."""
+    c = 96
+
+    def total(ones, first=0):
+        x = np.zeros(c, np.float32)
+        x[0] = 4096.0
+        for ch in ones:
+            x[8 * ch + first] = 1.0
+        return oracle.rms_sum_f16row(oracle.f16_round(x))
+
+    big, big2 = np.float32(2.0 ** 24), np.float32(2.0 ** 24 + 2)
+    assert total([1, 3]) == big and total([2, 3]) == big2
+    # chunks 8 and 9 meet chunk 0 only at distance 8, after pairing with each other
+    assert total([8, 9]) == big2
+    # within a chunk: elements 2 and 3 pair before meeting element 0 ((q0+q1)+(q2+q3))
+    x = np.zeros(c, np.float32)
+    x[0], x[2], x[3] = 4096.0, 1.0, 1.0
+    assert oracle.rms_sum_f16row(oracle.f16_round(x)) == big2
+    x[3], x[1] = 0.0, 1.0
+    assert oracle.rms_sum_f16row(oracle.f16_round(x)) == big     # (2^24 + 1) + 1, both lost
+    # the padding slots add +0: the c = 96 row equals the same chunks in a c = 128 row
+    g = np.random.Generator(np.random.PCG64(5))
+    v = oracle.f16_round(g.standard_normal(96).astype(np.float32) * 5)
+    assert oracle.rms_sum_f16row(v) == oracle.rms_sum_f16row(np.concatenate([v, np.zeros(32, np.uint16)]))
+
+
+def test_rms_silu_chain_matches_torch_eager_ops():
+    x, gamma = _rms_silu_case(61)
+    res = oracle.rms_silu_rows(x, gamma, 1e-6, 4.0, want_y=True)
+    H = torch.float16
+    xt = torch.from_numpy(x.view(np.int16).copy()).view(H)
+    gt = torch.from_numpy(gamma.view(np.int16).copy()).view(H)
+    rstd = torch.from_numpy(res["rstd"])[:, None]
+    nn = (xt.float() * rstd).to(H)
+    a = nn * gt                                       # fp16 tensor multiply
+    a16 = a.view(torch.int16).numpy().view(np.uint16)
+    want = oracle.silu_table_f16()[a16]
+    assert np.array_equal(res["y"], want)
+    # the table entries used are the correctly rounded silu of a (torch's own silu in fp64)
+    ref = torch.nn.functional.silu(a.double()).to(H).view(torch.int16).numpy().view(np.uint16)
+    assert np.mean(ref == want) > 0.999
+
+
+def test_rms_silu_hand_worked_block():
+    """x = 2 in every channel, eps = 0: sum = 4c exactly, rstd = 1/2, nn = 1, a = gamma, and
+    y = silu(gamma).  gamma's first block holds 96, 80, ..., 12 (silu rounds each back to
+    itself in fp16) and four zeros; global_amax = 43008 gives gsf = 1/16, block amax 96 ->
+    scale 96/6/16 = 1.0 (0x38), inverse 1/16: v = 6, 5, 4, 3.5, 3, 2.5, 2, 1.75, 1.5, 1.25,
+    1, 0.75 -> codes 7, 6, 6, 6, 5, 4, 4, 4, 3, 2, 2, 2 (ties to even), then 0, 0, 0, 0."""
+    c = 192
+    vals = [96, 80, 64, 56, 48, 40, 32, 28, 24, 20, 16, 12, 0, 0, 0, 0]
+    gamma = np.full(c, 16.0, np.float32)
+    gamma[:16] = vals
+    x = oracle.f16_round(np.full((1, c), 2.0, np.float32))
+    res = oracle.rms_silu_rows(x, oracle.f16_round(gamma), 0.0, 43008.0, want_y=True)
+    assert res["rstd"][0] == 0.5
+    assert np.array_equal(oracle.f16_to_f32(res["y"][0, :16]), np.array(vals, np.float32))
+    nib = [7, 6, 6, 6, 5, 4, 4, 4, 3, 2, 2, 2, 0, 0, 0, 0]
+    want = bytes(nib[2 * i] | (nib[2 * i + 1] << 4) for i in range(8))
+    assert res["codes"][0, :8].tobytes() == want and res["scale_bytes"][0, 0] == 0x38
+    # the other blocks: all 16 -> amax 16, scale 16/6/16 = 1/6 -> 0x23 (0.171875), v = 5.818 -> 7
+    assert np.all(res["scale_bytes"][0, 1:] == 0x23) and np.all(res["codes"][0, 8:] == 0x77)
+
+
+# --------------------------------------------------------------------------
 # SiLU table and the SwiGLU producer
 # --------------------------------------------------------------------------
 
@@ -798,6 +927,15 @@ def test_dynamic_gated_residual_adaln_is_static_at_its_own_amax():
                                          scales_rows=128)
     assert dyn["amax"] == float(np.abs(oracle.bf16_to_f32(ref["y"])).max())
     for key in ("codes", "scales", "y", "h", "rstd"):
+        assert np.array_equal(dyn[key], ref[key]), key
+
+
+def test_dynamic_rms_silu_is_static_at_its_own_amax():
+    x, gamma = _rms_silu_case(62, n=9)
+    dyn = oracle.rms_silu_dynamic(x, gamma, 1e-6, want_y=True)
+    ref = oracle.rms_silu_rows(x, gamma, 1e-6, dyn["amax"], want_y=True)
+    assert dyn["amax"] == float(np.abs(oracle.f16_to_f32(ref["y"])).max())
+    for key in ("codes", "scale_bytes", "y", "rstd"):
         assert np.array_equal(dyn[key], ref[key]), key
 
 

@@ -84,3 +84,13 @@ def test_residual_rms_workload():
     o = w.calibration_o()
     assert o.dtype == np.uint16 and o.shape == (w.cal_rows, w.k)
     del rows
+
+
+def test_rms_silu_workload():
+    w = workloads.get("rms_silu_16x120x216x192")
+    assert w.m == 414720 and w.k == 192 and w.padded_rows == w.m
+    assert w.algorithmic_bytes() == w.m * w.k * 2 + w.m * w.k // 2 + w.m * w.k // 16
+    x = w.x_rows(np.array([0, 4096, w.m - 1]))
+    xf = oracle.f16_to_f32(x)
+    assert x.dtype == np.uint16 and np.all(np.isfinite(xf)) and 0.5 < float(np.std(xf)) < 1.5
+    assert np.array_equal(oracle.f16_round(xf), x)                 # fp16 patterns

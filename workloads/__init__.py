@@ -27,9 +27,12 @@ a 34x60 latent grid per frame over 31 frames = 63,240 tokens from
                            table (31 x 7168, std 0.2) of the folding block, then RMSNorm
                            (bf16 weight) + adaLN with the next block's (shift, scale) table
                            (31 frames, frame = token // 2040, as rms_adaln_63240x7168)
+  rms_silu_16x120x216x192  fp16 channels-last VAE activations: 16 frames of 120 x 216
+                           voxels (half the 432 x 240 clip in each direction), 192
+                           channels; x ~ N(0,1), gamma = 1 + 0.1 N(0,1), eps = 1e-6
 
 Seeds: numpy ``PCG64``; the seed of role ``role`` in workload number ``i``
-(1..9 in the order above) is ``1000*i + role`` with roles 1 x (or h), 2 weight
+(1..10 in the order above) is ``1000*i + role`` with roles 1 x (or h), 2 weight
 (or bias), 3 modulation table (or residual scale), 4 calibration rows, 5
 outlier pick, 6 per-head std, 8 the residual branch o, 9 its calibration rows,
 10 the fp32 RMSNorm weight, 11 the gate table, 12 the bias where a weight is
@@ -51,6 +54,13 @@ ROLE_X, ROLE_W, ROLE_TABLE, ROLE_CAL, ROLE_OUTLIER, ROLE_HEADSTD = 1, 2, 3, 4, 5
 ROLE_O, ROLE_CAL_O, ROLE_GAMMA, ROLE_GATE, ROLE_BIAS = 8, 9, 10, 11, 12
 
 
+def to_f16(a: np.ndarray) -> np.ndarray:
+    """fp32 samples -> fp16 bit patterns (uint16), via torch's conversion."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(torch.float16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
 def to_bf16(a: np.ndarray) -> np.ndarray:
     """fp32 samples -> bf16 bit patterns (uint16), via torch's conversion."""
     import torch
@@ -70,7 +80,7 @@ def _threads() -> int:
 class Workload:
     name: str
     number: int               # 1..5, selects the seeds
-    kind: str                 # "rms_adaln" | "quantize" | "swiglu" | "residual_rms" | "residual_adaln"
+    kind: str                 # "rms_adaln" | "quantize" | "swiglu" | "residual_rms" | "residual_adaln" | "rms_silu"
     m: int                    # rows (tokens)
     k: int                    # output columns (hidden, or F for swiglu)
     frames: int = 0           # modulation table rows (rms_adaln)
@@ -85,6 +95,8 @@ class Workload:
     # ---- sizes -------------------------------------------------------------
     @property
     def padded_rows(self) -> int:
+        if self.kind == "rms_silu":
+            return self.m                      # plain scale layout: no padding rows
         return (self.m + 127) // 128 * 128
 
     @property
@@ -109,6 +121,8 @@ class Workload:
             return (2 + 4 + 4) * self.k
         if self.kind == "residual_adaln":
             return 2 * self.k + 2 * self.frames * self.k + 2 * self.k + 2 * self.frames * 2 * self.k + 4 * self.m
+        if self.kind == "rms_silu":
+            return 2 * self.k
         return 0
 
     # ---- generation ----------------------------------------------------------
@@ -151,9 +165,11 @@ class Workload:
         idx = range(self.n_chunks(rows)) if chunks is None else chunks
         idx = list(idx)
 
+        conv = to_f16 if self.kind == "rms_silu" else to_bf16
+
         def one(c):
             a = self._chunk_f32(role, rows, c, cols, hs)
-            return c, (a if fp32 else to_bf16(a))
+            return c, (a if fp32 else conv(a))
 
         parts = {}
         with ThreadPoolExecutor(_threads()) as ex:
@@ -220,7 +236,9 @@ class Workload:
         return self._rows_bf16(ROLE_CAL, self.cal_rows)
 
     def weight(self) -> np.ndarray:
-        return to_bf16(1.0 + 0.1 * rng(self.number, ROLE_W).standard_normal(self.k, dtype=np.float32))
+        """The RMSNorm weight [k]: bf16, or fp16 for the fp16 (rms_silu) workload."""
+        conv = to_f16 if self.kind == "rms_silu" else to_bf16
+        return conv(1.0 + 0.1 * rng(self.number, ROLE_W).standard_normal(self.k, dtype=np.float32))
 
     def bias(self) -> np.ndarray | None:
         """swiglu: the [2k] bf16 bias in the projection's column order; residual_rms: the
@@ -277,6 +295,7 @@ WORKLOADS = {
                  cal_rows=8192, bias_std=0.25),
         Workload("residual_adaln_63240x7168", 9, "residual_adaln", 63240, 7168, frames=31,
                  rows_per_frame=2040, outliers="cols36_x30", cal_rows=8192, bias_std=0.25),
+        Workload("rms_silu_16x120x216x192", 10, "rms_silu", 16 * 120 * 216, 192, cal_rows=32768),
     ]
 }
 
