@@ -88,6 +88,8 @@ def make_inputs(wl, torch, amax):
             return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dev)
         args = dict(x=f32(wl.h()), o=up(wl.o()), bias=up(wl.bias()), scale=f32(wl.residual_scale()),
                     gamma=f32(wl.gamma()))
+    elif wl.kind == "rms_silu":
+        args = dict(x=up(wl.x()), gamma=up(wl.weight()))
     elif wl.kind == "residual_adaln":
         args = dict(x=torch.from_numpy(wl.h()).to(dev), o=up(wl.o()), bias=up(wl.bias()), gate=up(wl.gate_table()),
                     weight=up(wl.weight()), table=up(wl.table()), frame_idx=torch.from_numpy(wl.frame_idx()).to(dev))
@@ -115,11 +117,24 @@ def main():
     amax = workloads.calibration_amax(wl.name)
     torch.cuda.set_device(0)
     inp = make_inputs(wl, torch, amax)
-    codes, scales = nq.new_quantized(wl.m, wl.k, "cuda:0")
+    if wl.kind == "rms_silu":
+        codes = torch.empty((wl.m, wl.k // 2), dtype=torch.uint8, device="cuda:0")
+        scales = torch.empty((wl.m, wl.k // 16), dtype=torch.uint8, device="cuda:0")
+    else:
+        codes, scales = nq.new_quantized(wl.m, wl.k, "cuda:0")
     amax_dev = torch.zeros(1, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
 
-    if wl.kind == "residual_adaln":
+    if wl.kind == "rms_silu":
+        if a.dynamic:
+            def step():
+                nq.rms_silu_nvfp4_dynamic(inp["x"], inp["gamma"], wl.eps, amax_out=amax_dev, codes=codes,
+                                          scales=scales, stream=stream)
+        else:
+            def step():
+                nq.rms_silu_nvfp4(inp["x"], inp["gamma"], wl.eps, amax, codes=codes, scales=scales, stream=stream)
+        nq.init()
+    elif wl.kind == "residual_adaln":
         # the stream is updated in place every step (the same work each time)
         residual = (inp["o"], inp["bias"], inp["gate"])
         fold_args = (inp["x"], inp["weight"], inp["table"], inp["frame_idx"], wl.eps)
@@ -272,7 +287,14 @@ def cpu_baseline(wl, amax, rows, np):
     rows = min(rows, wl.m)
     sel = np.arange(rows)
     x = wl.x_rows(sel) if not wl.kind.startswith("residual") else None
-    if wl.kind == "residual_adaln":
+    if wl.kind == "rms_silu":
+        gamma = wl.weight()
+        oracle.silu_table_f16()
+
+        def part(se):
+            s, e = se
+            oracle.rms_silu_rows(x[s:e], gamma, wl.eps, amax)
+    elif wl.kind == "residual_adaln":
         x, o = wl.h_rows(sel), wl.o_rows(sel)
         fold = (wl.bias(), wl.gate_table(), wl.weight(), wl.table())
         idx = wl.frame_idx(sel)

@@ -13,6 +13,8 @@
  *                       RMSNorm with an fp32 weight               -> NVFP4
  *   residual_rms_adaln_nvfp4  h += bf16(o + bias) * gate[t] (fp32, in place);
  *                       RMSNorm + adaLN of the next block         -> NVFP4
+ * and, for fp16 channels-last (VAE) activations:
+ *   rms_silu_nvfp4   RMSNorm over channels + SiLU                  -> NVFP4
  *
  * Sources: TensorRT-LLM PR #21483 "Fuse the MiniMax-H3 NVFP4 activation
  * quantize into the AdaLN, SwiGLU and attention-output producers" (Summary);
@@ -46,9 +48,9 @@
  *   current device).  bf16 data is passed as raw 16-bit patterns.
  * - Every compute call is asynchronous on `stream` (a hipStream_t passed as
  *   void*, NULL = the default stream), allocates nothing and never waits for
- *   the device.  The one exception is the first SwiGLU call (any swiglu_*
- *   entry point) on a device (or an explicit nvfp4act_init), which builds the
- *   device's SiLU table once and waits for it.
+ *   the device.  The one exception is the first SwiGLU or RMSNorm+SiLU call
+ *   on a device (or an explicit nvfp4act_init), which builds the device's SiLU
+ *   tables (bf16 and fp16) once and waits for it.
  * - Ownership: the caller allocates and frees every buffer.  Inputs must stay
  *   valid and unmodified, and outputs untouched, until the stream work is done.
  *   The library writes only codes, scales and the non-NULL side outputs.
@@ -94,9 +96,9 @@ const char* nvfp4act_status_string(int status);
 int nvfp4act_last_hip_error(void);
 
 /* Build the per-device constant tables on the current device (the SiLU table
-   of the swiglu_* calls) and wait for them.  Idempotent; optional (the
-   swiglu_* calls run it on first use).  Call it before capturing a swiglu_*
-   call into a HIP graph.  Returns a status. */
+   tables of the swiglu_* and rms_silu_* calls) and wait for them.
+   Idempotent; optional (those calls run it on first use).  Call it before
+   capturing one of them into a HIP graph.  Returns a status. */
 int nvfp4act_init(void);
 
 /* Standalone NVFP4 quantize of a bf16 tensor (the attention-output quantize).
@@ -250,6 +252,33 @@ int residual_rms_adaln_nvfp4(float* h, const void* o, const void* bias, const vo
                              float global_amax, void* codes, void* scales, float* rstd_out,
                              void* y_out, uint32_t* status_word, void* stream);
 
+/* Channels-last RMSNorm + SiLU -> NVFP4 of fp16 activations (FlashRT PR #142,
+   fp16_quant_nvfp4_ndhwc: the fused RMS_norm + SiLU + NVFP4 quantize of the
+   VAE's channels-last tensors, per-16-channel UE4M3 scales; fp32 statistics
+   with an fp16 affine as in its RMSNorm+RoPE kernel).  Per row (one voxel's c
+   channels):
+     rstd = 1 / sqrt(sum(x^2) / c + eps)   fp32; the tree of rms_adaln_nvfp4
+            with one 8-element chunk per lane over S lanes, S the smallest
+            power of two >= c/8 (lanes past c/8 hold 0), butterfly 1 .. S/2
+     a    = fp16(fp16(x * rstd) * gamma)
+     y    = fp16(a * sigmoid(a)) correctly rounded
+   then the NVFP4 quantizer above, with the scale bytes in plain row order.
+     x         [rows, c] fp16, row-major (channels-last), 16-byte aligned
+     gamma     [c] fp16, 16-byte aligned
+     eps       >= 0 and finite
+     rows, c   rows >= 0; c a multiple of 16 in [16, 512]
+     global_amax  as for nvfp4_quantize
+     codes     [rows, c/2] bytes (4-byte aligned)
+     scales    [rows, c/16] bytes: the E4M3 scale of block b of row r at
+               r*(c/16) + b (no swizzle, no padding rows)
+     rstd_out  [rows] fp32, nullable
+     y_out     [rows, c] fp16, nullable: the pre-quantization activation
+   The first call on a device builds the fp16 SiLU table (as the swiglu_*
+   calls build theirs).  Returns a status. */
+int rms_silu_nvfp4(const void* x, const void* gamma, float eps, int64_t rows, int64_t c,
+                   float global_amax, void* codes, void* scales, float* rstd_out, void* y_out,
+                   void* stream);
+
 /* Per-call (dynamic) global amax
    ------------------------------
    The *_dynamic forms take the global amax from the tensor itself instead of
@@ -299,6 +328,10 @@ int residual_rms_adaln_nvfp4_dynamic(float* h, const void* o, const void* bias, 
                                      const int32_t* frame_idx, float eps, int64_t m, int64_t k,
                                      float* amax_out, void* codes, void* scales, float* rstd_out,
                                      void* y_out, uint32_t* status_word, void* stream);
+
+int rms_silu_nvfp4_dynamic(const void* x, const void* gamma, float eps, int64_t rows, int64_t c,
+                           float* amax_out, void* codes, void* scales, float* rstd_out, void* y_out,
+                           void* stream);
 
 #ifdef __cplusplus
 }

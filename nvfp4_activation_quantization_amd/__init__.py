@@ -22,9 +22,12 @@ each returning ``(codes, scales)``; and the per-call (dynamic) amax forms
                            residual=(o, bias, gate_table))
                                                           gated residual (own table) + RMSNorm
                                                           + adaLN (next block's table)
+  rms_silu_nvfp4(x, gamma, eps, global_amax)              fp16 channels-last [rows, c]:
+                                                          RMSNorm + SiLU, plain scale layout
   swiglu_nvfp4_dynamic(projection), swiglu_packed_nvfp4_dynamic(projection, bias, interleaved),
   residual_rms_nvfp4_dynamic(h, gamma, eps, residual),
-  residual_rms_adaln_nvfp4_dynamic(h, weight, table, frame_idx, eps, residual)
+  residual_rms_adaln_nvfp4_dynamic(h, weight, table, frame_idx, eps, residual),
+  rms_silu_nvfp4_dynamic(x, gamma, eps)
 returning ``(codes, scales, amax)`` with ``amax`` a one-element float32 device tensor, codes ``[m, k/2]`` uint8, scales
 ``[pad(m), k/16]`` uint8 in the 128x4 swizzle (buffer shapes as the FastVideo
 API page's ``new_quantized``).
@@ -68,6 +71,8 @@ _SIGS = {
                                       _P, _P, _P, _P, _P, _P]),
     "residual_rms_adaln_nvfp4_dynamic": (_I, [_P, _P, _P, _P, _I64, _P, _P, _P, _I64, _I64, _P, _F, _I64, _I64,
                                               _P, _P, _P, _P, _P, _P, _P]),
+    "rms_silu_nvfp4": (_I, [_P, _P, _F, _I64, _I64, _F, _P, _P, _P, _P, _P]),
+    "rms_silu_nvfp4_dynamic": (_I, [_P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -491,4 +496,61 @@ def residual_rms_adaln_nvfp4_dynamic(h: torch.Tensor, weight: torch.Tensor, tabl
                                                           "y_out") if y_out is not None else 0,
                                                  status_word.data_ptr() if status_word is not None else 0,
                                                  _stream(stream, h.device)))
+    return codes, scales, amax_out
+
+
+def _f16_ptr(t, name):
+    if t.dtype not in (torch.float16, torch.int16, torch.uint16):
+        raise TypeError("%s must hold fp16 values (float16 or a 16-bit integer view)" % name)
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous device tensor" % name)
+    return t.data_ptr()
+
+
+def _rms_silu_args(x, gamma):
+    if x.dim() < 2:
+        raise ValueError("x must be channels-last with at least two dimensions")
+    c = x.shape[-1]
+    rows = x.numel() // c if c else 0
+    if gamma.numel() != c:
+        raise ValueError("gamma must hold c values")
+    return rows, c, _f16_ptr(x, "x"), _f16_ptr(gamma, "gamma")
+
+
+def rms_silu_nvfp4(x: torch.Tensor, gamma: torch.Tensor, eps: float, global_amax: float, codes=None, scales=None,
+                   rstd_out=None, y_out=None, stream=None):
+    """Channels-last fp16 x [..., c] (rows = every leading index): RMSNorm over c (fp32
+    statistic, fp16 affine gamma [c]) + SiLU -> NVFP4.  Returns (codes [rows, c/2], scales
+    [rows, c/16]) with the scale bytes in plain row order."""
+    rows, c, xp, gp = _rms_silu_args(x, gamma)
+    if codes is None:
+        codes = torch.empty((rows, c // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, c // 16), dtype=torch.uint8, device=x.device)
+    _check(_lib.rms_silu_nvfp4(xp, gp, float(eps), rows, c, float(global_amax),
+                               _out_ptr(codes, torch.uint8, (rows, c // 2), "codes"),
+                               _out_ptr(scales, torch.uint8, (rows, c // 16), "scales"),
+                               _out_ptr(rstd_out, torch.float32, (rows,), "rstd_out"),
+                               _out_ptr(y_out, y_out.dtype if y_out is not None else None, (rows, c), "y_out")
+                               if y_out is not None else 0,
+                               _stream(stream, x.device)))
+    return codes, scales
+
+
+def rms_silu_nvfp4_dynamic(x: torch.Tensor, gamma: torch.Tensor, eps: float, amax_out=None, codes=None,
+                           scales=None, rstd_out=None, y_out=None, stream=None):
+    """rms_silu_nvfp4 under the amax of this call's own y.  Returns (codes, scales, amax_out)."""
+    rows, c, xp, gp = _rms_silu_args(x, gamma)
+    if codes is None:
+        codes = torch.empty((rows, c // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, c // 16), dtype=torch.uint8, device=x.device)
+    amax_out, ap = _amax_ptr(amax_out, x.device)
+    _check(_lib.rms_silu_nvfp4_dynamic(xp, gp, float(eps), rows, c, ap,
+                                       _out_ptr(codes, torch.uint8, (rows, c // 2), "codes"),
+                                       _out_ptr(scales, torch.uint8, (rows, c // 16), "scales"),
+                                       _out_ptr(rstd_out, torch.float32, (rows,), "rstd_out"),
+                                       _out_ptr(y_out, y_out.dtype if y_out is not None else None, (rows, c),
+                                                "y_out") if y_out is not None else 0,
+                                       _stream(stream, x.device)))
     return codes, scales, amax_out

@@ -59,6 +59,7 @@ int current_device(const DeviceInfo** info, int* device_out) {
     hipError_t e = nvfp4act::prepare_rms_adaln();
     if (e == hipSuccess) e = nvfp4act::prepare_swiglu();
     if (e == hipSuccess) e = nvfp4act::prepare_residual_rms();
+    if (e == hipSuccess) e = nvfp4act::prepare_rms_silu();
     if (e != hipSuccess) {
       st.probed = false;
       return fail_hip(e);
@@ -76,9 +77,11 @@ int ensure_silu_table(int dev) {
   DeviceState& st = g_dev[dev];
   if (st.silu_ready) return NVFP4ACT_OK;
   if (st.silu_status != NVFP4ACT_OK) return st.silu_status;
-  unsigned int ambiguous = 0;
+  unsigned int ambiguous = 0, ambiguous16 = 0;
   hipError_t e = nvfp4act::build_silu_table(&ambiguous);
+  if (e == hipSuccess) e = nvfp4act::build_silu16_table(&ambiguous16);
   if (e != hipSuccess) return fail_hip(e);
+  ambiguous += ambiguous16;
   if (ambiguous != 0) {
     st.silu_status = NVFP4ACT_ERR_TABLE;
     return st.silu_status;
@@ -379,6 +382,41 @@ int residual_adaln_call(float* h, const void* o, const void* bias, const FoldTab
   return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
 }
 
+int rms_silu_call(const void* x, const void* gamma, float eps, int64_t rows, int64_t c, float global_amax,
+                  float* amax_dev, void* codes, void* scales, float* rstd_out, void* y_out, void* stream) {
+  if (rows < 0 || c < 16 || c > 512 || c % 16 != 0) return NVFP4ACT_ERR_SHAPE;
+  if (rows == 0) return NVFP4ACT_OK;
+  if (!x || !gamma || !codes || !scales) return NVFP4ACT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned4(codes) || (y_out && !aligned16(y_out)) ||
+      (rstd_out && !aligned4(rstd_out)))
+    return NVFP4ACT_ERR_ALIGN;
+  if (!std::isfinite(eps) || eps < 0.0f) return NVFP4ACT_ERR_VALUE;
+  if (!amax_dev) {
+    int st = check_amax(global_amax);
+    if (st != NVFP4ACT_OK) return st;
+  }
+  const DeviceInfo* info = nullptr;
+  int dev = -1;
+  int st = current_device(&info, &dev);
+  if (st != NVFP4ACT_OK) return st;
+  st = ensure_silu_table(dev);
+  if (st != NVFP4ACT_OK) return st;
+  nvfp4act::RmsSiluLaunch p{};
+  p.x = x;
+  p.gamma = gamma;
+  p.eps = eps;
+  p.rows = rows;
+  p.c = c;
+  p.global_amax = global_amax;
+  p.amax_dev = amax_dev;
+  p.codes = codes;
+  p.scales = scales;
+  p.rstd_out = rstd_out;
+  p.y_out = y_out;
+  hipError_t e = nvfp4act::launch_rms_silu(p, *info, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
+}
+
 // The per-call forms need the amax destination: one 4-byte aligned float (m == 0 aside).
 int check_amax_out(int64_t m, const float* amax_out) {
   if (m == 0) return NVFP4ACT_OK;
@@ -486,6 +524,19 @@ int residual_rms_adaln_nvfp4_dynamic(float* h, const void* o, const void* bias, 
   st = check_amax_out(m, amax_out);
   if (st != NVFP4ACT_OK) return st;
   return residual_adaln_call(h, o, bias, f, eps, m, k, 0.0f, amax_out, codes, scales, rstd_out, y_out, stream);
+}
+
+int rms_silu_nvfp4(const void* x, const void* gamma, float eps, int64_t rows, int64_t c, float global_amax,
+                   void* codes, void* scales, float* rstd_out, void* y_out, void* stream) {
+  return rms_silu_call(x, gamma, eps, rows, c, global_amax, nullptr, codes, scales, rstd_out, y_out, stream);
+}
+
+int rms_silu_nvfp4_dynamic(const void* x, const void* gamma, float eps, int64_t rows, int64_t c, float* amax_out,
+                           void* codes, void* scales, float* rstd_out, void* y_out, void* stream) {
+  if (rows < 0 || c < 16 || c > 512 || c % 16 != 0) return NVFP4ACT_ERR_SHAPE;
+  int st = check_amax_out(rows, amax_out);
+  if (st != NVFP4ACT_OK) return st;
+  return rms_silu_call(x, gamma, eps, rows, c, 0.0f, amax_out, codes, scales, rstd_out, y_out, stream);
 }
 
 }  // extern "C"

@@ -100,13 +100,32 @@ struct ResidualLaunch {
 
 hipError_t launch_residual_rms(const ResidualLaunch& p, hipStream_t stream);
 
+// The arguments of one rms_silu_nvfp4 call (see include/nvfp4act.h): x [rows, c] fp16
+// channels-last, gamma [c] fp16; codes [rows, c/2], scales [rows, c/16] (plain order).
+struct RmsSiluLaunch {
+  const void* x;
+  const void* gamma;
+  float eps;
+  int64_t rows, c;
+  float global_amax;
+  float* amax_dev;
+  void* codes;
+  void* scales;
+  float* rstd_out;
+  void* y_out;
+};
+
+hipError_t launch_rms_silu(const RmsSiluLaunch& p, const DeviceInfo& dev, hipStream_t stream);
+
 // Per-device, once: allow the LDS sizes the kernels use.
 hipError_t prepare_rms_adaln();
 hipError_t prepare_swiglu();
 hipError_t prepare_residual_rms();
+hipError_t prepare_rms_silu();
 
 // Build the SiLU table of the current device and wait for it; *ambiguous receives the
 // number of entries whose rounding fp64 could not decide (0 expected).
 hipError_t build_silu_table(unsigned int* ambiguous);
+hipError_t build_silu16_table(unsigned int* ambiguous);   // the fp16 SiLU table, likewise
 
 }  // namespace nvfp4act

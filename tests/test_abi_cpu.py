@@ -187,6 +187,34 @@ def test_residual_rms_adaln_status_codes(dynamic):
         assert fold(amax=0.0) == 4
 
 
+def rs(dynamic=False, **kw):
+    a = dict(x=A, gamma=A, eps=1e-6, rows=4, c=192, amax=1.0, amax_out=A, codes=A, scales=A, rstd=None, y=None)
+    a.update(kw)
+    f = ctypes.c_float(a["eps"])
+    if dynamic:
+        return lib.rms_silu_nvfp4_dynamic(a["x"], a["gamma"], f, a["rows"], a["c"], a["amax_out"], a["codes"],
+                                          a["scales"], a["rstd"], a["y"], None)
+    return lib.rms_silu_nvfp4(a["x"], a["gamma"], f, a["rows"], a["c"], a["amax"], a["codes"], a["scales"],
+                              a["rstd"], a["y"], None)
+
+
+@pytest.mark.parametrize("dynamic", [False, True])
+def test_rms_silu_status_codes(dynamic):
+    for key in ("x", "gamma", "codes", "scales"):
+        assert rs(dynamic, **{key: None}) == 1, key
+    for c in (0, 8, 24, 520, 1024):
+        assert rs(dynamic, c=c) == 2, c
+    assert rs(dynamic, rows=-1) == 2
+    assert rs(dynamic, x=U) == 3 and rs(dynamic, gamma=U) == 3 and rs(dynamic, codes=A + 2) == 3
+    assert rs(dynamic, y=U) == 3 and rs(dynamic, rstd=A + 2) == 3
+    assert rs(dynamic, eps=-1.0) == 4
+    assert rs(dynamic, rows=0) == 0
+    if dynamic:
+        assert rs(True, amax_out=None) == 1
+    else:
+        assert rs(amax=float("nan")) == 4
+
+
 def torch_has_gpu():
     import torch
     return torch.cuda.is_available()
@@ -200,6 +228,7 @@ def test_valid_call_without_a_gpu_reports_no_device():
     assert swp() == 5 and swp(bias=None, il=1) == 5 and swp(True) == 5
     assert rr() == 5 and rr(bias=None) == 5 and rr(True) == 5
     assert fold() == 5 and fold(o=None, gate=None) == 5 and fold(True) == 5
+    assert rs() == 5 and rs(c=96) == 5 and rs(True) == 5
     assert lib.nvfp4act_init() == 5
 
 

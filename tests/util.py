@@ -127,6 +127,22 @@ def oracle_residual_adaln(h, o, bias, gate, w, table, idx, eps, amax, want_y=Tru
     return out
 
 
+def oracle_rms_silu(x, gamma, eps, amax, want_y=True, gsf=None):
+    """oracle.rms_silu_rows over row blocks in parallel threads."""
+    n = x.shape[0]
+    oracle.silu_table_f16()
+
+    def part(se):
+        s, e = se
+        return oracle.rms_silu_rows(x[s:e], gamma, eps, amax, want_y=want_y, gsf=gsf)
+
+    with ThreadPoolExecutor(threads()) as ex:
+        res = list(ex.map(part, split_rows(n, 4 * threads())))
+    out = {key: np.concatenate([r[key] for r in res]) for key in ("codes", "scale_bytes", "rstd")}
+    out["y"] = np.concatenate([r["y"] for r in res]) if want_y else None
+    return out
+
+
 def scales_from_rows(scale_bytes: np.ndarray, m: int, k: int, rows=None) -> np.ndarray:
     """Place plain-order scale bytes of rows into a zeroed swizzled [pad(m), k/16] buffer."""
     buf = np.zeros(oracle.padded_rows(m) * (k // 16), np.uint8)
