@@ -86,6 +86,12 @@ def _load():
                                           P, P, P, P, P, P]),
             "orc_silu_table": (ctypes.c_int, [P]),
             "orc_silu_table_f16": (ctypes.c_int, [P]),
+            "orc_tree_sum_f32": (F, [P, I64, ctypes.c_int]),
+            "orc_e4m3_encode_signed": (None, [P, P, I64]),
+            "orc_ln_adaln_fp8_rows": (None, [P, P, P, F, I64, I64, F, P, P, P, P]),
+            "orc_fp8_inverse_scale": (F, [F]),
+            "orc_fp8_dynamic_scale": (F, [F]),
+            "orc_fp8_dynamic_inverse": (F, [F]),
             "orc_f16_round": (None, [P, P, I64]),
             "orc_rms_rstd_f16row": (F, [P, I64, F]),
             "orc_rms_sum_f16row": (F, [P, I64]),
@@ -539,6 +545,58 @@ def rms_silu_dynamic(x_u16, gamma_u16, eps: float, want_y: bool = False):
     amax = max_abs_f16(first["y"])
     out = rms_silu_rows(x_u16, gamma_u16, eps, 0.0, want_y=want_y, gsf=dynamic_global_scale(amax))
     out["amax"] = amax
+    return out
+
+
+def tree_sum_f32(v_f32, squares: bool = False) -> float:
+    """The fixed-tree sum (or sum of squares, fma) of one fp32 row, k % 512 == 0."""
+    v = _c(v_f32, np.float32).reshape(-1)
+    return _load().orc_tree_sum_f32(_ptr(v), v.size, int(bool(squares)))
+
+
+def e4m3_encode_signed(f32) -> np.ndarray:
+    a = _c(f32, np.float32)
+    out = np.empty(a.shape, np.uint8)
+    _load().orc_e4m3_encode_signed(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def fp8_inverse_scale(act_scale: float) -> float:
+    return _load().orc_fp8_inverse_scale(float(act_scale))
+
+
+def ln_adaln_fp8_rows(x_u16, scale_f32, shift_f32, eps: float, act_scale: float | None = None,
+                      inv_scale: float | None = None):
+    """LayerNorm (fp32 statistics) + adaLN -> per-tensor FP8 E4M3 over fp16 rows [n, k].
+
+    act_scale: the static per-tensor scale (codes = E4M3(y * (1 / act_scale))); or pass
+    inv_scale directly.  Returns dict(codes [n, k] u8, mean [n], rstd [n], y [n, k] fp32).
+    """
+    x = _c(x_u16, np.uint16)
+    n, k = x.shape
+    sc = _c(scale_f32, np.float32).reshape(-1)
+    sh = _c(shift_f32, np.float32).reshape(-1)
+    if sc.size != k or sh.size != k or k % 512:
+        raise ValueError("scale and shift hold k values; k % 512 == 0")
+    inv = fp8_inverse_scale(act_scale) if inv_scale is None else float(inv_scale)
+    codes = np.empty((n, k), np.uint8)
+    mean = np.empty(n, np.float32)
+    rstd = np.empty(n, np.float32)
+    y = np.empty((n, k), np.float32)
+    _load().orc_ln_adaln_fp8_rows(_ptr(x), _ptr(sc), _ptr(sh), float(eps), n, k, inv, _ptr(codes), _ptr(mean),
+                                  _ptr(rstd), _ptr(y))
+    return dict(codes=codes, mean=mean, rstd=rstd, y=y)
+
+
+def ln_adaln_fp8_dynamic(x_u16, scale_f32, shift_f32, eps: float):
+    """The per-call form: act_scale = max|y| / 448 from the call's own y, then the
+    quantizer with 1 / act_scale (0 when the scale is 0).  Adds 'amax' and 'act_scale'."""
+    first = ln_adaln_fp8_rows(x_u16, scale_f32, shift_f32, eps, inv_scale=1.0)
+    amax = float(np.abs(first["y"]).max()) if first["y"].size else 0.0
+    act = _load().orc_fp8_dynamic_scale(amax)
+    inv = _load().orc_fp8_dynamic_inverse(act)
+    out = ln_adaln_fp8_rows(x_u16, scale_f32, shift_f32, eps, inv_scale=inv)
+    out["amax"], out["act_scale"] = amax, act
     return out
 
 

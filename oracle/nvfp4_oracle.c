@@ -26,7 +26,9 @@
  *   [INT64]   FastVideo commit log, branch vae-parallel-decode: the int64
  *             indexing fix at 2^31 elements and the frame-index bounds
  *             contract of the modulation wrappers.
- *   [FlashRT] FlashRT PR #142 (MiniMax-Remover): fp16_quant_nvfp4_ndhwc, the
+ *   [FlashRT] FlashRT PR #142 (MiniMax-Remover): fp16_ada_layernorm_quant_fp8
+ *             (one-pass fp32-stat LayerNorm + adaLN + per-tensor FP8 E4M3
+ *             with one scale shared by Q/K/V); fp16_quant_nvfp4_ndhwc, the
  *             fused RMS_norm + SiLU + NVFP4 quantize of channels-last VAE
  *             activations, per-16-channel UE4M3 scales; the RMSNorm+RoPE
  *             kernel's fp32 statistics with an fp16 affine.
@@ -746,6 +748,123 @@ EXPORT void orc_rms_silu_rows_gsf(const uint16_t* x, const uint16_t* gamma, floa
     free(sb);
     free(y);
     leave_ieee(s);
+}
+
+/* ------------------------------------------------------------------------- */
+/* LayerNorm + adaLN -> per-tensor FP8 E4M3 (fp16 input)                     */
+/* ------------------------------------------------------------------------- */
+
+/* The fixed tree of rms_rstd over the values v[0..k) of an fp32 row
+   (k % 512 == 0): lane L owns chunks L + 64j, 8 accumulators a_e over its
+   chunks in ascending order, updated by add(a_e, v) (SUM) or by
+   fma(v, v, a_e) (SQUARES); lane value ((a0+a1)+(a2+a3))+((a4+a5)+(a6+a7));
+   butterfly over the 64 lanes. */
+static float tree_sum_f32(const float* v, int64_t k, int squares) {
+    float lane[64];
+    const int64_t chunks = k / 8;
+    for (int L = 0; L < 64; ++L) {
+        float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int64_t c = L; c < chunks; c += 64)
+            for (int e = 0; e < 8; ++e) {
+                float x = v[8 * c + e];
+                a[e] = squares ? fmaf(x, x, a[e]) : a[e] + x;
+            }
+        lane[L] = ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+    }
+    for (int s = 1; s < 64; s *= 2) {
+        float next[64];
+        for (int L = 0; L < 64; ++L) next[L] = lane[L] + lane[L ^ s];
+        memcpy(lane, next, sizeof lane);
+    }
+    return lane[0];
+}
+
+EXPORT float orc_tree_sum_f32(const float* v, int64_t k, int squares) {
+    unsigned int s = enter_ieee();
+    float r = tree_sum_f32(v, k, squares);
+    leave_ieee(s);
+    return r;
+}
+
+/* Signed E4M3 (OCP FN) code of an fp32 value: sign bit 7 (-0 -> 0x80), the
+   magnitude nearest-even and saturating at 448 (e4m3_encode). */
+static uint8_t e4m3_encode_signed(float v) {
+    uint8_t sign = signbit(v) ? 0x80u : 0;
+    return (uint8_t)(sign | e4m3_encode(fabsf(v)));
+}
+
+EXPORT void orc_e4m3_encode_signed(const float* in, uint8_t* out, int64_t n) {
+    unsigned int s = enter_ieee();
+    for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode_signed(in[i]);
+    leave_ieee(s);
+}
+
+/* LayerNorm with fp32 statistics + adaLN modulation, quantized per tensor to
+   FP8 E4M3 ([FlashRT] fp16_ada_layernorm_quant_fp8: one pass, fp32 statistics,
+   one shared FP8 scale for the three projections that read the result).
+   Row i of x [n, k] fp16 (k % 512 == 0), fp32 vectors scale, shift [k]:
+     mean = tree_sum(x) / k
+     d    = x - mean
+     var  = tree_sum_of_squares(d) / k          (fma accumulation)
+     rstd = 1 / sqrt(var + eps)
+     y    = ((d * rstd) * (1 + scale)) + shift  fp32, each operation rounded
+     q    = E4M3(y * inv_scale)                 inv_scale = 1 / act_scale (fp32)
+   codes [n, k] (one byte each); mean_out, rstd_out [n], y_out [n, k] fp32:
+   nullable. */
+EXPORT void orc_ln_adaln_fp8_rows(const uint16_t* x, const float* scale, const float* shift, float eps,
+                                  int64_t n, int64_t k, float inv_scale, uint8_t* codes,
+                                  float* mean_out, float* rstd_out, float* y_out) {
+    unsigned int s = enter_ieee();
+    float* v = (float*)malloc(sizeof(float) * (size_t)k);
+    for (int64_t i = 0; i < n; ++i) {
+        const uint16_t* xr = x + i * k;
+        for (int64_t d = 0; d < k; ++d) v[d] = f16_to_f32(xr[d]);
+        float mean = tree_sum_f32(v, k, 0) / (float)k;
+        for (int64_t d = 0; d < k; ++d) v[d] = v[d] - mean;
+        float var = tree_sum_f32(v, k, 1) / (float)k;
+        float rstd = 1.0f / sqrtf(var + eps);
+        if (mean_out) mean_out[i] = mean;
+        if (rstd_out) rstd_out[i] = rstd;
+        for (int64_t d = 0; d < k; ++d) {
+            float xh = v[d] * rstd;
+            float opl = 1.0f + scale[d];
+            float m = xh * opl;
+            float y = m + shift[d];
+            if (y_out) y_out[i * k + d] = y;
+            codes[i * k + d] = e4m3_encode_signed(y * inv_scale);
+        }
+    }
+    free(v);
+    leave_ieee(s);
+}
+
+/* The quantizer's inverse scale of a per-tensor scale: 1 / act_scale (fp32). */
+EXPORT float orc_fp8_inverse_scale(float act_scale) {
+    unsigned int s = enter_ieee();
+    float r = 1.0f / act_scale;
+    leave_ieee(s);
+    return r;
+}
+
+/* The per-call scale of the FP8 producer: act_scale = amax / 448 (fp32), 0 when
+   amax is 0; the inverse scale is then 1 / act_scale, or 0 when act_scale is 0
+   or the reciprocal overflows (every code a signed zero). */
+EXPORT float orc_fp8_dynamic_scale(float amax) {
+    unsigned int s = enter_ieee();
+    float r = amax / 448.0f;
+    leave_ieee(s);
+    return r;
+}
+
+EXPORT float orc_fp8_dynamic_inverse(float act_scale) {
+    unsigned int s = enter_ieee();
+    float r = 0.0f;
+    if (act_scale > 0.0f) {
+        r = 1.0f / act_scale;
+        if (isinf(r)) r = 0.0f;
+    }
+    leave_ieee(s);
+    return r;
 }
 
 /* ------------------------------------------------------------------------- */

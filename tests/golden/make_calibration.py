@@ -18,6 +18,8 @@ TensorRT-LLM fusions apply only to static NVFP4 scales).  For each workload:
   residual_adaln_63240x7168  the same for the gated residual + RMSNorm + adaLN, frame
                          (r * 31) // 8192
   rms_silu_16x120x216x192  max |y| of the oracle over 32,768 calibration voxel rows
+  ln_fp8_63240x7168      max |y| (fp32) of the oracle over 8,192 calibration rows; the
+                         static FP8 scale is this amax / 448
 
 Run:  python tests/golden/make_calibration.py
 """
@@ -50,6 +52,11 @@ def calibrate(w: workloads.Workload) -> dict:
     elif w.kind == "quantize":
         amax = amax_of_bf16(w.calibration_x())
         how = "max|x| over %d calibration rows" % w.cal_rows
+    elif w.kind == "ln_fp8":
+        sc, sh = w.modulation()
+        res = oracle.ln_adaln_fp8_rows(w.calibration_x(), sc, sh, w.eps, inv_scale=1.0)
+        amax = float(np.abs(res["y"]).max())
+        how = "max|y| of the oracle over %d calibration rows" % w.cal_rows
     elif w.kind == "rms_silu":
         res = oracle.rms_silu_rows(w.calibration_x(), w.weight(), w.eps, 1.0, want_y=True)
         amax = oracle.max_abs_f16(res["y"])

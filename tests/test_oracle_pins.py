@@ -687,6 +687,99 @@ def test_rms_silu_hand_worked_block():
 
 
 # --------------------------------------------------------------------------
+# LayerNorm + adaLN -> per-tensor FP8 E4M3
+# --------------------------------------------------------------------------
+
+def _torch_fp8(v_f32):
+    t = torch.from_numpy(np.ascontiguousarray(v_f32, np.float32)).clamp(-448.0, 448.0)
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def test_e4m3_signed_encoder_matches_torch_saturating_conversion():
+    g = np.random.Generator(np.random.PCG64(71))
+    vals = [g.standard_normal(200000).astype(np.float32) * s for s in (1e-3, 0.05, 1.0, 30.0, 300.0, 1e4)]
+    # every E4M3 value, its midpoints with the neighbours and a few ulps around them, both signs
+    grid = np.array([oracle.e4m3_value(c) for c in range(127)], np.float64)
+    mids = (grid[:-1] + grid[1:]) / 2
+    pts = np.concatenate([grid, mids, [448.0, 464.0, 480.0, 1e30, 2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11]])
+    pts32 = pts.astype(np.float32)
+    u = pts32.view(np.uint32)
+    near = np.concatenate([(u.astype(np.int64) + d).astype(np.uint32).view(np.float32) for d in range(-3, 4)])
+    near = near[np.isfinite(near)]          # stepping down from +0 wraps to NaN patterns
+    allv = np.concatenate(vals + [near, -near, np.array([0.0, -0.0], np.float32)])
+    assert np.array_equal(oracle.e4m3_encode_signed(allv), _torch_fp8(allv))
+    assert oracle.e4m3_encode_signed(np.array([-0.0], np.float32))[0] == 0x80
+    assert list(oracle.e4m3_encode_signed(np.array([1e30, -1e30], np.float32))) == [0x7E, 0xFE]
+
+
+def test_tree_sum_f32_order():
+    """The SUM tree: lane 0 holds 2^24 (chunk 0, element 0); 2^24 + 1 rounds back to 2^24
+    (tie to even), 1 + 1 = 2 and 2^24 + 2 are exact (k = 512: one chunk per lane)."""
+    def total(ones):
+        v = np.zeros(512, np.float32)
+        v[0] = 2.0 ** 24
+        for i in ones:
+            v[i] = 1.0
+        return oracle.tree_sum_f32(v)
+    big, big2 = np.float32(2.0 ** 24), np.float32(2.0 ** 24 + 2)
+    assert total([8, 24]) == big            # lanes 1 and 3: each one meets 2^24 alone
+    assert total([16, 24]) == big2          # lanes 2 and 3 pair first
+    assert total([2, 3]) == big2            # elements 2, 3 of lane 0 pair within the lane
+    assert total([1, 2]) == big             # (2^24 + 1) loses it, then (1 + 0) is added to 2^24
+    v = np.zeros(1024, np.float32)
+    v[0], v[512] = 2.0 ** -12, 1.0 + 2.0 ** -12     # lane 0, element 0, chunks 0 and 64
+    assert oracle.tree_sum_f32(v, squares=True) == np.float32(1.0 + 2.0 ** -11 + 2.0 ** -23)   # fma
+
+
+def _ln_case(seed, n=5, k=1024):
+    g = np.random.Generator(np.random.PCG64(seed))
+    x = oracle.f16_round((g.standard_normal((n, k)) * 3 + 0.5).astype(np.float32))
+    scale = (0.2 * g.standard_normal(k)).astype(np.float32)
+    shift = (0.2 * g.standard_normal(k)).astype(np.float32)
+    return x, scale, shift
+
+
+def test_ln_statistics():
+    x, scale, shift = _ln_case(72)
+    res = oracle.ln_adaln_fp8_rows(x, scale, shift, 1e-6, 0.05)
+    xf = oracle.f16_to_f32(x).astype(np.float64)
+    mean = xf.mean(axis=1)
+    var = xf.var(axis=1)
+    assert np.all(np.abs(res["mean"] - mean) <= 1e-6 * np.abs(xf).max())
+    assert np.all(np.abs(res["rstd"] / (1.0 / np.sqrt(var + 1e-6)) - 1) < 1e-6)
+    # a constant row: mean exact, var 0, rstd = 1 / sqrt(eps)
+    c = oracle.f16_round(np.full((1, 512), 1.5, np.float32))
+    r = oracle.ln_adaln_fp8_rows(c, np.zeros(512, np.float32), np.zeros(512, np.float32), 0.25, 1.0)
+    assert r["mean"][0] == 1.5 and r["rstd"][0] == 2.0 and not np.any(r["codes"] & 0x7F)
+
+
+def test_ln_adaln_chain_and_codes_match_torch_eager_ops():
+    x, scale, shift = _ln_case(73)
+    act = 0.03
+    res = oracle.ln_adaln_fp8_rows(x, scale, shift, 1e-6, act)
+    xt = torch.from_numpy(oracle.f16_to_f32(x))
+    d = xt - torch.from_numpy(res["mean"])[:, None]
+    y = ((d * torch.from_numpy(res["rstd"])[:, None]) * (1.0 + torch.from_numpy(scale))) + torch.from_numpy(shift)
+    assert np.array_equal(res["y"].view(np.uint32), y.numpy().view(np.uint32))
+    inv = np.float32(1.0) / np.float32(act)
+    assert oracle.fp8_inverse_scale(act) == inv
+    assert np.array_equal(res["codes"], _torch_fp8((y * torch.tensor(inv)).numpy()))
+
+
+def test_ln_adaln_hand_worked_row():
+    """x = +1, -1 alternating: mean 0, var 1; eps = 0 gives rstd 1, y = +-1 with no
+    modulation, and act_scale 1 codes them 0x38 (1.0) and 0xB8 (-1.0)."""
+    x = oracle.f16_round(np.tile([1.0, -1.0], 256).reshape(1, 512).astype(np.float32))
+    z = np.zeros(512, np.float32)
+    res = oracle.ln_adaln_fp8_rows(x, z, z, 0.0, 1.0)
+    assert res["mean"][0] == 0.0 and res["rstd"][0] == 1.0
+    assert list(res["codes"][0, :4]) == [0x38, 0xB8, 0x38, 0xB8]
+    # shift 2, scale 1: y = +-1 * 2 + 2 = 4 or 0 -> 0x48 (4.0) and 0x00
+    res = oracle.ln_adaln_fp8_rows(x, np.ones(512, np.float32), np.full(512, 2.0, np.float32), 0.0, 1.0)
+    assert list(res["codes"][0, :2]) == [0x48, 0x00]
+
+
+# --------------------------------------------------------------------------
 # SiLU table and the SwiGLU producer
 # --------------------------------------------------------------------------
 
@@ -937,6 +1030,22 @@ def test_dynamic_rms_silu_is_static_at_its_own_amax():
     assert dyn["amax"] == float(np.abs(oracle.f16_to_f32(ref["y"])).max())
     for key in ("codes", "scale_bytes", "y", "rstd"):
         assert np.array_equal(dyn[key], ref[key]), key
+
+
+def test_dynamic_ln_adaln_fp8():
+    x, scale, shift = _ln_case(74, n=7)
+    dyn = oracle.ln_adaln_fp8_dynamic(x, scale, shift, 1e-6)
+    assert dyn["amax"] == float(np.abs(dyn["y"]).max())
+    assert dyn["act_scale"] == np.float32(dyn["amax"]) / np.float32(448.0)
+    ref = oracle.ln_adaln_fp8_rows(x, scale, shift, 1e-6, dyn["act_scale"])
+    assert np.array_equal(ref["codes"], dyn["codes"])
+    # the element holding the maximum saturates to +-448
+    i = np.unravel_index(np.argmax(np.abs(dyn["y"])), dyn["y"].shape)
+    assert dyn["codes"][i] & 0x7F == 0x7E
+    # an all-zero tensor: scale 0, inverse 0, every code a zero (mean 0, y = shift = 0)
+    z = np.zeros(512, np.float32)
+    zero = oracle.ln_adaln_fp8_dynamic(np.zeros((2, 512), np.uint16), z, z, 1e-6)
+    assert zero["act_scale"] == 0.0 and not np.any(zero["codes"] & 0x7F)
 
 
 def test_dynamic_rms_adaln_and_swiglu_are_static_at_their_own_amax():

@@ -94,3 +94,12 @@ def test_rms_silu_workload():
     xf = oracle.f16_to_f32(x)
     assert x.dtype == np.uint16 and np.all(np.isfinite(xf)) and 0.5 < float(np.std(xf)) < 1.5
     assert np.array_equal(oracle.f16_round(xf), x)                 # fp16 patterns
+
+
+def test_ln_fp8_workload():
+    w = workloads.get("ln_fp8_63240x7168")
+    assert w.algorithmic_bytes() == 3 * w.m * w.k
+    sc, sh = w.modulation()
+    assert sc.dtype == np.float32 and sh.shape == (w.k,) and not np.array_equal(sc, sh)
+    act = workloads.fp8_act_scale(w.name)
+    assert act == np.float32(workloads.calibration_amax(w.name)) / np.float32(448.0)

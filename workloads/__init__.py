@@ -30,9 +30,12 @@ a 34x60 latent grid per frame over 31 frames = 63,240 tokens from
   rms_silu_16x120x216x192  fp16 channels-last VAE activations: 16 frames of 120 x 216
                            voxels (half the 432 x 240 clip in each direction), 192
                            channels; x ~ N(0,1), gamma = 1 + 0.1 N(0,1), eps = 1e-6
+  ln_fp8_63240x7168        LayerNorm + adaLN -> per-tensor FP8 over fp16 hidden states of
+                           the H3 block shape (the recipe of rms_adaln_63240x7168 in
+                           fp16); fp32 modulation vectors scale, shift ~ 0.1 N(0,1)
 
 Seeds: numpy ``PCG64``; the seed of role ``role`` in workload number ``i``
-(1..10 in the order above) is ``1000*i + role`` with roles 1 x (or h), 2 weight
+(1..11 in the order above) is ``1000*i + role`` with roles 1 x (or h), 2 weight
 (or bias), 3 modulation table (or residual scale), 4 calibration rows, 5
 outlier pick, 6 per-head std, 8 the residual branch o, 9 its calibration rows,
 10 the fp32 RMSNorm weight, 11 the gate table, 12 the bias where a weight is
@@ -108,6 +111,8 @@ class Workload:
         scale bytes over the padded rows (parameters not counted).  residual_rms: the
         fp32 stream read and written back, the bf16 branch read."""
         out = self.m * self.k // 2 + self.padded_rows * self.k // 16
+        if self.kind == "ln_fp8":
+            return 2 * self.m * self.k + self.m * self.k       # fp16 in, one FP8 byte out
         if self.kind in ("residual_rms", "residual_adaln"):
             return (4 + 2 + 4) * self.m * self.k + out
         return 2 * self.m * self.in_cols + out
@@ -123,6 +128,8 @@ class Workload:
             return 2 * self.k + 2 * self.frames * self.k + 2 * self.k + 2 * self.frames * 2 * self.k + 4 * self.m
         if self.kind == "rms_silu":
             return 2 * self.k
+        if self.kind == "ln_fp8":
+            return 2 * 4 * self.k
         return 0
 
     # ---- generation ----------------------------------------------------------
@@ -165,7 +172,7 @@ class Workload:
         idx = range(self.n_chunks(rows)) if chunks is None else chunks
         idx = list(idx)
 
-        conv = to_f16 if self.kind == "rms_silu" else to_bf16
+        conv = to_f16 if self.kind in ("rms_silu", "ln_fp8") else to_bf16
 
         def one(c):
             a = self._chunk_f32(role, rows, c, cols, hs)
@@ -212,6 +219,13 @@ class Workload:
 
     def calibration_o(self) -> np.ndarray:
         return self._rows_bf16(ROLE_CAL_O, self.cal_rows, plain=True)
+
+    def modulation(self) -> tuple[np.ndarray, np.ndarray]:
+        """ln_fp8: the fp32 adaLN (scale, shift) vectors [k]."""
+        g = rng(self.number, ROLE_TABLE)
+        sc = (0.1 * g.standard_normal(self.k, dtype=np.float32)).astype(np.float32)
+        sh = (0.1 * g.standard_normal(self.k, dtype=np.float32)).astype(np.float32)
+        return sc, sh
 
     def residual_scale(self) -> np.ndarray:
         """residual_rms: the fp32 per-channel scale [k] of the branch."""
@@ -296,6 +310,7 @@ WORKLOADS = {
         Workload("residual_adaln_63240x7168", 9, "residual_adaln", 63240, 7168, frames=31,
                  rows_per_frame=2040, outliers="cols36_x30", cal_rows=8192, bias_std=0.25),
         Workload("rms_silu_16x120x216x192", 10, "rms_silu", 16 * 120 * 216, 192, cal_rows=32768),
+        Workload("ln_fp8_63240x7168", 11, "ln_fp8", 63240, 7168, outliers="cols36_x30", cal_rows=8192),
     ]
 }
 
@@ -304,6 +319,11 @@ BENCH_WORKLOAD = "rms_adaln_63240x7168"
 
 def get(name: str) -> Workload:
     return WORKLOADS[name]
+
+
+def fp8_act_scale(name: str) -> float:
+    """The static per-tensor FP8 scale of an ln_fp8 workload: its calibrated amax / 448."""
+    return float(np.float32(calibration_amax(name)) / np.float32(448.0))
 
 
 def calibration_amax(name: str) -> float:
