@@ -90,6 +90,9 @@ def make_inputs(wl, torch, amax):
                     gamma=f32(wl.gamma()))
     elif wl.kind == "rms_silu":
         args = dict(x=up(wl.x()), gamma=up(wl.weight()))
+    elif wl.kind == "ln_fp8":
+        sc, sh = wl.modulation()
+        args = dict(x=up(wl.x()), scale=torch.from_numpy(sc).to(dev), shift=torch.from_numpy(sh).to(dev))
     elif wl.kind == "residual_adaln":
         args = dict(x=torch.from_numpy(wl.h()).to(dev), o=up(wl.o()), bias=up(wl.bias()), gate=up(wl.gate_table()),
                     weight=up(wl.weight()), table=up(wl.table()), frame_idx=torch.from_numpy(wl.frame_idx()).to(dev))
@@ -120,12 +123,23 @@ def main():
     if wl.kind == "rms_silu":
         codes = torch.empty((wl.m, wl.k // 2), dtype=torch.uint8, device="cuda:0")
         scales = torch.empty((wl.m, wl.k // 16), dtype=torch.uint8, device="cuda:0")
+    elif wl.kind == "ln_fp8":
+        codes, scales = torch.empty((wl.m, wl.k), dtype=torch.uint8, device="cuda:0"), None
     else:
         codes, scales = nq.new_quantized(wl.m, wl.k, "cuda:0")
     amax_dev = torch.zeros(1, dtype=torch.float32, device="cuda:0")
     stream = torch.cuda.current_stream()
 
-    if wl.kind == "rms_silu":
+    if wl.kind == "ln_fp8":
+        act_scale = workloads.fp8_act_scale(wl.name)
+        if a.dynamic:
+            def step():
+                nq.ln_adaln_fp8_dynamic(inp["x"], inp["scale"], inp["shift"], wl.eps, act_scale_out=amax_dev,
+                                        codes=codes, stream=stream)
+        else:
+            def step():
+                nq.ln_adaln_fp8(inp["x"], inp["scale"], inp["shift"], wl.eps, act_scale, codes=codes, stream=stream)
+    elif wl.kind == "rms_silu":
         if a.dynamic:
             def step():
                 nq.rms_silu_nvfp4_dynamic(inp["x"], inp["gamma"], wl.eps, amax_out=amax_dev, codes=codes,
@@ -261,7 +275,9 @@ def main():
         "config": {"workload": wl.name, "rows": wl.m, "hidden": wl.k,
                    "frames": wl.frames if wl.frames else None,
                    "algorithmic_bytes_per_step": alg_bytes,
-                   "global_amax": "per-call (device amax pass)" if a.dynamic else amax},
+                   ("act_scale" if wl.kind == "ln_fp8" else "global_amax"):
+                       "per-call (device amax pass)" if a.dynamic
+                       else (workloads.fp8_act_scale(wl.name) if wl.kind == "ln_fp8" else amax)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic},
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
@@ -287,7 +303,15 @@ def cpu_baseline(wl, amax, rows, np):
     rows = min(rows, wl.m)
     sel = np.arange(rows)
     x = wl.x_rows(sel) if not wl.kind.startswith("residual") else None
-    if wl.kind == "rms_silu":
+    if wl.kind == "ln_fp8":
+        import workloads
+        sc, sh = wl.modulation()
+        act_scale = workloads.fp8_act_scale(wl.name)
+
+        def part(se):
+            s, e = se
+            oracle.ln_adaln_fp8_rows(x[s:e], sc, sh, wl.eps, act_scale=act_scale, want_y=False)
+    elif wl.kind == "rms_silu":
         gamma = wl.weight()
         oracle.silu_table_f16()
 

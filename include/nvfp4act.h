@@ -279,6 +279,48 @@ int rms_silu_nvfp4(const void* x, const void* gamma, float eps, int64_t rows, in
                    float global_amax, void* codes, void* scales, float* rstd_out, void* y_out,
                    void* stream);
 
+/* LayerNorm (fp32 statistics) + adaLN -> per-tensor FP8 E4M3 (FlashRT PR #142,
+   commit notes on fp16_ada_layernorm_quant_fp8: one pass, fp32 LayerNorm
+   statistics, adaLN modulation, one FP8 scale shared by the three projections
+   that read the result; it also feeds the FFN's first projection).  Per row of
+   k elements:
+     mean = sum(x) / k              fp32; the tree of rms_adaln_nvfp4 (lane L
+                                    owns the 8-element chunks L + 64 j, eight
+                                    accumulators, pairwise lane fold, butterfly)
+     var  = sum((x - mean)^2) / k   the same tree, fused multiply-adds
+     rstd = 1 / sqrt(var + eps)
+     y    = (((x - mean) * rstd) * (1 + scale)) + shift   fp32, each op rounded
+     code = E4M3(y * (1 / act_scale)), nearest-even, saturating at +-448, the
+            sign kept (a negative zero or a negative value that rounds to zero
+            gives 0x80)
+     x         [m, k] fp16, row-major, 16-byte aligned
+     scale, shift  [k] fp32 each (the call's adaLN modulation row), 16-byte
+               aligned
+     eps       >= 0 and finite
+     m, k      m >= 0; k a multiple of 512 in [512, 8192]
+     act_scale the static per-tensor scale: finite, > 0, with 1 / act_scale
+               finite
+     codes     [m, k] bytes (8-byte aligned)
+     mean_out, rstd_out  [m] fp32 each, nullable
+     y_out     [m, k] fp32, nullable (16-byte aligned): the pre-quantization y
+   Returns a status. */
+int ln_adaln_fp8(const void* x, const float* scale, const float* shift, float eps, int64_t m,
+                 int64_t k, float act_scale, void* codes, float* mean_out, float* rstd_out,
+                 float* y_out, void* stream);
+
+/* The per-call form of ln_adaln_fp8 (FlashRT PR #142: 2-pass device-side amax
+   then quantize, no host sync): *act_scale_out = 0, an amax pass folds max |y|
+   over all rows into it, a one-thread kernel turns it into act_scale =
+   amax / 448, then ln_adaln_fp8 runs with 1 / act_scale taken on the device
+   (0 when act_scale is 0 or its reciprocal overflows: every code a signed
+   zero).  act_scale_out: one float in device memory (4-byte aligned, required
+   unless m == 0; not written when m == 0); it holds the call's scale afterwards
+   (the dequantization factor of the codes).  Calls that share it and overlap
+   on the device race on it. */
+int ln_adaln_fp8_dynamic(const void* x, const float* scale, const float* shift, float eps,
+                         int64_t m, int64_t k, float* act_scale_out, void* codes, float* mean_out,
+                         float* rstd_out, float* y_out, void* stream);
+
 /* Per-call (dynamic) global amax
    ------------------------------
    The *_dynamic forms take the global amax from the tensor itself instead of

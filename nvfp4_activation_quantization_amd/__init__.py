@@ -24,6 +24,10 @@ each returning ``(codes, scales)``; and the per-call (dynamic) amax forms
                                                           + adaLN (next block's table)
   rms_silu_nvfp4(x, gamma, eps, global_amax)              fp16 channels-last [rows, c]:
                                                           RMSNorm + SiLU, plain scale layout
+  ln_adaln_fp8(x, scale, shift, eps, act_scale)            fp16 [m, k]: LayerNorm (fp32 statistics)
+                                                          + adaLN -> per-tensor FP8 E4M3 codes
+                                                          [m, k]; ln_adaln_fp8_dynamic(x, scale,
+                                                          shift, eps) returns (codes, act_scale)
   swiglu_nvfp4_dynamic(projection), swiglu_packed_nvfp4_dynamic(projection, bias, interleaved),
   residual_rms_nvfp4_dynamic(h, gamma, eps, residual),
   residual_rms_adaln_nvfp4_dynamic(h, weight, table, frame_idx, eps, residual),
@@ -73,6 +77,8 @@ _SIGS = {
                                               _P, _P, _P, _P, _P, _P, _P]),
     "rms_silu_nvfp4": (_I, [_P, _P, _F, _I64, _I64, _F, _P, _P, _P, _P, _P]),
     "rms_silu_nvfp4_dynamic": (_I, [_P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "ln_adaln_fp8": (_I, [_P, _P, _P, _F, _I64, _I64, _F, _P, _P, _P, _P, _P]),
+    "ln_adaln_fp8_dynamic": (_I, [_P, _P, _P, _F, _I64, _I64, _P, _P, _P, _P, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -554,3 +560,44 @@ def rms_silu_nvfp4_dynamic(x: torch.Tensor, gamma: torch.Tensor, eps: float, ama
                                                 "y_out") if y_out is not None else 0,
                                        _stream(stream, x.device)))
     return codes, scales, amax_out
+
+
+def _ln_args(x, scale, shift):
+    if x.dim() != 2:
+        raise ValueError("x must be [m, k]")
+    m, k = x.shape
+    for t, name in ((scale, "scale"), (shift, "shift")):
+        if t.dtype != torch.float32 or t.numel() != k or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("%s must be a contiguous float32 device tensor of k values" % name)
+    return m, k, _f16_ptr(x, "x")
+
+
+def _ln_outs(m, k, device, codes, mean_out, rstd_out, y_out):
+    if codes is None:
+        codes = torch.empty((m, k), dtype=torch.uint8, device=device)
+    return codes, (_out_ptr(codes, torch.uint8, (m, k), "codes"), _out_ptr(mean_out, torch.float32, (m,), "mean_out"),
+                   _out_ptr(rstd_out, torch.float32, (m,), "rstd_out"),
+                   _out_ptr(y_out, torch.float32, (m, k), "y_out"))
+
+
+def ln_adaln_fp8(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float, act_scale: float,
+                 codes=None, mean_out=None, rstd_out=None, y_out=None, stream=None):
+    """fp16 x [m, k]: LayerNorm with fp32 statistics, adaLN (fp32 scale and shift [k]), then
+    per-tensor FP8 E4M3 codes of y / act_scale.  Returns codes [m, k] uint8."""
+    m, k, xp = _ln_args(x, scale, shift)
+    codes, outs = _ln_outs(m, k, x.device, codes, mean_out, rstd_out, y_out)
+    _check(_lib.ln_adaln_fp8(xp, scale.data_ptr(), shift.data_ptr(), float(eps), m, k, float(act_scale), *outs,
+                             _stream(stream, x.device)))
+    return codes
+
+
+def ln_adaln_fp8_dynamic(x: torch.Tensor, scale: torch.Tensor, shift: torch.Tensor, eps: float,
+                         act_scale_out=None, codes=None, mean_out=None, rstd_out=None, y_out=None, stream=None):
+    """ln_adaln_fp8 under this call's own scale max|y| / 448, computed on the device.
+    Returns (codes, act_scale_out) with act_scale_out a one-element float32 device tensor."""
+    m, k, xp = _ln_args(x, scale, shift)
+    codes, outs = _ln_outs(m, k, x.device, codes, mean_out, rstd_out, y_out)
+    act_scale_out, ap = _amax_ptr(act_scale_out, x.device)
+    _check(_lib.ln_adaln_fp8_dynamic(xp, scale.data_ptr(), shift.data_ptr(), float(eps), m, k, ap, *outs,
+                                     _stream(stream, x.device)))
+    return codes, act_scale_out

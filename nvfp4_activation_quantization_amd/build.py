@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libnvfp4act.so")
-SOURCES = ["quantize.hip", "rms_adaln.hip", "swiglu.hip", "residual_rms.hip", "rms_silu.hip", "abi.cpp"]
+SOURCES = ["quantize.hip", "rms_adaln.hip", "swiglu.hip", "residual_rms.hip", "rms_silu.hip", "ln_fp8.hip", "abi.cpp"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

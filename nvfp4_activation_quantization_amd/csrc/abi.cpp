@@ -60,6 +60,7 @@ int current_device(const DeviceInfo** info, int* device_out) {
     if (e == hipSuccess) e = nvfp4act::prepare_swiglu();
     if (e == hipSuccess) e = nvfp4act::prepare_residual_rms();
     if (e == hipSuccess) e = nvfp4act::prepare_rms_silu();
+    if (e == hipSuccess) e = nvfp4act::prepare_ln_fp8();
     if (e != hipSuccess) {
       st.probed = false;
       return fail_hip(e);
@@ -417,6 +418,40 @@ int rms_silu_call(const void* x, const void* gamma, float eps, int64_t rows, int
   return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
 }
 
+bool ln_shape_ok(int64_t m, int64_t k) { return m >= 0 && k >= 512 && k % 512 == 0 && k <= nvfp4act::kMaxLnK; }
+
+int ln_fp8_call(const void* x, const float* scale, const float* shift, float eps, int64_t m, int64_t k,
+                float act_scale, float* scale_dev, void* codes, float* mean_out, float* rstd_out, float* y_out,
+                void* stream) {
+  if (!ln_shape_ok(m, k)) return NVFP4ACT_ERR_SHAPE;
+  if (m == 0) return NVFP4ACT_OK;
+  if (!x || !scale || !shift || !codes) return NVFP4ACT_ERR_NULL;
+  if (!aligned16(x) || !aligned16(scale) || !aligned16(shift) || (reinterpret_cast<uintptr_t>(codes) & 7u) ||
+      (y_out && !aligned16(y_out)) || (mean_out && !aligned4(mean_out)) || (rstd_out && !aligned4(rstd_out)))
+    return NVFP4ACT_ERR_ALIGN;
+  if (!std::isfinite(eps) || eps < 0.0f) return NVFP4ACT_ERR_VALUE;
+  if (!scale_dev && (!std::isfinite(act_scale) || !(act_scale > 0.0f) || !std::isfinite(1.0f / act_scale)))
+    return NVFP4ACT_ERR_VALUE;
+  const DeviceInfo* info = nullptr;
+  int st = current_device(&info, nullptr);
+  if (st != NVFP4ACT_OK) return st;
+  nvfp4act::LnFp8Launch p{};
+  p.x = x;
+  p.scale = scale;
+  p.shift = shift;
+  p.eps = eps;
+  p.m = m;
+  p.k = k;
+  p.act_scale = act_scale;
+  p.scale_dev = scale_dev;
+  p.codes = codes;
+  p.mean_out = mean_out;
+  p.rstd_out = rstd_out;
+  p.y_out = y_out;
+  hipError_t e = nvfp4act::launch_ln_fp8(p, *info, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
+}
+
 // The per-call forms need the amax destination: one 4-byte aligned float (m == 0 aside).
 int check_amax_out(int64_t m, const float* amax_out) {
   if (m == 0) return NVFP4ACT_OK;
@@ -537,6 +572,20 @@ int rms_silu_nvfp4_dynamic(const void* x, const void* gamma, float eps, int64_t 
   int st = check_amax_out(rows, amax_out);
   if (st != NVFP4ACT_OK) return st;
   return rms_silu_call(x, gamma, eps, rows, c, 0.0f, amax_out, codes, scales, rstd_out, y_out, stream);
+}
+
+int ln_adaln_fp8(const void* x, const float* scale, const float* shift, float eps, int64_t m, int64_t k,
+                 float act_scale, void* codes, float* mean_out, float* rstd_out, float* y_out, void* stream) {
+  return ln_fp8_call(x, scale, shift, eps, m, k, act_scale, nullptr, codes, mean_out, rstd_out, y_out, stream);
+}
+
+int ln_adaln_fp8_dynamic(const void* x, const float* scale, const float* shift, float eps, int64_t m, int64_t k,
+                         float* act_scale_out, void* codes, float* mean_out, float* rstd_out, float* y_out,
+                         void* stream) {
+  if (!ln_shape_ok(m, k)) return NVFP4ACT_ERR_SHAPE;
+  int st = check_amax_out(m, act_scale_out);
+  if (st != NVFP4ACT_OK) return st;
+  return ln_fp8_call(x, scale, shift, eps, m, k, 0.0f, act_scale_out, codes, mean_out, rstd_out, y_out, stream);
 }
 
 }  // extern "C"

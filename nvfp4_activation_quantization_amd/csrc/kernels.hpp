@@ -117,11 +117,33 @@ struct RmsSiluLaunch {
 
 hipError_t launch_rms_silu(const RmsSiluLaunch& p, const DeviceInfo& dev, hipStream_t stream);
 
+// The arguments of one ln_adaln_fp8 call (see include/nvfp4act.h): x [m, k] fp16, scale and
+// shift [k] fp32; codes [m, k] E4M3 bytes.  scale_dev: null for the static act_scale; else
+// the device float that receives this call's scale max|y| / 448 (an amax pass runs first).
+struct LnFp8Launch {
+  const void* x;
+  const float* scale;
+  const float* shift;
+  float eps;
+  int64_t m, k;
+  float act_scale;
+  float* scale_dev;
+  void* codes;
+  float* mean_out;
+  float* rstd_out;
+  float* y_out;
+};
+
+constexpr int64_t kMaxLnK = 8192;   // the row is held in registers
+
+hipError_t launch_ln_fp8(const LnFp8Launch& p, const DeviceInfo& dev, hipStream_t stream);
+
 // Per-device, once: allow the LDS sizes the kernels use.
 hipError_t prepare_rms_adaln();
 hipError_t prepare_swiglu();
 hipError_t prepare_residual_rms();
 hipError_t prepare_rms_silu();
+hipError_t prepare_ln_fp8();
 
 // Build the SiLU table of the current device and wait for it; *ambiguous receives the
 // number of entries whose rounding fp64 could not decide (0 expected).

@@ -565,12 +565,23 @@ def fp8_inverse_scale(act_scale: float) -> float:
     return _load().orc_fp8_inverse_scale(float(act_scale))
 
 
+def fp8_dynamic_scale(amax: float) -> float:
+    """The per-call FP8 scale amax / 448 (fp32)."""
+    return _load().orc_fp8_dynamic_scale(float(amax))
+
+
+def fp8_dynamic_inverse(act_scale: float) -> float:
+    """1 / act_scale, or 0 when act_scale is 0 or the reciprocal overflows."""
+    return _load().orc_fp8_dynamic_inverse(float(act_scale))
+
+
 def ln_adaln_fp8_rows(x_u16, scale_f32, shift_f32, eps: float, act_scale: float | None = None,
-                      inv_scale: float | None = None):
+                      inv_scale: float | None = None, want_y: bool = True):
     """LayerNorm (fp32 statistics) + adaLN -> per-tensor FP8 E4M3 over fp16 rows [n, k].
 
     act_scale: the static per-tensor scale (codes = E4M3(y * (1 / act_scale))); or pass
-    inv_scale directly.  Returns dict(codes [n, k] u8, mean [n], rstd [n], y [n, k] fp32).
+    inv_scale directly.  Returns dict(codes [n, k] u8, mean [n], rstd [n], y [n, k] fp32,
+    or None without want_y).
     """
     x = _c(x_u16, np.uint16)
     n, k = x.shape
@@ -582,9 +593,9 @@ def ln_adaln_fp8_rows(x_u16, scale_f32, shift_f32, eps: float, act_scale: float 
     codes = np.empty((n, k), np.uint8)
     mean = np.empty(n, np.float32)
     rstd = np.empty(n, np.float32)
-    y = np.empty((n, k), np.float32)
+    y = np.empty((n, k), np.float32) if want_y else None
     _load().orc_ln_adaln_fp8_rows(_ptr(x), _ptr(sc), _ptr(sh), float(eps), n, k, inv, _ptr(codes), _ptr(mean),
-                                  _ptr(rstd), _ptr(y))
+                                  _ptr(rstd), _ptr(y) if want_y else None)
     return dict(codes=codes, mean=mean, rstd=rstd, y=y)
 
 
@@ -593,8 +604,8 @@ def ln_adaln_fp8_dynamic(x_u16, scale_f32, shift_f32, eps: float):
     quantizer with 1 / act_scale (0 when the scale is 0).  Adds 'amax' and 'act_scale'."""
     first = ln_adaln_fp8_rows(x_u16, scale_f32, shift_f32, eps, inv_scale=1.0)
     amax = float(np.abs(first["y"]).max()) if first["y"].size else 0.0
-    act = _load().orc_fp8_dynamic_scale(amax)
-    inv = _load().orc_fp8_dynamic_inverse(act)
+    act = fp8_dynamic_scale(amax)
+    inv = fp8_dynamic_inverse(act)
     out = ln_adaln_fp8_rows(x_u16, scale_f32, shift_f32, eps, inv_scale=inv)
     out["amax"], out["act_scale"] = amax, act
     return out

@@ -215,6 +215,37 @@ def test_rms_silu_status_codes(dynamic):
         assert rs(amax=float("nan")) == 4
 
 
+def ln(dynamic=False, **kw):
+    a = dict(x=A, scale=A, shift=A, eps=1e-6, m=4, k=7168, act=0.25, act_out=A, codes=A, mean=None, rstd=None,
+             y=None)
+    a.update(kw)
+    f = ctypes.c_float(a["eps"])
+    if dynamic:
+        return lib.ln_adaln_fp8_dynamic(a["x"], a["scale"], a["shift"], f, a["m"], a["k"], a["act_out"], a["codes"],
+                                        a["mean"], a["rstd"], a["y"], None)
+    return lib.ln_adaln_fp8(a["x"], a["scale"], a["shift"], f, a["m"], a["k"], a["act"], a["codes"], a["mean"],
+                            a["rstd"], a["y"], None)
+
+
+@pytest.mark.parametrize("dynamic", [False, True])
+def test_ln_fp8_status_codes(dynamic):
+    for key in ("x", "scale", "shift", "codes"):
+        assert ln(dynamic, **{key: None}) == 1, key
+    for k in (0, 256, 520, 7000, 8704, -512):
+        assert ln(dynamic, k=k) == 2, k
+    assert ln(dynamic, m=-1) == 2
+    assert ln(dynamic, x=U) == 3 and ln(dynamic, scale=U) == 3 and ln(dynamic, shift=U) == 3
+    assert ln(dynamic, codes=A + 4) == 3 and ln(dynamic, y=U) == 3
+    assert ln(dynamic, mean=A + 2) == 3 and ln(dynamic, rstd=A + 2) == 3
+    assert ln(dynamic, eps=-1.0) == 4 and ln(dynamic, eps=float("inf")) == 4
+    assert ln(dynamic, m=0) == 0
+    if dynamic:
+        assert ln(True, act_out=None) == 1 and ln(True, act_out=A + 2) == 3
+    else:
+        for bad in (0.0, -1.0, float("nan"), float("inf"), 1e-39):
+            assert ln(act=bad) == 4, bad
+
+
 def torch_has_gpu():
     import torch
     return torch.cuda.is_available()
@@ -229,6 +260,7 @@ def test_valid_call_without_a_gpu_reports_no_device():
     assert rr() == 5 and rr(bias=None) == 5 and rr(True) == 5
     assert fold() == 5 and fold(o=None, gate=None) == 5 and fold(True) == 5
     assert rs() == 5 and rs(c=96) == 5 and rs(True) == 5
+    assert ln() == 5 and ln(k=512) == 5 and ln(k=8192) == 5 and ln(True) == 5
     assert lib.nvfp4act_init() == 5
 
 

@@ -162,3 +162,31 @@ def first_mismatch(a: np.ndarray, b: np.ndarray) -> str:
         return "equal"
     i = tuple(d[0])
     return "%d mismatches; first at %s: got %r want %r" % (len(d), i, a[i], b[i])
+
+
+def oracle_ln_fp8(x, scale, shift, eps, inv_scale, want_y=True):
+    """oracle.ln_adaln_fp8_rows (codes under inv_scale) over row blocks in parallel threads."""
+    n = x.shape[0]
+
+    def part(se):
+        s, e = se
+        return oracle.ln_adaln_fp8_rows(x[s:e], scale, shift, eps, inv_scale=inv_scale, want_y=want_y)
+
+    with ThreadPoolExecutor(threads()) as ex:
+        res = list(ex.map(part, split_rows(n, 4 * threads())))
+    out = {key: np.concatenate([r[key] for r in res]) for key in ("codes", "mean", "rstd")}
+    out["y"] = np.concatenate([r["y"] for r in res]) if want_y else None
+    return out
+
+
+def oracle_ln_fp8_amax(x, scale, shift, eps) -> float:
+    """max |y| of the LayerNorm + adaLN output over all rows (the per-call amax), by blocks."""
+    n = x.shape[0]
+
+    def part(se):
+        s, e = se
+        y = oracle.ln_adaln_fp8_rows(x[s:e], scale, shift, eps, inv_scale=1.0)["y"]
+        return float(np.abs(y).max()) if y.size else 0.0
+
+    with ThreadPoolExecutor(threads()) as ex:
+        return max(ex.map(part, split_rows(n, 16 * threads())), default=0.0)
