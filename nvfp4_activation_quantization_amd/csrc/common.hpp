@@ -293,6 +293,16 @@ __device__ __forceinline__ uint2 load_stream(const uint2* p) {
   return make_uint2(v.x, v.y);
 }
 
+__device__ __forceinline__ void store_stream(uint2* p, const uint2& v) {
+  const u32x2 w = {v.x, v.y};
+  __builtin_nontemporal_store(w, reinterpret_cast<NVFP4_GLOBAL u32x2*>(global_ptr(p)));
+}
+
+__device__ __forceinline__ void store_stream(float4* p, const float4& v) {
+  const u32x4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+  __builtin_nontemporal_store(w, reinterpret_cast<NVFP4_GLOBAL u32x4*>(global_ptr(p)));
+}
+
 // ---- workgroup -> row-group mapping ----------------------------------------------------
 
 // A workgroup of four wavefronts owns the rows r, r + 32, r + 64, r + 96 of a 128-row tile

@@ -12,7 +12,7 @@
 //
 // One workgroup of 8 wavefronts per CU, persistent over rows (wavefront w of workgroup b
 // takes rows 8b + w, 8b + w + 8 G, ... for a grid of G workgroups, so the rows in flight
-// at any time are consecutive).  bf16-free: the only parameters are two fp32 vectors,
+// at any time are consecutive); codes and y are written with non-temporal stores.  bf16-free: the only parameters are two fp32 vectors,
 // 1 + scale (computed once) and shift, staged in LDS as float2 planes (consecutive across
 // the wavefront: each ds_read_b64 covers 512 contiguous bytes).  Each wavefront keeps its
 // row unpacked in registers from the statistics to the output pass and prefetches the
@@ -137,16 +137,26 @@ __global__ __launch_bounds__(kThreads) void ln_fp8_kernel(const LnArgs a) {
   // this iteration's loads were waited for: the wait then sits in straight-line code after
   // the row's stores and can leave them in flight (at the loop head it would also cover
   // the stores).
+  //
+  // The eight wavefronts of a workgroup take the same number of iterations (that of
+  // wavefront 0) and meet at a barrier after each, so that they keep working on eight
+  // consecutive rows: left to drift apart they spread the rows in flight over the tensor,
+  // which costs HBM efficiency.  A wavefront whose row is past the end recomputes row
+  // m - 1 and stores the same bytes as the wavefront that owns it.
   float xf[CPL][8];
   float acc[8];
   unpack_sum(xr, xf, acc);
   float lane_amax = 0.0f;
-  for (int64_t r = first; r < m; r += stride) {
+  const int64_t wg_first = (int64_t)blockIdx.x * kWaves;
+  const int64_t iters = wg_first < m ? (m - wg_first + stride - 1) / stride : 0;
+  for (int64_t it = 0; it < iters; ++it) {
+    const int64_t r_own = first + it * stride;
+    const int64_t r = r_own < m ? r_own : m - 1;
     // wide rows: keep the parameters in LDS rather than let them be hoisted into registers
     if constexpr (CPL >= 5) asm volatile("" ::: "memory");
     // the next row of this wavefront, in flight during the rest of this one
     {
-      const int64_t rn = (r + stride < m) ? r + stride : m - 1;
+      const int64_t rn = (r_own + stride < m) ? r_own + stride : m - 1;
 #pragma unroll
       for (int j = 0; j < CPL; ++j) xr[j] = load_stream(a.x + rn * kChunks + lane + kWave * j);
     }
@@ -189,15 +199,16 @@ __global__ __launch_bounds__(kThreads) void ln_fp8_kernel(const LnArgs a) {
       }
       const uint32_t lo = fp8_quad(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv);
       const uint32_t hi = fp8_quad(y[4] * inv, y[5] * inv, y[6] * inv, y[7] * inv);
-      global_ptr(a.codes)[r * kChunks + c] = make_uint2(lo, hi);
+      store_stream(a.codes + r * kChunks + c, make_uint2(lo, hi));
       if (MODE == kCodesAndY) {
-        global_ptr(a.y_out)[2 * (r * kChunks + c)] = make_float4(y[0], y[1], y[2], y[3]);
-        global_ptr(a.y_out)[2 * (r * kChunks + c) + 1] = make_float4(y[4], y[5], y[6], y[7]);
+        store_stream(a.y_out + 2 * (r * kChunks + c), make_float4(y[0], y[1], y[2], y[3]));
+        store_stream(a.y_out + 2 * (r * kChunks + c) + 1, make_float4(y[4], y[5], y[6], y[7]));
       }
     }
     // the old row's registers are free before the next row is unpacked into them
     __builtin_amdgcn_sched_barrier(0);
     unpack_sum(xr, xf, acc);
+    __builtin_amdgcn_s_barrier();
   }
   if (AMAX) workgroup_max_to(a.amax_out, lane_amax, amax_red, kWaves);
 }
