@@ -649,7 +649,9 @@ def test_rms_f16row_tree_over_padded_slots():
 
 
 def test_rms_silu_chain_matches_torch_eager_ops():
-    x, gamma = _rms_silu_case(61)
+    # 2048 rows: enough elements (~390k) that some fp32 products x * rstd round onto an fp16
+    # midpoint, where one fused rounding to fp16 would differ from the two of the chain
+    x, gamma = _rms_silu_case(61, n=2048)
     res = oracle.rms_silu_rows(x, gamma, 1e-6, 4.0, want_y=True)
     H = torch.float16
     xt = torch.from_numpy(x.view(np.int16).copy()).view(H)
@@ -751,6 +753,32 @@ def test_ln_statistics():
     c = oracle.f16_round(np.full((1, 512), 1.5, np.float32))
     r = oracle.ln_adaln_fp8_rows(c, np.zeros(512, np.float32), np.zeros(512, np.float32), 0.25, 1.0)
     assert r["mean"][0] == 1.5 and r["rstd"][0] == 2.0 and not np.any(r["codes"] & 0x7F)
+
+
+def test_ln_statistics_follow_the_documented_trees():
+    """Hand-derived rows (k = 512, one chunk per lane; k = 1024 for the variance) whose mean
+    and variance tell the documented trees from other orders.  Mean: 2048 in lane 0 with two
+    2^-13 (half an fp32 ulp of 2048: alone each is lost, tie to even) where the tree pairs them
+    first (elements 2 and 3 of lane 0; lanes 2 and 3) or not (lanes 1 and 3; elements 1 and 2).
+    Variance: 64 and -64 in lane 0 (chunks 0 and 64) and +-2^-6 likewise in lanes 2 and 3, so
+    the mean is exactly 0; the squares' tree gives 8192 + 2^-10, a left-to-right sum 8192."""
+    zeros = np.zeros(1024, np.float32)
+
+    def mean_of(smalls):
+        v = np.zeros((1, 512), np.float32)
+        v[0, 0] = 2048.0
+        v[0, smalls] = 2.0 ** -13
+        r = oracle.ln_adaln_fp8_rows(oracle.f16_round(v), zeros[:512], zeros[:512], 0.0, 1.0)
+        return r["mean"][0]
+    lost, kept = np.float32(2048.0 / 512), np.float32((2048.0 + 2.0 ** -12) / 512)
+    assert mean_of([2, 3]) == kept and mean_of([16, 24]) == kept
+    assert mean_of([1, 2]) == lost and mean_of([8, 24]) == lost
+    v = np.zeros((1, 1024), np.float32)
+    v[0, 0], v[0, 512] = 64.0, -64.0
+    v[0, 16], v[0, 528], v[0, 24], v[0, 536] = 2.0 ** -6, -(2.0 ** -6), 2.0 ** -6, -(2.0 ** -6)
+    r = oracle.ln_adaln_fp8_rows(oracle.f16_round(v), zeros, zeros, 0.0, 1.0)
+    assert r["mean"][0] == 0.0
+    assert r["rstd"][0] == np.float32(1.0) / np.sqrt(np.float32(8.0 + 2.0 ** -20))
 
 
 def test_ln_adaln_chain_and_codes_match_torch_eager_ops():
