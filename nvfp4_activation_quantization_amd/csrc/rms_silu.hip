@@ -17,7 +17,11 @@
 //
 // One 1024-thread workgroup per CU, persistent over groups of rows; the 128 KiB fp16 SiLU
 // table (built once per device in fp64, like the bf16 one) is copied into LDS; each lane's
-// 8 gamma values stay in registers (a lane's chunk index never changes).
+// 8 gamma values stay in registers (a lane's chunk index never changes).  The kernel is
+// bound by its instruction count, so the per-element work is kept small: the statistic's
+// pairs as fused multiply-adds (squares of fp16 values are exact), one reciprocal square
+// root for four row groups, fp16(nn * gamma) as a packed fp16 multiply (exact products),
+// table addresses as one shift each, wave-uniform output bases with 32-bit lane offsets.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -93,6 +97,27 @@ __device__ __forceinline__ uint32_t f16_bits(float f) {
 }
 __device__ __forceinline__ float round_f16(float f) { return (float)(_Float16)f; }
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+
+// base + off bytes, in the global address space (a wave-uniform base and a 32-bit lane offset
+// let the compiler use the scalar-base addressing form)
+template <typename T>
+__device__ __forceinline__ NVFP4_GLOBAL T* at_byte(T* base, uint32_t off) {
+  return reinterpret_cast<NVFP4_GLOBAL T*>(reinterpret_cast<NVFP4_GLOBAL char*>(global_ptr(base)) + off);
+}
+template <typename T>
+__device__ __forceinline__ const NVFP4_GLOBAL T* at_byte(const T* base, uint32_t off) {
+  return reinterpret_cast<const NVFP4_GLOBAL T*>(reinterpret_cast<const NVFP4_GLOBAL char*>(global_ptr(base)) + off);
+}
+
+// The value of lane (L & ~3) + I of each quad, on every lane of the quad (DPP broadcast).
+template <int I>
+__device__ __forceinline__ float quad_lane(float v) {
+  constexpr int sel = I | (I << 2) | (I << 4) | (I << 6);
+  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)__float_as_uint(v), (int)__float_as_uint(v),
+                                                               sel, 0xF, 0xF, false));
+}
+
 // Butterfly sum over the S lanes of a row (distances 1 .. S/2; S = 16, 32 or 64), as
 // lane_sum_butterfly for the first log2(S) steps.
 template <int S>
@@ -134,90 +159,155 @@ struct RsArgs {
   uint4* y_out;             // [rows, c] fp16
 };
 
-// S: slots (lanes) per row.  AMAX: the amax pass -- the same chain, no stores.
-template <int S, bool AMAX>
+enum Mode { kAmaxPass = 0, kCodes = 1, kCodesAndSide = 2 };
+
+// The S-lane row slots of one row group: loads of kUnroll groups of a wavefront.  Group g
+// (clamped to the last group: a wavefront past the end redoes it and stores the same bytes)
+// covers rows g R .. g R + R - 1; a slot past the last row reads (and later writes) that
+// row again.
+template <int S>
+__device__ __forceinline__ void load_groups(const RsArgs& a, int64_t g_first, int64_t last_group, int sub,
+                                            int eff, uint4 (&v)[kUnroll]) {
+  constexpr int R = kWave / S;
+  const int chunks = (int)(a.c >> 3);
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t g = g_first + u < last_group ? g_first + u : last_group;
+    const int64_t r0 = g * R;                                             // wave-uniform
+    const int64_t lim = a.rows - 1 - r0;                                  // >= 0
+    const int limc = lim < R - 1 ? (int)lim : R - 1;                      // wave-uniform
+    const uint32_t off = __umul24((uint32_t)(sub < limc ? sub : limc), (uint32_t)chunks) + eff;   // < 2^24
+    v[u] = load_stream(at_byte(a.x + r0 * chunks, off * 16u));
+  }
+}
+
+// S: slots (lanes) per row.  MODE: the amax pass (the same chain, no stores), codes and
+// scales, or also the nullable rstd_out / y_out.
+//
+// Every lane does the same work: a lane whose slot lies past the row's c/8 chunks takes the
+// chunk (slot mod c/8) -- same parity, so block partners stay partners -- but adds 0 to the
+// statistic, and so computes and stores exactly what the lane owning that chunk does.  Both
+// lanes of a block store its scale byte.  The loop body therefore has no divergent branch,
+// which would make the compiler wait for every outstanding store before the next loads are
+// used (vmcnt counts stores too).
+//
+// The 16 wavefronts of a workgroup take consecutive groups (kUnroll per wavefront, 64 per
+// workgroup step; workgroups interleave), run the same number of steps and meet at a
+// barrier after each, so the rows in flight stay compact; the next step's groups are loaded
+// before the current ones are computed.
+template <int S, int MODE>
 __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
-  constexpr int R = kWave / S;             // rows per wavefront step
+  constexpr bool AMAX = MODE == kAmaxPass;
+  constexpr int R = kWave / S;             // rows per wavefront group
+  constexpr int kStepGroups = kWaves * kUnroll;
+  // static LDS, so that every address is known when compiling: a lookup is then one shift
+  // of the pattern plus an immediate offset
+  __shared__ uint4 lds4[kTableBytes / 16];
   __shared__ float inv_tab[128];
   __shared__ float amax_red[kWaves];
-  extern __shared__ uint4 lds4[];
   const uint16_t* table = reinterpret_cast<const uint16_t*>(lds4);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int chunk = lane % S, sub = lane / S;
-  const int64_t chunks = a.c >> 3;
+  const int chunks = (int)(a.c >> 3);
   const bool lane_ok = chunk < chunks;
+  const int eff = lane_ok ? chunk : chunk % chunks;
+
+  const int64_t groups = (a.rows + R - 1) / R;
+  const int64_t last_group = groups - 1;
+  const int64_t span = (int64_t)gridDim.x * kStepGroups;
+  const int64_t wg_first = (int64_t)blockIdx.x * kStepGroups;
+  const int64_t steps = wg_first < groups ? (groups - wg_first + span - 1) / span : 0;
+  const int64_t my_first = wg_first + wave * kUnroll;
+
+  uint4 cur[kUnroll];
+  load_groups<S>(a, my_first, last_group, sub, eff, cur);
 
   const float gsf = call_global_scale(a.global_amax, a.amax_dev);
   if (!AMAX) fill_inverse_table(inv_tab, gsf, tid);
   const uint4* src = reinterpret_cast<const uint4*>(g_silu16_table);
   for (int i = tid; i < (int)(kTableBytes / 16); i += kThreads) lds4[i] = src[i];
-  uint4 gv = make_uint4(0, 0, 0, 0);
-  if (lane_ok) gv = global_ptr(a.gamma)[chunk];
-  const float g8[8] = {f16_lo(gv.x), f16_hi(gv.x), f16_lo(gv.y), f16_hi(gv.y),
-                       f16_lo(gv.z), f16_hi(gv.z), f16_lo(gv.w), f16_hi(gv.w)};
+  const uint4 gv = global_ptr(a.gamma)[eff];
+  const h2 g2[4] = {__builtin_bit_cast(h2, gv.x), __builtin_bit_cast(h2, gv.y), __builtin_bit_cast(h2, gv.z),
+                    __builtin_bit_cast(h2, gv.w)};
   __syncthreads();
 
   float lane_amax = 0.0f;
-  const int64_t groups = (a.rows + R - 1) / R;
-  const int64_t step = (int64_t)gridDim.x * kWaves;
-  // per-lane offsets within a row group (32-bit); the group's base is wave-uniform
-  const int lane_chunk = sub * (int)chunks + chunk;
-  const int lane_block = sub * (int)(a.c >> 4) + (chunk >> 1);
-  for (int64_t g0 = (int64_t)blockIdx.x * kWaves + wave; g0 < groups; g0 += step * kUnroll) {
-    uint4 v[kUnroll];
+  const int blocks = (int)(a.c >> 4);
+  for (int64_t st = 0; st < steps; ++st) {
+    const int64_t g_first = my_first + st * span;
+    uint4 nxt[kUnroll];
+    load_groups<S>(a, g_first + span, last_group, sub, eff, nxt);
+    // the four groups' statistics: one reciprocal square root for all of them (lane L
+    // works on group L % 4's sum, then each quad hands group u's result to its lanes)
+    float x8[kUnroll][8];
+    float sums[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t r0 = (g0 + step * u) * R;                        // wave-uniform
-      const int64_t r = r0 + sub;
-      v[u] = (lane_ok && r < a.rows) ? load_stream(a.x + r0 * chunks + lane_chunk) : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t r0 = (g0 + step * u) * R;
-      const int64_t r = r0 + sub;
-      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      float x8[8];
+      const uint32_t w[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        x8[2 * q] = f16_lo(w[q]);
-        x8[2 * q + 1] = f16_hi(w[q]);
+        x8[u][2 * q] = f16_lo(w[q]);
+        x8[u][2 * q + 1] = f16_hi(w[q]);
       }
-      float sq[8];
+      // squares of fp16 values are exact in fp32, so sq0 + sq1 == fma(x0, x0, sq1)
+      float pr[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sq[e] = x8[e] * x8[e];         // exact for fp16 inputs
-      const float lane_v = ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
-      const float sum = slot_sum_butterfly<S>(lane_v);
-      const float rstd = 1.0f / sqrtf(sum / (float)a.c + a.eps);
+      for (int e = 0; e < 4; ++e)
+        pr[e] = __builtin_fmaf(x8[u][2 * e], x8[u][2 * e], x8[u][2 * e + 1] * x8[u][2 * e + 1]);
+      float lane_v = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      lane_v = lane_ok ? lane_v : 0.0f;
+      sums[u] = slot_sum_butterfly<S>(lane_v);
+    }
+    static_assert(kUnroll == 4, "one group per lane of a quad");
+    const int q = lane & 3;
+    const float mine = q == 0 ? sums[0] : q == 1 ? sums[1] : q == 2 ? sums[2] : sums[3];
+    const float rq = 1.0f / sqrtf(mine / (float)a.c + a.eps);
+    const float rstds[kUnroll] = {quad_lane<0>(rq), quad_lane<1>(rq), quad_lane<2>(rq), quad_lane<3>(rq)};
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t g = g_first + u < last_group ? g_first + u : last_group;
+      const int64_t r0 = g * R;
+      const int64_t lim = a.rows - 1 - r0;
+      const int limc = lim < R - 1 ? (int)lim : R - 1;        // wave-uniform
+      const int rs = sub < limc ? sub : limc;                 // this lane's row, r0 + rs
+      const float rstd = rstds[u];
       float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 8; e += 2) {
         // the product rounded to fp32 first, then to fp16: without the opaque step the
         // compiler forms one v_fma_mix (a single rounding of the exact product to fp16)
-        float p = x8[e] * rstd;
-        asm volatile("" : "+v"(p));
-        const float nn = round_f16(p);
-        const uint32_t ab = f16_bits(nn * g8[e]);
-        y[e] = (float)__builtin_bit_cast(_Float16, table[ab]);
+        float p0 = x8[u][e] * rstd, p1 = x8[u][e + 1] * rstd;
+        asm volatile("" : "+v"(p0), "+v"(p1));
+        // fp16(nn * gamma): the product of two fp16 values is exact in fp32, so its fp16
+        // rounding is the fp16 multiply's (one v_pk_mul_f16 for the pair)
+        h2 nn;
+        nn.x = (_Float16)p0;
+        nn.y = (_Float16)p1;
+        const uint32_t ab = __builtin_bit_cast(uint32_t, nn * g2[e / 2]);
+        y[e] = (float)__builtin_bit_cast(_Float16, table[ab & 0xFFFFu]);
+        y[e + 1] = (float)__builtin_bit_cast(_Float16, table[ab >> 16]);
       }
-      const bool row_ok = r < a.rows;
       if (AMAX) {
-        if (row_ok && lane_ok) lane_amax = fold_abs8(lane_amax, y);
+        lane_amax = fold_abs8(lane_amax, y);
         continue;
       }
       uint32_t s;
       const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
-      if (row_ok && lane_ok) {
-        global_ptr(a.codes + r0 * chunks)[lane_chunk] = code;
-        if ((chunk & 1) == 0) global_ptr(a.scales + r0 * (a.c >> 4))[lane_block] = (uint8_t)s;
-        if (chunk == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
+      *at_byte(a.codes + r0 * chunks, (__umul24((uint32_t)rs, (uint32_t)chunks) + eff) * 4u) = code;
+      *at_byte(a.scales + r0 * blocks, __umul24((uint32_t)rs, (uint32_t)blocks) + (eff >> 1)) = (uint8_t)s;
+      if (MODE == kCodesAndSide) {
+        if (a.rstd_out) global_ptr(a.rstd_out)[r0 + rs] = rstd;
         if (a.y_out)
-          global_ptr(a.y_out + r0 * chunks)[lane_chunk] =
+          global_ptr(a.y_out + r0 * chunks)[rs * chunks + eff] =
               make_uint4(f16_bits(y[0]) | (f16_bits(y[1]) << 16), f16_bits(y[2]) | (f16_bits(y[3]) << 16),
                          f16_bits(y[4]) | (f16_bits(y[5]) << 16), f16_bits(y[6]) | (f16_bits(y[7]) << 16));
       }
     }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
+    __builtin_amdgcn_s_barrier();
   }
   if (AMAX) workgroup_max_to(a.amax_out, lane_amax, amax_red, kWaves);
 }
@@ -226,9 +316,12 @@ template <int S, bool AMAX>
 hipError_t launch_s(const RsArgs& a, const DeviceInfo& dev, hipStream_t stream) {
   constexpr int R = kWave / S;
   const int64_t groups = (a.rows + R - 1) / R;
-  int64_t grid = (groups + kWaves - 1) / kWaves;
+  int64_t grid = (groups + kWaves * kUnroll - 1) / (kWaves * kUnroll);
   if (grid > dev.cu_count) grid = dev.cu_count;
-  hipLaunchKernelGGL((rms_silu_kernel<S, AMAX>), dim3((uint32_t)grid), dim3(kThreads), kTableBytes, stream, a);
+  const dim3 g((uint32_t)grid), b(kThreads);
+  if (AMAX) hipLaunchKernelGGL((rms_silu_kernel<S, kAmaxPass>), g, b, 0, stream, a);
+  else if (a.rstd_out || a.y_out) hipLaunchKernelGGL((rms_silu_kernel<S, kCodesAndSide>), g, b, 0, stream, a);
+  else hipLaunchKernelGGL((rms_silu_kernel<S, kCodes>), g, b, 0, stream, a);
   return hipGetLastError();
 }
 
@@ -240,10 +333,10 @@ hipError_t launch_pass(const RsArgs& a, const DeviceInfo& dev, hipStream_t strea
   return launch_s<64, AMAX>(a, dev, stream);
 }
 
-template <int S, bool AMAX>
+template <int S, int MODE>
 hipError_t allow_lds_s() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&rms_silu_kernel<S, AMAX>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kTableBytes);
+  (void)&rms_silu_kernel<S, MODE>;   // static LDS only: nothing to allow
+  return hipSuccess;
 }
 
 }  // namespace
@@ -261,12 +354,16 @@ hipError_t build_silu16_table(unsigned int* ambiguous) {
 }
 
 hipError_t prepare_rms_silu() {
-  hipError_t e = allow_lds_s<16, false>();
-  if (e == hipSuccess) e = allow_lds_s<16, true>();
-  if (e == hipSuccess) e = allow_lds_s<32, false>();
-  if (e == hipSuccess) e = allow_lds_s<32, true>();
-  if (e == hipSuccess) e = allow_lds_s<64, false>();
-  if (e == hipSuccess) e = allow_lds_s<64, true>();
+  hipError_t e = hipSuccess;
+  if (e == hipSuccess) e = allow_lds_s<16, kAmaxPass>();
+  if (e == hipSuccess) e = allow_lds_s<16, kCodes>();
+  if (e == hipSuccess) e = allow_lds_s<16, kCodesAndSide>();
+  if (e == hipSuccess) e = allow_lds_s<32, kAmaxPass>();
+  if (e == hipSuccess) e = allow_lds_s<32, kCodes>();
+  if (e == hipSuccess) e = allow_lds_s<32, kCodesAndSide>();
+  if (e == hipSuccess) e = allow_lds_s<64, kAmaxPass>();
+  if (e == hipSuccess) e = allow_lds_s<64, kCodes>();
+  if (e == hipSuccess) e = allow_lds_s<64, kCodesAndSide>();
   return e;
 }
 
