@@ -36,6 +36,7 @@ constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr size_t kTableBytes = 65536 * sizeof(uint16_t);
 constexpr int kUnroll = 4;                 // row groups per wavefront in flight
+constexpr int64_t kPieceRows = 1 << 30;    // rows per launch (row groups are numbered in 32 bits)
 
 // Round hi + lo to fp16, nearest-even (quantum 2^(E-10) for 2^E <= |v| < 2^(E+1), E >= -14,
 // subnormal quantum 2^-24; infinity from 65520 up).  lo only breaks an exact tie of hi; a
@@ -99,6 +100,26 @@ __device__ __forceinline__ float round_f16(float f) { return (float)(_Float16)f;
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
+// fp16 half (HI: the high one) of w, exactly widened, times f, one IEEE fp32 rounding
+// (v_fma_mix_f32 with a -0 addend, which leaves every product, signed zeros included,
+// unchanged): the widening of the fp16 input costs no instruction of its own.
+template <bool HI>
+__device__ __forceinline__ float mul_f16_f32(uint32_t w, float f) {
+  float d;
+  if (HI) asm("v_fma_mix_f32 %0, %1, %2, neg(0) op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(f));
+  else asm("v_fma_mix_f32 %0, %1, %2, neg(0) op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(f));
+  return d;
+}
+
+// lo^2 + hi^2 of the two fp16 halves of w, as fma(lo, lo, hi * hi): both squares are exact
+// in fp32, so this is the rounded sum of the two squares.
+__device__ __forceinline__ float sum_sq_f16x2(uint32_t w) {
+  float hh, d;
+  asm("v_fma_mix_f32 %0, %1, %1, neg(0) op_sel:[1,1,0] op_sel_hi:[1,1,0]" : "=v"(hh) : "v"(w));
+  asm("v_fma_mix_f32 %0, %1, %1, %2 op_sel_hi:[1,1,0]" : "=v"(d) : "v"(w), "v"(hh));
+  return d;
+}
+
 // base + off bytes, in the global address space (a wave-uniform base and a 32-bit lane offset
 // let the compiler use the scalar-base addressing form)
 template <typename T>
@@ -161,23 +182,36 @@ struct RsArgs {
 
 enum Mode { kAmaxPass = 0, kCodes = 1, kCodesAndSide = 2 };
 
-// The S-lane row slots of one row group: loads of kUnroll groups of a wavefront.  Group g
-// (clamped to the last group: a wavefront past the end redoes it and stores the same bytes)
-// covers rows g R .. g R + R - 1; a slot past the last row reads (and later writes) that
-// row again.
+// Row groups are numbered in 32 bits (rows < 2^31, checked on the host), so every clamp
+// below is scalar arithmetic.  Group g (clamped to the last group: a wavefront past the end
+// redoes it and stores the same bytes) covers rows g R .. g R + R - 1; a slot past the last
+// row reads (and later writes) that row again.
+struct GroupAt {
+  int64_t r0;     // first row of the group (wave-uniform)
+  int rs;         // this lane's row within it
+};
+
 template <int S>
-__device__ __forceinline__ void load_groups(const RsArgs& a, int64_t g_first, int64_t last_group, int sub,
-                                            int eff, uint4 (&v)[kUnroll]) {
+__device__ __forceinline__ GroupAt group_at(const RsArgs& a, int g, int last_group, int sub) {
   constexpr int R = kWave / S;
-  const int chunks = (int)(a.c >> 3);
+  const int gc = g < last_group ? g : last_group;
+  GroupAt o;
+  o.r0 = (int64_t)gc * R;
+  const int lim = (int)a.rows - 1 - gc * R;                  // >= 0
+  const int limc = lim < R - 1 ? lim : R - 1;
+  o.rs = sub < limc ? sub : limc;
+  return o;
+}
+
+template <int S>
+__device__ __forceinline__ void load_groups(const RsArgs& a, int g_first, int last_group, int sub, int eff,
+                                            uint4 (&v)[kUnroll]) {
+  const uint32_t chunks = (uint32_t)(a.c >> 3);
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    const int64_t g = g_first + u < last_group ? g_first + u : last_group;
-    const int64_t r0 = g * R;                                             // wave-uniform
-    const int64_t lim = a.rows - 1 - r0;                                  // >= 0
-    const int limc = lim < R - 1 ? (int)lim : R - 1;                      // wave-uniform
-    const uint32_t off = __umul24((uint32_t)(sub < limc ? sub : limc), (uint32_t)chunks) + eff;   // < 2^24
-    v[u] = load_stream(at_byte(a.x + r0 * chunks, off * 16u));
+    const GroupAt at = group_at<S>(a, g_first + u, last_group, sub);
+    const uint32_t off = __umul24((uint32_t)at.rs, chunks) + eff;   // < 2^24
+    v[u] = load_stream(at_byte(a.x + at.r0 * chunks, off * 16u));
   }
 }
 
@@ -194,7 +228,7 @@ __device__ __forceinline__ void load_groups(const RsArgs& a, int64_t g_first, in
 // The 16 wavefronts of a workgroup take consecutive groups (kUnroll per wavefront, 64 per
 // workgroup step; workgroups interleave), run the same number of steps and meet at a
 // barrier after each, so the rows in flight stay compact; the next step's groups are loaded
-// before the current ones are computed.
+// before the current ones are computed (two register sets, used in turn).
 template <int S, int MODE>
 __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
   constexpr bool AMAX = MODE == kAmaxPass;
@@ -211,18 +245,19 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int chunk = lane % S, sub = lane / S;
   const int chunks = (int)(a.c >> 3);
+  const int blocks = (int)(a.c >> 4);
   const bool lane_ok = chunk < chunks;
   const int eff = lane_ok ? chunk : chunk % chunks;
 
-  const int64_t groups = (a.rows + R - 1) / R;
-  const int64_t last_group = groups - 1;
-  const int64_t span = (int64_t)gridDim.x * kStepGroups;
-  const int64_t wg_first = (int64_t)blockIdx.x * kStepGroups;
-  const int64_t steps = wg_first < groups ? (groups - wg_first + span - 1) / span : 0;
-  const int64_t my_first = wg_first + wave * kUnroll;
+  const int groups = (int)((a.rows + R - 1) / R);
+  const int last_group = groups - 1;
+  const int span = (int)gridDim.x * kStepGroups;
+  const int wg_first = (int)blockIdx.x * kStepGroups;
+  const int steps = wg_first < groups ? (groups - wg_first + span - 1) / span : 0;
+  const int my_first = wg_first + wave * kUnroll;
 
-  uint4 cur[kUnroll];
-  load_groups<S>(a, my_first, last_group, sub, eff, cur);
+  uint4 buf0[kUnroll], buf1[kUnroll];
+  load_groups<S>(a, my_first, last_group, sub, eff, buf0);
 
   const float gsf = call_global_scale(a.global_amax, a.amax_dev);
   if (!AMAX) fill_inverse_table(inv_tab, gsf, tid);
@@ -234,28 +269,19 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
   __syncthreads();
 
   float lane_amax = 0.0f;
-  const int blocks = (int)(a.c >> 4);
-  for (int64_t st = 0; st < steps; ++st) {
-    const int64_t g_first = my_first + st * span;
-    uint4 nxt[kUnroll];
+  // one step: the groups g_first .. + kUnroll - 1 held in cur; the next step's into nxt
+  auto step = [&](int g_first, const uint4 (&cur)[kUnroll], uint4 (&nxt)[kUnroll]) {
     load_groups<S>(a, g_first + span, last_group, sub, eff, nxt);
     // the four groups' statistics: one reciprocal square root for all of them (lane L
     // works on group L % 4's sum, then each quad hands group u's result to its lanes)
-    float x8[kUnroll][8];
     float sums[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const uint32_t w[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        x8[u][2 * q] = f16_lo(w[q]);
-        x8[u][2 * q + 1] = f16_hi(w[q]);
-      }
-      // squares of fp16 values are exact in fp32, so sq0 + sq1 == fma(x0, x0, sq1)
+      // the pairwise fold's first level: sq0 + sq1 of each fp16 pair
       float pr[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        pr[e] = __builtin_fmaf(x8[u][2 * e], x8[u][2 * e], x8[u][2 * e + 1] * x8[u][2 * e + 1]);
+      for (int e = 0; e < 4; ++e) pr[e] = sum_sq_f16x2(w[e]);
       float lane_v = (pr[0] + pr[1]) + (pr[2] + pr[3]);
       lane_v = lane_ok ? lane_v : 0.0f;
       sums[u] = slot_sum_butterfly<S>(lane_v);
@@ -267,19 +293,15 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
     const float rstds[kUnroll] = {quad_lane<0>(rq), quad_lane<1>(rq), quad_lane<2>(rq), quad_lane<3>(rq)};
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t g = g_first + u < last_group ? g_first + u : last_group;
-      const int64_t r0 = g * R;
-      const int64_t lim = a.rows - 1 - r0;
-      const int limc = lim < R - 1 ? (int)lim : R - 1;        // wave-uniform
-      const int rs = sub < limc ? sub : limc;                 // this lane's row, r0 + rs
+      const GroupAt at = group_at<S>(a, g_first + u, last_group, sub);
       const float rstd = rstds[u];
+      const uint32_t w[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
       float y[8];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        // the product rounded to fp32 first, then to fp16: without the opaque step the
-        // compiler forms one v_fma_mix (a single rounding of the exact product to fp16)
-        float p0 = x8[u][e] * rstd, p1 = x8[u][e + 1] * rstd;
-        asm volatile("" : "+v"(p0), "+v"(p1));
+        // the product rounded to fp32 first, then to fp16 (the opaque multiply also keeps the
+        // compiler from forming one v_fma_mixlo, a single rounding to fp16)
+        const float p0 = mul_f16_f32<false>(w[e / 2], rstd), p1 = mul_f16_f32<true>(w[e / 2], rstd);
         // fp16(nn * gamma): the product of two fp16 values is exact in fp32, so its fp16
         // rounding is the fp16 multiply's (one v_pk_mul_f16 for the pair)
         h2 nn;
@@ -295,20 +317,25 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
       }
       uint32_t s;
       const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
-      *at_byte(a.codes + r0 * chunks, (__umul24((uint32_t)rs, (uint32_t)chunks) + eff) * 4u) = code;
-      *at_byte(a.scales + r0 * blocks, __umul24((uint32_t)rs, (uint32_t)blocks) + (eff >> 1)) = (uint8_t)s;
+      const uint32_t row_chunk = __umul24((uint32_t)at.rs, (uint32_t)chunks) + eff;
+      *at_byte(a.codes + at.r0 * chunks, row_chunk * 4u) = code;
+      *at_byte(a.scales + at.r0 * blocks, __umul24((uint32_t)at.rs, (uint32_t)blocks) + (eff >> 1)) = (uint8_t)s;
       if (MODE == kCodesAndSide) {
-        if (a.rstd_out) global_ptr(a.rstd_out)[r0 + rs] = rstd;
+        if (a.rstd_out) global_ptr(a.rstd_out)[at.r0 + at.rs] = rstd;
         if (a.y_out)
-          global_ptr(a.y_out + r0 * chunks)[rs * chunks + eff] =
+          *at_byte(a.y_out + at.r0 * chunks, row_chunk * 16u) =
               make_uint4(f16_bits(y[0]) | (f16_bits(y[1]) << 16), f16_bits(y[2]) | (f16_bits(y[3]) << 16),
                          f16_bits(y[4]) | (f16_bits(y[5]) << 16), f16_bits(y[6]) | (f16_bits(y[7]) << 16));
       }
     }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) cur[u] = nxt[u];
     __builtin_amdgcn_s_barrier();
+  };
+  int st = 0;
+  for (; st + 2 <= steps; st += 2) {
+    step(my_first + st * span, buf0, buf1);
+    step(my_first + (st + 1) * span, buf1, buf0);
   }
+  if (st < steps) step(my_first + st * span, buf0, buf1);
   if (AMAX) workgroup_max_to(a.amax_out, lane_amax, amax_red, kWaves);
 }
 
@@ -381,6 +408,18 @@ hipError_t launch_rms_silu(const RmsSiluLaunch& p, const DeviceInfo& dev, hipStr
   a.scales = static_cast<uint8_t*>(p.scales);
   a.rstd_out = p.rstd_out;
   a.y_out = static_cast<uint4*>(p.y_out);
+  // the kernel numbers rows in 32 bits: longer tensors go in pieces of kPieceRows rows
+  const int64_t chunks = p.c >> 3, blocks = p.c >> 4;
+  auto piece = [&](const RsArgs& whole, int64_t r) {
+    RsArgs q = whole;
+    q.rows = whole.rows - r < kPieceRows ? whole.rows - r : kPieceRows;
+    q.x = whole.x + r * chunks;
+    if (q.codes) q.codes = whole.codes + r * chunks;
+    if (q.scales) q.scales = whole.scales + r * blocks;
+    if (q.rstd_out) q.rstd_out = whole.rstd_out + r;
+    if (q.y_out) q.y_out = whole.y_out + r * chunks;
+    return q;
+  };
   if (p.amax_dev) {
     hipError_t e = launch_zero_amax(p.amax_dev, stream);
     if (e != hipSuccess) return e;
@@ -390,11 +429,17 @@ hipError_t launch_rms_silu(const RmsSiluLaunch& p, const DeviceInfo& dev, hipStr
     pass.rstd_out = nullptr;
     pass.y_out = nullptr;
     pass.amax_out = p.amax_dev;
-    e = launch_pass<true>(pass, dev, stream);
-    if (e != hipSuccess) return e;
+    for (int64_t r = 0; r < a.rows; r += kPieceRows) {
+      e = launch_pass<true>(piece(pass, r), dev, stream);
+      if (e != hipSuccess) return e;
+    }
     a.amax_dev = p.amax_dev;
   }
-  return launch_pass<false>(a, dev, stream);
+  for (int64_t r = 0; r < a.rows; r += kPieceRows) {
+    const hipError_t e = launch_pass<false>(piece(a, r), dev, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace nvfp4act
