@@ -217,18 +217,19 @@ __device__ __forceinline__ void zero_row_scales(uint8_t* scales, int64_t r, int6
 // swaps rather than LDS permutes: s = 1, 2 are quad permutations; s = 4 is row_shl:4 on
 // the even 4-lane banks of each 16-lane row and row_shr:4 on the odd ones; s = 8 is
 // row_ror:8; s = 16 and 32 use v_permlane16_swap / v_permlane32_swap, whose two results
-// are the lane's value and its partner's.
+// are the lane's value and its partner's.  The quad and row_ror steps read every lane of
+// the row (no masked banks), so their moves fold into one v_add_f32_dpp each.
 __device__ __forceinline__ float lane_sum_butterfly(float v) {
   uint32_t u = __float_as_uint(v);
-  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0xB1, 0xF, 0xF, false));
+  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));
   u = __float_as_uint(v);
-  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x4E, 0xF, 0xF, false));
+  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));
   u = __float_as_uint(v);
   int t = __builtin_amdgcn_update_dpp((int)u, (int)u, 0x104, 0xF, 0x5, false);   // banks 0, 2: lane + 4
   t = __builtin_amdgcn_update_dpp(t, (int)u, 0x114, 0xF, 0xA, false);            // banks 1, 3: lane - 4
   v = v + __uint_as_float((uint32_t)t);
   u = __float_as_uint(v);
-  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x128, 0xF, 0xF, false));
+  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xF, 0xF, true));
   u = __float_as_uint(v);
   const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
   v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);

@@ -144,15 +144,15 @@ __device__ __forceinline__ float quad_lane(float v) {
 template <int S>
 __device__ __forceinline__ float slot_sum_butterfly(float v) {
   uint32_t u = __float_as_uint(v);
-  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0xB1, 0xF, 0xF, false));
+  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));
   u = __float_as_uint(v);
-  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x4E, 0xF, 0xF, false));
+  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));
   u = __float_as_uint(v);
   int t = __builtin_amdgcn_update_dpp((int)u, (int)u, 0x104, 0xF, 0x5, false);   // banks 0, 2: lane + 4
   t = __builtin_amdgcn_update_dpp(t, (int)u, 0x114, 0xF, 0xA, false);            // banks 1, 3: lane - 4
   v = v + __uint_as_float((uint32_t)t);
   u = __float_as_uint(v);
-  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)u, (int)u, 0x128, 0xF, 0xF, false));
+  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xF, 0xF, true));
   if (S >= 32) {
     u = __float_as_uint(v);
     const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
