@@ -12,12 +12,12 @@
 //
 // One workgroup of 8 wavefronts per CU, persistent over rows (wavefront w of workgroup b
 // takes rows 8b + w, 8b + w + 8 G, ... for a grid of G workgroups, so the rows in flight
-// at any time are consecutive); codes and y are written with non-temporal stores.  bf16-free: the only parameters are two fp32 vectors,
-// 1 + scale (computed once) and shift, staged in LDS as float2 planes (consecutive across
-// the wavefront: each ds_read_b64 covers 512 contiguous bytes).  Each wavefront keeps its
-// row unpacked in registers from the statistics to the output pass and prefetches the
-// next row's 16-byte chunks right after the statistics.  The output is 1 byte an element:
-// 8 bytes a chunk, two dword stores per lane.
+// at any time are consecutive).  The only parameters are two fp32 vectors, 1 + scale
+// (computed once) and shift, staged in LDS as float2 planes (consecutive across the
+// wavefront: each ds_read_b64 covers 512 contiguous bytes).  Each wavefront keeps its row
+// unpacked in registers from the statistics to the output pass and loads the next row's
+// 16-byte chunks at the top of each row.  The output is 1 byte an element: 8 bytes a
+// chunk, one non-temporal store per lane (y, when asked for, likewise).
 #include "common.hpp"
 #include "kernels.hpp"
 
