@@ -279,10 +279,14 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// 16- and 2-byte stores that are not expected to be re-read soon (non-temporal hint).
+// 16-, 4- and 2-byte stores that are not expected to be re-read soon (non-temporal hint).
 __device__ __forceinline__ void store_stream(uint4* p, const uint4& v) {
   const u32x4 w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<NVFP4_GLOBAL u32x4*>(global_ptr(p)));
+}
+
+__device__ __forceinline__ void store_stream(uint32_t* p, uint32_t v) {
+  __builtin_nontemporal_store(v, global_ptr(p));
 }
 
 __device__ __forceinline__ void store_stream(uint16_t* p, uint16_t v) {

@@ -8,9 +8,10 @@
 //
 // S is a 65,536-entry bf16 table indexed by the gate's bit pattern, built once per
 // device in fp64 by silu_table_kernel.  Each workgroup (one per CU, persistent over a
-// set of 128-row x 512-column tiles) copies the 128 KiB table into LDS; every element then
-// costs one LDS lookup, one multiply and one bf16 rounding before the quantizer.  Each
-// tile's scale bytes are gathered in LDS and leave with 16-byte stores.
+// set of 128-row x 512-column tiles) copies the 128 KiB table into its static LDS; every
+// element then costs one LDS lookup, one multiply and one bf16 rounding before the
+// quantizer.  Each tile's scale bytes are gathered in LDS and leave with 16-byte stores;
+// codes are written with non-temporal stores.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -105,106 +106,139 @@ __device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b) {
   return pack_bf16x2(bf16_lo(a) + bf16_lo(b), bf16_hi(a) + bf16_hi(b));
 }
 
-// One 128-row x kTileCols tile: each wavefront takes rows wave, wave + 16, ... (8 rows),
-// kRowBatch at a time; scale bytes go to the tile's LDS block.  AMAX (the amax pass of a
-// per-call scale): nothing is quantized or stored; max |y| is folded into *lane_amax.
-template <bool AMAX, bool PAIRED, bool BIAS>
-__device__ __forceinline__ void swiglu_tile(const SwArgs& a, int64_t row_chunks, int64_t tile_row, int64_t c0,
-                                            int64_t tchunks, int lane, int wave, const uint16_t* table, float gsf,
-                                            const float* inv_tab, uint8_t* sc_lane, float* lane_amax) {
-  const int64_t r0 = tile_row << 7;
-  const int64_t rows = (a.m - r0 < 128) ? (a.m - r0 > 0 ? a.m - r0 : 0) : 128;
-  const int64_t c = c0 + lane;
-  const bool lane_ok = lane < tchunks;
-  // this lane's 16 bias values: (value, gate) of its 8 columns, laid out like one row's loads
-  uint4 b0 = make_uint4(0, 0, 0, 0), b1 = make_uint4(0, 0, 0, 0);
-  if (BIAS && lane_ok) {
+// One batch: kRowBatch rows of one lane's chunk of a 128-row x kTileCols tile (wavefront w
+// takes rows 4w .. 4w + 3 in batch 0 and 64 + 4w .. in batch 1), with the lane's 16 bias
+// values.  Rows past the tensor repeat row m - 1 and lanes past the tile's chunks repeat
+// the tile's last chunk pair (same parity), so every lane loads, computes and stores like
+// a real one and the loop has no divergent branch; the duplicates store the same bytes
+// as the lanes they repeat.
+struct Batch {
+  uint4 u[kRowBatch], g[kRowBatch];
+  uint4 b0, b1;
+};
+
+struct TileAt {
+  int64_t r0, c0, c;   // first row, first chunk, this lane's chunk
+  int64_t tchunks;
+};
+
+__device__ __forceinline__ TileAt tile_at(const SwArgs& a, int64_t t, int lane) {
+  const int64_t row_chunks = a.f >> 3;
+  const int64_t tile_row = t / a.col_tiles, col_tile = t % a.col_tiles;
+  TileAt o;
+  o.r0 = tile_row << 7;
+  o.c0 = col_tile * (kTileCols / 8);
+  o.tchunks = (row_chunks - o.c0 < kTileCols / 8) ? row_chunks - o.c0 : kTileCols / 8;   // even
+  o.c = o.c0 + (lane < o.tchunks ? lane : o.tchunks - 2 + (lane & 1));
+  return o;
+}
+
+template <bool PAIRED, bool BIAS>
+__device__ __forceinline__ void load_batch(const SwArgs& a, const TileAt& at, int rb, Batch& b) {
+#pragma unroll
+  for (int i = 0; i < kRowBatch; ++i) {
+    const int64_t r_own = at.r0 + rb + i;
+    const int64_t r = r_own < a.m ? r_own : a.m - 1;
     if (PAIRED) {
-      b0 = global_ptr(a.bias_up)[2 * c];
-      b1 = global_ptr(a.bias_up)[2 * c + 1];
+      // 32 contiguous bytes per lane: each of the two loads covers half of every 128-byte
+      // line of the wave's 2 KiB, so the second must find the line still in the L1 cache
+      // -- plain loads, not the streaming (nontemporal) ones
+      b.u[i] = global_ptr(a.up)[r * a.ld8 + 2 * at.c];
+      b.g[i] = global_ptr(a.up)[r * a.ld8 + 2 * at.c + 1];
     } else {
-      b0 = global_ptr(a.bias_up)[c];
-      b1 = global_ptr(a.bias_gate)[c];
+      b.u[i] = load_stream(a.up + r * a.ld8 + at.c);
+      b.g[i] = load_stream(a.gate + r * a.ld8 + at.c);
     }
   }
-  for (int64_t rb = wave * kRowBatch; rb < rows; rb += kWaves * kRowBatch) {
-    uint4 u[kRowBatch], g[kRowBatch];
-#pragma unroll
-    for (int i = 0; i < kRowBatch; ++i) {
-      const int64_t r = r0 + rb + i;
-      if (rb + i < rows && lane_ok) {
-        if (PAIRED) {
-          // 32 contiguous bytes per lane: each of the two loads covers half of every
-          // 128-byte line of the wave's 2 KiB, so the second must find the line still in
-          // the L1 cache -- plain loads, not the streaming (nontemporal) ones
-          u[i] = global_ptr(a.up)[r * a.ld8 + 2 * c];
-          g[i] = global_ptr(a.up)[r * a.ld8 + 2 * c + 1];
-        } else {
-          u[i] = load_stream(a.up + r * a.ld8 + c);
-          g[i] = load_stream(a.gate + r * a.ld8 + c);
-        }
-      } else {
-        u[i] = make_uint4(0, 0, 0, 0);
-        g[i] = make_uint4(0, 0, 0, 0);
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < kRowBatch; ++i) {
-      const int64_t rr = rb + i;
-      float y[8];
-      if (PAIRED) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          uint32_t w = words_at(e < 4 ? u[i] : g[i], e & 3);
-          if (BIAS) w = add_bf16x2(w, words_at(e < 4 ? b0 : b1, e & 3));
-          const float s = __uint_as_float((uint32_t)table[w >> 16] << 16);
-          y[e] = round_bf16(s * bf16_lo(w));
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t uw = words_at(u[i], q), gw = words_at(g[i], q);
-          if (BIAS) {
-            uw = add_bf16x2(uw, words_at(b0, q));
-            gw = add_bf16x2(gw, words_at(b1, q));
-          }
-          const float s0 = __uint_as_float((uint32_t)table[gw & 0xFFFFu] << 16);
-          const float s1 = __uint_as_float((uint32_t)table[gw >> 16] << 16);
-          y[2 * q] = round_bf16(s0 * bf16_lo(uw));
-          y[2 * q + 1] = round_bf16(s1 * bf16_hi(uw));
-        }
-      }
-      if (AMAX) {
-        // rows past the tensor loaded zeros, but a bias would make their y nonzero
-        if (rr < rows && lane_ok) *lane_amax = fold_abs8(*lane_amax, y);
-        continue;
-      }
-      uint32_t s;
-      const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
-      if (rr < rows && lane_ok) {
-        const int64_t r = r0 + rr;
-        global_ptr(a.codes)[r * row_chunks + c] = code;
-        sc_lane[(rr & 31) * 16 + ((rr >> 5) & 3) * 4] = (uint8_t)s;
-        if (a.y_out)
-          global_ptr(a.y_out)[r * row_chunks + c] =
-              make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
-                         pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
-      }
+  if (BIAS) {
+    if (PAIRED) {
+      b.b0 = global_ptr(a.bias_up)[2 * at.c];
+      b.b1 = global_ptr(a.bias_up)[2 * at.c + 1];
+    } else {
+      b.b0 = global_ptr(a.bias_up)[at.c];
+      b.b1 = global_ptr(a.bias_gate)[at.c];
     }
   }
 }
 
+// Quantize one batch; scale bytes go to the tile's LDS block (zero for rows past m).
+// AMAX (the amax pass of a per-call scale): nothing is quantized or stored; max |y| is
+// folded into *lane_amax.
+template <bool AMAX, bool PAIRED, bool BIAS>
+__device__ __forceinline__ void compute_batch(const SwArgs& a, const TileAt& at, int rb, const Batch& b,
+                                              const uint16_t* table, float gsf, const float* inv_tab,
+                                              uint8_t* tile_bytes, float* lane_amax) {
+  const int64_t row_chunks = a.f >> 3;
+  uint8_t* sc = tile_bytes + scale_lane_offset((int)(at.c - at.c0));
+#pragma unroll
+  for (int i = 0; i < kRowBatch; ++i) {
+    const int rr = rb + i;
+    float y[8];
+    if (PAIRED) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t w = words_at(e < 4 ? b.u[i] : b.g[i], e & 3);
+        if (BIAS) w = add_bf16x2(w, words_at(e < 4 ? b.b0 : b.b1, e & 3));
+        const float s = __uint_as_float((uint32_t)table[w >> 16] << 16);
+        y[e] = round_bf16(s * bf16_lo(w));
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t uw = words_at(b.u[i], q), gw = words_at(b.g[i], q);
+        if (BIAS) {
+          uw = add_bf16x2(uw, words_at(b.b0, q));
+          gw = add_bf16x2(gw, words_at(b.b1, q));
+        }
+        const float s0 = __uint_as_float((uint32_t)table[gw & 0xFFFFu] << 16);
+        const float s1 = __uint_as_float((uint32_t)table[gw >> 16] << 16);
+        y[2 * q] = round_bf16(s0 * bf16_lo(uw));
+        y[2 * q + 1] = round_bf16(s1 * bf16_hi(uw));
+      }
+    }
+    if (AMAX) {
+      *lane_amax = fold_abs8(*lane_amax, y);
+      continue;
+    }
+    uint32_t s;
+    const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
+    const int64_t r_own = at.r0 + rr;
+    const int64_t r = r_own < a.m ? r_own : a.m - 1;
+    store_stream(reinterpret_cast<uint32_t*>(a.codes) + r * row_chunks + at.c, code);
+    sc[(rr & 31) * 16 + ((rr >> 5) & 3) * 4] = r_own < a.m ? (uint8_t)s : (uint8_t)0;
+    if (a.y_out)
+      global_ptr(a.y_out)[r * row_chunks + at.c] =
+          make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
+                     pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
+  }
+}
+
+// A barrier that orders LDS only: __syncthreads would also wait for the prefetched loads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One workgroup per CU, persistent over tiles t, t + grid, ...; each wavefront holds two
+// batch buffers: while one batch is computed, the next one (the tile's second batch, or the
+// next tile's first) is loading.
 template <bool AMAX, bool PAIRED, bool BIAS>
 __global__ __launch_bounds__(kThreads) void swiglu_kernel(const SwArgs a) {
   __shared__ float amax_red[kWaves];
-  extern __shared__ uint4 lds4[];
+  __shared__ uint4 lds4[kTableBytes / 16];
+  __shared__ float inv_tab[128];
+  __shared__ uint4 tile_sc[kScaleBytes / 16];
   uint16_t* table = reinterpret_cast<uint16_t*>(lds4);
-  float* inv_tab = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(lds4) + kTableBytes);
-  uint4* tile_sc = reinterpret_cast<uint4*>(reinterpret_cast<uint8_t*>(lds4) + kTableBytes + 512);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   if ((int64_t)blockIdx.x >= a.ntiles) return;            // idle workgroup (uniform)
+  const int rb0 = wave * kRowBatch, rb1 = kWaves * kRowBatch + wave * kRowBatch;
+
+  Batch A, B;
+  TileAt at = tile_at(a, blockIdx.x, lane);
+  load_batch<PAIRED, BIAS>(a, at, rb0, A);
 
   const float gsf = call_global_scale(a.global_amax, a.amax_dev);
   float lane_amax = 0.0f;
@@ -214,36 +248,36 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const SwArgs a) {
   for (int i = tid; i < kScaleBytes / 16; i += kThreads) tile_sc[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  const int64_t row_chunks = a.f >> 3;
-  uint8_t* sc_lane = reinterpret_cast<uint8_t*>(tile_sc) + scale_lane_offset(lane);
+  uint8_t* tile_bytes = reinterpret_cast<uint8_t*>(tile_sc);
   for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
-    const int64_t tile_row = t / a.col_tiles, col_tile = t % a.col_tiles;
-    const int64_t c0 = col_tile * (kTileCols / 8);
-    const int64_t tchunks = (row_chunks - c0 < kTileCols / 8) ? row_chunks - c0 : kTileCols / 8;
-    swiglu_tile<AMAX, PAIRED, BIAS>(a, row_chunks, tile_row, c0, tchunks, lane, wave, table, gsf, inv_tab,
-                                    sc_lane, &lane_amax);
-    if (AMAX) continue;
-    __syncthreads();
-    // copy the tile's scale slice out and zero it for the next tile (each thread clears
-    // exactly the words it copied)
-    NVFP4_GLOBAL uint4* dst = reinterpret_cast<NVFP4_GLOBAL uint4*>(
-        global_ptr(a.scales) + (tile_row * (a.f >> 6) + c0 / 8) * 512);
-    const int words = (int)(tchunks / 8) * 32;
-    for (int i = tid; i < words; i += kThreads) {
-      dst[i] = tile_sc[i];
-      tile_sc[i] = make_uint4(0, 0, 0, 0);
+    const int64_t tn = t + gridDim.x < a.ntiles ? t + gridDim.x : a.ntiles - 1;
+    const TileAt next = tile_at(a, tn, lane);
+    load_batch<PAIRED, BIAS>(a, at, rb1, B);
+    compute_batch<AMAX, PAIRED, BIAS>(a, at, rb0, A, table, gsf, inv_tab, tile_bytes, &lane_amax);
+    load_batch<PAIRED, BIAS>(a, next, rb0, A);
+    compute_batch<AMAX, PAIRED, BIAS>(a, at, rb1, B, table, gsf, inv_tab, tile_bytes, &lane_amax);
+    if (!AMAX) {
+      lds_barrier();
+      // copy the tile's scale slice out and zero it for the next tile (each thread clears
+      // exactly the words it copied)
+      NVFP4_GLOBAL uint4* dst = reinterpret_cast<NVFP4_GLOBAL uint4*>(
+          global_ptr(a.scales) + ((at.r0 >> 7) * (a.f >> 6) + at.c0 / 8) * 512);
+      const int words = (int)(at.tchunks / 8) * 32;
+      for (int i = tid; i < words; i += kThreads) {
+        dst[i] = tile_sc[i];
+        tile_sc[i] = make_uint4(0, 0, 0, 0);
+      }
+      lds_barrier();
     }
-    __syncthreads();
+    at = next;
   }
   if (AMAX) workgroup_max_to(a.amax_out, lane_amax, amax_red, kWaves);
 }
 
-constexpr size_t kSwigluLds = kTableBytes + 512 + kScaleBytes;
-
 template <bool AMAX, bool PAIRED, bool BIAS>
 hipError_t allow_lds() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&swiglu_kernel<AMAX, PAIRED, BIAS>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kSwigluLds);
+  (void)&swiglu_kernel<AMAX, PAIRED, BIAS>;   // static LDS only: nothing to allow
+  return hipSuccess;
 }
 
 template <bool PAIRED, bool BIAS>
@@ -257,15 +291,13 @@ hipError_t launch_form(SwArgs a, int64_t grid, hipStream_t stream) {
     p.codes = nullptr;
     p.scales = nullptr;
     p.y_out = nullptr;
-    hipLaunchKernelGGL((swiglu_kernel<true, PAIRED, BIAS>), dim3((uint32_t)grid), dim3(kThreads), kSwigluLds,
-                       stream, p);
+    hipLaunchKernelGGL((swiglu_kernel<true, PAIRED, BIAS>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.amax_dev = a.amax_out;
     a.amax_out = nullptr;
   }
-  hipLaunchKernelGGL((swiglu_kernel<false, PAIRED, BIAS>), dim3((uint32_t)grid), dim3(kThreads), kSwigluLds,
-                     stream, a);
+  hipLaunchKernelGGL((swiglu_kernel<false, PAIRED, BIAS>), dim3((uint32_t)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
