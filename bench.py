@@ -283,6 +283,8 @@ def main():
         "pct_of_peak": round(100.0 * value / PEAK_HBM_GBPS, 2),
         "rows_per_s": round(wl.m / (ms_per_step * 1e-3), 1),
         "kernel_us": round(kernel_ms * 1e3, 2),
+        "kernel_us_median": round(float(np.median(per_launch_ms)) * 1e3, 2),
+        "kernel_us_min": round(float(np.min(per_launch_ms)) * 1e3, 2),
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "wall_s": round(wall, 3),
     }

@@ -204,7 +204,7 @@ __device__ __forceinline__ void load_params(const float4* lds, uint32_t pw, uint
 // y_out.
 template <bool Y, bool TILE>
 __device__ __forceinline__ void emit_encoded(const RowOut& o, int j, const float* y, float inv, uint32_t s) {
-  o.codes[kWave * j] = encode_chunk(y, inv);
+  __builtin_nontemporal_store(encode_chunk(y, inv), o.codes + kWave * j);   // not read back
   if (TILE) o.scales_lds[4224 * j] = (uint8_t)s;
   else o.scales[(int64_t)4096 * j] = (uint8_t)s;
   if (Y)
