@@ -75,20 +75,6 @@ struct ResArgs {
   uint32_t* status;
 };
 
-// max over the four lanes 4i .. 4i + 3 of non-negative fp32 bit patterns (DPP quad
-// permutations [1,0,3,2] and [2,3,0,1]).
-__device__ __forceinline__ uint32_t max_over_lane_quad(uint32_t v) {
-  v = __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));
-  return __builtin_elementwise_max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));
-}
-
-// Four E2M1 codes of v[0..3] in the low 16 bits (v[0] in bits 0..3); see pack_e2m1x8.
-__device__ __forceinline__ uint32_t pack_e2m1x4(float v0, float v1, float v2, float v3) {
-  uint32_t w = __float_as_uint(v0);       // bytes 0 and 1 are overwritten below
-  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v0, v1, 1.0f, 0);
-  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v2, v3, 1.0f, 1);
-}
-
 // bf16(a + b) for the two bf16 values of a word each.
 __device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b) {
   return pack_bf16x2(bf16_lo(a) + bf16_lo(b), bf16_hi(a) + bf16_hi(b));

@@ -118,7 +118,8 @@ struct Batch {
 };
 
 struct TileAt {
-  int64_t r0, c0, c;   // first row, first chunk, this lane's chunk
+  int64_t r0, c0, c;   // first row, first chunk, this lane's chunk (value-first)
+  int64_t q[2];        // paired: this lane's two 16-byte column quads (row-relative index)
   int64_t tchunks;
 };
 
@@ -130,6 +131,15 @@ __device__ __forceinline__ TileAt tile_at(const SwArgs& a, int64_t t, int lane) 
   o.c0 = col_tile * (kTileCols / 8);
   o.tchunks = (row_chunks - o.c0 < kTileCols / 8) ? row_chunks - o.c0 : kTileCols / 8;   // even
   o.c = o.c0 + (lane < o.tchunks ? lane : o.tchunks - 2 + (lane & 1));
+  // paired: the tile row is 2 tchunks quads of four (value, gate) columns; lane L takes quads
+  // L and L + 64, and a lane past the end repeats the last four quads (same position in its
+  // block and pair)
+  const int64_t nq = 2 * o.tchunks;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int64_t k = lane + kWave * h;
+    o.q[h] = 2 * o.c0 + (k < nq ? k : nq - 4 + (lane & 3));
+  }
   return o;
 }
 
@@ -140,11 +150,9 @@ __device__ __forceinline__ void load_batch(const SwArgs& a, const TileAt& at, in
     const int64_t r_own = at.r0 + rb + i;
     const int64_t r = r_own < a.m ? r_own : a.m - 1;
     if (PAIRED) {
-      // 32 contiguous bytes per lane: each of the two loads covers half of every 128-byte
-      // line of the wave's 2 KiB, so the second must find the line still in the L1 cache
-      // -- plain loads, not the streaming (nontemporal) ones
-      b.u[i] = global_ptr(a.up)[r * a.ld8 + 2 * at.c];
-      b.g[i] = global_ptr(a.up)[r * a.ld8 + 2 * at.c + 1];
+      // quads L and L + 64: each load instruction reads 1 KiB contiguous
+      b.u[i] = load_stream(a.up + r * a.ld8 + at.q[0]);
+      b.g[i] = load_stream(a.up + r * a.ld8 + at.q[1]);
     } else {
       b.u[i] = load_stream(a.up + r * a.ld8 + at.c);
       b.g[i] = load_stream(a.gate + r * a.ld8 + at.c);
@@ -152,8 +160,8 @@ __device__ __forceinline__ void load_batch(const SwArgs& a, const TileAt& at, in
   }
   if (BIAS) {
     if (PAIRED) {
-      b.b0 = global_ptr(a.bias_up)[2 * at.c];
-      b.b1 = global_ptr(a.bias_up)[2 * at.c + 1];
+      b.b0 = global_ptr(a.bias_up)[at.q[0]];
+      b.b1 = global_ptr(a.bias_up)[at.q[1]];
     } else {
       b.b0 = global_ptr(a.bias_up)[at.c];
       b.b1 = global_ptr(a.bias_gate)[at.c];
@@ -169,32 +177,63 @@ __device__ __forceinline__ void compute_batch(const SwArgs& a, const TileAt& at,
                                               const uint16_t* table, float gsf, const float* inv_tab,
                                               uint8_t* tile_bytes, float* lane_amax) {
   const int64_t row_chunks = a.f >> 3;
+  if (PAIRED) {
+    // a 16-column block is the four quads of lanes 4i .. 4i + 3; each lane encodes its four
+    // columns into 16 bits, and the lane pair (2i, 2i + 1) stores the 32-bit word of both
+#pragma unroll
+    for (int i = 0; i < kRowBatch; ++i) {
+      const int rr = rb + i;
+      const int64_t r_own = at.r0 + rr;
+      const int64_t r = r_own < a.m ? r_own : a.m - 1;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint4 v = h == 0 ? b.u[i] : b.g[i];
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t w = words_at(v, e);
+          if (BIAS) w = add_bf16x2(w, words_at(h == 0 ? b.b0 : b.b1, e));
+          const float s = __uint_as_float((uint32_t)table[w >> 16] << 16);
+          y[e] = round_bf16(s * bf16_lo(w));
+        }
+        if (AMAX) {
+          *lane_amax = max_abs2(max_abs2(*lane_amax, y[0], y[1]), y[2], y[3]);
+          continue;
+        }
+        float am = max_abs2(max_abs2(0.0f, y[0], y[1]), y[2], y[3]);
+        am = __uint_as_float(max_over_lane_quad(__float_as_uint(am)));
+        const uint32_t s = e4m3_code(gsf * (am * __uint_as_float(kRcp6Bits)));
+        const float inv = inv_tab[s];
+        const uint32_t c16 = pack_e2m1x4(y[0] * inv, y[1] * inv, y[2] * inv, y[3] * inv) & 0xFFFFu;
+        const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)c16, 0xB1, 0xF, 0xF, true);
+        const uint32_t word = (at.q[h] & 1) ? (other | (c16 << 16)) : (c16 | (other << 16));
+        store_stream(reinterpret_cast<uint32_t*>(a.codes) + r * row_chunks + (at.q[h] >> 1), word);
+        const int bt = (int)((at.q[h] - 2 * at.c0) >> 2);          // block within the tile
+        tile_bytes[(bt >> 2) * 512 + (bt & 3) + (rr & 31) * 16 + ((rr >> 5) & 3) * 4] =
+            r_own < a.m ? (uint8_t)s : (uint8_t)0;
+        if (a.y_out)
+          reinterpret_cast<NVFP4_GLOBAL uint2*>(global_ptr(a.y_out))[r * (a.f >> 2) + at.q[h]] =
+              make_uint2(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]));
+      }
+    }
+    return;
+  }
   uint8_t* sc = tile_bytes + scale_lane_offset((int)(at.c - at.c0));
 #pragma unroll
   for (int i = 0; i < kRowBatch; ++i) {
     const int rr = rb + i;
     float y[8];
-    if (PAIRED) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint32_t w = words_at(e < 4 ? b.u[i] : b.g[i], e & 3);
-        if (BIAS) w = add_bf16x2(w, words_at(e < 4 ? b.b0 : b.b1, e & 3));
-        const float s = __uint_as_float((uint32_t)table[w >> 16] << 16);
-        y[e] = round_bf16(s * bf16_lo(w));
+    for (int q = 0; q < 4; ++q) {
+      uint32_t uw = words_at(b.u[i], q), gw = words_at(b.g[i], q);
+      if (BIAS) {
+        uw = add_bf16x2(uw, words_at(b.b0, q));
+        gw = add_bf16x2(gw, words_at(b.b1, q));
       }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t uw = words_at(b.u[i], q), gw = words_at(b.g[i], q);
-        if (BIAS) {
-          uw = add_bf16x2(uw, words_at(b.b0, q));
-          gw = add_bf16x2(gw, words_at(b.b1, q));
-        }
-        const float s0 = __uint_as_float((uint32_t)table[gw & 0xFFFFu] << 16);
-        const float s1 = __uint_as_float((uint32_t)table[gw >> 16] << 16);
-        y[2 * q] = round_bf16(s0 * bf16_lo(uw));
-        y[2 * q + 1] = round_bf16(s1 * bf16_hi(uw));
-      }
+      const float s0 = __uint_as_float((uint32_t)table[gw & 0xFFFFu] << 16);
+      const float s1 = __uint_as_float((uint32_t)table[gw >> 16] << 16);
+      y[2 * q] = round_bf16(s0 * bf16_lo(uw));
+      y[2 * q + 1] = round_bf16(s1 * bf16_hi(uw));
     }
     if (AMAX) {
       *lane_amax = fold_abs8(*lane_amax, y);
