@@ -222,7 +222,8 @@ def check_swiglu(got, proj, amax):
         assert_equal(got["y"], want["y"], "y_out")
 
 
-@pytest.mark.parametrize("m,f", [(1, 64), (127, 128), (129, 192), (300, 512), (64, 19456), (257, 1024)])
+@pytest.mark.parametrize("m,f", [(1, 64), (127, 128), (129, 192), (300, 512), (64, 19456), (257, 1024),
+                                 (300, 1088), (131, 2624)])
 def test_swiglu_shapes(nq, m, f):
     print("swiglu", m, f, flush=True)
     proj = rand_bf16((m, 2 * f), m + f, 2.0)
