@@ -364,10 +364,27 @@ def cpu_baseline(wl, amax, rows, np):
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(part, blocks))
     dt = time.perf_counter() - t0
+    # the same code on one thread, over the first sixteenth of the sample
+    one = max(1, rows // 16)
+    t1 = time.perf_counter()
+    part((0, one))
+    dt1 = time.perf_counter() - t1
     bytes_per_row = wl.algorithmic_bytes() / wl.m
     return {"value": round(rows * bytes_per_row / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "rows_per_s": round(rows / dt, 1), "seconds": round(dt, 3),
-            "sample": "first %d rows of %s, %d threads, row blocks" % (rows, wl.name, threads)}
+            "single_thread_rows_per_s": round(one / dt1, 1), "cpu_model": cpu_model(),
+            "sample": "first %d rows of %s, %d threads, row blocks (single thread: first %d rows)"
+                      % (rows, wl.name, threads, one)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 if __name__ == "__main__":
