@@ -43,12 +43,6 @@ struct LnArgs {
   float4* y_out;            // [m, k] fp32, two float4 per chunk
 };
 
-__device__ __forceinline__ float f16_lo(uint32_t w) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-}
-__device__ __forceinline__ float f16_hi(uint32_t w) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
 
 // Four signed E4M3 codes (nearest-even, saturating at +-448), a in the low byte.
 // v_cvt_pk_fp8_f32 rounds to nearest-even but turns magnitudes beyond 448 into NaN, so the

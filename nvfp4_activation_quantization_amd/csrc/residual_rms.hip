@@ -75,10 +75,6 @@ struct ResArgs {
   uint32_t* status;
 };
 
-// bf16(a + b) for the two bf16 values of a word each.
-__device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b) {
-  return pack_bf16x2(bf16_lo(a) + bf16_lo(b), bf16_hi(a) + bf16_hi(b));
-}
 
 // s_waitcnt vmcnt(N) (N < 64), leaving the other counters alone.
 template <int N>

@@ -86,12 +86,6 @@ __global__ void silu16_table_kernel() {
   g_silu16_table[g] = (uint16_t)out;
 }
 
-__device__ __forceinline__ float f16_lo(uint32_t w) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
-}
-__device__ __forceinline__ float f16_hi(uint32_t w) {
-  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-}
 // fp16(f) and its bit pattern (round to nearest even: the default mode)
 __device__ __forceinline__ uint32_t f16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);

@@ -101,10 +101,6 @@ __device__ __forceinline__ uint32_t words_at(const uint4& v, int q) {
   return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
 }
 
-// bf16(a + b) for the two bf16 values of a word each (the bias add).
-__device__ __forceinline__ uint32_t add_bf16x2(uint32_t a, uint32_t b) {
-  return pack_bf16x2(bf16_lo(a) + bf16_lo(b), bf16_hi(a) + bf16_hi(b));
-}
 
 // One batch: kRowBatch rows of one lane's chunk of a 128-row x kTileCols tile (wavefront w
 // takes rows 4w .. 4w + 3 in batch 0 and 64 + 4w .. in batch 1), with the lane's 16 bias
