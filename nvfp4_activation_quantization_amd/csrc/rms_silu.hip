@@ -35,7 +35,7 @@ namespace {
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / kWave;
 constexpr size_t kTableBytes = 65536 * sizeof(uint16_t);
-constexpr int kUnroll = 4;                 // row groups per wavefront in flight
+constexpr int kMaxUnroll = 2;             // row groups per wavefront in flight (one with 3 slots)
 constexpr int64_t kPieceRows = 1 << 30;    // rows per launch (row groups are numbered in 32 bits)
 
 // Round hi + lo to fp16, nearest-even (quantum 2^(E-10) for 2^E <= |v| < 2^(E+1), E >= -14,
@@ -125,34 +125,43 @@ __device__ __forceinline__ const NVFP4_GLOBAL T* at_byte(const T* base, uint32_t
   return reinterpret_cast<const NVFP4_GLOBAL T*>(reinterpret_cast<const NVFP4_GLOBAL char*>(global_ptr(base)) + off);
 }
 
-// The value of lane (L & ~3) + I of each quad, on every lane of the quad (DPP broadcast).
+// The value of lane (L & ~1) + I of each lane pair, on both lanes (DPP broadcast).
 template <int I>
-__device__ __forceinline__ float quad_lane(float v) {
-  constexpr int sel = I | (I << 2) | (I << 4) | (I << 6);
+__device__ __forceinline__ float pair_lane(float v) {
+  constexpr int sel = I | (I << 2) | ((2 + I) << 4) | ((2 + I) << 6);
   return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp((int)__float_as_uint(v), (int)__float_as_uint(v),
                                                                sel, 0xF, 0xF, false));
 }
 
-// Butterfly sum over the S lanes of a row (distances 1 .. S/2; S = 16, 32 or 64), as
-// lane_sum_butterfly for the first log2(S) steps.
-template <int S>
-__device__ __forceinline__ float slot_sum_butterfly(float v) {
-  uint32_t u = __float_as_uint(v);
-  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));
-  u = __float_as_uint(v);
-  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));
-  u = __float_as_uint(v);
-  int t = __builtin_amdgcn_update_dpp((int)u, (int)u, 0x104, 0xF, 0x5, false);   // banks 0, 2: lane + 4
-  t = __builtin_amdgcn_update_dpp(t, (int)u, 0x114, 0xF, 0xA, false);            // banks 1, 3: lane - 4
-  v = v + __uint_as_float((uint32_t)t);
-  u = __float_as_uint(v);
-  v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xF, 0xF, true));
-  if (S >= 32) {
+// The butterfly's lane levels: v + v[lane ^ d] for d = 1, 2, .. P/2 (P a power of two <= 64),
+// the partner values from DPP and the gfx950 row swaps as in lane_sum_butterfly.
+template <int P>
+__device__ __forceinline__ float lane_levels(float v) {
+  uint32_t u;
+  if (P >= 2) {
+    u = __float_as_uint(v);
+    v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));
+  }
+  if (P >= 4) {
+    u = __float_as_uint(v);
+    v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));
+  }
+  if (P >= 8) {
+    u = __float_as_uint(v);
+    int t = __builtin_amdgcn_update_dpp((int)u, (int)u, 0x104, 0xF, 0x5, false);   // banks 0, 2: lane + 4
+    t = __builtin_amdgcn_update_dpp(t, (int)u, 0x114, 0xF, 0xA, false);            // banks 1, 3: lane - 4
+    v = v + __uint_as_float((uint32_t)t);
+  }
+  if (P >= 16) {
+    u = __float_as_uint(v);
+    v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xF, 0xF, true));
+  }
+  if (P >= 32) {
     u = __float_as_uint(v);
     const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
     v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
   }
-  if (S >= 64) {
+  if (P >= 64) {
     u = __float_as_uint(v);
     const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
     v = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
@@ -176,18 +185,29 @@ struct RsArgs {
 
 enum Mode { kAmaxPass = 0, kCodes = 1, kCodesAndSide = 2 };
 
-// Row groups are numbered in 32 bits (rows < 2^31, checked on the host), so every clamp
-// below is scalar arithmetic.  Group g (clamped to the last group: a wavefront past the end
-// redoes it and stores the same bytes) covers rows g R .. g R + R - 1; a slot past the last
-// row reads (and later writes) that row again.
+// Lanes and slots.  A row's c/8 chunks are the specification's slots 0 .. c/8 - 1 (slots up
+// to the power of two S >= c/8 hold zeros).  A row takes P lanes (a power of two) and each
+// lane C slots: lane L of the row holds slots L, L + P, .., L + (C - 1) P, one register per
+// slot.  The butterfly's distances below P are then lane levels (DPP) on every register and
+// the distances from P up are pairwise adds between a lane's registers (zero registers
+// above C); its result is the specification's sum.  P C = c/8 where c/8 = P or 3 P (no
+// idle lanes); otherwise C = 1 and P = S, and a lane whose slot lies past c/8 takes the
+// chunk (slot mod c/8) -- same parity, so block partners stay partners -- adding 0 to the
+// statistic, so it computes and stores exactly what the lane owning that chunk does.
+// A 16-channel block is a chunk pair (2b, 2b + 1): the same register of lanes L, L ^ 1.
+//
+// Row groups (the R = 64 / P rows of a wavefront) are numbered in 32 bits (rows < 2^31,
+// launched in pieces), so every clamp is scalar arithmetic.  Group g (clamped to the last
+// group: a wavefront past the end redoes it and stores the same bytes) covers rows
+// g R .. g R + R - 1; a lane past the last row reads (and later writes) that row again.
 struct GroupAt {
   int64_t r0;     // first row of the group (wave-uniform)
   int rs;         // this lane's row within it
 };
 
-template <int S>
+template <int P>
 __device__ __forceinline__ GroupAt group_at(const RsArgs& a, int g, int last_group, int sub) {
-  constexpr int R = kWave / S;
+  constexpr int R = kWave / P;
   const int gc = g < last_group ? g : last_group;
   GroupAt o;
   o.r0 = (int64_t)gc * R;
@@ -197,36 +217,42 @@ __device__ __forceinline__ GroupAt group_at(const RsArgs& a, int g, int last_gro
   return o;
 }
 
-template <int S>
-__device__ __forceinline__ void load_groups(const RsArgs& a, int g_first, int last_group, int sub, int eff,
-                                            uint4 (&v)[kUnroll]) {
+template <int P, int C, int kUnroll>
+__device__ __forceinline__ void load_groups(const RsArgs& a, int g_first, int last_group, int sub,
+                                            const int (&eff)[C], uint4 (&v)[kUnroll][C]) {
   const uint32_t chunks = (uint32_t)(a.c >> 3);
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
-    const GroupAt at = group_at<S>(a, g_first + u, last_group, sub);
-    const uint32_t off = __umul24((uint32_t)at.rs, chunks) + eff;   // < 2^24
-    v[u] = load_stream(at_byte(a.x + at.r0 * chunks, off * 16u));
+    const GroupAt at = group_at<P>(a, g_first + u, last_group, sub);
+    const uint32_t row_off = __umul24((uint32_t)at.rs, chunks);   // < 2^24
+#pragma unroll
+    for (int i = 0; i < C; ++i) v[u][i] = load_stream(at_byte(a.x + at.r0 * chunks, (row_off + eff[i]) * 16u));
   }
 }
 
-// S: slots (lanes) per row.  MODE: the amax pass (the same chain, no stores), codes and
-// scales, or also the nullable rstd_out / y_out.
+// The butterfly's register levels: the pairwise sum of r[0 .. C), padded with zeros to a
+// power of two (a zero partner leaves the value unchanged: sums of squares are >= +0).
+template <int C>
+__device__ __forceinline__ float register_levels(const float (&r)[C]) {
+  static_assert(C == 1 || C == 3, "one or three slots per lane");
+  if (C == 1) return r[0];
+  return (r[0] + r[1]) + r[C - 1];
+}
+
+// P: lanes per row, C: slots per lane.  MODE: the amax pass (the same chain, no stores),
+// codes and scales, or also the nullable rstd_out / y_out.  The loop body has no divergent
+// branch, which would make the compiler wait for every outstanding store before the next
+// loads are used (vmcnt counts stores too).
 //
-// Every lane does the same work: a lane whose slot lies past the row's c/8 chunks takes the
-// chunk (slot mod c/8) -- same parity, so block partners stay partners -- but adds 0 to the
-// statistic, and so computes and stores exactly what the lane owning that chunk does.  Both
-// lanes of a block store its scale byte.  The loop body therefore has no divergent branch,
-// which would make the compiler wait for every outstanding store before the next loads are
-// used (vmcnt counts stores too).
-//
-// The 16 wavefronts of a workgroup take consecutive groups (kUnroll per wavefront, 64 per
-// workgroup step; workgroups interleave), run the same number of steps and meet at a
-// barrier after each, so the rows in flight stay compact; the next step's groups are loaded
-// before the current ones are computed (two register sets, used in turn).
-template <int S, int MODE>
+// The 16 wavefronts of a workgroup take consecutive groups (kUnroll per wavefront per
+// step; workgroups interleave), run the same number of steps and meet at a barrier after
+// each, so the rows in flight stay compact; the next step's groups are loaded before the
+// current ones are computed (two register sets, used in turn).
+template <int P, int C, int MODE>
 __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
+  constexpr int kUnroll = C == 1 ? kMaxUnroll : 1;
   constexpr bool AMAX = MODE == kAmaxPass;
-  constexpr int R = kWave / S;             // rows per wavefront group
+  constexpr int R = kWave / P;             // rows per wavefront group
   constexpr int kStepGroups = kWaves * kUnroll;
   // static LDS, so that every address is known when compiling: a lookup is then one shift
   // of the pattern plus an immediate offset
@@ -237,11 +263,17 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int chunk = lane % S, sub = lane / S;
+  const int L = lane % P, sub = lane / P;
   const int chunks = (int)(a.c >> 3);
   const int blocks = (int)(a.c >> 4);
-  const bool lane_ok = chunk < chunks;
-  const int eff = lane_ok ? chunk : chunk % chunks;
+  bool live[C];
+  int eff[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const int ch = L + P * i;
+    live[i] = ch < chunks;
+    eff[i] = live[i] ? ch : ch % chunks;
+  }
 
   const int groups = (int)((a.rows + R - 1) / R);
   const int last_group = groups - 1;
@@ -250,76 +282,95 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
   const int steps = wg_first < groups ? (groups - wg_first + span - 1) / span : 0;
   const int my_first = wg_first + wave * kUnroll;
 
-  uint4 buf0[kUnroll], buf1[kUnroll];
-  load_groups<S>(a, my_first, last_group, sub, eff, buf0);
+  uint4 buf0[kUnroll][C], buf1[kUnroll][C];
+  load_groups<P, C, kUnroll>(a, my_first, last_group, sub, eff, buf0);
 
   const float gsf = call_global_scale(a.global_amax, a.amax_dev);
   if (!AMAX) fill_inverse_table(inv_tab, gsf, tid);
   const uint4* src = reinterpret_cast<const uint4*>(g_silu16_table);
   for (int i = tid; i < (int)(kTableBytes / 16); i += kThreads) lds4[i] = src[i];
-  const uint4 gv = global_ptr(a.gamma)[eff];
-  const h2 g2[4] = {__builtin_bit_cast(h2, gv.x), __builtin_bit_cast(h2, gv.y), __builtin_bit_cast(h2, gv.z),
-                    __builtin_bit_cast(h2, gv.w)};
+  h2 g2[C][4];
+#pragma unroll
+  for (int i = 0; i < C; ++i) {
+    const uint4 gv = global_ptr(a.gamma)[eff[i]];
+    g2[i][0] = __builtin_bit_cast(h2, gv.x);
+    g2[i][1] = __builtin_bit_cast(h2, gv.y);
+    g2[i][2] = __builtin_bit_cast(h2, gv.z);
+    g2[i][3] = __builtin_bit_cast(h2, gv.w);
+  }
   __syncthreads();
 
   float lane_amax = 0.0f;
   // one step: the groups g_first .. + kUnroll - 1 held in cur; the next step's into nxt
-  auto step = [&](int g_first, const uint4 (&cur)[kUnroll], uint4 (&nxt)[kUnroll]) {
-    load_groups<S>(a, g_first + span, last_group, sub, eff, nxt);
-    // the four groups' statistics: one reciprocal square root for all of them (lane L
-    // works on group L % 4's sum, then each quad hands group u's result to its lanes)
+  auto step = [&](int g_first, const uint4 (&cur)[kUnroll][C], uint4 (&nxt)[kUnroll][C]) {
+    load_groups<P, C, kUnroll>(a, g_first + span, last_group, sub, eff, nxt);
+    // the groups' statistics: one reciprocal square root for both (lane L works on group
+    // L % 2's sum, then each lane pair hands group u's result to both lanes)
     float sums[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t w[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
-      // the pairwise fold's first level: sq0 + sq1 of each fp16 pair
-      float pr[4];
+      float slot[C];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pr[e] = sum_sq_f16x2(w[e]);
-      float lane_v = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-      lane_v = lane_ok ? lane_v : 0.0f;
-      sums[u] = slot_sum_butterfly<S>(lane_v);
+      for (int i = 0; i < C; ++i) {
+        const uint32_t w[4] = {cur[u][i].x, cur[u][i].y, cur[u][i].z, cur[u][i].w};
+        // the slot's pairwise fold, its first level as fma(x0, x0, x1 * x1) per fp16 pair
+        float pr[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[e] = sum_sq_f16x2(w[e]);
+        const float v = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+        slot[i] = lane_levels<P>(live[i] ? v : 0.0f);
+      }
+      sums[u] = register_levels<C>(slot);
     }
-    static_assert(kUnroll == 4, "one group per lane of a quad");
-    const int q = lane & 3;
-    const float mine = q == 0 ? sums[0] : q == 1 ? sums[1] : q == 2 ? sums[2] : sums[3];
-    const float rq = 1.0f / sqrtf(mine / (float)a.c + a.eps);
-    const float rstds[kUnroll] = {quad_lane<0>(rq), quad_lane<1>(rq), quad_lane<2>(rq), quad_lane<3>(rq)};
+    float rstds[kUnroll];
+    if constexpr (kUnroll == 1) {
+      rstds[0] = 1.0f / sqrtf(sums[0] / (float)a.c + a.eps);
+    } else {
+      static_assert(kUnroll == 2, "one group per lane of a pair");
+      const float mine = (lane & 1) ? sums[1] : sums[0];
+      const float rq = 1.0f / sqrtf(mine / (float)a.c + a.eps);
+      rstds[0] = pair_lane<0>(rq);
+      rstds[1] = pair_lane<1>(rq);
+    }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const GroupAt at = group_at<S>(a, g_first + u, last_group, sub);
+      const GroupAt at = group_at<P>(a, g_first + u, last_group, sub);
       const float rstd = rstds[u];
-      const uint32_t w[4] = {cur[u].x, cur[u].y, cur[u].z, cur[u].w};
-      float y[8];
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        // the product rounded to fp32 first, then to fp16 (the opaque multiply also keeps the
-        // compiler from forming one v_fma_mixlo, a single rounding to fp16)
-        const float p0 = mul_f16_f32<false>(w[e / 2], rstd), p1 = mul_f16_f32<true>(w[e / 2], rstd);
-        // fp16(nn * gamma): the product of two fp16 values is exact in fp32, so its fp16
-        // rounding is the fp16 multiply's (one v_pk_mul_f16 for the pair)
-        h2 nn;
-        nn.x = (_Float16)p0;
-        nn.y = (_Float16)p1;
-        const uint32_t ab = __builtin_bit_cast(uint32_t, nn * g2[e / 2]);
-        y[e] = (float)__builtin_bit_cast(_Float16, table[ab & 0xFFFFu]);
-        y[e + 1] = (float)__builtin_bit_cast(_Float16, table[ab >> 16]);
-      }
-      if (AMAX) {
-        lane_amax = fold_abs8(lane_amax, y);
-        continue;
-      }
-      uint32_t s;
-      const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
-      const uint32_t row_chunk = __umul24((uint32_t)at.rs, (uint32_t)chunks) + eff;
-      *at_byte(a.codes + at.r0 * chunks, row_chunk * 4u) = code;
-      *at_byte(a.scales + at.r0 * blocks, __umul24((uint32_t)at.rs, (uint32_t)blocks) + (eff >> 1)) = (uint8_t)s;
-      if (MODE == kCodesAndSide) {
-        if (a.rstd_out) global_ptr(a.rstd_out)[at.r0 + at.rs] = rstd;
-        if (a.y_out)
-          *at_byte(a.y_out + at.r0 * chunks, row_chunk * 16u) =
-              make_uint4(f16_bits(y[0]) | (f16_bits(y[1]) << 16), f16_bits(y[2]) | (f16_bits(y[3]) << 16),
-                         f16_bits(y[4]) | (f16_bits(y[5]) << 16), f16_bits(y[6]) | (f16_bits(y[7]) << 16));
+      for (int i = 0; i < C; ++i) {
+        const uint32_t w[4] = {cur[u][i].x, cur[u][i].y, cur[u][i].z, cur[u][i].w};
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          // the product rounded to fp32 first, then to fp16 (the opaque multiply also keeps
+          // the compiler from forming one v_fma_mixlo, a single rounding to fp16)
+          const float p0 = mul_f16_f32<false>(w[e / 2], rstd), p1 = mul_f16_f32<true>(w[e / 2], rstd);
+          // fp16(nn * gamma): the product of two fp16 values is exact in fp32, so its fp16
+          // rounding is the fp16 multiply's (one v_pk_mul_f16 for the pair)
+          h2 nn;
+          nn.x = (_Float16)p0;
+          nn.y = (_Float16)p1;
+          const uint32_t ab = __builtin_bit_cast(uint32_t, nn * g2[i][e / 2]);
+          y[e] = (float)__builtin_bit_cast(_Float16, table[ab & 0xFFFFu]);
+          y[e + 1] = (float)__builtin_bit_cast(_Float16, table[ab >> 16]);
+        }
+        if (AMAX) {
+          lane_amax = fold_abs8(lane_amax, y);
+          continue;
+        }
+        uint32_t s;
+        const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
+        const uint32_t row_chunk = __umul24((uint32_t)at.rs, (uint32_t)chunks) + eff[i];
+        *at_byte(a.codes + at.r0 * chunks, row_chunk * 4u) = code;
+        *at_byte(a.scales + at.r0 * blocks, __umul24((uint32_t)at.rs, (uint32_t)blocks) + (eff[i] >> 1)) =
+            (uint8_t)s;
+        if (MODE == kCodesAndSide) {
+          if (a.rstd_out) global_ptr(a.rstd_out)[at.r0 + at.rs] = rstd;
+          if (a.y_out)
+            *at_byte(a.y_out + at.r0 * chunks, row_chunk * 16u) =
+                make_uint4(f16_bits(y[0]) | (f16_bits(y[1]) << 16), f16_bits(y[2]) | (f16_bits(y[3]) << 16),
+                           f16_bits(y[4]) | (f16_bits(y[5]) << 16), f16_bits(y[6]) | (f16_bits(y[7]) << 16));
+        }
       }
     }
     __builtin_amdgcn_s_barrier();
@@ -333,31 +384,41 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
   if (AMAX) workgroup_max_to(a.amax_out, lane_amax, amax_red, kWaves);
 }
 
-template <int S, bool AMAX>
-hipError_t launch_s(const RsArgs& a, const DeviceInfo& dev, hipStream_t stream) {
-  constexpr int R = kWave / S;
+template <int P, int C, bool AMAX>
+hipError_t launch_pc(const RsArgs& a, const DeviceInfo& dev, hipStream_t stream) {
+  constexpr int R = kWave / P;
   const int64_t groups = (a.rows + R - 1) / R;
+  constexpr int kUnroll = C == 1 ? kMaxUnroll : 1;
   int64_t grid = (groups + kWaves * kUnroll - 1) / (kWaves * kUnroll);
   if (grid > dev.cu_count) grid = dev.cu_count;
   const dim3 g((uint32_t)grid), b(kThreads);
-  if (AMAX) hipLaunchKernelGGL((rms_silu_kernel<S, kAmaxPass>), g, b, 0, stream, a);
-  else if (a.rstd_out || a.y_out) hipLaunchKernelGGL((rms_silu_kernel<S, kCodesAndSide>), g, b, 0, stream, a);
-  else hipLaunchKernelGGL((rms_silu_kernel<S, kCodes>), g, b, 0, stream, a);
+  if (AMAX) hipLaunchKernelGGL((rms_silu_kernel<P, C, kAmaxPass>), g, b, 0, stream, a);
+  else if (a.rstd_out || a.y_out) hipLaunchKernelGGL((rms_silu_kernel<P, C, kCodesAndSide>), g, b, 0, stream, a);
+  else hipLaunchKernelGGL((rms_silu_kernel<P, C, kCodes>), g, b, 0, stream, a);
   return hipGetLastError();
 }
 
+// c/8 = P (a power of two) or 3 P: every lane busy; otherwise P = the power of two above
+// c/8 with one slot per lane.
 template <bool AMAX>
 hipError_t launch_pass(const RsArgs& a, const DeviceInfo& dev, hipStream_t stream) {
+  switch ((int)(a.c >> 3)) {
+    case 2: return launch_pc<2, 1, AMAX>(a, dev, stream);
+    case 4: return launch_pc<4, 1, AMAX>(a, dev, stream);
+    case 6: return launch_pc<2, 3, AMAX>(a, dev, stream);
+    case 8: return launch_pc<8, 1, AMAX>(a, dev, stream);
+    case 12: return launch_pc<4, 3, AMAX>(a, dev, stream);
+    case 16: return launch_pc<16, 1, AMAX>(a, dev, stream);
+    case 24: return launch_pc<8, 3, AMAX>(a, dev, stream);
+    case 32: return launch_pc<32, 1, AMAX>(a, dev, stream);
+    case 48: return launch_pc<16, 3, AMAX>(a, dev, stream);
+    case 64: return launch_pc<64, 1, AMAX>(a, dev, stream);
+    default: break;
+  }
   const int64_t chunks = a.c >> 3;
-  if (chunks <= 16) return launch_s<16, AMAX>(a, dev, stream);
-  if (chunks <= 32) return launch_s<32, AMAX>(a, dev, stream);
-  return launch_s<64, AMAX>(a, dev, stream);
-}
-
-template <int S, int MODE>
-hipError_t allow_lds_s() {
-  (void)&rms_silu_kernel<S, MODE>;   // static LDS only: nothing to allow
-  return hipSuccess;
+  if (chunks <= 16) return launch_pc<16, 1, AMAX>(a, dev, stream);
+  if (chunks <= 32) return launch_pc<32, 1, AMAX>(a, dev, stream);
+  return launch_pc<64, 1, AMAX>(a, dev, stream);
 }
 
 }  // namespace
@@ -375,17 +436,7 @@ hipError_t build_silu16_table(unsigned int* ambiguous) {
 }
 
 hipError_t prepare_rms_silu() {
-  hipError_t e = hipSuccess;
-  if (e == hipSuccess) e = allow_lds_s<16, kAmaxPass>();
-  if (e == hipSuccess) e = allow_lds_s<16, kCodes>();
-  if (e == hipSuccess) e = allow_lds_s<16, kCodesAndSide>();
-  if (e == hipSuccess) e = allow_lds_s<32, kAmaxPass>();
-  if (e == hipSuccess) e = allow_lds_s<32, kCodes>();
-  if (e == hipSuccess) e = allow_lds_s<32, kCodesAndSide>();
-  if (e == hipSuccess) e = allow_lds_s<64, kAmaxPass>();
-  if (e == hipSuccess) e = allow_lds_s<64, kCodes>();
-  if (e == hipSuccess) e = allow_lds_s<64, kCodesAndSide>();
-  return e;
+  return hipSuccess;   // static LDS only: nothing to allow
 }
 
 hipError_t launch_rms_silu(const RmsSiluLaunch& p, const DeviceInfo& dev, hipStream_t stream) {
