@@ -106,8 +106,8 @@ def make_inputs(wl, torch, amax):
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(rows are independent; see DESIGN.md for how the path would shard).", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path (rows are "
+              "independent, so each GPU would quantize its own range of rows).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -36,7 +36,7 @@
  *             h += bf16(o + bias) * scale, then NVFP4 of bf16(rms_norm(h,
  *             gamma, eps)) with fp32 gamma; hidden size a multiple of 512.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - global scale gsf = 2688 / global_amax (448 * 6), IEEE fp32 division;
  *   - 1/6 is the correctly rounded fp32 constant, not an approximate rcp;
  *   - inverse scale = gsf / dec(s) (IEEE), and 0 when the scale code is 0;
