@@ -125,6 +125,34 @@ def test_dynamic(nq, rows, c):
     check(got, want)
 
 
+@pytest.mark.parametrize("pattern", [0x0000, 0x8000])
+def test_signed_zero_rows(nq, pattern):
+    """Rows of +0 or of -0 only: the statistic is 0 (rstd = 1/sqrt(eps)), y is the signed
+    zero that SiLU keeps, the call's own amax is 0 (global scale 0), and every code carries
+    y's sign alone; the static form under a positive amax gives the same codes."""
+    rows, c = 300, 192
+    print("rms_silu zero rows", hex(pattern), flush=True)
+    _, gamma = case(rows, c, 11)
+    x = np.full((rows, c), pattern, np.uint16)
+    got = gpu(nq, x, gamma, 1e-6, None, dynamic=True)
+    want = oracle.rms_silu_dynamic(x, gamma, 1e-6, want_y=True)
+    assert want["amax"] == 0.0 and u32(got["amax"]) == 0
+    check(got, want)
+    assert set(np.unique(want["codes"])) <= {0x00, 0x08, 0x80, 0x88}
+    check(gpu(nq, x, gamma, 1e-6, 6.0), oracle_rms_silu(x, gamma, 1e-6, 6.0))
+
+
+def test_full_rms_silu_16x120x216x192_dynamic(nq):
+    wl = workloads.get("rms_silu_16x120x216x192")
+    print("generating", wl.name, flush=True)
+    x, gamma = wl.x(), wl.weight()
+    got = gpu(nq, x, gamma, wl.eps, None, y=False, dynamic=True)
+    print("oracle", flush=True)
+    want = oracle.rms_silu_dynamic(x, gamma, wl.eps, want_y=False)
+    assert u32(got["amax"]) == u32(want["amax"])
+    check(got, want)
+
+
 def test_full_rms_silu_16x120x216x192(nq):
     wl = workloads.get("rms_silu_16x120x216x192")
     amax = workloads.calibration_amax(wl.name)
