@@ -60,7 +60,10 @@ def check(got, want):
     assert_equal(got["scales"], want["scale_bytes"], "scales")
 
 
-@pytest.mark.parametrize("c", [16, 64, 96, 128, 192, 256, 384, 512])
+# c/8 chunks per row: 2 .. 64 on P lanes with one slot each (16, 32, 64, 128, 256, 512),
+# on P = 2, 4, 8, 16 lanes with three slots (48, 96, 192, 384), and padded to the next
+# power of two with repeated chunks (80, 160, 320, 496)
+@pytest.mark.parametrize("c", [16, 32, 48, 64, 80, 96, 128, 160, 192, 256, 320, 384, 496, 512])
 @pytest.mark.parametrize("rows", [1, 3, 257, 4099])
 def test_shapes(nq, rows, c):
     print("rms_silu", rows, c, flush=True)
@@ -115,7 +118,7 @@ def test_channels_last_view(nq):
     assert_equal(to_host(scales), want["scale_bytes"], "scales")
 
 
-@pytest.mark.parametrize("c", [96, 192, 384])
+@pytest.mark.parametrize("c", [64, 80, 96, 192, 384])
 @pytest.mark.parametrize("rows", [1, 300, 5000])
 def test_dynamic(nq, rows, c):
     x, gamma = case(rows, c, 7 * rows + c, scale=3.0)
