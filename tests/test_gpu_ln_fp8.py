@@ -80,6 +80,17 @@ def test_shapes(nq, m, k):
         check(gpu(nq, x, sc, sh, 1e-6, act), oracle_ln_fp8(x, sc, sh, 1e-6, inv))
 
 
+@pytest.mark.parametrize("k", [512 * c for c in range(1, 17) if c not in (1, 2, 6, 9, 14, 16)])
+def test_every_row_length(nq, k):
+    """The row lengths test_shapes leaves out, so that every instantiation (k/512 = 1 .. 16
+    chunks per lane; LDS planes past 64 KiB from 9 up) runs over 2,051 rows."""
+    m = 2051
+    print("ln_fp8", m, k, flush=True)
+    x, sc, sh = case(m, k, 17 * k + 1)
+    inv = oracle.fp8_inverse_scale(0.05)
+    check(gpu(nq, x, sc, sh, 1e-6, 0.05), oracle_ln_fp8(x, sc, sh, 1e-6, inv))
+
+
 def test_saturation_rounding_and_signed_zero(nq):
     """act_scale small enough that most |y / act_scale| pass 448 (saturated codes), large
     enough that they underflow (signed zeros), and adaLN columns with scale = -1 and

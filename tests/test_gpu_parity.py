@@ -152,6 +152,22 @@ def test_rms_adaln_shapes(nq, m, k, frames, order):
         check_rms(got, x, w, table, idx, 1e-6, amax)
 
 
+@pytest.mark.parametrize("k", [512 * c for c in range(1, 17)])
+def test_rms_adaln_every_row_length(nq, k):
+    """Every row length the kernel is instantiated for (k/512 = 1 .. 16 chunks per lane)
+    over 2,100 rows, several per workgroup, so the next row's prefetch and the tile's
+    scale block run at each."""
+    m, frames = 2100, 3
+    print("rms_adaln", m, k, flush=True)
+    g = np.random.Generator(np.random.PCG64(7 * k + 1))
+    x = rand_bf16((m, k), k + 3, 2.0)
+    w = bf16(1 + 0.1 * g.standard_normal(k).astype(np.float32))
+    table = bf16(0.1 * g.standard_normal((frames, 2, k)).astype(np.float32))
+    idx = (np.arange(m) * frames // m).astype(np.int32)
+    got = gpu_rms(nq, x, w, table, idx, 1e-6, 8.0)
+    check_rms(got, x, w, table, idx, 1e-6, 8.0)
+
+
 def test_rms_adaln_tiny_workload(nq):
     wl = workloads.get("rms_adaln_256x2048")
     amax = workloads.calibration_amax(wl.name)
