@@ -63,6 +63,22 @@ def test_quantize_shapes(nq, m, k):
         assert_equal(scales, want_s, "scales amax=%g" % amax)
 
 
+@pytest.mark.parametrize("slots", range(1, 17))
+def test_quantize_every_slot_count(nq, slots):
+    """Every row-piece instantiation (slots 16-byte chunks per lane, 1 .. 16): rows whose
+    last slot is full (k = 512 slots) and rows whose last slot holds one 64-column group
+    (k = 512 (slots - 1) + 64), over a ragged row tile."""
+    m = 300
+    for k in sorted({512 * slots, 512 * (slots - 1) + 64}):
+        print("quantize", m, k, flush=True)
+        g = np.random.Generator(np.random.PCG64(k + 11))
+        x = bf16(g.standard_normal((m, k)).astype(np.float32))
+        codes, scales = gpu_quantize(nq, x, 5.0)
+        want_c, want_s = oracle.nvfp4_quantize(x, 5.0)
+        assert_equal(codes, want_c, "codes k=%d" % k)
+        assert_equal(scales, want_s, "scales k=%d" % k)
+
+
 FIXED15 = np.array([0.75, -1.3125, 0.2, 2.5, -0.046875, 1.0, -3.0, 0.5, 1.75, -0.625, 0.0, 4.0,
                     -2.25, 0.09375, 1.5], np.float32)
 
