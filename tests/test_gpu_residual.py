@@ -83,7 +83,8 @@ def check(got, h, o, bias, scale, gamma, eps, amax):
 
 
 @pytest.mark.parametrize("form", ["bias", "nobias", "none"])
-@pytest.mark.parametrize("m,k", [(1, 512), (127, 1024), (129, 2048), (64, 3584), (300, 7168), (257, 8192)])
+@pytest.mark.parametrize("m,k", [(1, 512), (127, 1024), (129, 1536), (129, 2048), (64, 3584), (200, 4608),
+                                 (64, 6144), (300, 7168), (257, 8192)])
 def test_shapes(nq, m, k, form):
     print("residual_rms", m, k, form, flush=True)
     h, o, bias, scale, gamma = case(m, k, 13 * m + k + len(form), form)
@@ -195,7 +196,8 @@ def check_fold(got, want, m, k):
 
 
 @pytest.mark.parametrize("form", ["bias", "nobias", "none"])
-@pytest.mark.parametrize("m,k", [(1, 512), (127, 1024), (129, 2048), (64, 3584), (300, 7168), (257, 8192)])
+@pytest.mark.parametrize("m,k", [(1, 512), (127, 1024), (129, 1536), (129, 2048), (64, 3584), (200, 4608),
+                                 (64, 6144), (300, 7168), (257, 8192)])
 def test_fold_shapes(nq, m, k, form):
     print("residual_rms_adaln", m, k, form, flush=True)
     h, o, bias, gate, w, table, idx = fold_case(m, k, 17 * m + k + len(form), form)
