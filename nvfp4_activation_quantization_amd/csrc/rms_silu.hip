@@ -304,8 +304,9 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
   // one step: the groups g_first .. + kUnroll - 1 held in cur; the next step's into nxt
   auto step = [&](int g_first, const uint4 (&cur)[kUnroll][C], uint4 (&nxt)[kUnroll][C]) {
     load_groups<P, C, kUnroll>(a, g_first + span, last_group, sub, eff, nxt);
-    // the groups' statistics: one reciprocal square root for both (lane L works on group
-    // L % 2's sum, then each lane pair hands group u's result to both lanes)
+    // the groups' statistics; with two groups one reciprocal square root serves both
+    // (lane L works on group L % 2's sum, then each lane pair hands group u's result to
+    // both lanes)
     float sums[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
