@@ -255,7 +255,7 @@ def check_swiglu(got, proj, amax):
 
 
 @pytest.mark.parametrize("m,f", [(1, 64), (127, 128), (129, 192), (300, 512), (64, 19456), (257, 1024),
-                                 (300, 1088), (131, 2624)])
+                                 (300, 1088), (131, 2624), (130, 320), (257, 960), (129, 1792)])
 def test_swiglu_shapes(nq, m, f):
     print("swiglu", m, f, flush=True)
     proj = rand_bf16((m, 2 * f), m + f, 2.0)

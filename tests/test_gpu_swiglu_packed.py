@@ -95,7 +95,7 @@ def test_hand_worked_blocks(nq, interleaved):
 @pytest.mark.parametrize("interleaved", [False, True])
 @pytest.mark.parametrize("with_bias", [False, True])
 @pytest.mark.parametrize("m,f", [(1, 64), (127, 128), (129, 192), (300, 512), (64, 19456), (257, 1024),
-                                 (300, 1088), (131, 2624)])
+                                 (300, 1088), (131, 2624), (130, 320), (257, 960), (129, 1792)])
 def test_shapes(nq, m, f, with_bias, interleaved):
     print("swiglu_packed", m, f, "bias" if with_bias else "no bias", "paired" if interleaved else "value-first",
           flush=True)
