@@ -130,6 +130,24 @@ def test_rms_adaln_dynamic(nq, m, k, frames, order):
     assert got["status"] == want["status"]
 
 
+@pytest.mark.parametrize("k", [512 * c for c in range(1, 17)])
+def test_rms_adaln_dynamic_every_row_length(nq, k):
+    """The amax pass and the producer at every row length they are instantiated for
+    (k/512 = 1 .. 16), 2,100 rows over three frames."""
+    m, frames = 2100, 3
+    print("rms_adaln_dynamic", m, k, flush=True)
+    g = np.random.Generator(np.random.PCG64(5 * k + 2))
+    x = bf16(g.standard_normal((m, k)).astype(np.float32) * 2)
+    w = bf16(1 + 0.1 * g.standard_normal(k).astype(np.float32))
+    table = bf16(0.1 * g.standard_normal((frames, 2, k)).astype(np.float32))
+    idx = (np.arange(m) * frames // m).astype(np.int32)
+    got = gpu_rms_dynamic(nq, x, w, table, idx, 1e-6, y=False)
+    want = oracle.rms_adaln_dynamic(x, w, table, idx, 1e-6, want_y=False, scales_rows=oracle.padded_rows(m))
+    assert f32_bits(got["amax"]) == f32_bits(want["amax"])
+    assert_equal(got["codes"], want["codes"], "codes")
+    assert_equal(got["scales"], want["scales"], "scales")
+
+
 @pytest.mark.parametrize("m,f", [(1, 64), (129, 192), (300, 512), (64, 19456)])
 def test_swiglu_dynamic(nq, m, f):
     print("swiglu_dynamic", m, f, flush=True)

@@ -91,6 +91,18 @@ def test_every_row_length(nq, k):
     check(gpu(nq, x, sc, sh, 1e-6, 0.05), oracle_ln_fp8(x, sc, sh, 1e-6, inv))
 
 
+@pytest.mark.parametrize("k", [512 * c for c in range(1, 17)])
+def test_dynamic_every_row_length(nq, k):
+    """The per-call form (amax pass, scale kernel, producer) at every row length, 2,051 rows."""
+    m = 2051
+    print("ln_fp8 dynamic", m, k, flush=True)
+    x, sc, sh = case(m, k, 19 * k + 5, xscale=3.0, mscale=0.3)
+    got = gpu(nq, x, sc, sh, 1e-6, None, dynamic=True)
+    want = oracle.ln_adaln_fp8_dynamic(x, sc, sh, 1e-6)
+    assert u32(got["act_scale"])[0] == u32(np.float32(want["act_scale"]))
+    check(got, want)
+
+
 def test_saturation_rounding_and_signed_zero(nq):
     """act_scale small enough that most |y / act_scale| pass 448 (saturated codes), large
     enough that they underflow (signed zeros), and adaLN columns with scale = -1 and
