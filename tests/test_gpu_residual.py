@@ -135,7 +135,7 @@ def test_special_rows(nq):
 
 
 @pytest.mark.parametrize("form", ["bias", "none"])
-@pytest.mark.parametrize("m,k", [(1, 512), (129, 2048), (300, 7168), (64, 8192)])
+@pytest.mark.parametrize("m,k", [(1, 512), (129, 2048), (64, 3584), (200, 4608), (300, 7168), (64, 8192)])
 def test_dynamic(nq, m, k, form):
     print("residual_rms_dynamic", m, k, form, flush=True)
     h, o, bias, scale, gamma = case(m, k, 7 * m + k, form)
@@ -222,7 +222,7 @@ def test_fold_out_of_range_frames(nq):
 
 
 @pytest.mark.parametrize("form", ["bias", "none"])
-@pytest.mark.parametrize("m,k", [(1, 512), (129, 2048), (300, 7168)])
+@pytest.mark.parametrize("m,k", [(1, 512), (129, 2048), (64, 3584), (200, 4608), (300, 7168)])
 def test_fold_dynamic(nq, m, k, form):
     print("residual_rms_adaln_dynamic", m, k, form, flush=True)
     h, o, bias, gate, w, table, idx = fold_case(m, k, 3 * m + k, form)
