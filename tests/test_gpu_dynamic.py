@@ -148,7 +148,7 @@ def test_rms_adaln_dynamic_every_row_length(nq, k):
     assert_equal(got["scales"], want["scales"], "scales")
 
 
-@pytest.mark.parametrize("m,f", [(1, 64), (129, 192), (300, 512), (64, 19456)])
+@pytest.mark.parametrize("m,f", [(1, 64), (129, 192), (130, 320), (300, 512), (129, 1792), (64, 19456)])
 def test_swiglu_dynamic(nq, m, f):
     print("swiglu_dynamic", m, f, flush=True)
     g = np.random.Generator(np.random.PCG64(m * 5 + f))

@@ -141,7 +141,7 @@ def test_row_strided_view(nq, interleaved):
 
 
 @pytest.mark.parametrize("interleaved", [False, True])
-@pytest.mark.parametrize("m,f", [(1, 64), (129, 192), (300, 512), (64, 19456)])
+@pytest.mark.parametrize("m,f", [(1, 64), (129, 192), (130, 320), (300, 512), (129, 1792), (64, 19456)])
 def test_dynamic(nq, m, f, interleaved):
     print("swiglu_packed_dynamic", m, f, "paired" if interleaved else "value-first", flush=True)
     # a large bias so that rows past m (which load zeros) would raise the amax if counted
