@@ -287,9 +287,14 @@ __global__ __launch_bounds__(kThreads) void swiglu_kernel(const SwArgs a) {
   for (int64_t t = blockIdx.x; t < a.ntiles; t += gridDim.x) {
     const int64_t tn = t + gridDim.x < a.ntiles ? t + gridDim.x : a.ntiles - 1;
     const TileAt next = tile_at(a, tn, lane);
+    // the loads go out at a raised wavefront priority, ahead of other wavefronts' encoding
+    __builtin_amdgcn_s_setprio(1);
     load_batch<PAIRED, BIAS>(a, at, rb1, B);
+    __builtin_amdgcn_s_setprio(0);
     compute_batch<AMAX, PAIRED, BIAS>(a, at, rb0, A, table, gsf, inv_tab, tile_bytes, &lane_amax);
+    __builtin_amdgcn_s_setprio(1);
     load_batch<PAIRED, BIAS>(a, next, rb0, A);
+    __builtin_amdgcn_s_setprio(0);
     compute_batch<AMAX, PAIRED, BIAS>(a, at, rb1, B, table, gsf, inv_tab, tile_bytes, &lane_amax);
     if (!AMAX) {
       lds_barrier();
