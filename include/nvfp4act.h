@@ -48,9 +48,10 @@
  *   current device).  bf16 data is passed as raw 16-bit patterns.
  * - Every compute call is asynchronous on `stream` (a hipStream_t passed as
  *   void*, NULL = the default stream), allocates nothing and never waits for
- *   the device.  The one exception is the first SwiGLU or RMSNorm+SiLU call
- *   on a device (or an explicit nvfp4act_init), which builds the device's SiLU
- *   tables (bf16 and fp16) once and waits for it.
+ *   the device.  The first call on a device probes it once (its properties and
+ *   kernel attributes; no device work, no stream use).  The SiLU tables of the
+ *   swiglu_* and rms_silu_* calls are constants generated when the library is
+ *   built, so those calls may be captured into a HIP graph from the first one.
  * - Ownership: the caller allocates and frees every buffer.  Inputs must stay
  *   valid and unmodified, and outputs untouched, until the stream work is done.
  *   The library writes only codes, scales and the non-NULL side outputs.
@@ -80,7 +81,7 @@ extern "C" {
 #define NVFP4ACT_ERR_VALUE     4  /* global_amax not finite or too small; eps not finite or < 0 */
 #define NVFP4ACT_ERR_DEVICE    5  /* no usable gfx950 device is current                  */
 #define NVFP4ACT_ERR_LAUNCH    6  /* a HIP call failed; see nvfp4act_last_hip_error()   */
-#define NVFP4ACT_ERR_TABLE     7  /* the SiLU table could not be built exactly           */
+#define NVFP4ACT_ERR_TABLE     7  /* reserved: no longer returned (SiLU tables are built in) */
 
 /* ceil(m / 128) * 128: rows of the swizzled scale buffer */
 int64_t nvfp4act_padded_rows(int64_t m);
@@ -94,11 +95,14 @@ float nvfp4act_global_scale(float global_amax);
 const char* nvfp4act_status_string(int status);
 /* HIP error code behind the last NVFP4ACT_ERR_LAUNCH of the calling thread */
 int nvfp4act_last_hip_error(void);
+/* Hex sha256 of the sources the library was built from (the files of csrc/ and
+   this header, in name order, each preceded by its file name), so that a
+   caller can check that a binary matches the sources beside it.  Static text. */
+const char* nvfp4act_source_digest(void);
 
-/* Build the per-device constant tables on the current device (the SiLU table
-   tables of the swiglu_* and rms_silu_* calls) and wait for them.
-   Idempotent; optional (those calls run it on first use).  Call it before
-   capturing one of them into a HIP graph.  Returns a status. */
+/* Probe the current device (gfx950, CU count, kernel attributes).  Idempotent
+   and optional: every entry point does it on its first call on a device.
+   Returns a status. */
 int nvfp4act_init(void);
 
 /* Standalone NVFP4 quantize of a bf16 tensor (the attention-output quantize).
@@ -273,8 +277,7 @@ int residual_rms_adaln_nvfp4(float* h, const void* o, const void* bias, const vo
                r*(c/16) + b (no swizzle, no padding rows)
      rstd_out  [rows] fp32, nullable
      y_out     [rows, c] fp16, nullable: the pre-quantization activation
-   The first call on a device builds the fp16 SiLU table (as the swiglu_*
-   calls build theirs).  Returns a status. */
+   Returns a status. */
 int rms_silu_nvfp4(const void* x, const void* gamma, float eps, int64_t rows, int64_t c,
                    float global_amax, void* codes, void* scales, float* rstd_out, void* y_out,
                    void* stream);

@@ -19,13 +19,11 @@ namespace {
 
 using nvfp4act::DeviceInfo;
 
-constexpr int kMaxDevices = 64;
+constexpr int kMaxDevices = nvfp4act::kMaxDeviceSlots;
 
 struct DeviceState {
   bool probed = false;
   bool usable = false;
-  bool silu_ready = false;
-  int silu_status = NVFP4ACT_OK;
   DeviceInfo info{0};
 };
 
@@ -56,7 +54,7 @@ int current_device(const DeviceInfo** info, int* device_out) {
     }
     if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return NVFP4ACT_ERR_DEVICE;
     st.info.cu_count = prop.multiProcessorCount;
-    hipError_t e = nvfp4act::prepare_rms_adaln();
+    hipError_t e = nvfp4act::prepare_rms_adaln(dev);
     if (e == hipSuccess) e = nvfp4act::prepare_swiglu();
     if (e == hipSuccess) e = nvfp4act::prepare_residual_rms();
     if (e == hipSuccess) e = nvfp4act::prepare_rms_silu();
@@ -70,24 +68,6 @@ int current_device(const DeviceInfo** info, int* device_out) {
   if (!st.usable) return NVFP4ACT_ERR_DEVICE;
   *info = &st.info;
   if (device_out) *device_out = dev;
-  return NVFP4ACT_OK;
-}
-
-int ensure_silu_table(int dev) {
-  std::lock_guard<std::mutex> lock(g_mutex);
-  DeviceState& st = g_dev[dev];
-  if (st.silu_ready) return NVFP4ACT_OK;
-  if (st.silu_status != NVFP4ACT_OK) return st.silu_status;
-  unsigned int ambiguous = 0, ambiguous16 = 0;
-  hipError_t e = nvfp4act::build_silu_table(&ambiguous);
-  if (e == hipSuccess) e = nvfp4act::build_silu16_table(&ambiguous16);
-  if (e != hipSuccess) return fail_hip(e);
-  ambiguous += ambiguous16;
-  if (ambiguous != 0) {
-    st.silu_status = NVFP4ACT_ERR_TABLE;
-    return st.silu_status;
-  }
-  st.silu_ready = true;
   return NVFP4ACT_OK;
 }
 
@@ -120,19 +100,22 @@ const char* nvfp4act_status_string(int status) {
     case NVFP4ACT_ERR_VALUE: return "global_amax or eps out of range";
     case NVFP4ACT_ERR_DEVICE: return "no usable gfx950 device is current";
     case NVFP4ACT_ERR_LAUNCH: return "a HIP call failed (see nvfp4act_last_hip_error)";
-    case NVFP4ACT_ERR_TABLE: return "the SiLU table could not be built exactly";
+    case NVFP4ACT_ERR_TABLE: return "the SiLU table could not be built exactly (no longer returned: the tables are fixed when the library is built)";
     default: return "unknown status";
   }
 }
 
 int nvfp4act_last_hip_error(void) { return t_last_hip_error; }
 
+// The build passes the sha256 of the sources it compiled (csrc/* and include/nvfp4act.h).
+#ifndef NVFP4ACT_SOURCE_DIGEST
+#define NVFP4ACT_SOURCE_DIGEST "unknown"
+#endif
+const char* nvfp4act_source_digest(void) { return NVFP4ACT_SOURCE_DIGEST; }
+
 int nvfp4act_init(void) {
   const DeviceInfo* info = nullptr;
-  int dev = -1;
-  int st = current_device(&info, &dev);
-  if (st != NVFP4ACT_OK) return st;
-  return ensure_silu_table(dev);
+  return current_device(&info, nullptr);
 }
 
 }  // extern "C"
@@ -214,10 +197,7 @@ int swiglu_launch(const nvfp4act::SwigluLaunch& p, void* stream) {
     if (st != NVFP4ACT_OK) return st;
   }
   const DeviceInfo* info = nullptr;
-  int dev = -1;
-  int st = current_device(&info, &dev);
-  if (st != NVFP4ACT_OK) return st;
-  st = ensure_silu_table(dev);
+  int st = current_device(&info, nullptr);
   if (st != NVFP4ACT_OK) return st;
   hipError_t e = nvfp4act::launch_swiglu(p, *info, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? NVFP4ACT_OK : fail_hip(e);
@@ -397,10 +377,7 @@ int rms_silu_call(const void* x, const void* gamma, float eps, int64_t rows, int
     if (st != NVFP4ACT_OK) return st;
   }
   const DeviceInfo* info = nullptr;
-  int dev = -1;
-  int st = current_device(&info, &dev);
-  if (st != NVFP4ACT_OK) return st;
-  st = ensure_silu_table(dev);
+  int st = current_device(&info, nullptr);
   if (st != NVFP4ACT_OK) return st;
   nvfp4act::RmsSiluLaunch p{};
   p.x = x;

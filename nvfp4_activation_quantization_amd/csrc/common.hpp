@@ -53,6 +53,11 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
+// The fp16 bit pattern of fp16(f), round to nearest even (v_cvt_f16_f32 in the default mode).
+__device__ __forceinline__ uint32_t f16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+}
+
 // Round two fp32 values to bf16 (nearest, ties to even; gfx950 v_cvt_pk_bf16_f32,
 // which matches the integer rule on every non-NaN fp32 input) and pack them.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -86,6 +91,18 @@ __device__ __forceinline__ uint32_t pack_exact_bf16x2(float lo, float hi) {
 __device__ __forceinline__ uint32_t e4m3_code(float sf) {
   float c = __builtin_fminf(sf, 448.0f);
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, 0.0f, 0, false);
+}
+
+// Four signed E4M3 codes (nearest-even, saturating at +-448), a in the low byte.
+// v_cvt_pk_fp8_f32 rounds to nearest-even but turns magnitudes beyond 448 into NaN, so the
+// values are clamped first (v_med3 keeps the sign of zero).
+__device__ __forceinline__ uint32_t fp8_quad(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
+  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
+  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
+  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
 }
 
 // Exact value of an E4M3 code 0..126: exponent field 0 is m * 2^-9, else 2^(e-7)(1+m/8).

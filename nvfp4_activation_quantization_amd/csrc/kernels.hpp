@@ -139,15 +139,14 @@ constexpr int64_t kMaxLnK = 8192;   // the row is held in registers
 hipError_t launch_ln_fp8(const LnFp8Launch& p, const DeviceInfo& dev, hipStream_t stream);
 
 // Per-device, once: allow the LDS sizes the kernels use.
-hipError_t prepare_rms_adaln();
+// Devices the library keeps per-device state for (device ordinals 0 .. kMaxDeviceSlots - 1).
+constexpr int kMaxDeviceSlots = 64;
+// Once per device, with that device current: kernel attributes.
+hipError_t prepare_rms_adaln(int device);
 hipError_t prepare_swiglu();
 hipError_t prepare_residual_rms();
 hipError_t prepare_rms_silu();
 hipError_t prepare_ln_fp8();
 
-// Build the SiLU table of the current device and wait for it; *ambiguous receives the
-// number of entries whose rounding fp64 could not decide (0 expected).
-hipError_t build_silu_table(unsigned int* ambiguous);
-hipError_t build_silu16_table(unsigned int* ambiguous);   // the fp16 SiLU table, likewise
 
 }  // namespace nvfp4act

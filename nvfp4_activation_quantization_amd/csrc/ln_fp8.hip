@@ -44,18 +44,6 @@ struct LnArgs {
 };
 
 
-// Four signed E4M3 codes (nearest-even, saturating at +-448), a in the low byte.
-// v_cvt_pk_fp8_f32 rounds to nearest-even but turns magnitudes beyond 448 into NaN, so the
-// values are clamped first (v_med3 keeps the sign of zero).
-__device__ __forceinline__ uint32_t fp8_quad(float a, float b, float c, float d) {
-  a = __builtin_amdgcn_fmed3f(a, -448.0f, 448.0f);
-  b = __builtin_amdgcn_fmed3f(b, -448.0f, 448.0f);
-  c = __builtin_amdgcn_fmed3f(c, -448.0f, 448.0f);
-  d = __builtin_amdgcn_fmed3f(d, -448.0f, 448.0f);
-  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
-}
-
 // The inverse scale of the call: 1 / act_scale (static, checked on the host), or from the
 // device scale of a per-call form: 0 when that scale is 0 or its reciprocal overflows.
 __device__ __forceinline__ float call_inverse_scale(const LnArgs& a) {

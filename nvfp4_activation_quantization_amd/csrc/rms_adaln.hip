@@ -64,17 +64,34 @@ __device__ __forceinline__ void store_planes(float2* planes, int chunks, int c, 
   planes[3 * chunks + c] = make_float2(f[6], f[7]);
 }
 
-// y = bf16(bf16(bf16(bf16(x * rstd) * w) * opl) + shift) for the 8 elements of a chunk;
-// every rounding yields the fp32 encoding of the bf16 result directly (round_bf16).
+// y = bf16(bf16(bf16(bf16(x * rstd) * w) * opl) + shift) for the 8 elements of a chunk.
+// Every rounding is v_cvt_pk_bf16_f32 with a zero low operand, whose result is the fp32
+// encoding of the rounded value (round_bf16).  Each step is issued for all eight elements
+// before the next one starts (volatile asm keeps that order): left to itself the scheduler
+// runs the eight dependent chains one after another when registers are scarce, and a
+// wavefront then waits on every result.  The operations are those of the definition, in its
+// order, so the results are the same bits.
 __device__ __forceinline__ void modulate8(const float* x8, const float* w8, const float* o8,
                                           const float* h8, float rstd, float* y) {
+  float t[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float n = round_bf16(x8[e] * rstd);
-    float nw = round_bf16(n * w8[e]);
-    float mm = round_bf16(nw * o8[e]);
-    y[e] = round_bf16(mm + h8[e]);
-  }
+  for (int e = 0; e < 8; ++e) asm volatile("v_mul_f32 %0, %1, %2" : "=v"(t[e]) : "v"(x8[e]), "v"(rstd));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) asm volatile("v_cvt_pk_bf16_f32 %0, 0, %0" : "+v"(t[e]));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(t[e]) : "v"(w8[e]));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) asm volatile("v_cvt_pk_bf16_f32 %0, 0, %0" : "+v"(t[e]));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(t[e]) : "v"(o8[e]));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) asm volatile("v_cvt_pk_bf16_f32 %0, 0, %0" : "+v"(t[e]));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) asm volatile("v_add_f32 %0, %0, %1" : "+v"(t[e]) : "v"(h8[e]));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) asm volatile("v_cvt_pk_bf16_f32 %0, 0, %0" : "+v"(t[e]));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = t[e];
 }
 
 // Per-row output cursors of one lane: chunk j of the lane is chunk c = lane + 64 j.
@@ -226,9 +243,10 @@ __device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr,
 // every wavefront has the same 16 rows of work per tile.
 //
 // Each wavefront keeps its current row unpacked to fp32 in registers (8 CPL values per
-// lane) from the statistic to the output pass, so every element is unpacked once; right
-// after the statistic it issues the loads of its next row (4 CPL registers), which then
-// arrive while the output pass runs.
+// lane) from the statistic to the output pass, so every element is unpacked once.  The
+// packed registers (4 CPL) are free once the statistic has unpacked them: in the output
+// pass the load of the next row's chunk j is issued as soon as chunk j has been modulated,
+// so the next row arrives during the rest of the pass.
 //
 // LDS: inverse-scale table (128 fp32); twelve fp32 planes of float2 indexed by chunk (weight
 // elements 0-1, 2-3, 4-5, 6-7, then bf16(1 + scale) and shift alike), so each ds_read_b64
@@ -327,11 +345,12 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
         if (!TILE && !AMAX) zero_row_scales(a.scales, r, kK, lane);   // TILE: already zero in LDS
         continue;
       }
-      // this wavefront's next row (prefetched right after the statistic)
+      // this wavefront's next row (loaded chunk by chunk during the output pass)
       int64_t rn = (i + 1 < kRowsPerWave) ? r + WAVES : next_first;
       rn = rn < m ? rn : m - 1;
-      // the row arrived during the previous row's output pass: unpack it once, take the
-      // statistic, then prefetch the next row into the packed registers
+      // the row arrived during the previous row's output pass: unpack it once and take the
+      // statistic; the next row's chunks are loaded into the packed registers one by one in
+      // the output pass, each as soon as the chunk that occupied its place is modulated
       float xf[CPL][8];
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -340,7 +359,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(xf[j][e], xf[j][e], acc[e]);
       }
-      load_row<CPL>(xr, x + rn * kChunks, lane);
+      const NVFP4_GLOBAL uint4* xn = x + rn * kChunks;
       const float sum = lane_sum_butterfly(((acc[0] + acc[1]) + (acc[2] + acc[3])) +
                                            ((acc[4] + acc[5]) + (acc[6] + acc[7])));
       const float rstd = 1.0f / sqrtf(sum / (float)kK + a.eps);
@@ -348,6 +367,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
       const int64_t t = frame_idx[r];
       if (t < 0 || t >= a.num_frames) {
         if (!AMAX) zero_row(a, r, lane, !TILE);
+        load_row<CPL>(xr, xn, lane);
         continue;
       }
       RowOut o = row_out(a, r, lane);
@@ -357,6 +377,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
         const float u = emit_row_unstaged(a.x, a.shift, a.scale, a.frame_stride, o, kK, r, t, wp, rstd, gsf,
                                           inv_tab, TILE, AMAX);
         lane_amax = __builtin_fmaxf(lane_amax, u);
+        load_row<CPL>(xr, xn, lane);
         continue;
       }
       // Output pass, software-pipelined over the lane's chunks: the parameters of chunk j + 1
@@ -376,6 +397,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
         split8(pc[4], pc[5], pc[6], pc[7], o8);
         split8(pc[8], pc[9], pc[10], pc[11], h8);
         modulate8(xf[j], w8, o8, h8, rstd, y);
+        xr[j] = load_stream(reinterpret_cast<const uint4*>(xn + lane + kWave * j));
         if (AMAX) {
           lane_amax = fold_abs8(lane_amax, y);
           if (j + 1 < CPL) {
@@ -542,7 +564,8 @@ hipError_t launch_rms(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev, h
 
 }  // namespace
 
-hipError_t prepare_rms_adaln() {
+hipError_t prepare_rms_adaln(int device) {
+  if (device < 0 || device >= kMaxDeviceSlots) return hipErrorInvalidDevice;
   hipError_t (*fns[16])() = {allow_lds<1>,  allow_lds<2>,  allow_lds<3>,  allow_lds<4>,
                              allow_lds<5>,  allow_lds<6>,  allow_lds<7>,  allow_lds<8>,
                              allow_lds<9>,  allow_lds<10>, allow_lds<11>, allow_lds<12>,

@@ -16,7 +16,7 @@
 // as in the other producers.
 //
 // One 1024-thread workgroup per CU, persistent over groups of rows; the 128 KiB fp16 SiLU
-// table (built once per device in fp64, like the bf16 one) is copied into LDS; each lane's
+// table (generated at build time, like the bf16 one) is copied into LDS; each lane's
 // 8 gamma values stay in registers (a lane's chunk index never changes).  The kernel is
 // bound by its instruction count, so the per-element work is kept small: the statistic's
 // pairs as fused multiply-adds (squares of fp16 values are exact), one reciprocal square
@@ -27,8 +27,12 @@
 
 namespace nvfp4act {
 
-__device__ uint16_t g_silu16_table[65536];
-__device__ unsigned int g_silu16_ambiguous;
+// fp16(g * sigmoid(g)) for every fp16 pattern g, generated when the library is built
+// (silu_tables_gen.cpp: fp64 evaluation, nearest-even, the build fails on an entry fp64
+// cannot decide) and loaded with the code object.
+__device__ const uint16_t g_silu16_table[65536] = {
+#include "silu_f16.inc"
+};
 
 namespace {
 
@@ -38,59 +42,6 @@ constexpr size_t kTableBytes = 65536 * sizeof(uint16_t);
 constexpr int kMaxUnroll = 2;             // row groups per wavefront in flight (one with 3 slots)
 constexpr int64_t kPieceRows = 1 << 30;    // rows per launch (row groups are numbered in 32 bits)
 
-// Round hi + lo to fp16, nearest-even (quantum 2^(E-10) for 2^E <= |v| < 2^(E+1), E >= -14,
-// subnormal quantum 2^-24; infinity from 65520 up).  lo only breaks an exact tie of hi; a
-// value within 2^-36 quanta of a midpoint is counted as undecidable by fp64.
-__device__ uint32_t round_to_f16(double hi, double lo, unsigned int* ambiguous) {
-  const uint32_t sign = __builtin_signbit(hi) ? 0x8000u : 0u;
-  const double a = fabs(hi);
-  if (a == 0.0) return sign;
-  if (a >= 65520.0) return sign | 0x7C00u;
-  const int e = ilogb(a);
-  const int qexp = e < -14 ? -24 : e - 10;
-  const double n = ldexp(a, -qexp);
-  const double fl = floor(n);
-  const double frac = n - fl;
-  bool up;
-  if (frac == 0.5 && lo != 0.0) {
-    up = (lo > 0.0) == (hi > 0.0);
-  } else {
-    if (fabs(frac - 0.5) < 0x1p-36) atomicAdd(ambiguous, 1u);
-    up = frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) == 1.0);
-  }
-  // the rounded magnitude (<= 11 significant bits) as fp16: exact conversion
-  const _Float16 h = (_Float16)(float)ldexp(up ? fl + 1.0 : fl, qexp);
-  return sign | (uint32_t)__builtin_bit_cast(uint16_t, h);
-}
-
-// One thread per fp16 pattern; |g| < 2^-30 through g/2 + (g/2) tanh(g/2) as for bf16.
-__global__ void silu16_table_kernel() {
-  const uint32_t g = blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= 65536u) return;
-  const uint32_t ex = (g >> 10) & 0x1Fu, mant = g & 0x3FFu;
-  uint32_t out;
-  if (ex == 0x1Fu) {
-    out = mant ? 0x7E00u : ((g & 0x8000u) ? 0x8000u : 0x7C00u);
-  } else {
-    const double x = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)g);
-    double hi, lo;
-    if (fabs(x) < 0x1p-30) {
-      hi = 0.5 * x;
-      lo = hi * hi;
-    } else {
-      hi = x / (1.0 + exp(-x));
-      lo = 0.0;
-    }
-    out = round_to_f16(hi, lo, &g_silu16_ambiguous);
-  }
-  g_silu16_table[g] = (uint16_t)out;
-}
-
-// fp16(f) and its bit pattern (round to nearest even: the default mode)
-__device__ __forceinline__ uint32_t f16_bits(float f) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
-}
-__device__ __forceinline__ float round_f16(float f) { return (float)(_Float16)f; }
 
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
@@ -423,18 +374,6 @@ hipError_t launch_pass(const RsArgs& a, const DeviceInfo& dev, hipStream_t strea
 }
 
 }  // namespace
-
-hipError_t build_silu16_table(unsigned int* ambiguous) {
-  const unsigned int zero = 0;
-  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(g_silu16_ambiguous), &zero, sizeof zero);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(silu16_table_kernel, dim3(256), dim3(256), 0, 0);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = hipDeviceSynchronize();
-  if (e != hipSuccess) return e;
-  return hipMemcpyFromSymbol(ambiguous, HIP_SYMBOL(g_silu16_ambiguous), sizeof *ambiguous);
-}
 
 hipError_t prepare_rms_silu() {
   return hipSuccess;   // static LDS only: nothing to allow

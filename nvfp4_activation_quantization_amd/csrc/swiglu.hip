@@ -6,8 +6,9 @@
 // up = bf16(up + bias_up), gate = bf16(gate + bias_gate)), and the paired column layout of
 // the FastVideo branch compare's quant_probe (value of column j at 2j, gate at 2j + 1).
 //
-// S is a 65,536-entry bf16 table indexed by the gate's bit pattern, built once per
-// device in fp64 by silu_table_kernel.  Each workgroup (one per CU, persistent over a
+// S is a 65,536-entry bf16 table indexed by the gate's bit pattern, generated when the
+// library is built (silu_tables_gen.cpp: fp64 evaluation, nearest-even, the build fails on
+// an entry fp64 cannot decide) and loaded with the code object.  Each workgroup (one per CU, persistent over a
 // set of 128-row x 512-column tiles) copies the 128 KiB table into its static LDS; every
 // element then costs one LDS lookup, one multiply and one bf16 rounding before the
 // quantizer.  Each tile's scale bytes are gathered in LDS and leave with 16-byte stores;
@@ -17,8 +18,9 @@
 
 namespace nvfp4act {
 
-__device__ uint16_t g_silu_table[65536];
-__device__ unsigned int g_silu_ambiguous;
+__device__ const uint16_t g_silu_table[65536] = {
+#include "silu_bf16.inc"
+};
 
 namespace {
 
@@ -28,54 +30,6 @@ constexpr size_t kTableBytes = 65536 * sizeof(uint16_t);
 constexpr int kTileCols = 512;                     // 64 chunks: one per lane per row
 constexpr int kRowBatch = 4;                       // rows per wavefront in flight
 constexpr int kScaleBytes = kTileCols / 64 * 512;  // 4 KiB
-
-// Round hi + lo to bf16, nearest-even.  lo is a tiny residual that only breaks an exact
-// tie of hi; otherwise a value within 2^-36 of a midpoint (in units of the bf16 quantum)
-// is counted as undecidable by the fp64 evaluation.
-__device__ uint32_t round_to_bf16(double hi, double lo, unsigned int* ambiguous) {
-  const uint32_t sign = __builtin_signbit(hi) ? 0x8000u : 0u;
-  const double a = fabs(hi);
-  if (a == 0.0) return sign;
-  const int e = ilogb(a);                                // 2^e <= a < 2^(e+1)
-  const int qexp = e < -126 ? -133 : e - 7;              // bf16 quantum exponent
-  const double n = ldexp(a, -qexp);                      // exact scaling
-  const double fl = floor(n);
-  const double frac = n - fl;
-  bool up;
-  if (frac == 0.5 && lo != 0.0) {
-    up = (lo > 0.0) == (hi > 0.0);                       // residual moves the magnitude
-  } else {
-    if (fabs(frac - 0.5) < 0x1p-36) atomicAdd(ambiguous, 1u);
-    up = frac > 0.5 || (frac == 0.5 && fmod(fl, 2.0) == 1.0);
-  }
-  const float v = (float)ldexp(up ? fl + 1.0 : fl, qexp); // <= 9 significant bits
-  return sign | (__float_as_uint(v) >> 16);
-}
-
-// One thread per bf16 pattern.  For |g| < 2^-30, e^-g rounds to 1 in fp64 and g/2 can sit
-// exactly on a bf16 midpoint; there silu(g) = g/2 + (g/2) tanh(g/2) and the second term,
-// about (g/2)^2 > 0, decides the tie.
-__global__ void silu_table_kernel() {
-  const uint32_t g = blockIdx.x * blockDim.x + threadIdx.x;
-  if (g >= 65536u) return;
-  const uint32_t ex = (g >> 7) & 0xFFu, mant = g & 0x7Fu;
-  uint32_t out;
-  if (ex == 0xFFu) {
-    out = mant ? 0x7FC0u : ((g & 0x8000u) ? 0x8000u : 0x7F80u);
-  } else {
-    const double x = (double)__uint_as_float(g << 16);
-    double hi, lo;
-    if (fabs(x) < 0x1p-30) {
-      hi = 0.5 * x;
-      lo = hi * hi;
-    } else {
-      hi = x / (1.0 + exp(-x));
-      lo = 0.0;
-    }
-    out = round_to_bf16(hi, lo, &g_silu_ambiguous);
-  }
-  g_silu_table[g] = (uint16_t)out;
-}
 
 // The kernel arguments.  Two-pointer / value-first form: value row r at up + r*ld8 and gate
 // row r at gate + r*ld8 (uint4 units).  Paired form: row r of the projection at up + r*ld8,
@@ -342,18 +296,6 @@ hipError_t launch_form(SwArgs a, int64_t grid, hipStream_t stream) {
 }
 
 }  // namespace
-
-hipError_t build_silu_table(unsigned int* ambiguous) {
-  const unsigned int zero = 0;
-  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(g_silu_ambiguous), &zero, sizeof zero);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(silu_table_kernel, dim3(256), dim3(256), 0, 0);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = hipDeviceSynchronize();
-  if (e != hipSuccess) return e;
-  return hipMemcpyFromSymbol(ambiguous, HIP_SYMBOL(g_silu_ambiguous), sizeof *ambiguous);
-}
 
 hipError_t prepare_swiglu() {
   hipError_t e = allow_lds<false, false, false>();
