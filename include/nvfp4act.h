@@ -100,9 +100,9 @@ int nvfp4act_last_hip_error(void);
    caller can check that a binary matches the sources beside it.  Static text. */
 const char* nvfp4act_source_digest(void);
 
-/* Probe the current device (gfx950, CU count, kernel attributes).  Idempotent
-   and optional: every entry point does it on its first call on a device.
-   Returns a status. */
+/* Probe the current device (gfx950, CU count, kernel attributes, the device
+   address of the library's scratch).  Idempotent and optional: every entry
+   point does it on its first call on a device.  Returns a status. */
 int nvfp4act_init(void);
 
 /* Standalone NVFP4 quantize of a bf16 tensor (the attention-output quantize).
@@ -352,6 +352,26 @@ int rms_adaln_nvfp4_dynamic(const void* x, const void* weight, const void* shift
                             float eps, int64_t m, int64_t k, float* amax_out,
                             void* codes, void* scales, float* rstd_out, void* y_out,
                             uint32_t* status_word, void* stream);
+
+/* rms_adaln_nvfp4_dynamic without the amax_out argument, for callers that
+   cannot allocate device memory (code under HIP graph capture, tight serving
+   loops, harnesses that forbid hipMalloc): the call's amax word lives in a
+   256-byte scratch array that the library holds in device memory for each
+   device, from the first call on that device until the process ends.  The
+   call itself allocates nothing (no hipMalloc, hipFree or allocating library
+   routine); it enqueues the same three kernels as rms_adaln_nvfp4_dynamic (a
+   fill kernel zeroes the word, the amax pass, the producer) on `stream`.
+   Every call needs exactly one word of that scratch whatever m and k are, so
+   no input size exceeds it.  All calls on one device share the word: calls
+   that overlap on the device (different streams, or host threads without
+   ordering) race on it and may quantize with each other's amax; serialize
+   them.  The amax itself is not returned.  Arguments, outputs and status
+   codes are those of rms_adaln_nvfp4_dynamic. */
+int rms_adaln_nvfp4_dynamic_noalloc(const void* x, const void* weight, const void* shift,
+                                    const void* scale, int64_t frame_stride, int64_t num_frames,
+                                    const int32_t* frame_idx, float eps, int64_t m, int64_t k,
+                                    void* codes, void* scales, float* rstd_out, void* y_out,
+                                    uint32_t* status_word, void* stream);
 
 int swiglu_nvfp4_dynamic(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f,
                          float* amax_out, void* codes, void* scales, void* y_out, void* stream);

@@ -28,7 +28,10 @@ Entry points (see ``include/nvfp4act.h`` for the exact contract):
 each returning ``(codes, scales)`` (ln_adaln_fp8: codes); the per-call (dynamic) amax
 forms ``<name>_dynamic(...)`` take ``amax_out`` instead of the static amax and return
 ``(codes, scales, amax)`` with ``amax`` a one-element float32 device tensor
-(ln_adaln_fp8_dynamic: ``(codes, act_scale)``).
+(ln_adaln_fp8_dynamic: ``(codes, act_scale)``); and
+  rms_adaln_nvfp4_dynamic_noalloc(x, weight, table, frame_idx, eps)
+                                                          the per-call form whose amax word lives
+                                                          in the library's device scratch
 codes are ``[m, k/2]`` uint8 and scales ``[pad(m), k/16]`` uint8 in the 128x4 swizzle
 (buffer shapes as the FastVideo API page's ``new_quantized``).
 """
@@ -79,6 +82,8 @@ _SIGS = {
     "swiglu_nvfp4": (_I, [_P, _P, _I64, _I64, _I64, _F, _P, _P, _P, _P]),
     "nvfp4_quantize_dynamic": (_I, [_P, _I64, _I64, _P, _P, _P, _P]),
     "rms_adaln_nvfp4_dynamic": (_I, [_P, _P, _P, _P, _I64, _I64, _P, _F, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "rms_adaln_nvfp4_dynamic_noalloc": (_I, [_P, _P, _P, _P, _I64, _I64, _P, _F, _I64, _I64, _P, _P, _P, _P, _P,
+                                            _P]),
     "swiglu_nvfp4_dynamic": (_I, [_P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "swiglu_packed_nvfp4": (_I, [_P, _P, _I, _I64, _I64, _I64, _F, _P, _P, _P, _P]),
     "swiglu_packed_nvfp4_dynamic": (_I, [_P, _P, _I, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
@@ -303,6 +308,18 @@ def rms_adaln_nvfp4_dynamic(x: torch.Tensor, weight: torch.Tensor, table: torch.
                                                    status_word, stream)
     amax = _call(None, _lib.rms_adaln_nvfp4_dynamic, before, after, 0.0, amax_out, x.device, True)
     return codes, scales, amax
+
+
+def rms_adaln_nvfp4_dynamic_noalloc(x: torch.Tensor, weight: torch.Tensor, table: torch.Tensor,
+                                    frame_idx: torch.Tensor, eps: float, codes=None, scales=None, rstd_out=None,
+                                    y_out=None, status_word=None, stream=None):
+    """rms_adaln_nvfp4_dynamic whose amax word is the library's device scratch (the entry
+    point allocates nothing; pass codes and scales to allocate nothing here either).
+    Calls that overlap on one device race on that word."""
+    codes, scales, before, after = _rms_adaln_args(x, weight, table, frame_idx, eps, codes, scales, rstd_out, y_out,
+                                                   status_word, stream)
+    _check(_lib.rms_adaln_nvfp4_dynamic_noalloc(*before, *after))
+    return codes, scales
 
 
 # ---- SwiGLU ----------------------------------------------------------------------------------

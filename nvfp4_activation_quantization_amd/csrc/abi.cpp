@@ -473,6 +473,22 @@ int rms_adaln_nvfp4_dynamic(const void* x, const void* weight, const void* shift
                         codes, scales, rstd_out, y_out, status_word, stream);
 }
 
+int rms_adaln_nvfp4_dynamic_noalloc(const void* x, const void* weight, const void* shift, const void* scale,
+                                    int64_t frame_stride, int64_t num_frames, const int32_t* frame_idx, float eps,
+                                    int64_t m, int64_t k, void* codes, void* scales, float* rstd_out, void* y_out,
+                                    uint32_t* status_word, void* stream) {
+  if (m < 0 || k <= 0 || k % 512 != 0 || num_frames < 1 || frame_stride < k) return NVFP4ACT_ERR_SHAPE;
+  if (m == 0) return NVFP4ACT_OK;
+  const DeviceInfo* info = nullptr;
+  int dev = -1;
+  int st = current_device(&info, &dev);
+  if (st != NVFP4ACT_OK) return st;
+  float* amax_dev = nvfp4act::rms_adaln_scratch(dev);   // one word of the library's device scratch
+  if (!amax_dev) return NVFP4ACT_ERR_DEVICE;
+  return rms_adaln_call(x, weight, shift, scale, frame_stride, num_frames, frame_idx, eps, m, k, 0.0f, amax_dev,
+                        codes, scales, rstd_out, y_out, status_word, stream);
+}
+
 int swiglu_nvfp4(const void* up, const void* gate, int64_t ld, int64_t m, int64_t f, float global_amax,
                  void* codes, void* scales, void* y_out, void* stream) {
   return swiglu_call(up, gate, ld, m, f, global_amax, nullptr, codes, scales, y_out, stream);

@@ -141,8 +141,11 @@ hipError_t launch_ln_fp8(const LnFp8Launch& p, const DeviceInfo& dev, hipStream_
 // Per-device, once: allow the LDS sizes the kernels use.
 // Devices the library keeps per-device state for (device ordinals 0 .. kMaxDeviceSlots - 1).
 constexpr int kMaxDeviceSlots = 64;
-// Once per device, with that device current: kernel attributes.
+// Once per device, with that device current: kernel attributes, and the device address of the
+// scratch word of rms_adaln_nvfp4_dynamic_noalloc.
 hipError_t prepare_rms_adaln(int device);
+// That address (null before prepare_rms_adaln ran for the device).
+float* rms_adaln_scratch(int device);
 hipError_t prepare_swiglu();
 hipError_t prepare_residual_rms();
 hipError_t prepare_rms_silu();

@@ -564,8 +564,23 @@ hipError_t launch_rms(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev, h
 
 }  // namespace
 
+// Device scratch of the allocation-free per-call entry point: element 0 is the word its amax
+// pass folds max |y| into (zeroed by a fill kernel first), which the producer then reads.
+// Every call needs that one word, whatever its m and k, so no input size can exceed it.  Each
+// device holds its own copy until the process ends; calls that overlap on one device race on
+// it.  Host code never uses the symbol itself (on the host it is only a stand-in): it uses
+// the device address looked up once per device below.
+constexpr int kScratchFloats = 64;   // 256 bytes
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+static float* g_scratch_dev[kMaxDeviceSlots] = {};   // per device: the address of scratch
+
 hipError_t prepare_rms_adaln(int device) {
   if (device < 0 || device >= kMaxDeviceSlots) return hipErrorInvalidDevice;
+  void* ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  g_scratch_dev[device] = static_cast<float*>(ptr);
   hipError_t (*fns[16])() = {allow_lds<1>,  allow_lds<2>,  allow_lds<3>,  allow_lds<4>,
                              allow_lds<5>,  allow_lds<6>,  allow_lds<7>,  allow_lds<8>,
                              allow_lds<9>,  allow_lds<10>, allow_lds<11>, allow_lds<12>,
@@ -575,6 +590,10 @@ hipError_t prepare_rms_adaln(int device) {
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+float* rms_adaln_scratch(int device) {
+  return (device >= 0 && device < kMaxDeviceSlots) ? g_scratch_dev[device] : nullptr;
 }
 
 hipError_t launch_rms_adaln(const RmsLaunch& p, const DeviceInfo& dev, hipStream_t stream) {
