@@ -10,7 +10,13 @@ Prints ONE JSON line:
   roofline   the kernel's algorithmic GB/s (per-launch HIP events) against 8 TB/s peak,
              plus measured HBM traffic per launch from the committed rocprofv3 counter
              summary when it was taken on the current kernel sources (else null)
-  cpu_baseline  the CPU oracle timed on a bounded row sample of the same workload
+  stream_ceiling_GBps  a bench-side kernel (libnvfp4act_selftest.so) that moves the same
+             bytes as a bf16 NVFP4 producer (2 B read, 0.5625 B written per element) with no
+             arithmetic: what the memory system delivers for this mix
+  cpu_baseline  the CPU oracle timed over the whole workload on every CPU this process may
+             use, and on one thread
+When one set of inputs and outputs is smaller than 512 MB (so that it could stay in the
+256 MB Infinity Cache between steps) the steps rotate over enough copies to exceed it.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -40,8 +46,56 @@ def parse():
     p.add_argument("--dynamic", action="store_true",
                    help="time the per-call (dynamic) amax form: amax pass + quantize pass")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=32768, help="rows of the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=0, help="rows of the oracle sample (0: all rows)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also time a device-to-device copy of the input (the HBM counter calibration)")
     return p.parse_args()
+
+
+def cpu_share():
+    """(CPUs this process may run on, CPUs its cgroup quota allows or None)."""
+    avail = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        q, period = open("/sys/fs/cgroup/cpu.max").read().split()[:2]
+        if q != "max":
+            quota = max(1, int(int(q) // int(period)))
+    except (OSError, ValueError):
+        pass
+    return avail, quota
+
+
+def stream_ceiling(torch, wl, stream):
+    """GB/s of the bench-side stream kernel over this workload's [m, k] shape, or None when
+    the workload is not a single bf16 input of k <= 8192 columns quantized to NVFP4."""
+    import ctypes
+    if wl.kind not in ("rms_adaln", "quantize") or wl.k > 8192 or wl.k % 512:
+        return None
+    lib = ctypes.CDLL(os.path.join(ROOT, "nvfp4_activation_quantization_amd", "libnvfp4act_selftest.so"))
+    fn = lib.nvfp4act_selftest_stream
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    fn.restype = ctypes.c_int
+    x = torch.empty((wl.m, wl.k), dtype=torch.int16, device="cuda:0")
+    x.fill_(0x3F80)
+    codes = torch.empty((wl.m, wl.k // 2), dtype=torch.uint8, device="cuda:0")
+    scales = torch.empty(((wl.m + 127) // 128 * 128, wl.k // 16), dtype=torch.uint8, device="cuda:0")
+
+    def run():
+        rc = fn(x.data_ptr(), wl.m, wl.k, codes.data_ptr(), scales.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("nvfp4act_selftest_stream returned %d" % rc)
+
+    for _ in range(20):
+        run()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for s, e in ev:
+        s.record(stream)
+        run()
+        e.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(s.elapsed_time(e) for s, e in ev) / len(ev)
+    nbytes = wl.m * wl.k * 2 + wl.m * wl.k // 2 + (wl.m + 127) // 128 * 128 * (wl.k // 16)
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 def kernel_source_digest() -> str:
@@ -103,23 +157,9 @@ def make_inputs(wl, torch, amax):
     return args
 
 
-def main():
-    a = parse()
-    if a.gpus != 1:
-        print("bench.py measures one GPU only: there is no multi-GPU path (rows are "
-              "independent, so each GPU would quantize its own range of rows).", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def make_step(wl, a, nq, workloads, inp, amax, amax_dev, stream):
+    """The step function of one input/output set: one launch of the workload's entry point."""
     import torch
-
-    import nvfp4_activation_quantization_amd as nq
-    import workloads
-
-    wl = workloads.get(a.workload)
-    amax = workloads.calibration_amax(wl.name)
-    torch.cuda.set_device(0)
-    inp = make_inputs(wl, torch, amax)
     if wl.kind == "rms_silu":
         codes = torch.empty((wl.m, wl.k // 2), dtype=torch.uint8, device="cuda:0")
         scales = torch.empty((wl.m, wl.k // 16), dtype=torch.uint8, device="cuda:0")
@@ -127,8 +167,6 @@ def main():
         codes, scales = torch.empty((wl.m, wl.k), dtype=torch.uint8, device="cuda:0"), None
     else:
         codes, scales = nq.new_quantized(wl.m, wl.k, "cuda:0")
-    amax_dev = torch.zeros(1, dtype=torch.float32, device="cuda:0")
-    stream = torch.cuda.current_stream()
 
     if wl.kind == "ln_fp8":
         act_scale = workloads.fp8_act_scale(wl.name)
@@ -203,6 +241,43 @@ def main():
         def step():
             nq.swiglu_nvfp4(inp["x"], amax, codes=codes, scales=scales, stream=stream)
         nq.init()
+    return step
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print("bench.py measures one GPU only: there is no multi-GPU path (rows are "
+              "independent, so each GPU would quantize its own range of rows).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nvfp4_activation_quantization_amd as nq
+    import workloads
+
+    wl = workloads.get(a.workload)
+    amax = workloads.calibration_amax(wl.name)
+    torch.cuda.set_device(0)
+    inp = make_inputs(wl, torch, amax)
+    amax_dev = torch.zeros(1, dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+
+    # input/output sets: enough that one step's working set does not stay in the 256 MB
+    # Infinity Cache from one step to the next
+    working_set = wl.algorithmic_bytes()
+    n_sets = 1 if working_set >= (512 << 20) else min(8, -(-(512 << 20) // working_set))
+    steps_fns = []
+    for set_i in range(n_sets):
+        inp_i = inp if set_i == 0 else {key: v.clone() for key, v in inp.items()}
+        steps_fns.append(make_step(wl, a, nq, workloads, inp_i, amax, amax_dev, stream))
+    torch.cuda.synchronize()
+    step_count = [0]
+
+    def step():
+        steps_fns[step_count[0] % n_sets]()
+        step_count[0] += 1
 
     # GPU clock warm-up (untimed): a fresh process runs the first tens of milliseconds
     # of work at a lower clock, so run the step for ~0.3 s before the W warmup steps.
@@ -241,20 +316,23 @@ def main():
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
 
-    # practical ceiling for context: a device-to-device copy of the input bytes
-    x = inp["x"]
-    dst = torch.empty_like(x)
-    for _ in range(3):
-        dst.copy_(x)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(10):
-        dst.copy_(x)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_ms = c0.elapsed_time(c1) / 10
-    copy_gbps = 2 * x.numel() * x.element_size() / (copy_ms * 1e-3) / 1e9
-    del dst
+    # practical ceiling for context: the same bytes moved with no arithmetic
+    ceiling = stream_ceiling(torch, wl, stream)
+    copy_gbps = None
+    if a.copy_calibration:
+        # a device-to-device copy of the input: the kernel the HBM counters are scaled by
+        x = inp["x"]
+        dst = torch.empty_like(x)
+        for _ in range(3):
+            dst.copy_(x)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(10):
+            dst.copy_(x)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        copy_gbps = 2 * x.numel() * x.element_size() / (c0.elapsed_time(c1) / 10 * 1e-3) / 1e9
+        del dst
 
     traffic = None if a.dynamic else measured_traffic(wl.name)
 
@@ -275,6 +353,7 @@ def main():
         "config": {"workload": wl.name, "rows": wl.m, "hidden": wl.k,
                    "frames": wl.frames if wl.frames else None,
                    "algorithmic_bytes_per_step": alg_bytes,
+                   "working_set_bytes": working_set, "rotated_sets": n_sets,
                    ("act_scale" if wl.kind == "ln_fp8" else "global_amax"):
                        "per-call (device amax pass)" if a.dynamic
                        else (workloads.fp8_act_scale(wl.name) if wl.kind == "ln_fp8" else amax)},
@@ -285,23 +364,29 @@ def main():
         "kernel_us": round(kernel_ms * 1e3, 2),
         "kernel_us_median": round(float(np.median(per_launch_ms)) * 1e3, 2),
         "kernel_us_min": round(float(np.min(per_launch_ms)) * 1e3, 2),
-        "copy_ceiling_GBps": round(copy_gbps, 1),
+        "stream_ceiling_GBps": None if ceiling is None else round(ceiling, 1),
         "wall_s": round(wall, 3),
     }
+    if ceiling is not None:
+        out["roofline"]["frac_of_stream_ceiling"] = round(achieved / ceiling, 4)
+    if copy_gbps is not None:
+        out["copy_GBps"] = round(copy_gbps, 1)
 
     if not a.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, amax, a.cpu_rows, np)
+        out["cpu_baseline"] = cpu_baseline(wl, amax, a.cpu_rows or wl.m, np)
     print(json.dumps(out), flush=True)
 
 
 def cpu_baseline(wl, amax, rows, np):
-    """The CPU oracle (unchanged) on the first `rows` rows of the workload, split into
-    contiguous row blocks over the host's threads (rows are independent)."""
+    """The CPU oracle (unchanged) on the first `rows` rows of the workload (all rows by
+    default), split into contiguous row blocks over every CPU this process may use (rows are
+    independent), then the same rows on one thread."""
     from concurrent.futures import ThreadPoolExecutor
 
     import oracle
 
-    threads = max(1, min(16, len(os.sched_getaffinity(0))))
+    avail, quota = cpu_share()
+    threads = max(1, min(avail, quota) if quota else avail)
     rows = min(rows, wl.m)
     sel = np.arange(rows)
     x = wl.x_rows(sel) if not wl.kind.startswith("residual") else None
@@ -364,27 +449,43 @@ def cpu_baseline(wl, amax, rows, np):
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(part, blocks))
     dt = time.perf_counter() - t0
-    # the same code on one thread, over the first sixteenth of the sample
-    one = max(1, rows // 16)
+    # the same rows on one thread
     t1 = time.perf_counter()
-    part((0, one))
+    part((0, rows))
     dt1 = time.perf_counter() - t1
     bytes_per_row = wl.algorithmic_bytes() / wl.m
     return {"value": round(rows * bytes_per_row / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "threads": threads, "cores_available": avail, "cpu_quota": quota,
             "kind": "oracle", "rows_per_s": round(rows / dt, 1), "seconds": round(dt, 3),
-            "single_thread_rows_per_s": round(one / dt1, 1), "cpu_model": cpu_model(),
-            "sample": "first %d rows of %s, %d threads, row blocks (single thread: first %d rows)"
-                      % (rows, wl.name, threads, one)}
+            "single_thread_seconds": round(dt1, 3), "single_thread_rows_per_s": round(rows / dt1, 1),
+            "single_thread_value": round(rows * bytes_per_row / dt1 / 1e9, 5), "cpu_model": cpu_model(),
+            "sample": "%s %d rows of %s on %d threads (contiguous row blocks), then the same rows on one thread"
+                      % ("all" if rows == wl.m else "first", rows, wl.name, threads)}
 
 
 def cpu_model() -> str:
+    """The host CPU: /proc/cpuinfo's model name with its family / model / stepping numbers
+    (a virtual machine may shorten the name), and the socket / core counts lscpu reports."""
+    fields = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                fields.setdefault(k.strip(), v.strip())
     except OSError:
         pass
-    return "unknown"
+    desc = "%s (family %s, model %s, stepping %s)" % (fields.get("model name", "unknown"), fields.get("cpu family", "?"),
+                                                    fields.get("model", "?"), fields.get("stepping", "?"))
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        info = dict(l.split(":", 1) for l in out.splitlines() if ":" in l)
+        extra = [("Socket(s)", "sockets"), ("Core(s) per socket", "cores/socket"), ("Thread(s) per core", "threads/core"),
+                 ("CPU(s)", "cpus")]
+        desc += ", " + ", ".join("%s %s" % (name, info[key].strip()) for key, name in extra if key in info)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        pass
+    return desc
 
 
 if __name__ == "__main__":

@@ -221,12 +221,12 @@ int residual_rms_nvfp4(float* h, const void* o, const void* bias, const float* s
                        const float* gamma, float eps, int64_t m, int64_t k, float global_amax,
                        void* codes, void* scales, float* rstd_out, void* y_out, void* stream);
 
-/* The gated MLP residual of a DiT block folded into the next block's RMSNorm +
-   adaLN producer, over an fp32 residual stream (TensorRT-LLM PR #21483,
-   Summary: the MLP residual add is folded into the next block's norm, and the
-   folding block reads the gate from its own AdaLN table while shift and scale
-   come from the next block's; FastVideo API page, residual_norm_quantize: the
-   fp32 stream updated in place).  Per row r with t = frame_idx[r], element d:
+/* The gated MLP residual of a DiT block carried out by the next block's RMSNorm
+   + adaLN producer, over an fp32 residual stream (TensorRT-LLM PR #21483,
+   Summary: the next block's normalization performs the MLP branch's residual
+   add, taking the gate from the current block's AdaLN table and the shift and
+   scale from its own; FastVideo API page, residual_norm_quantize: the fp32
+   stream updated in place).  Per row r with t = frame_idx[r], element d:
      u    = bf16(o[d] + bias[d])               (u = o[d] without a bias)
      h[d] = h[d] + u * gate_t[d]               fp32, the product rounded, then
                                                the add; written back into h

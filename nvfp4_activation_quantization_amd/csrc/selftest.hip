@@ -10,7 +10,7 @@
 //      kind 3  pack_e2m1x8(x[8i .. 8i+7])     (v_cvt_scalef32_pk_fp4_f32, scale 1.0)
 //      kind 4  fp8_quad(x[4i .. 4i+3])        (signed E4M3 with med3 clamping)
 //      kind 5  f16_bits(x)                    (fp32 -> fp16, nearest even)
-// 2. nvfp4act_selftest_stream: the memory traffic of the 63,240 x 7168 producers (a 2-byte
+// 2. nvfp4act_selftest_stream: the memory traffic of an [m, k] bf16 NVFP4 producer (a 2-byte
 //    element read, half a byte of codes and 1/16 byte of swizzled scale written per
 //    element) with no arithmetic, launched like the standalone quantize kernel (one row per
 //    wavefront, four rows per workgroup forming whole scale units): what the memory system
@@ -92,7 +92,10 @@ __global__ __launch_bounds__(256) void stream_kernel(const uint4* __restrict__ x
   __syncthreads();
   for (int q = tid; q < kChunks / 8; q += 256) {
     const uint4 u = make_uint4(sc[0][q], sc[1][q], sc[2][q], sc[3][q]);
-    store_stream(reinterpret_cast<uint4*>(scales + g.tile * (kChunks / 8) * 512 + (int64_t)q * 512 + g.rr * 16), u);
+    // a plain store, as the producers use for scales: a 16-byte piece of a cache line must
+    // meet the other pieces in L2 (a non-temporal store sends it on alone)
+    *reinterpret_cast<NVFP4_GLOBAL uint4*>(global_ptr(scales) + g.tile * (kChunks / 8) * 512 + (int64_t)q * 512 +
+                                           g.rr * 16) = u;
   }
 }
 
@@ -126,11 +129,16 @@ int nvfp4act_selftest_convert(int kind, uint32_t first, int64_t count, void* out
   return hipGetLastError() == hipSuccess ? 0 : 6;
 }
 
-// The bare traffic of an [m, 7168] producer call (see the file comment): x [m, 7168] bf16,
-// codes [m, 3584] bytes, scales [pad(m), 448] bytes, all 16-byte aligned device memory.
+// The bare traffic of an [m, k] producer call (see the file comment; k a multiple of 512, at
+// most 8192): x [m, k] bf16, codes [m, k/2] bytes, scales [pad(m), k/16] bytes, all 16-byte
+// aligned device memory.  Returns 0, 2 for bad arguments, or 6 for a launch error.
 int nvfp4act_selftest_stream(const void* x, int64_t m, int64_t k, void* codes, void* scales, void* stream) {
-  if (k != 7168 || m <= 0 || !x || !codes || !scales) return 2;
-  hipLaunchKernelGGL(stream_kernel<14>, dim3((uint32_t)row_group_blocks(m)), dim3(256), 0,
+  if (k <= 0 || k % 512 != 0 || k > 8192 || m <= 0 || !x || !codes || !scales) return 2;
+  void (*kernels[16])(const uint4*, int64_t, uint32_t*, uint8_t*) = {
+      stream_kernel<1>,  stream_kernel<2>,  stream_kernel<3>,  stream_kernel<4>,  stream_kernel<5>,  stream_kernel<6>,
+      stream_kernel<7>,  stream_kernel<8>,  stream_kernel<9>,  stream_kernel<10>, stream_kernel<11>, stream_kernel<12>,
+      stream_kernel<13>, stream_kernel<14>, stream_kernel<15>, stream_kernel<16>};
+  hipLaunchKernelGGL(kernels[k / 512 - 1], dim3((uint32_t)row_group_blocks(m)), dim3(256), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint4*>(x), m, static_cast<uint32_t*>(codes),
                      static_cast<uint8_t*>(scales));
   return hipGetLastError() == hipSuccess ? 0 : 6;

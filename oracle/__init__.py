@@ -29,7 +29,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nvfp4_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# NVFP4_ORACLE_LIB names another build of the same source to load instead (the test suite's
+# AddressSanitizer / UndefinedBehaviorSanitizer build, see build_sanitized)
+_LIB_PATH = os.environ.get("NVFP4_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -44,6 +46,20 @@ def build(force: bool = True) -> str:
         subprocess.run(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
+
+
+# the sanitizers replace -O2 (they need frame pointers and keep every access)
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"]
+
+
+def build_sanitized(path: str) -> str:
+    """Compile the same source with AddressSanitizer and UndefinedBehaviorSanitizer into
+    ``path`` (host code only: the oracle has no GPU code).  A process that loads it needs the
+    ASan runtime preloaded and NVFP4_ORACLE_LIB=path."""
+    flags = [f for f in GCC_FLAGS if f != "-O2"] + SANITIZE_FLAGS
+    subprocess.run(["gcc", *flags, _SRC, "-o", path, "-lm"], check=True)
+    return path
 
 
 def _load():

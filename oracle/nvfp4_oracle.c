@@ -588,10 +588,10 @@ EXPORT void orc_residual_rms_rows_gsf(float* h, const uint16_t* o, const uint16_
     leave_ieee(s);
 }
 
-/* The residual add of a DiT block's gated MLP branch folded into the next
-   block's RMSNorm + adaLN producer ([TRT] Summary: the MLP residual add is
-   folded into the next block's norm; the folding block reads the gate from its
-   own AdaLN table while shift and scale come from the next block's table),
+/* The residual add of a DiT block's gated MLP branch carried out by the next
+   block's RMSNorm + adaLN producer ([TRT] Summary: the next block's
+   normalization performs the MLP branch's residual add, with the gate from the
+   current block's AdaLN table and shift and scale from its own),
    over an fp32 residual stream as in orc_residual_rms_rows_gsf.  Row i with
    t = frame_idx[i] in [0, num_frames), element d:
      u    = bf16(o[d] + bias[d])            (u = o[d] when bias is NULL)

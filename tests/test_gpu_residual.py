@@ -151,7 +151,7 @@ def test_dynamic(nq, m, k, form):
 
 
 # --------------------------------------------------------------------------------------
-# the gated residual folded into the next block's RMSNorm + adaLN
+# the gated residual applied by the next block's RMSNorm + adaLN
 # --------------------------------------------------------------------------------------
 
 def fold_case(m, k, seed, form="bias", frames=3):
