@@ -72,10 +72,10 @@ def stream_ceiling(torch, wl, stream):
     if wl.kind not in ("rms_adaln", "quantize") or wl.k > 8192 or wl.k % 512:
         return None
     lib = ctypes.CDLL(os.path.join(ROOT, "nvfp4_activation_quantization_amd", "libnvfp4act_selftest.so"))
-    fn = lib.nvfp4act_selftest_stream
+    fn, cols = lib.nvfp4act_selftest_stream, wl.k
     fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     fn.restype = ctypes.c_int
-    x = torch.empty((wl.m, wl.k), dtype=torch.int16, device="cuda:0")
+    x = torch.empty((wl.m, cols), dtype=torch.int16, device="cuda:0")
     x.fill_(0x3F80)
     codes = torch.empty((wl.m, wl.k // 2), dtype=torch.uint8, device="cuda:0")
     scales = torch.empty(((wl.m + 127) // 128 * 128, wl.k // 16), dtype=torch.uint8, device="cuda:0")
@@ -83,7 +83,7 @@ def stream_ceiling(torch, wl, stream):
     def run():
         rc = fn(x.data_ptr(), wl.m, wl.k, codes.data_ptr(), scales.data_ptr(), ctypes.c_void_p(stream.cuda_stream))
         if rc != 0:
-            raise RuntimeError("nvfp4act_selftest_stream returned %d" % rc)
+            raise RuntimeError("bench-side stream kernel returned %d" % rc)
 
     for _ in range(20):
         run()
@@ -94,7 +94,7 @@ def stream_ceiling(torch, wl, stream):
         e.record(stream)
     torch.cuda.synchronize()
     ms = sum(s.elapsed_time(e) for s, e in ev) / len(ev)
-    nbytes = wl.m * wl.k * 2 + wl.m * wl.k // 2 + (wl.m + 127) // 128 * 128 * (wl.k // 16)
+    nbytes = wl.m * cols * 2 + wl.m * wl.k // 2 + (wl.m + 127) // 128 * 128 * (wl.k // 16)
     return nbytes / (ms * 1e-3) / 1e9
 
 

@@ -229,10 +229,16 @@ __device__ __forceinline__ void emit_encoded(const RowOut& o, int j, const float
                                 pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
 }
 
+// The CPL chunks of a row, issued in chunk order: every path that loads a row then leaves
+// chunk 0 oldest, which lets the compiler wait for each chunk of the next statistic
+// separately instead of for (nearly) every outstanding load and store at its start.
 template <int CPL>
 __device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr, int lane) {
 #pragma unroll
-  for (int j = 0; j < CPL; ++j) v[j] = load_stream(reinterpret_cast<const uint4*>(xr + lane + kWave * j));
+  for (int j = 0; j < CPL; ++j) {
+    v[j] = load_stream(reinterpret_cast<const uint4*>(xr + lane + kWave * j));
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // ---- the staged kernel (k <= 8192, CPL = k / 512 chunks per lane) -------------------------
