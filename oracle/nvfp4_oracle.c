@@ -158,6 +158,14 @@ static double e4m3_value(uint8_t code) {
     return ldexp(1.0 + (double)m / 8.0, e - 7);
 }
 
+/* The values of codes 0..126 (e4m3_value), filled once when the library is
+   loaded so that the encoder's search reads a table. */
+static double e4m3_values[127];
+
+__attribute__((constructor)) static void fill_e4m3_values(void) {
+    for (int c = 0; c < 127; ++c) e4m3_values[c] = e4m3_value((uint8_t)c);
+}
+
 /* Round a non-negative fp32 to the nearest finite E4M3 value, ties to the
    even code, saturating (everything at or above 448, +inf included, maps to
    448).  The finite codes 0..126 are increasing in value, so the encoder
@@ -169,9 +177,9 @@ static uint8_t e4m3_encode(float x) {
     int lo = 0, hi = 126;                    /* invariant: value(lo) <= v < value(hi) */
     while (hi - lo > 1) {
         int mid = (lo + hi) / 2;
-        if (e4m3_value((uint8_t)mid) <= v) lo = mid; else hi = mid;
+        if (e4m3_values[mid] <= v) lo = mid; else hi = mid;
     }
-    double a = e4m3_value((uint8_t)lo), b = e4m3_value((uint8_t)hi);
+    double a = e4m3_values[lo], b = e4m3_values[hi];
     double midpoint = 0.5 * (a + b);         /* exact: few significant bits */
     if (v < midpoint) return (uint8_t)lo;
     if (v > midpoint) return (uint8_t)hi;
