@@ -67,31 +67,40 @@ __device__ __forceinline__ void store_planes(float2* planes, int chunks, int c, 
 // y = bf16(bf16(bf16(bf16(x * rstd) * w) * opl) + shift) for the 8 elements of a chunk.
 // Every rounding is v_cvt_pk_bf16_f32 with a zero low operand, whose result is the fp32
 // encoding of the rounded value (round_bf16).  Each step is issued for all eight elements
-// before the next one starts (volatile asm keeps that order): left to itself the scheduler
-// runs the eight dependent chains one after another when registers are scarce, and a
-// wavefront then waits on every result.  The operations are those of the definition, in its
-// order, so the results are the same bits.
+// before the next one starts: left to itself the scheduler runs the eight dependent chains
+// one after another when registers are scarce, and a wavefront then waits on every result.
+// A scheduling barrier that no vector ALU instruction may cross (memory, LDS and scalar
+// instructions may) separates the steps; inline assembly would order them too, but the
+// compiler pads the uses of an assembly result with wait states.  The operations are those
+// of the definition, in its order, so the results are the same bits.
+#define NVFP4_STEP_FENCE() __builtin_amdgcn_sched_barrier(0x3F4)
 __device__ __forceinline__ void modulate8(const float* x8, const float* w8, const float* o8,
                                           const float* h8, float rstd, float* y) {
   float t[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) asm volatile("v_mul_f32 %0, %1, %2" : "=v"(t[e]) : "v"(x8[e]), "v"(rstd));
+  for (int e = 0; e < 8; ++e) t[e] = x8[e] * rstd;
+  NVFP4_STEP_FENCE();
 #pragma unroll
-  for (int e = 0; e < 8; ++e) asm volatile("v_cvt_pk_bf16_f32 %0, 0, %0" : "+v"(t[e]));
+  for (int e = 0; e < 8; ++e) t[e] = round_bf16(t[e]);
+  NVFP4_STEP_FENCE();
 #pragma unroll
-  for (int e = 0; e < 8; ++e) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(t[e]) : "v"(w8[e]));
+  for (int e = 0; e < 8; ++e) t[e] = t[e] * w8[e];
+  NVFP4_STEP_FENCE();
 #pragma unroll
-  for (int e = 0; e < 8; ++e) asm volatile("v_cvt_pk_bf16_f32 %0, 0, %0" : "+v"(t[e]));
+  for (int e = 0; e < 8; ++e) t[e] = round_bf16(t[e]);
+  NVFP4_STEP_FENCE();
 #pragma unroll
-  for (int e = 0; e < 8; ++e) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(t[e]) : "v"(o8[e]));
+  for (int e = 0; e < 8; ++e) t[e] = t[e] * o8[e];
+  NVFP4_STEP_FENCE();
 #pragma unroll
-  for (int e = 0; e < 8; ++e) asm volatile("v_cvt_pk_bf16_f32 %0, 0, %0" : "+v"(t[e]));
+  for (int e = 0; e < 8; ++e) t[e] = round_bf16(t[e]);
+  NVFP4_STEP_FENCE();
 #pragma unroll
-  for (int e = 0; e < 8; ++e) asm volatile("v_add_f32 %0, %0, %1" : "+v"(t[e]) : "v"(h8[e]));
+  for (int e = 0; e < 8; ++e) t[e] = t[e] + h8[e];
+  NVFP4_STEP_FENCE();
 #pragma unroll
-  for (int e = 0; e < 8; ++e) asm volatile("v_cvt_pk_bf16_f32 %0, 0, %0" : "+v"(t[e]));
-#pragma unroll
-  for (int e = 0; e < 8; ++e) y[e] = t[e];
+  for (int e = 0; e < 8; ++e) y[e] = round_bf16(t[e]);
+  NVFP4_STEP_FENCE();
 }
 
 // Per-row output cursors of one lane: chunk j of the lane is chunk c = lane + 64 j.

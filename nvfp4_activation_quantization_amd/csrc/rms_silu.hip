@@ -17,11 +17,12 @@
 //
 // One 1024-thread workgroup per CU, persistent over groups of rows; the 128 KiB fp16 SiLU
 // table (generated at build time, like the bf16 one) is copied into LDS; each lane's
-// 8 gamma values stay in registers (a lane's chunk index never changes).  The kernel is
-// bound by its instruction count, so the per-element work is kept small: the statistic's
-// pairs as fused multiply-adds (squares of fp16 values are exact), one reciprocal square
-// root for four row groups, fp16(nn * gamma) as a packed fp16 multiply (exact products),
-// table addresses as one shift each, wave-uniform output bases with 32-bit lane offsets.
+// 8 gamma values stay in registers (a lane's chunk index never changes).  The per-element
+// work is kept small: the statistic's pairs as fused multiply-adds (squares of fp16 values
+// are exact), fp16(nn * gamma) as a packed fp16 multiply (exact products), table addresses
+// as one shift each, y kept in fp16 through the quantizer (its block maximum and its
+// products with the inverse scale read the fp16 values directly), wave-uniform output
+// bases with 32-bit lane offsets.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -65,6 +66,46 @@ __device__ __forceinline__ float sum_sq_f16x2(uint32_t w) {
   return d;
 }
 
+// The fp16 y of a chunk arrive from the table one per register, in the low half (ds_read_u16
+// zero-extends); packing them in pairs would cost a v_perm per pair (the compiler does not
+// load into high halves for this target).  The helpers below read the low halves directly.
+
+// max(t, |y[0]|, .., |y[7]|) of fp16 values (t >= 0, also fp16 in the low half), as four
+// v_max3_f16 with abs modifiers: the maximum is exact, so it is the fp32 maximum of the
+// widened values.
+__device__ __forceinline__ uint32_t fold_abs_f16x8(uint32_t t, const uint32_t (&y)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; e += 2) asm("v_max3_f16 %0, %1, |%2|, |%3|" : "=v"(t) : "v"(t), "v"(y[e]), "v"(y[e + 1]));
+  return t;
+}
+__device__ __forceinline__ uint32_t abs_max_f16x8(const uint32_t (&y)[8]) {
+  uint32_t t;
+  asm("v_max3_f16 %0, |%1|, |%2|, |%3|" : "=v"(t) : "v"(y[0]), "v"(y[1]), "v"(y[2]));
+  asm("v_max3_f16 %0, %1, |%2|, |%3|" : "=v"(t) : "v"(t), "v"(y[3]), "v"(y[4]));
+  asm("v_max3_f16 %0, %1, |%2|, |%3|" : "=v"(t) : "v"(t), "v"(y[5]), "v"(y[6]));
+  asm("v_max3_f16 %0, %1, |%2|, |%2|" : "=v"(t) : "v"(t), "v"(y[7]));
+  return t;
+}
+
+// The block quantizer of the other producers on the fp16 y of a chunk: the block amax from
+// the fp16 values, then each value widened exactly and multiplied by the inverse scale with
+// one fp32 rounding (mul_f16_f32), so the codes and the scale byte are those of the fp32
+// quantizer on the widened values.
+__device__ __forceinline__ uint32_t quantize_chunk_f16(const uint32_t (&y)[8], float gsf, const float* inv_tab,
+                                                       uint32_t* scale) {
+  float amax = f16_lo(abs_max_f16x8(y));
+  // the partner lane's half: amax >= 0, so the larger bit pattern is the larger value
+  amax = __uint_as_float(max_with_lane_xor1(__float_as_uint(amax)));
+  const float rcp6 = __uint_as_float(kRcp6Bits);
+  const uint32_t s = e4m3_code(gsf * (amax * rcp6));
+  const float inv = inv_tab[s];
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = mul_f16_f32<false>(y[i], inv);
+  *scale = s;
+  return pack_e2m1x8(v);
+}
+
 // base + off bytes, in the global address space (a wave-uniform base and a 32-bit lane offset
 // let the compiler use the scalar-base addressing form)
 template <typename T>
@@ -84,40 +125,77 @@ __device__ __forceinline__ float pair_lane(float v) {
                                                                sel, 0xF, 0xF, false));
 }
 
-// The butterfly's lane levels: v + v[lane ^ d] for d = 1, 2, .. P/2 (P a power of two <= 64),
-// the partner values from DPP and the gfx950 row swaps as in lane_sum_butterfly.
-template <int P>
-__device__ __forceinline__ float lane_levels(float v) {
-  uint32_t u;
+// v + v[lane ^ 4] on every register of v: the partner is lane + 4 in the even 4-lane banks
+// of a 16-lane row (row_shl:4) and lane - 4 in the odd ones (row_shr:4), so two DPP adds
+// with complementary bank masks write every lane.  Their destination is a new register
+// (the second add reads the inputs of lanes the first one has written); the s_nop covers
+// the wait a DPP read needs after a VALU write of its operand.
+template <int C>
+__device__ __forceinline__ void add_lane_xor4(float (&v)[C]) {
+  static_assert(C == 1 || C == 3, "one or three slots per lane");
+  float t[C];
+  if constexpr (C == 1) {
+    asm("s_nop 1\n\t"
+        "v_add_f32_dpp %0, %1, %1 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+        "v_add_f32_dpp %0, %1, %1 row_shr:4 row_mask:0xf bank_mask:0xa"
+        : "=&v"(t[0]) : "v"(v[0]));
+  } else {
+    asm("s_nop 1\n\t"
+        "v_add_f32_dpp %0, %3, %3 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+        "v_add_f32_dpp %1, %4, %4 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+        "v_add_f32_dpp %2, %5, %5 row_shl:4 row_mask:0xf bank_mask:0x5\n\t"
+        "v_add_f32_dpp %0, %3, %3 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+        "v_add_f32_dpp %1, %4, %4 row_shr:4 row_mask:0xf bank_mask:0xa\n\t"
+        "v_add_f32_dpp %2, %5, %5 row_shr:4 row_mask:0xf bank_mask:0xa"
+        : "=&v"(t[0]), "=&v"(t[1]), "=&v"(t[2]) : "v"(v[0]), "v"(v[1]), "v"(v[2]));
+  }
+#pragma unroll
+  for (int i = 0; i < C; ++i) v[i] = t[i];
+}
+
+// The butterfly's lane levels on every register of v: v + v[lane ^ d] for d = 1, 2, ..
+// P/2 (P a power of two <= 64), the partner values from DPP and the gfx950 row swaps as in
+// lane_sum_butterfly.  (v + partner and partner + v are the same IEEE sum.)
+template <int P, int C>
+__device__ __forceinline__ void lane_levels(float (&v)[C]) {
   if (P >= 2) {
-    u = __float_as_uint(v);
-    v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const uint32_t u = __float_as_uint(v[i]);
+      v[i] = v[i] + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0xB1, 0xF, 0xF, true));
+    }
   }
   if (P >= 4) {
-    u = __float_as_uint(v);
-    v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const uint32_t u = __float_as_uint(v[i]);
+      v[i] = v[i] + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x4E, 0xF, 0xF, true));
+    }
   }
-  if (P >= 8) {
-    u = __float_as_uint(v);
-    int t = __builtin_amdgcn_update_dpp((int)u, (int)u, 0x104, 0xF, 0x5, false);   // banks 0, 2: lane + 4
-    t = __builtin_amdgcn_update_dpp(t, (int)u, 0x114, 0xF, 0xA, false);            // banks 1, 3: lane - 4
-    v = v + __uint_as_float((uint32_t)t);
-  }
+  if (P >= 8) add_lane_xor4<C>(v);
   if (P >= 16) {
-    u = __float_as_uint(v);
-    v = v + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xF, 0xF, true));
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const uint32_t u = __float_as_uint(v[i]);
+      v[i] = v[i] + __uint_as_float((uint32_t)__builtin_amdgcn_mov_dpp((int)u, 0x128, 0xF, 0xF, true));
+    }
   }
   if (P >= 32) {
-    u = __float_as_uint(v);
-    const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    v = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const uint32_t u = __float_as_uint(v[i]);
+      const auto p16 = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      v[i] = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+    }
   }
   if (P >= 64) {
-    u = __float_as_uint(v);
-    const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    v = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const uint32_t u = __float_as_uint(v[i]);
+      const auto p32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      v[i] = __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
+    }
   }
-  return v;
 }
 
 struct RsArgs {
@@ -251,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
   }
   __syncthreads();
 
-  float lane_amax = 0.0f;
+  uint32_t lane_amax = 0;   // fp16 max |y| in the low half
   // one step: the groups g_first .. + kUnroll - 1 held in cur; the next step's into nxt
   auto step = [&](int g_first, const uint4 (&cur)[kUnroll][C], uint4 (&nxt)[kUnroll][C]) {
     load_groups<P, C, kUnroll>(a, g_first + span, last_group, sub, eff, nxt);
@@ -270,8 +348,9 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) pr[e] = sum_sq_f16x2(w[e]);
         const float v = (pr[0] + pr[1]) + (pr[2] + pr[3]);
-        slot[i] = lane_levels<P>(live[i] ? v : 0.0f);
+        slot[i] = live[i] ? v : 0.0f;
       }
+      lane_levels<P, C>(slot);
       sums[u] = register_levels<C>(slot);
     }
     float rstds[kUnroll];
@@ -291,27 +370,27 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
 #pragma unroll
       for (int i = 0; i < C; ++i) {
         const uint32_t w[4] = {cur[u][i].x, cur[u][i].y, cur[u][i].z, cur[u][i].w};
-        float y[8];
+        uint32_t y[8];    // fp16 y, one per register (low half)
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
+        for (int e = 0; e < 4; ++e) {
           // the product rounded to fp32 first, then to fp16 (the opaque multiply also keeps
           // the compiler from forming one v_fma_mixlo, a single rounding to fp16)
-          const float p0 = mul_f16_f32<false>(w[e / 2], rstd), p1 = mul_f16_f32<true>(w[e / 2], rstd);
+          const float p0 = mul_f16_f32<false>(w[e], rstd), p1 = mul_f16_f32<true>(w[e], rstd);
           // fp16(nn * gamma): the product of two fp16 values is exact in fp32, so its fp16
           // rounding is the fp16 multiply's (one v_pk_mul_f16 for the pair)
           h2 nn;
           nn.x = (_Float16)p0;
           nn.y = (_Float16)p1;
-          const uint32_t ab = __builtin_bit_cast(uint32_t, nn * g2[i][e / 2]);
-          y[e] = (float)__builtin_bit_cast(_Float16, table[ab & 0xFFFFu]);
-          y[e + 1] = (float)__builtin_bit_cast(_Float16, table[ab >> 16]);
+          const uint32_t ab = __builtin_bit_cast(uint32_t, nn * g2[i][e]);
+          y[2 * e] = table[ab & 0xFFFFu];
+          y[2 * e + 1] = table[ab >> 16];
         }
         if (AMAX) {
-          lane_amax = fold_abs8(lane_amax, y);
+          lane_amax = fold_abs_f16x8(lane_amax, y);
           continue;
         }
         uint32_t s;
-        const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
+        const uint32_t code = quantize_chunk_f16(y, gsf, inv_tab, &s);
         const uint32_t row_chunk = __umul24((uint32_t)at.rs, (uint32_t)chunks) + eff[i];
         *at_byte(a.codes + at.r0 * chunks, row_chunk * 4u) = code;
         *at_byte(a.scales + at.r0 * blocks, __umul24((uint32_t)at.rs, (uint32_t)blocks) + (eff[i] >> 1)) =
@@ -320,8 +399,7 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
           if (a.rstd_out) global_ptr(a.rstd_out)[at.r0 + at.rs] = rstd;
           if (a.y_out)
             *at_byte(a.y_out + at.r0 * chunks, row_chunk * 16u) =
-                make_uint4(f16_bits(y[0]) | (f16_bits(y[1]) << 16), f16_bits(y[2]) | (f16_bits(y[3]) << 16),
-                           f16_bits(y[4]) | (f16_bits(y[5]) << 16), f16_bits(y[6]) | (f16_bits(y[7]) << 16));
+                make_uint4(y[0] | (y[1] << 16), y[2] | (y[3] << 16), y[4] | (y[5] << 16), y[6] | (y[7] << 16));
         }
       }
     }
@@ -333,7 +411,8 @@ __global__ __launch_bounds__(kThreads) void rms_silu_kernel(const RsArgs a) {
     step(my_first + (st + 1) * span, buf1, buf0);
   }
   if (st < steps) step(my_first + st * span, buf0, buf1);
-  if (AMAX) workgroup_max_to(a.amax_out, lane_amax, amax_red, kWaves);
+  if (AMAX)
+    workgroup_max_to(a.amax_out, f16_lo(lane_amax), amax_red, kWaves);
 }
 
 template <int P, int C, bool AMAX>
