@@ -43,6 +43,7 @@ struct RmsArgs {
   uint32_t* status;
   const float* amax_dev;   // per-call scale: the amax pass's result (null: static global_amax)
   float* amax_out;         // the amax pass: where max |y| is folded
+  int unit_shift;          // staged kernel without the LDS tile: rows per unit = 1 << unit_shift (3 .. 7)
 };
 
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
@@ -255,7 +256,9 @@ __device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr,
 // One workgroup of 8 wavefronts per CU, persistent over 128-row tiles (tile t, t + grid,
 // ...).  Wavefront w takes rows 8i + w (i = 0..15) of each tile, so the eight rows in
 // flight at any time are consecutive and share a frame except at frame boundaries, and
-// every wavefront has the same 16 rows of work per tile.
+// every wavefront has the same 16 rows of work per tile.  A tensor with fewer tiles than
+// CUs is cut into smaller units instead (64 rows down to 8, one row per wavefront), enough
+// of them to occupy the CUs, and stores its scale bytes directly.
 //
 // Each wavefront keeps its current row unpacked to fp32 in registers (8 CPL values per
 // lane) from the statistic to the output pass, so every element is unpacked once.  The
@@ -284,7 +287,6 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
   __shared__ float amax_red[kStagedWaves];
   constexpr int WAVES = kStagedWaves;
   constexpr int kThreads = WAVES * kWave;
-  constexpr int kRowsPerWave = 128 / WAVES;
   constexpr int kChunks = CPL * kWave;          // chunks per row (k / 8)
   constexpr int kTileWords = kChunks * 4;        // 128 rows x k/16 bytes, in uint4
   constexpr int kTileLdsWords = kTileWords / 32 * 33;   // with one padding uint4 per 32
@@ -300,8 +302,12 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const NVFP4_GLOBAL uint4* x = global_ptr(a.x);
   const int64_t m = a.m;
-  const int64_t ntiles = a.padded >> 7;
-  if ((int64_t)blockIdx.x >= ntiles) return;            // idle workgroup (uniform)
+  // Units of rows: 128-row tiles with the LDS scale block, else 2^unit_shift rows (at least
+  // one per wavefront), so that a short tensor still spreads over many CUs.
+  const int ushift = TILE ? 7 : a.unit_shift;
+  const int rows_per_wave = (1 << ushift) / WAVES;
+  const int64_t nunits = a.padded >> ushift;
+  if ((int64_t)blockIdx.x >= nunits) return;            // idle workgroup (uniform)
   // Byte offsets of this lane's chunk 0 in the weight, 1 + scale and shift planes.  The
   // four planes of one parameter and their 64-lane steps then lie within the 16-bit
   // immediate offset of one ds_read_b64 base; hiding the three bases from the optimiser
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
   // are unconditional: a row past the end re-reads row m - 1, which is never used).
   uint4 xr[CPL];
   {
-    const int64_t r0 = ((int64_t)blockIdx.x << 7) + wave;
+    const int64_t r0 = ((int64_t)blockIdx.x << ushift) + wave;
     load_row<CPL>(xr, x + (r0 < m ? r0 : m - 1) * kChunks, lane);
   }
 
@@ -333,10 +339,10 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
   __syncthreads();
 
   int64_t staged = -1;
-  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const int64_t base = tile << 7;
-    const int64_t next_first = ((tile + gridDim.x) << 7) + wave;   // this wave's row in the next tile
-    for (int i = 0; i < kRowsPerWave; ++i) {
+  for (int64_t tile = blockIdx.x; tile < nunits; tile += gridDim.x) {
+    const int64_t base = tile << ushift;
+    const int64_t next_first = ((tile + gridDim.x) << ushift) + wave;   // this wave's row in the next unit
+    for (int i = 0; i < rows_per_wave; ++i) {
       const int64_t g = base + WAVES * i;
       // restage the modulation row when the group's first row needs another frame (uniform)
       int64_t want = staged;
@@ -361,7 +367,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
         continue;
       }
       // this wavefront's next row (loaded chunk by chunk during the output pass)
-      int64_t rn = (i + 1 < kRowsPerWave) ? r + WAVES : next_first;
+      int64_t rn = (i + 1 < rows_per_wave) ? r + WAVES : next_first;
       rn = rn < m ? rn : m - 1;
       // the row arrived during the previous row's output pass: unpack it once and take the
       // statistic; the next row's chunks are loaded into the packed registers one by one in
@@ -517,19 +523,38 @@ inline size_t staged_lds_bytes(int64_t k, bool tile) {
 
 template <int CPL>
 hipError_t launch_staged(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev, hipStream_t stream) {
-  const bool tile = !amax_pass && staged_lds_bytes(a.k, true) <= kLdsLimit;
+  // A tensor of fewer 128-row tiles than CUs leaves CUs idle; it runs in smaller units
+  // instead (64 rows down to 8, one per wavefront), without the LDS scale tile, when that
+  // takes the rows of the busiest CU to 3/4 of what 128-row tiles give it or fewer
+  // (measured: a row costs up to ~20 % more without the tile).  The unit is the one with
+  // the fewest rows of x on the busiest CU, the larger one on equal counts; padding rows
+  // (only scale bytes to zero) are not counted.
+  RmsArgs s = a;
+  s.unit_shift = 7;
+  if ((a.padded >> 7) < dev.cu_count) {
+    auto busiest = [&](int u) {
+      const int64_t units = (a.m + (1 << u) - 1) >> u;
+      const int64_t rows = ((units + dev.cu_count - 1) / dev.cu_count) << u;
+      return rows < a.m ? rows : a.m;
+    };
+    int best = 7;
+    for (int u = 6; u >= 3; --u)
+      if (busiest(u) < busiest(best)) best = u;
+    if (4 * busiest(best) <= 3 * busiest(7)) s.unit_shift = best;
+  }
+  const bool tile = !amax_pass && s.unit_shift == 7 && staged_lds_bytes(a.k, true) <= kLdsLimit;
   const size_t lds = staged_lds_bytes(a.k, tile);
-  const int64_t ntiles = a.padded >> 7;
-  const int64_t grid = ntiles < dev.cu_count ? ntiles : dev.cu_count;
+  const int64_t units = a.padded >> s.unit_shift;
+  const int64_t grid = units < dev.cu_count ? units : dev.cu_count;
   const dim3 g((uint32_t)grid), b(kStagedWaves * kWave);
   if (amax_pass) {
-    hipLaunchKernelGGL((rms_adaln_staged<CPL, false, false, true>), g, b, lds, stream, a, a.frame_idx);
+    hipLaunchKernelGGL((rms_adaln_staged<CPL, false, false, true>), g, b, lds, stream, s, a.frame_idx);
   } else if (tile) {
-    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, true, true, false>), g, b, lds, stream, a, a.frame_idx);
-    else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, true, false>), g, b, lds, stream, a, a.frame_idx);
+    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, true, true, false>), g, b, lds, stream, s, a.frame_idx);
+    else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, true, false>), g, b, lds, stream, s, a.frame_idx);
   } else {
-    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, true, false, false>), g, b, lds, stream, a, a.frame_idx);
-    else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, false, false>), g, b, lds, stream, a, a.frame_idx);
+    if (a.y_out) hipLaunchKernelGGL((rms_adaln_staged<CPL, true, false, false>), g, b, lds, stream, s, a.frame_idx);
+    else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, false, false>), g, b, lds, stream, s, a.frame_idx);
   }
   return hipGetLastError();
 }
@@ -632,6 +657,7 @@ hipError_t launch_rms_adaln(const RmsLaunch& p, const DeviceInfo& dev, hipStream
   a.status = p.status_word;
   a.amax_dev = p.amax_dev;
   a.amax_out = nullptr;
+  a.unit_shift = 7;
   if (p.amax_dev) {
     // per-call scale: zero the amax, fold max |y| into it, then quantize with it
     RmsArgs pass = a;

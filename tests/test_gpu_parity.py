@@ -171,8 +171,8 @@ def test_rms_adaln_shapes(nq, m, k, frames, order):
 @pytest.mark.parametrize("k", [512 * c for c in range(1, 17)])
 def test_rms_adaln_every_row_length(nq, k):
     """Every row length the kernel is instantiated for (k/512 = 1 .. 16 chunks per lane)
-    over 2,100 rows, several per workgroup, so the next row's prefetch and the tile's
-    scale block run at each."""
+    over 2,100 rows: 17 tiles, fewer than the CUs, so the rows run in 16-row units (two rows
+    per wavefront, the next row's prefetch between them) with direct scale stores."""
     m, frames = 2100, 3
     print("rms_adaln", m, k, flush=True)
     g = np.random.Generator(np.random.PCG64(7 * k + 1))
@@ -181,6 +181,49 @@ def test_rms_adaln_every_row_length(nq, k):
     table = bf16(0.1 * g.standard_normal((frames, 2, k)).astype(np.float32))
     idx = (np.arange(m) * frames // m).astype(np.int32)
     got = gpu_rms(nq, x, w, table, idx, 1e-6, 8.0)
+    check_rms(got, x, w, table, idx, 1e-6, 8.0)
+
+
+@pytest.fixture(scope="module")
+def tile_rows():
+    """32,845 rows of 8192 bf16 columns: 257 tiles of 128 rows (77 in the last), more than
+    the device's CUs, so RMSNorm + adaLN runs in 128-row tiles (with the LDS scale block
+    where it fits, k <= 7680).  Each k takes the first k columns."""
+    return rand_bf16((32845, 8192), 4242, 2.0)
+
+
+@pytest.mark.parametrize("k", [512 * c for c in range(1, 17)])
+def test_rms_adaln_tile_path_every_row_length(nq, tile_rows, k):
+    """The 128-row tile path at every row length: two tiles on most workgroups, the next
+    row's prefetch across tiles, the ragged last tile and its zero padding rows, frame
+    changes inside tiles."""
+    m, frames = tile_rows.shape[0], 5
+    print("rms_adaln tiles", m, k, flush=True)
+    g = np.random.Generator(np.random.PCG64(11 * k + 5))
+    x = np.ascontiguousarray(tile_rows[:, :k])
+    w = bf16(1 + 0.1 * g.standard_normal(k).astype(np.float32))
+    table = bf16(0.1 * g.standard_normal((frames, 2, k)).astype(np.float32))
+    idx = (np.arange(m) * frames // m).astype(np.int32)
+    got = gpu_rms(nq, x, w, table, idx, 1e-6, 16.0)
+    check_rms(got, x, w, table, idx, 1e-6, 16.0)
+
+
+@pytest.mark.parametrize("m", [9, 12, 129, 2047, 4089, 8189, 16379, 16512, 24583, 28000])
+def test_rms_adaln_unit_sizes(nq, m):
+    """Row counts that take each unit of a short tensor on 256 CUs: 8 rows (12, 129, 2047,
+    16512), 16 (4089), 32 (8189), 64 (16379), each but the first with a ragged last unit,
+    and 128-row tiles where smaller units would not unload the busiest CU (9, 24583,
+    28000); unsorted frames, an out-of-range frame index and y_out."""
+    k, frames = 1024, 6
+    print("rms_adaln units", m, k, flush=True)
+    g = np.random.Generator(np.random.PCG64(m + 17))
+    x = rand_bf16((m, k), m + 19, 2.0)
+    w = bf16(1 + 0.1 * g.standard_normal(k).astype(np.float32))
+    table = bf16(0.1 * g.standard_normal((frames, 2, k)).astype(np.float32))
+    idx = g.integers(0, frames, m).astype(np.int32)
+    idx[m // 2] = frames
+    got = gpu_rms(nq, x, w, table, idx, 1e-6, 8.0)
+    assert got["status"] == 1
     check_rms(got, x, w, table, idx, 1e-6, 8.0)
 
 
