@@ -274,7 +274,9 @@ __device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr,
 // would put them all in one LDS bank.  With TILE the scale bytes are gathered in LDS and the
 // tile's block, which is contiguous in the swizzled layout, leaves with 16-byte stores
 // (padding rows stay zero); without TILE (when the block does not fit beside the
-// parameters) each byte is stored directly.
+// parameters, or for a short tensor's small units) each byte is stored directly.  With
+// TILE the tile's 128 rstd values (for rstd_out) are gathered after the block (512 bytes)
+// and leave with it.
 
 constexpr int kStagedWaves = 8;
 
@@ -297,6 +299,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
   float2* op = wp + 4 * kChunks;
   float2* hp = op + 4 * kChunks;
   uint4* tile_sc = reinterpret_cast<uint4*>(hp + 4 * kChunks);
+  float* rstd_tile = reinterpret_cast<float*>(tile_sc + kTileLdsWords);   // TILE: the tile's 128 rstd
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -384,7 +387,13 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
       const float sum = lane_sum_butterfly(((acc[0] + acc[1]) + (acc[2] + acc[3])) +
                                            ((acc[4] + acc[5]) + (acc[6] + acc[7])));
       const float rstd = 1.0f / sqrtf(sum / (float)kK + a.eps);
-      if (!AMAX && lane == 0 && a.rstd_out) global_ptr(a.rstd_out)[r] = rstd;
+      // rstd_out: with TILE gathered per tile in LDS and written whole at the tile's end
+      // (4-byte stores one row apart cost ~11 % of the kernel's time: each leaves a partial
+      // cache line), else stored directly
+      if (!AMAX && a.rstd_out && lane == 0) {
+        if (TILE) rstd_tile[r & 127] = rstd;
+        else global_ptr(a.rstd_out)[r] = rstd;
+      }
       const int64_t t = frame_idx[r];
       if (t < 0 || t >= a.num_frames) {
         if (!AMAX) zero_row(a, r, lane, !TILE);
@@ -450,6 +459,8 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
         dst[i] = tile_sc[i + (i >> 5)];
         tile_sc[i + (i >> 5)] = make_uint4(0, 0, 0, 0);
       }
+      if (a.rstd_out)
+        for (int i = tid; i < 128 && base + i < m; i += kThreads) global_ptr(a.rstd_out)[base + i] = rstd_tile[i];
       __syncthreads();
     }
   }
@@ -518,11 +529,11 @@ __global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
 // Dynamic LDS cap: the 160 KiB of a CU less a little for the kernels' static arrays.
 constexpr size_t kLdsLimit = 160 * 1024 - 256;
 inline size_t staged_lds_bytes(int64_t k, bool tile) {
-  return 512 + 12 * (size_t)k + (tile ? 8 * (size_t)k / 32 * 33 : 0);
+  return 512 + 12 * (size_t)k + (tile ? 8 * (size_t)k / 32 * 33 + 512 : 0);
 }
 
 template <int CPL>
-hipError_t launch_staged(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev, hipStream_t stream) {
+hipError_t launch_staged_one(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev, hipStream_t stream) {
   // A tensor of fewer 128-row tiles than CUs leaves CUs idle; it runs in smaller units
   // instead (64 rows down to 8, one per wavefront), without the LDS scale tile, when that
   // takes the rows of the busiest CU to 3/4 of what 128-row tiles give it or fewer
@@ -557,6 +568,39 @@ hipError_t launch_staged(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev
     else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, false, false>), g, b, lds, stream, s, a.frame_idx);
   }
   return hipGetLastError();
+}
+
+// Rows [r0, end) of a as a launch of their own: every row-indexed pointer moves to row r0
+// (a multiple of 128, so the swizzled scale block moves by whole tiles).
+inline RmsArgs rows_from(const RmsArgs& a, int64_t r0) {
+  const int64_t chunks = a.k >> 3;
+  RmsArgs t = a;
+  t.x = a.x + r0 * chunks;
+  t.frame_idx = a.frame_idx + r0;
+  t.m = a.m - r0;
+  t.padded = a.padded - r0;
+  t.codes = a.codes + r0 * chunks;
+  t.scales = a.scales ? a.scales + (r0 >> 7) * (a.k >> 6) * 512 : nullptr;
+  t.rstd_out = a.rstd_out ? a.rstd_out + r0 : nullptr;
+  t.y_out = a.y_out ? a.y_out + r0 * chunks : nullptr;
+  return t;
+}
+
+// When the tiles fill some rounds of the CUs and leave a last round of at most half the
+// CUs, that round would keep a few CUs busy for a whole tile's time: the full rounds run as
+// one launch and the rest as a second, short-tensor launch (smaller units over all CUs).
+template <int CPL>
+hipError_t launch_staged(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev, hipStream_t stream) {
+  const int64_t ntiles = a.padded >> 7;
+  const int64_t rounds = ntiles / dev.cu_count, rest = ntiles % dev.cu_count;
+  if (rounds == 0 || rest == 0 || 2 * rest > dev.cu_count) return launch_staged_one<CPL>(a, amax_pass, dev, stream);
+  const int64_t r0 = rounds * dev.cu_count * 128;
+  RmsArgs head = a;
+  head.m = r0;
+  head.padded = r0;
+  const hipError_t e = launch_staged_one<CPL>(head, amax_pass, dev, stream);
+  if (e != hipSuccess) return e;
+  return launch_staged_one<CPL>(rows_from(a, r0), amax_pass, dev, stream);
 }
 
 template <int CPL, bool Y, bool TILE, bool AMAX>
