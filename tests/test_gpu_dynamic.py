@@ -130,6 +130,28 @@ def test_rms_adaln_dynamic(nq, m, k, frames, order):
     assert got["status"] == want["status"]
 
 
+@pytest.mark.parametrize("m,k,hot", [(32845, 1024, 32840), (40000, 512, 39999), (40000, 512, 5)])
+def test_rms_adaln_dynamic_last_round(nq, m, k, hot):
+    """More than one round of 128-row tiles with a short last round (257 and 313 tiles on
+    256 CUs): the full rounds and the rest run as two launches, in the amax pass as in the
+    producer.  The row holding max |y| sits in the second launch's rows, or in the first's."""
+    print("rms_adaln_dynamic last round", m, k, hot, flush=True)
+    frames = 5
+    g = np.random.Generator(np.random.PCG64(m + k + hot))
+    xf = g.standard_normal((m, k)).astype(np.float32)
+    xf[hot] *= 8
+    x = bf16(xf)
+    w = bf16(1 + 0.1 * g.standard_normal(k).astype(np.float32))
+    table = bf16(0.1 * g.standard_normal((frames, 2, k)).astype(np.float32))
+    idx = g.integers(0, frames, m).astype(np.int32)
+    got = gpu_rms_dynamic(nq, x, w, table, idx, 1e-6, y=False)
+    want = oracle.rms_adaln_dynamic(x, w, table, idx, 1e-6, want_y=False, scales_rows=oracle.padded_rows(m))
+    assert f32_bits(got["amax"]) == f32_bits(want["amax"])
+    assert_equal(got["codes"], want["codes"], "codes")
+    assert_equal(got["scales"], want["scales"], "scales")
+    assert_equal(got["rstd"].view(np.uint32), want["rstd"].view(np.uint32), "rstd")
+
+
 @pytest.mark.parametrize("k", [512 * c for c in range(1, 17)])
 def test_rms_adaln_dynamic_every_row_length(nq, k):
     """The amax pass and the producer at every row length they are instantiated for
