@@ -109,8 +109,22 @@ struct RowOut {
   NVFP4_GLOBAL uint32_t* codes;    // codes of chunk c at codes[64 j]
   NVFP4_GLOBAL uint8_t* scales;    // scale byte of chunk c's block at scales[4096 j]
   NVFP4_GLOBAL uint4* y;           // y_out of chunk c at y[64 j], or null
-  uint8_t* scales_lds;             // the same byte in the tile's padded LDS block, at [4224 j] (TILE)
+  uint8_t* scales_lds;             // the same byte in the unit's padded LDS block, at [lds_chunk_stride(CPL) j] (TILE)
 };
+
+// Units of a full-size tensor (see the staged kernel): S consecutive rows of each of the
+// four 32-row groups of a 128-row tile, 4 S rows in all; S = 16 from k = 2048 to 7680, 8 at
+// k = 8192 (where two 16-row blocks do not fit beside the parameters), 32 below 2048.
+// Smaller units keep the rows in flight closer together but restage the frame's modulation
+// row more often when frames change every few thousand rows (measured at 63,240 x 7168, 31
+// frames: 229 us with S = 16, 231 with 8, 234 in 128-row tiles; at 300,000 x 7168: 1,056 /
+// 1,043 / 1,077; k = 4096 prefers 16, k <= 2048 is within 1 % either way).  The unit's
+// scale bytes are 16 S contiguous bytes of each column group's 512-byte swizzled run; its
+// LDS block holds them padded to 16 S + 16 bytes per group, so that the eight column groups
+// one wavefront writes for a chunk fall in different banks.
+constexpr int unit_rows_per_group(int cpl) { return cpl >= 16 ? 8 : cpl >= 4 ? 16 : 32; }
+constexpr int lds_group_bytes(int cpl) { return 16 * unit_rows_per_group(cpl) + 16; }
+constexpr int lds_chunk_stride(int cpl) { return 8 * lds_group_bytes(cpl); }   // chunk j + 1: 8 groups on
 
 __device__ __forceinline__ RowOut make_row_out(uint32_t* codes, uint8_t* scales, uint4* y_out, int64_t k,
                                                int64_t r, int lane) {
@@ -132,25 +146,26 @@ __device__ __forceinline__ RowOut row_out(const RmsArgs& a, int64_t r, int lane)
 // chunks can be scheduled together.
 template <bool Y, bool TILE>
 __device__ __forceinline__ void emit_chunk(const RowOut& o, int j, const float* y, float gsf,
-                                           const float* inv_tab) {
+                                           const float* inv_tab, int lds_stride) {
   uint32_t s;
   const uint32_t q = quantize_chunk(y, gsf, inv_tab, &s);
   o.codes[kWave * j] = q;
-  if (TILE) o.scales_lds[4224 * j] = (uint8_t)s;
+  if (TILE) o.scales_lds[lds_stride * j] = (uint8_t)s;
   else o.scales[(int64_t)4096 * j] = (uint8_t)s;
   if (Y)
     o.y[kWave * j] = make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
                                 pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
 }
 
+// lds_stride: with tile, the byte distance between a lane's chunks in the unit's LDS block
 __device__ __forceinline__ void store_chunk(const RowOut& o, int j, const float* y, float gsf,
-                                            const float* inv_tab, bool tile) {
+                                            const float* inv_tab, bool tile, int lds_stride) {
   if (tile) {
-    if (o.y) emit_chunk<true, true>(o, j, y, gsf, inv_tab);
-    else emit_chunk<false, true>(o, j, y, gsf, inv_tab);
+    if (o.y) emit_chunk<true, true>(o, j, y, gsf, inv_tab, lds_stride);
+    else emit_chunk<false, true>(o, j, y, gsf, inv_tab, lds_stride);
   } else {
-    if (o.y) emit_chunk<true, false>(o, j, y, gsf, inv_tab);
-    else emit_chunk<false, false>(o, j, y, gsf, inv_tab);
+    if (o.y) emit_chunk<true, false>(o, j, y, gsf, inv_tab, 0);
+    else emit_chunk<false, false>(o, j, y, gsf, inv_tab, 0);
   }
 }
 
@@ -190,7 +205,7 @@ __device__ __forceinline__ void load_frame_chunk(const RmsArgs& a, int64_t t, in
 __device__ __noinline__ float emit_row_unstaged(const uint4* x, const uint16_t* shift, const uint16_t* scale,
                                                 int64_t frame_stride, RowOut o, int64_t k, int64_t r, int64_t t,
                                                 const float2* wp, float rstd, float gsf,
-                                                const float* inv_tab, bool tile, bool amax_only) {
+                                                const float* inv_tab, bool tile, int lds_stride, bool amax_only) {
   const int lane = threadIdx.x & (kWave - 1);
   const NVFP4_GLOBAL uint4* xr = global_ptr(x) + r * (k >> 3);
   float lane_amax = 0.0f;
@@ -204,7 +219,7 @@ __device__ __noinline__ float emit_row_unstaged(const uint4* x, const uint16_t* 
     load_frame_chunk(shift, scale, frame_stride, t, c, o8, h8);
     modulate8(x8, w8, o8, h8, rstd, y);
     if (amax_only) lane_amax = fold_abs8(lane_amax, y);
-    else store_chunk(o, j, y, gsf, inv_tab, tile);
+    else store_chunk(o, j, y, gsf, inv_tab, tile, lds_stride);
   }
   return lane_amax;
 }
@@ -229,10 +244,10 @@ __device__ __forceinline__ void load_params(const float4* lds, uint32_t pw, uint
 // Encode chunk j (its y, scale code s and inverse scale inv) and store its codes, its
 // block's scale byte (into the tile's LDS block with TILE, else to memory) and, with Y,
 // y_out.
-template <bool Y, bool TILE>
+template <int CPL, bool Y, bool TILE>
 __device__ __forceinline__ void emit_encoded(const RowOut& o, int j, const float* y, float inv, uint32_t s) {
   __builtin_nontemporal_store(encode_chunk(y, inv), o.codes + kWave * j);   // not read back
-  if (TILE) o.scales_lds[4224 * j] = (uint8_t)s;
+  if (TILE) o.scales_lds[lds_chunk_stride(CPL) * j] = (uint8_t)s;
   else o.scales[(int64_t)4096 * j] = (uint8_t)s;
   if (Y)
     o.y[kWave * j] = make_uint4(pack_exact_bf16x2(y[0], y[1]), pack_exact_bf16x2(y[2], y[3]),
@@ -253,12 +268,12 @@ __device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr,
 
 // ---- the staged kernel (k <= 8192, CPL = k / 512 chunks per lane) -------------------------
 //
-// One workgroup of 8 wavefronts per CU, persistent over 128-row tiles (tile t, t + grid,
-// ...).  Wavefront w takes rows 8i + w (i = 0..15) of each tile, so the eight rows in
-// flight at any time are consecutive and share a frame except at frame boundaries, and
-// every wavefront has the same 16 rows of work per tile.  A tensor with fewer tiles than
-// CUs is cut into smaller units instead (64 rows down to 8, one row per wavefront), enough
-// of them to occupy the CUs, and stores its scale bytes directly.
+// One workgroup of 8 wavefronts per CU, persistent over 32-row units (unit v, v + grid,
+// ...; see unit_row): the eight rows in flight at any time are consecutive and share a
+// frame except at frame boundaries, every wavefront has the same 4 rows of work per unit,
+// and consecutive units run on consecutive CUs.  A tensor with fewer 128-row tiles than
+// CUs is cut into contiguous units instead (64 rows down to 8, one row per wavefront),
+// enough of them to occupy the CUs, and stores its scale bytes directly.
 //
 // Each wavefront keeps its current row unpacked to fp32 in registers (8 CPL values per
 // lane) from the statistic to the output pass, so every element is unpacked once.  The
@@ -268,15 +283,12 @@ __device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr,
 //
 // LDS: inverse-scale table (128 fp32); twelve fp32 planes of float2 indexed by chunk (weight
 // elements 0-1, 2-3, 4-5, 6-7, then bf16(1 + scale) and shift alike), so each ds_read_b64
-// of a wavefront is one contiguous 512 bytes; and, with TILE, the swizzled scale block of the
-// current 128-row tile (8k bytes), with a 16-byte pad after every 512 bytes: the eight
-// 4-byte groups a wavefront writes for one chunk are 512 bytes apart in the layout, which
-// would put them all in one LDS bank.  With TILE the scale bytes are gathered in LDS and the
-// tile's block, which is contiguous in the swizzled layout, leaves with 16-byte stores
-// (padding rows stay zero); without TILE (when the block does not fit beside the
-// parameters, or for a short tensor's small units) each byte is stored directly.  With
-// TILE the tile's 128 rstd values (for rstd_out) are gathered after the block (512 bytes)
-// and leave with it.
+// of a wavefront is one contiguous 512 bytes; and, with TILE, two scale blocks of a 32-row
+// unit (the unit's 128-byte line of each column group, padded to 144 bytes: unpadded, the
+// eight groups a wavefront writes for one chunk would share one LDS bank) and two blocks of
+// the unit's 32 rstd values.  With TILE the scale bytes are gathered in LDS and leave as
+// whole 128-byte lines, 16 bytes per store (padding rows stay zero); without TILE (the
+// amax pass, or a short tensor's small units) each byte is stored directly.
 
 constexpr int kStagedWaves = 8;
 
@@ -290,27 +302,44 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
   constexpr int WAVES = kStagedWaves;
   constexpr int kThreads = WAVES * kWave;
   constexpr int kChunks = CPL * kWave;          // chunks per row (k / 8)
-  constexpr int kTileWords = kChunks * 4;        // 128 rows x k/16 bytes, in uint4
-  constexpr int kTileLdsWords = kTileWords / 32 * 33;   // with one padding uint4 per 32
+  constexpr int kGroups = kChunks / 8;           // 512-byte column groups of the swizzled layout (k/64)
+  constexpr int kS = unit_rows_per_group(CPL);    // a full-size unit: kS rows of each 32-row group
+  constexpr int kGroupBytes = lds_group_bytes(CPL);
+  constexpr int kUnitLdsBytes = kGroups * kGroupBytes;     // one unit's scale block
   constexpr int kK = kChunks * 8;
   extern __shared__ float4 lds4[];
   float* inv_tab = reinterpret_cast<float*>(lds4);
   float2* wp = reinterpret_cast<float2*>(lds4 + 32);   // after 128 floats = 32 float4
   float2* op = wp + 4 * kChunks;
   float2* hp = op + 4 * kChunks;
-  uint4* tile_sc = reinterpret_cast<uint4*>(hp + 4 * kChunks);
-  float* rstd_tile = reinterpret_cast<float*>(tile_sc + kTileLdsWords);   // TILE: the tile's 128 rstd
+  // TILE: two unit scale blocks (used in turn, so one barrier per unit suffices), then
+  // two blocks of the unit's 4 kS rstd values
+  uint8_t* unit_sc = reinterpret_cast<uint8_t*>(hp + 4 * kChunks);
+  float* rstd_unit = reinterpret_cast<float*>(unit_sc + 2 * kUnitLdsBytes);
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const NVFP4_GLOBAL uint4* x = global_ptr(a.x);
   const int64_t m = a.m;
-  // Units of rows: 128-row tiles with the LDS scale block, else 2^unit_shift rows (at least
-  // one per wavefront), so that a short tensor still spreads over many CUs.
-  const int ushift = TILE ? 7 : a.unit_shift;
-  const int rows_per_wave = (1 << ushift) / WAVES;
-  const int64_t nunits = a.padded >> ushift;
+  // Units of rows.  A full-size tensor (unit_shift 7) is cut into units of 4 kS rows: unit
+  // v holds rows kS j .. kS j + kS - 1 (j = v mod 32 / kS) of each 32-row group of tile
+  // v / (32 / kS).  Those rows own 16 kS contiguous bytes of every column group's 512-byte
+  // run in the swizzled scale layout (whole 128-byte lines), and consecutive units run on
+  // consecutive CUs, so the rows in flight stay within a window of 4 kS rows per CU.  The
+  // unit's n-th eight rows (n = 0 .. kS / 2 - 1) are consecutive: item 8 n + w of the unit is
+  // row s = (8 n + w) mod kS of group (8 n + w) / kS, taken by wavefront w.  A short tensor
+  // runs in contiguous units of 2^unit_shift rows (8 .. 64), 2^unit_shift / 8 per wavefront.
+  constexpr int kUnitsPerTile = 32 / kS;
+  const bool quarter = TILE || a.unit_shift == 7;
+  const int ushift = a.unit_shift;
+  const int rows_per_wave = quarter ? kS / 2 : (1 << ushift) / WAVES;
+  const int64_t nunits = quarter ? (a.padded >> 7) * kUnitsPerTile : a.padded >> ushift;
   if ((int64_t)blockIdx.x >= nunits) return;            // idle workgroup (uniform)
+  auto unit_row = [&](int64_t v, int n) -> int64_t {
+    if (!quarter) return (v << ushift) + WAVES * n + wave;
+    const int item = 8 * n + wave;
+    return (v / kUnitsPerTile) * 128 + 32 * (item / kS) + kS * (int)(v % kUnitsPerTile) + item % kS;
+  };
   // Byte offsets of this lane's chunk 0 in the weight, 1 + scale and shift planes.  The
   // four planes of one parameter and their 64-lane steps then lie within the 16-bit
   // immediate offset of one ds_read_b64 base; hiding the three bases from the optimiser
@@ -325,7 +354,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
   // are unconditional: a row past the end re-reads row m - 1, which is never used).
   uint4 xr[CPL];
   {
-    const int64_t r0 = ((int64_t)blockIdx.x << ushift) + wave;
+    const int64_t r0 = unit_row(blockIdx.x, 0);
     load_row<CPL>(xr, x + (r0 < m ? r0 : m - 1) * kChunks, lane);
   }
 
@@ -338,15 +367,16 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
     store_planes(wp, kChunks, c, f);
   }
   if (TILE)
-    for (int i = tid; i < kTileLdsWords; i += kThreads) tile_sc[i] = make_uint4(0, 0, 0, 0);
+    for (int i = tid; i < 2 * kUnitLdsBytes / 16; i += kThreads)
+      reinterpret_cast<uint4*>(unit_sc)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
   int64_t staged = -1;
-  for (int64_t tile = blockIdx.x; tile < nunits; tile += gridDim.x) {
-    const int64_t base = tile << ushift;
-    const int64_t next_first = ((tile + gridDim.x) << ushift) + wave;   // this wave's row in the next unit
+  int par = 0;                                          // TILE: the unit's scale block
+  for (int64_t v = blockIdx.x; v < nunits; v += gridDim.x) {
+    const int64_t next_first = unit_row(v + gridDim.x, 0);   // this wave's row in the next unit
     for (int i = 0; i < rows_per_wave; ++i) {
-      const int64_t g = base + WAVES * i;
+      const int64_t g = unit_row(v, i) - wave;         // the first row of the 8 in flight
       // restage the modulation row when the group's first row needs another frame (uniform)
       int64_t want = staged;
       if (g < m) {
@@ -370,7 +400,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
         continue;
       }
       // this wavefront's next row (loaded chunk by chunk during the output pass)
-      int64_t rn = (i + 1 < rows_per_wave) ? r + WAVES : next_first;
+      int64_t rn = (i + 1 < rows_per_wave) ? unit_row(v, i + 1) : next_first;
       rn = rn < m ? rn : m - 1;
       // the row arrived during the previous row's output pass: unpack it once and take the
       // statistic; the next row's chunks are loaded into the packed registers one by one in
@@ -391,7 +421,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
       // (4-byte stores one row apart cost ~11 % of the kernel's time: each leaves a partial
       // cache line), else stored directly
       if (!AMAX && a.rstd_out && lane == 0) {
-        if (TILE) rstd_tile[r & 127] = rstd;
+        if (TILE) rstd_unit[4 * kS * par + 8 * i + wave] = rstd;
         else global_ptr(a.rstd_out)[r] = rstd;
       }
       const int64_t t = frame_idx[r];
@@ -401,11 +431,15 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
         continue;
       }
       RowOut o = row_out(a, r, lane);
-      if (TILE) o.scales_lds = reinterpret_cast<uint8_t*>(tile_sc) + (row_scale_base(r, kK) & 511) +
-                               (lane >> 3) * 528 + ((lane >> 1) & 3);
+      // item 8 i + w (row s of group g) sits at byte 16 s + 4 g of the unit's 16 kS bytes
+      if (TILE) {
+        const int item = 8 * i + wave;
+        o.scales_lds = unit_sc + par * kUnitLdsBytes + (lane >> 3) * kGroupBytes + 16 * (item % kS) +
+                       4 * (item / kS) + ((lane >> 1) & 3);
+      }
       if (t != staged) {
         const float u = emit_row_unstaged(a.x, a.shift, a.scale, a.frame_stride, o, kK, r, t, wp, rstd, gsf,
-                                          inv_tab, TILE, AMAX);
+                                          inv_tab, TILE, lds_chunk_stride(CPL), AMAX);
         lane_amax = __builtin_fmaxf(lane_amax, u);
         load_row<CPL>(xr, xn, lane);
         continue;
@@ -438,7 +472,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
         }
         const uint32_t s = block_scale_code(y, gsf);
         const float inv = inv_tab[s];
-        if (j > 0) emit_encoded<Y, TILE>(o, j - 1, yp, invp, sp);
+        if (j > 0) emit_encoded<CPL, Y, TILE>(o, j - 1, yp, invp, sp);
 #pragma unroll
         for (int e = 0; e < 8; ++e) yp[e] = y[e];
         sp = s;
@@ -448,20 +482,28 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
           for (int q = 0; q < 12; ++q) pc[q] = pn[q];
         }
       }
-      if (!AMAX) emit_encoded<Y, TILE>(o, CPL - 1, yp, invp, sp);
+      if (!AMAX) emit_encoded<CPL, Y, TILE>(o, CPL - 1, yp, invp, sp);
     }
     if (TILE) {
-      // the tile's scale block is complete: copy it out and zero it for the next tile (each
-      // thread clears exactly the words it copied, so no barrier is needed in between)
+      // the unit's scale block is complete: copy its 128-byte lines out and zero them (each
+      // thread clears exactly the words it copied); the next unit fills the other block, and
+      // this one is filled again only after the next unit's barrier, when every thread has
+      // finished copying it
       __syncthreads();
-      NVFP4_GLOBAL uint4* dst = reinterpret_cast<NVFP4_GLOBAL uint4*>(global_ptr(a.scales) + tile * (kK >> 6) * 512);
-      for (int i = tid; i < kTileWords; i += kThreads) {
-        dst[i] = tile_sc[i + (i >> 5)];
-        tile_sc[i + (i >> 5)] = make_uint4(0, 0, 0, 0);
+      uint8_t* blk = unit_sc + par * kUnitLdsBytes;
+      NVFP4_GLOBAL uint8_t* dst =
+          global_ptr(a.scales) + (v / kUnitsPerTile) * kGroups * 512 + 16 * kS * (int)(v % kUnitsPerTile);
+      for (int q = tid; q < kGroups * kS; q += kThreads) {
+        uint4* src = reinterpret_cast<uint4*>(blk + (q / kS) * kGroupBytes + 16 * (q % kS));
+        *reinterpret_cast<NVFP4_GLOBAL uint4*>(dst + (int64_t)(q / kS) * 512 + 16 * (q % kS)) = *src;
+        *src = make_uint4(0, 0, 0, 0);
       }
-      if (a.rstd_out)
-        for (int i = tid; i < 128 && base + i < m; i += kThreads) global_ptr(a.rstd_out)[base + i] = rstd_tile[i];
-      __syncthreads();
+      if (a.rstd_out && tid < 4 * kS) {
+        // item tid of the unit: row tid mod kS of group tid / kS
+        const int64_t rr = (v / kUnitsPerTile) * 128 + 32 * (tid / kS) + kS * (int)(v % kUnitsPerTile) + tid % kS;
+        if (rr < m) global_ptr(a.rstd_out)[rr] = rstd_unit[4 * kS * par + tid];
+      }
+      par ^= 1;
     }
   }
   if (AMAX) workgroup_max_to(a.amax_out, lane_amax, amax_red, kStagedWaves);
@@ -505,7 +547,7 @@ __device__ __forceinline__ float general_row(const RmsArgs& a, int64_t r, int la
     load_frame_chunk(a, t, c, o8, h8);
     modulate8(x8, w8, o8, h8, rstd, y);
     if (AMAX) lane_amax = fold_abs8(lane_amax, y);
-    else store_chunk(o, j, y, gsf, inv_tab, false);
+    else store_chunk(o, j, y, gsf, inv_tab, false, 0);
   }
   return lane_amax;
 }
@@ -524,12 +566,14 @@ __global__ __launch_bounds__(256) void rms_adaln_general(RmsArgs a) {
   if (AMAX) workgroup_max_to(a.amax_out, lane_amax, amax_red, 4);
 }
 
-// The tile's scale block (128 rows x k/16 bytes) is staged in LDS when it fits beside the
-// parameters (k <= 7680).
+// Two 32-row units' scale blocks are staged in LDS beside the parameters (TILE), which fits
+// for every k of the staged kernel.
 // Dynamic LDS cap: the 160 KiB of a CU less a little for the kernels' static arrays.
 constexpr size_t kLdsLimit = 160 * 1024 - 256;
 inline size_t staged_lds_bytes(int64_t k, bool tile) {
-  return 512 + 12 * (size_t)k + (tile ? 8 * (size_t)k / 32 * 33 + 512 : 0);
+  const int cpl = (int)(k / 512);
+  return 512 + 12 * (size_t)k +
+         (tile ? 2 * (size_t)(k / 64) * lds_group_bytes(cpl) + 2 * 4 * unit_rows_per_group(cpl) * sizeof(float) : 0);
 }
 
 template <int CPL>
@@ -555,7 +599,7 @@ hipError_t launch_staged_one(const RmsArgs& a, bool amax_pass, const DeviceInfo&
   }
   const bool tile = !amax_pass && s.unit_shift == 7 && staged_lds_bytes(a.k, true) <= kLdsLimit;
   const size_t lds = staged_lds_bytes(a.k, tile);
-  const int64_t units = a.padded >> s.unit_shift;
+  const int64_t units = s.unit_shift == 7 ? (a.padded >> 7) * (32 / unit_rows_per_group(CPL)) : a.padded >> s.unit_shift;
   const int64_t grid = units < dev.cu_count ? units : dev.cu_count;
   const dim3 g((uint32_t)grid), b(kStagedWaves * kWave);
   if (amax_pass) {
@@ -586,15 +630,18 @@ inline RmsArgs rows_from(const RmsArgs& a, int64_t r0) {
   return t;
 }
 
-// When the tiles fill some rounds of the CUs and leave a last round of at most half the
-// CUs, that round would keep a few CUs busy for a whole tile's time: the full rounds run as
-// one launch and the rest as a second, short-tensor launch (smaller units over all CUs).
+// When the units of a full-size tensor fill some rounds of the CUs and leave a last
+// round of at most half the CUs, that round would keep a few CUs busy while the others
+// idle: the full rounds (to a whole tile) run as one launch and the rest as a second,
+// short-tensor launch (smaller units over all CUs).
 template <int CPL>
 hipError_t launch_staged(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev, hipStream_t stream) {
-  const int64_t ntiles = a.padded >> 7;
-  const int64_t rounds = ntiles / dev.cu_count, rest = ntiles % dev.cu_count;
-  if (rounds == 0 || rest == 0 || 2 * rest > dev.cu_count) return launch_staged_one<CPL>(a, amax_pass, dev, stream);
-  const int64_t r0 = rounds * dev.cu_count * 128;
+  constexpr int kUnitRows = 4 * unit_rows_per_group(CPL);
+  const int64_t ntiles = a.padded >> 7, units = a.padded / kUnitRows;
+  const int64_t rounds = units / dev.cu_count, rest = units % dev.cu_count;
+  if (ntiles < dev.cu_count || rest == 0 || 2 * rest > dev.cu_count)
+    return launch_staged_one<CPL>(a, amax_pass, dev, stream);
+  const int64_t r0 = rounds * dev.cu_count * kUnitRows / 128 * 128;
   RmsArgs head = a;
   head.m = r0;
   head.padded = r0;
