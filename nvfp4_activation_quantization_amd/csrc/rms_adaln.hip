@@ -43,7 +43,8 @@ struct RmsArgs {
   uint32_t* status;
   const float* amax_dev;   // per-call scale: the amax pass's result (null: static global_amax)
   float* amax_out;         // the amax pass: where max |y| is folded
-  int unit_shift;          // staged kernel without the LDS tile: rows per unit = 1 << unit_shift (3 .. 7)
+  int unit_shift;          // staged kernel: 7 for a full-size tensor (4S-row units), else a short tensor's
+                           // contiguous units of 1 << unit_shift rows (3 .. 6)
 };
 
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
@@ -141,7 +142,7 @@ __device__ __forceinline__ RowOut row_out(const RmsArgs& a, int64_t r, int lane)
   return make_row_out(a.codes, a.scales, a.y_out, a.k, r, lane);
 }
 
-// Quantize chunk j of a row and store its codes, its block's scale byte (into the tile's
+// Quantize chunk j of a row and store its codes, its block's scale byte (into the unit's
 // LDS block with TILE, else to memory) and, with Y, y_out.  No branches, so consecutive
 // chunks can be scheduled together.
 template <bool Y, bool TILE>
@@ -157,7 +158,8 @@ __device__ __forceinline__ void emit_chunk(const RowOut& o, int j, const float* 
                                 pack_exact_bf16x2(y[4], y[5]), pack_exact_bf16x2(y[6], y[7]));
 }
 
-// lds_stride: with tile, the byte distance between a lane's chunks in the unit's LDS block
+// lds_stride: with tile (the unit's LDS scale block), the byte distance between a lane's
+// chunks in that block
 __device__ __forceinline__ void store_chunk(const RowOut& o, int j, const float* y, float gsf,
                                             const float* inv_tab, bool tile, int lds_stride) {
   if (tile) {
@@ -170,7 +172,7 @@ __device__ __forceinline__ void store_chunk(const RowOut& o, int j, const float*
 }
 
 // Write row r as zeros (frame index outside [0, num_frames)); its scale bytes go to
-// memory only when they are not gathered in a zeroed LDS tile block.
+// memory only when they are not gathered in a zeroed LDS block.
 __device__ void zero_row(const RmsArgs& a, int64_t r, int lane, bool scales_too) {
   const int64_t chunks = a.k >> 3;
   for (int64_t c = lane; c < chunks; c += kWave) {
@@ -242,7 +244,7 @@ __device__ __forceinline__ void load_params(const float4* lds, uint32_t pw, uint
 }
 
 // Encode chunk j (its y, scale code s and inverse scale inv) and store its codes, its
-// block's scale byte (into the tile's LDS block with TILE, else to memory) and, with Y,
+// block's scale byte (into the unit's LDS block with TILE, else to memory) and, with Y,
 // y_out.
 template <int CPL, bool Y, bool TILE>
 __device__ __forceinline__ void emit_encoded(const RowOut& o, int j, const float* y, float inv, uint32_t s) {
@@ -283,10 +285,10 @@ __device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr,
 //
 // LDS: inverse-scale table (128 fp32); twelve fp32 planes of float2 indexed by chunk (weight
 // elements 0-1, 2-3, 4-5, 6-7, then bf16(1 + scale) and shift alike), so each ds_read_b64
-// of a wavefront is one contiguous 512 bytes; and, with TILE, two scale blocks of a 32-row
-// unit (the unit's 128-byte line of each column group, padded to 144 bytes: unpadded, the
-// eight groups a wavefront writes for one chunk would share one LDS bank) and two blocks of
-// the unit's 32 rstd values.  With TILE the scale bytes are gathered in LDS and leave as
+// of a wavefront is one contiguous 512 bytes; and, with TILE, two scale blocks of a unit
+// (the unit's 16 S bytes of each column group, padded to 16 S + 16: unpadded, the eight
+// groups a wavefront writes for one chunk would share one LDS bank) and two blocks of the
+// unit's 4 S rstd values.  With TILE the scale bytes are gathered in LDS and leave as
 // whole 128-byte lines, 16 bytes per store (padding rows stay zero); without TILE (the
 // amax pass, or a short tensor's small units) each byte is stored directly.
 
@@ -417,9 +419,9 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
       const float sum = lane_sum_butterfly(((acc[0] + acc[1]) + (acc[2] + acc[3])) +
                                            ((acc[4] + acc[5]) + (acc[6] + acc[7])));
       const float rstd = 1.0f / sqrtf(sum / (float)kK + a.eps);
-      // rstd_out: with TILE gathered per tile in LDS and written whole at the tile's end
-      // (4-byte stores one row apart cost ~11 % of the kernel's time: each leaves a partial
-      // cache line), else stored directly
+      // rstd_out: with TILE gathered per unit in LDS and written at the unit's end
+      // (4-byte stores one row apart, each leaving a partial cache line, cost up to 7 % of
+      // the kernel's time at k = 2048), else stored directly
       if (!AMAX && a.rstd_out && lane == 0) {
         if (TILE) rstd_unit[4 * kS * par + 8 * i + wave] = rstd;
         else global_ptr(a.rstd_out)[r] = rstd;
