@@ -45,6 +45,7 @@ struct RmsArgs {
   float* amax_out;         // the amax pass: where max |y| is folded
   int unit_shift;          // staged kernel: 7 for a full-size tensor (4S-row units), else a short tensor's
                            // contiguous units of 1 << unit_shift rows (3 .. 6)
+  int64_t head_units;      // full-size tensor: the units of 4S rows; the rows after them form 8-row units
 };
 
 __device__ __forceinline__ void unpack8(const uint4& v, float* f) {
@@ -271,12 +272,14 @@ __device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr,
 
 // ---- the staged kernel (k <= 8192, CPL = k / 512 chunks per lane) -------------------------
 //
-// One workgroup of 8 wavefronts per CU, persistent over 32-row units (unit v, v + grid,
-// ...; see unit_row): the eight rows in flight at any time are consecutive and share a
-// frame except at frame boundaries, every wavefront has the same 4 rows of work per unit,
-// and consecutive units run on consecutive CUs.  A tensor with fewer 128-row tiles than
-// CUs is cut into contiguous units instead (64 rows down to 8, one row per wavefront),
-// enough of them to occupy the CUs, and stores its scale bytes directly.
+// One workgroup of 8 wavefronts per CU, persistent over units of 4 S rows (unit v, v +
+// grid, ...; see unit_row): the eight rows in flight at any time are consecutive and share
+// a frame except at frame boundaries, every wavefront has the same S / 2 rows of work per
+// unit, and consecutive units run on consecutive CUs.  The rows after the last full round
+// of units run in 8-row units, a contiguous run of them per workgroup, when that takes rows
+// off the busiest CU.  A tensor with fewer 128-row tiles than CUs is cut into contiguous
+// units instead (64 rows down to 8, one row per wavefront), enough of them to occupy the
+// CUs, and stores its scale bytes directly.
 //
 // Each wavefront keeps its current row unpacked to fp32 in registers (8 CPL values per
 // lane) from the statistic to the output pass, so every element is unpacked once.  The
@@ -330,18 +333,33 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
   // run in the swizzled scale layout (whole 128-byte lines), and consecutive units run on
   // consecutive CUs, so the rows in flight stay within a window of 4 kS rows per CU.  The
   // unit's n-th eight rows (n = 0 .. kS / 2 - 1) are consecutive: item 8 n + w of the unit is
-  // row s = (8 n + w) mod kS of group (8 n + w) / kS, taken by wavefront w.  A short tensor
-  // runs in contiguous units of 2^unit_shift rows (8 .. 64), 2^unit_shift / 8 per wavefront.
+  // row s = (8 n + w) mod kS of group (8 n + w) / kS, taken by wavefront w.  When the units
+  // would leave a last round that keeps some CUs busy while others idle, only the first
+  // head_units are such units and the tiles after them run in units of 8 consecutive rows,
+  // one per wavefront, whose scale bytes are 4-byte pieces of the swizzled layout.  Units
+  // of 4 kS rows go round-robin over the workgroups; each workgroup then takes a contiguous
+  // run of the 8-row units (the pieces of one 128-byte line come mostly from one CU, where
+  // the cache merges them).  A short tensor runs in contiguous units of 2^unit_shift rows
+  // (8 .. 64), 2^unit_shift / 8 per wavefront, round-robin.
   constexpr int kUnitsPerTile = 32 / kS;
   const bool quarter = TILE || a.unit_shift == 7;
   const int ushift = a.unit_shift;
-  const int rows_per_wave = quarter ? kS / 2 : (1 << ushift) / WAVES;
-  const int64_t nunits = quarter ? (a.padded >> 7) * kUnitsPerTile : a.padded >> ushift;
-  if ((int64_t)blockIdx.x >= nunits) return;            // idle workgroup (uniform)
-  auto unit_row = [&](int64_t v, int n) -> int64_t {
-    if (!quarter) return (v << ushift) + WAVES * n + wave;
-    const int item = 8 * n + wave;
-    return (v / kUnitsPerTile) * 128 + 32 * (item / kS) + kS * (int)(v % kUnitsPerTile) + item % kS;
+  const int64_t head = quarter ? a.head_units : 0;
+  const int64_t nunits = quarter ? head + ((a.padded - head * 4 * kS) >> 3) : a.padded >> ushift;
+  const int64_t nrr = quarter ? head : nunits;          // units taken round-robin
+  const int64_t bid = blockIdx.x, nwg = gridDim.x;
+  const int64_t mine_rr = nrr > bid ? (nrr - bid + nwg - 1) / nwg : 0;
+  const int64_t t0 = bid * (nunits - nrr) / nwg, t1 = (bid + 1) * (nunits - nrr) / nwg;
+  const int64_t mine = mine_rr + (t1 - t0);
+  if (mine == 0) return;                                 // idle workgroup (uniform)
+  auto unit_of = [&](int64_t n) -> int64_t { return n < mine_rr ? bid + n * nwg : nrr + t0 + (n - mine_rr); };
+  auto unit_row = [&](int64_t v, int n, int w) -> int64_t {
+    if (!quarter) return (v << ushift) + WAVES * n + w;
+    if (v < head) {
+      const int item = 8 * n + w;
+      return (v / kUnitsPerTile) * 128 + 32 * (item / kS) + kS * (int)(v % kUnitsPerTile) + item % kS;
+    }
+    return (head / kUnitsPerTile) * 128 + 8 * (v - head) + w;   // an 8-row unit (n == 0)
   };
   // Byte offsets of this lane's chunk 0 in the weight, 1 + scale and shift planes.  The
   // four planes of one parameter and their 64-lane steps then lie within the 16-bit
@@ -357,7 +375,7 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
   // are unconditional: a row past the end re-reads row m - 1, which is never used).
   uint4 xr[CPL];
   {
-    const int64_t r0 = unit_row(blockIdx.x, 0);
+    const int64_t r0 = unit_row(unit_of(0), 0, wave);
     load_row<CPL>(xr, x + (r0 < m ? r0 : m - 1) * kChunks, lane);
   }
 
@@ -376,10 +394,13 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
 
   int64_t staged = -1;
   int par = 0;                                          // TILE: the unit's scale block
-  for (int64_t v = blockIdx.x; v < nunits; v += gridDim.x) {
-    const int64_t next_first = unit_row(v + gridDim.x, 0);   // this wave's row in the next unit
+  for (int64_t n = 0; n < mine; ++n) {
+    const int64_t v = unit_of(n);
+    // this wave's row in the next unit (after the last unit: any row, loaded and not used)
+    const int64_t next_first = n + 1 < mine ? unit_row(unit_of(n + 1), 0, wave) : m - 1;
+    const int rows_per_wave = !quarter ? (1 << ushift) / WAVES : v < head ? kS / 2 : 1;
     for (int i = 0; i < rows_per_wave; ++i) {
-      const int64_t g = unit_row(v, i) - wave;         // the first row of the 8 in flight
+      const int64_t g = unit_row(v, i, 0);             // the first row of the 8 in flight
       // restage the modulation row when the group's first row needs another frame (uniform)
       int64_t want = staged;
       if (g < m) {
@@ -397,13 +418,13 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
         __syncthreads();
         staged = want;
       }
-      const int64_t r = g + wave;
+      const int64_t r = unit_row(v, i, wave);
       if (r >= m) {                        // a padding row (and so is every later row)
         if (!TILE && !AMAX) zero_row_scales(a.scales, r, kK, lane);   // TILE: already zero in LDS
         continue;
       }
       // this wavefront's next row (loaded chunk by chunk during the output pass)
-      int64_t rn = (i + 1 < rows_per_wave) ? unit_row(v, i + 1) : next_first;
+      int64_t rn = (i + 1 < rows_per_wave) ? unit_row(v, i + 1, wave) : next_first;
       rn = rn < m ? rn : m - 1;
       // the row arrived during the previous row's output pass: unpack it once and take the
       // statistic; the next row's chunks are loaded into the packed registers one by one in
@@ -434,11 +455,12 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
         continue;
       }
       RowOut o = row_out(a, r, lane);
-      // item 8 i + w (row s of group g) sits at byte 16 s + 4 g of the unit's 16 kS bytes
+      // item 8 i + w (row s of group g) sits at byte 16 s + 4 g of the unit's bytes in a column
+      // group (an 8-row unit: row w at byte 4 w)
       if (TILE) {
         const int item = 8 * i + wave;
-        o.scales_lds = unit_sc + par * kUnitLdsBytes + (lane >> 3) * kGroupBytes + 16 * (item % kS) +
-                       4 * (item / kS) + ((lane >> 1) & 3);
+        const int at = v < head ? 16 * (item % kS) + 4 * (item / kS) : 4 * wave;
+        o.scales_lds = unit_sc + par * kUnitLdsBytes + (lane >> 3) * kGroupBytes + at + ((lane >> 1) & 3);
       }
       if (t != staged) {
         const float u = emit_row_unstaged(a.x, a.shift, a.scale, a.frame_stride, o, kK, r, t, wp, rstd, gsf,
@@ -494,17 +516,32 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
       // finished copying it
       __syncthreads();
       uint8_t* blk = unit_sc + par * kUnitLdsBytes;
-      NVFP4_GLOBAL uint8_t* dst =
-          global_ptr(a.scales) + (v / kUnitsPerTile) * kGroups * 512 + 16 * kS * (int)(v % kUnitsPerTile);
-      for (int q = tid; q < kGroups * kS; q += kThreads) {
-        uint4* src = reinterpret_cast<uint4*>(blk + (q / kS) * kGroupBytes + 16 * (q % kS));
-        *reinterpret_cast<NVFP4_GLOBAL uint4*>(dst + (int64_t)(q / kS) * 512 + 16 * (q % kS)) = *src;
-        *src = make_uint4(0, 0, 0, 0);
-      }
-      if (a.rstd_out && tid < 4 * kS) {
-        // item tid of the unit: row tid mod kS of group tid / kS
-        const int64_t rr = (v / kUnitsPerTile) * 128 + 32 * (tid / kS) + kS * (int)(v % kUnitsPerTile) + tid % kS;
-        if (rr < m) global_ptr(a.rstd_out)[rr] = rstd_unit[4 * kS * par + tid];
+      if (v < head) {
+        NVFP4_GLOBAL uint8_t* dst =
+            global_ptr(a.scales) + (v / kUnitsPerTile) * kGroups * 512 + 16 * kS * (int)(v % kUnitsPerTile);
+        for (int q = tid; q < kGroups * kS; q += kThreads) {
+          uint4* src = reinterpret_cast<uint4*>(blk + (q / kS) * kGroupBytes + 16 * (q % kS));
+          *reinterpret_cast<NVFP4_GLOBAL uint4*>(dst + (int64_t)(q / kS) * 512 + 16 * (q % kS)) = *src;
+          *src = make_uint4(0, 0, 0, 0);
+        }
+        if (a.rstd_out && tid < 4 * kS) {
+          // item tid of the unit: row tid mod kS of group tid / kS
+          const int64_t rr =
+              (v / kUnitsPerTile) * 128 + 32 * (tid / kS) + kS * (int)(v % kUnitsPerTile) + tid % kS;
+          if (rr < m) global_ptr(a.rstd_out)[rr] = rstd_unit[4 * kS * par + tid];
+        }
+      } else {
+        // rows r0 .. r0 + 7 (one 8-row block of a 32-row group): row r0 + w's 4 bytes of a
+        // column group go to byte 16 (r mod 32) + 4 (r mod 128 / 32) of its 512-byte run
+        const int64_t r0 = (head / kUnitsPerTile) * 128 + 8 * (v - head);
+        NVFP4_GLOBAL uint8_t* dst = global_ptr(a.scales) + (r0 >> 7) * kGroups * 512 +
+                                    16 * (int)(r0 & 31) + 4 * (int)((r0 >> 5) & 3);
+        for (int q = tid; q < kGroups * 8; q += kThreads) {
+          uint32_t* src = reinterpret_cast<uint32_t*>(blk + (q >> 3) * kGroupBytes + 4 * (q & 7));
+          *reinterpret_cast<NVFP4_GLOBAL uint32_t*>(dst + (int64_t)(q >> 3) * 512 + 16 * (q & 7)) = *src;
+          *src = 0;
+        }
+        if (a.rstd_out && tid < 8 && r0 + tid < m) global_ptr(a.rstd_out)[r0 + tid] = rstd_unit[4 * kS * par + tid];
       }
       par ^= 1;
     }
@@ -580,7 +617,7 @@ inline size_t staged_lds_bytes(int64_t k, bool tile) {
 }
 
 template <int CPL>
-hipError_t launch_staged_one(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev, hipStream_t stream) {
+hipError_t launch_staged(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev, hipStream_t stream) {
   // A tensor of fewer 128-row tiles than CUs leaves CUs idle; it runs in smaller units
   // instead (64 rows down to 8, one per wavefront), without the LDS scale tile, when that
   // takes the rows of the busiest CU to 3/4 of what 128-row tiles give it or fewer
@@ -600,9 +637,25 @@ hipError_t launch_staged_one(const RmsArgs& a, bool amax_pass, const DeviceInfo&
       if (busiest(u) < busiest(best)) best = u;
     if (4 * busiest(best) <= 3 * busiest(7)) s.unit_shift = best;
   }
+  // A full-size tensor whose units of 4S rows leave a last round that keeps some CUs busy
+  // while others idle runs its full rounds (down to a whole tile) in those units and the
+  // tiles after them in 8-row units over every CU, when that takes at least S rows off the
+  // busiest CU.  An 8-row unit ends with a barrier after one row per wavefront, so a tail
+  // that saves less costs more than it gains (measured on random input with four frames:
+  // 63,240 x 7168, 8 of 64 rows saved, 227 -> 235 us; 40,000 x 7168, 32 saved,
+  // 161 -> 151 us).
+  constexpr int kS = unit_rows_per_group(CPL), kPerTile = 32 / kS;
+  s.head_units = (a.padded >> 7) * kPerTile;
+  if (s.unit_shift == 7) {
+    const int64_t cus = dev.cu_count, rounds = s.head_units / cus;
+    const int64_t head = rounds * cus / kPerTile * kPerTile;
+    const int64_t tail = (a.padded - head * 4 * kS) / 8;
+    if (rounds > 0 && head < s.head_units && 8 * ((tail + cus - 1) / cus) + kS <= 4 * kS) s.head_units = head;
+  }
   const bool tile = !amax_pass && s.unit_shift == 7 && staged_lds_bytes(a.k, true) <= kLdsLimit;
   const size_t lds = staged_lds_bytes(a.k, tile);
-  const int64_t units = s.unit_shift == 7 ? (a.padded >> 7) * (32 / unit_rows_per_group(CPL)) : a.padded >> s.unit_shift;
+  const int64_t units =
+      s.unit_shift == 7 ? s.head_units + (a.padded - s.head_units * 4 * kS) / 8 : a.padded >> s.unit_shift;
   const int64_t grid = units < dev.cu_count ? units : dev.cu_count;
   const dim3 g((uint32_t)grid), b(kStagedWaves * kWave);
   if (amax_pass) {
@@ -615,42 +668,6 @@ hipError_t launch_staged_one(const RmsArgs& a, bool amax_pass, const DeviceInfo&
     else hipLaunchKernelGGL((rms_adaln_staged<CPL, false, false, false>), g, b, lds, stream, s, a.frame_idx);
   }
   return hipGetLastError();
-}
-
-// Rows [r0, end) of a as a launch of their own: every row-indexed pointer moves to row r0
-// (a multiple of 128, so the swizzled scale block moves by whole tiles).
-inline RmsArgs rows_from(const RmsArgs& a, int64_t r0) {
-  const int64_t chunks = a.k >> 3;
-  RmsArgs t = a;
-  t.x = a.x + r0 * chunks;
-  t.frame_idx = a.frame_idx + r0;
-  t.m = a.m - r0;
-  t.padded = a.padded - r0;
-  t.codes = a.codes + r0 * chunks;
-  t.scales = a.scales ? a.scales + (r0 >> 7) * (a.k >> 6) * 512 : nullptr;
-  t.rstd_out = a.rstd_out ? a.rstd_out + r0 : nullptr;
-  t.y_out = a.y_out ? a.y_out + r0 * chunks : nullptr;
-  return t;
-}
-
-// When the units of a full-size tensor fill some rounds of the CUs and leave a last
-// round of at most half the CUs, that round would keep a few CUs busy while the others
-// idle: the full rounds (to a whole tile) run as one launch and the rest as a second,
-// short-tensor launch (smaller units over all CUs).
-template <int CPL>
-hipError_t launch_staged(const RmsArgs& a, bool amax_pass, const DeviceInfo& dev, hipStream_t stream) {
-  constexpr int kUnitRows = 4 * unit_rows_per_group(CPL);
-  const int64_t ntiles = a.padded >> 7, units = a.padded / kUnitRows;
-  const int64_t rounds = units / dev.cu_count, rest = units % dev.cu_count;
-  if (ntiles < dev.cu_count || rest == 0 || 2 * rest > dev.cu_count)
-    return launch_staged_one<CPL>(a, amax_pass, dev, stream);
-  const int64_t r0 = rounds * dev.cu_count * kUnitRows / 128 * 128;
-  RmsArgs head = a;
-  head.m = r0;
-  head.padded = r0;
-  const hipError_t e = launch_staged_one<CPL>(head, amax_pass, dev, stream);
-  if (e != hipSuccess) return e;
-  return launch_staged_one<CPL>(rows_from(a, r0), amax_pass, dev, stream);
 }
 
 template <int CPL, bool Y, bool TILE, bool AMAX>

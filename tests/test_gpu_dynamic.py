@@ -132,9 +132,9 @@ def test_rms_adaln_dynamic(nq, m, k, frames, order):
 
 @pytest.mark.parametrize("m,k,hot", [(32845, 1024, 32840), (40000, 512, 39999), (40000, 512, 5)])
 def test_rms_adaln_dynamic_last_round(nq, m, k, hot):
-    """More than one round of 128-row tiles with a short last round (257 and 313 tiles on
-    256 CUs): the full rounds and the rest run as two launches, in the amax pass as in the
-    producer.  The row holding max |y| sits in the second launch's rows, or in the first's."""
+    """More than one round of units with a short last round (257 and 313 tiles on 256
+    CUs): the rows after the full rounds run in 8-row units, in the amax pass as in the
+    producer.  The row holding max |y| sits in those rows, or in the full rounds'."""
     print("rms_adaln_dynamic last round", m, k, hot, flush=True)
     frames = 5
     g = np.random.Generator(np.random.PCG64(m + k + hot))

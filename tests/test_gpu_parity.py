@@ -187,17 +187,17 @@ def test_rms_adaln_every_row_length(nq, k):
 @pytest.fixture(scope="module")
 def tile_rows():
     """32,845 rows of 8192 bf16 columns: 257 tiles of 128 rows (77 in the last), more than
-    the device's 256 CUs, so RMSNorm + adaLN runs the first 256 tiles in 128-row tiles (with
-    the LDS scale block where it fits, k <= 7680) and the last, lone tile as a second,
-    short-tensor launch.  Each k takes the first k columns."""
+    the device's 256 CUs, so RMSNorm + adaLN runs the first 256 tiles in full rounds of its
+    units of 4 S rows and the last, lone tile in 8-row units (16 of them, on 16
+    workgroups).  Each k takes the first k columns."""
     return rand_bf16((32845, 8192), 4242, 2.0)
 
 
 @pytest.mark.parametrize("k", [512 * c for c in range(1, 17)])
 def test_rms_adaln_tile_path_every_row_length(nq, tile_rows, k):
-    """The 128-row tile path at every row length (the next row's prefetch across rows of a
-    tile, frame changes inside tiles) and the split of a short last round into its own
-    launch (the ragged last tile and its zero padding rows, rows offset by 256 tiles)."""
+    """The tile path at every row length (the next row's prefetch across rows and units,
+    frame changes inside tiles) and the 8-row units after the full rounds (the ragged last
+    tile, its zero padding rows and their scale bytes as 4-byte pieces)."""
     m, frames = tile_rows.shape[0], 5
     print("rms_adaln tiles", m, k, flush=True)
     g = np.random.Generator(np.random.PCG64(11 * k + 5))
