@@ -249,8 +249,7 @@ __device__ __forceinline__ void load_params(const float4* lds, uint32_t pw, uint
 // y_out.
 template <int CPL, bool Y, bool TILE>
 __device__ __forceinline__ void emit_encoded(const RowOut& o, int j, const float* y, float inv, uint32_t s) {
-  // a plain store: with the 4S-row units, non-temporal code stores measured 1 % slower
-  o.codes[kWave * j] = encode_chunk(y, inv);
+  __builtin_nontemporal_store(encode_chunk(y, inv), o.codes + kWave * j);   // not read back
   if (TILE) o.scales_lds[lds_chunk_stride(CPL) * j] = (uint8_t)s;
   else o.scales[(int64_t)4096 * j] = (uint8_t)s;
   if (Y)

@@ -12,10 +12,9 @@
 // set of 128-row x 512-column tiles) copies the 128 KiB table into its static LDS; every
 // element then costs one LDS lookup, one multiply and one bf16 rounding before the
 // quantizer.  Each tile's scale bytes are gathered in LDS and leave with 16-byte stores;
-// codes are written with plain stores in the value-first form without a bias (non-temporal
-// ones measured 2 % slower there: 254.5 against 248.9 us at 16,384 x 19,456) and with
-// non-temporal stores in the others (plain ones measured 1.4 % slower with a bias and 3 %
-// in the paired form).
+// codes are written with non-temporal stores (plain ones measured faster only for 16,384 to
+// 24,576 rows, by 2.5 %, and 1 to 7 % slower at 4,096, 8,192, 32,768 and 49,152 rows and in
+// the paired and bias forms).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -196,10 +195,7 @@ __device__ __forceinline__ void compute_batch(const SwArgs& a, const TileAt& at,
     const uint32_t code = quantize_chunk(y, gsf, inv_tab, &s);
     const int64_t r_own = at.r0 + rr;
     const int64_t r = r_own < a.m ? r_own : a.m - 1;
-    // value-first without a bias: plain stores (2 % faster); with a bias non-temporal ones
-    // (1 % faster)
-    if (BIAS) store_stream(reinterpret_cast<uint32_t*>(a.codes) + r * row_chunks + at.c, code);
-    else global_ptr(reinterpret_cast<uint32_t*>(a.codes))[r * row_chunks + at.c] = code;
+    store_stream(reinterpret_cast<uint32_t*>(a.codes) + r * row_chunks + at.c, code);
     sc[(rr & 31) * 16 + ((rr >> 5) & 3) * 4] = r_own < a.m ? (uint8_t)s : (uint8_t)0;
     if (a.y_out)
       global_ptr(a.y_out)[r * row_chunks + at.c] =
