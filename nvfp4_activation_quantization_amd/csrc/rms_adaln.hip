@@ -283,8 +283,9 @@ __device__ __forceinline__ void load_row(uint4* v, const NVFP4_GLOBAL uint4* xr,
 // Each wavefront keeps its current row unpacked to fp32 in registers (8 CPL values per
 // lane) from the statistic to the output pass, so every element is unpacked once.  The
 // packed registers (4 CPL) are free once the statistic has unpacked them: in the output
-// pass the load of the next row's chunk j is issued as soon as chunk j has been modulated,
-// so the next row arrives during the rest of the pass.
+// pass the loads of the next row's chunks are issued as chunks are modulated (one per
+// chunk, or two for k <= 4096, into the registers each modulated chunk frees), so the next
+// row arrives during the rest of the pass.
 //
 // LDS: inverse-scale table (128 fp32); twelve fp32 planes of float2 indexed by chunk (weight
 // elements 0-1, 2-3, 4-5, 6-7, then bf16(1 + scale) and shift alike), so each ds_read_b64
@@ -341,6 +342,12 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
   // the cache merges them).  A short tensor runs in contiguous units of 2^unit_shift rows
   // (8 .. 64), 2^unit_shift / 8 per wavefront, round-robin.
   constexpr int kUnitsPerTile = 32 / kS;
+  // Next-row loads issued per modulated chunk of the output pass.  Two per chunk put the
+  // whole next row in flight by mid-pass, which short rows need (random input, 63,240 /
+  // 150,000 rows: k = 2048 82.0 -> 78.9 / 180.6 -> 172.9 us, k = 3072 110.9 -> 107.4 /
+  // 246.0 -> 243.3, k = 4096 136.0 -> 133.4 / 309.3 -> 301.2); from k = 5120 on, where the
+  // pass is long, it gains nothing and costs 1 % at k = 7168 (229.6 -> 233.1 us).
+  constexpr int kAhead = CPL <= 8 ? 2 : 1;
   const bool quarter = TILE || a.unit_shift == 7;
   const int ushift = a.unit_shift;
   const int64_t head = quarter ? a.head_units : 0;
@@ -485,7 +492,11 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
         split8(pc[4], pc[5], pc[6], pc[7], o8);
         split8(pc[8], pc[9], pc[10], pc[11], h8);
         modulate8(xf[j], w8, o8, h8, rstd, y);
-        xr[j] = load_stream(reinterpret_cast<const uint4*>(xn + lane + kWave * j));
+        // the next row's chunks: kAhead per modulated chunk (the freed registers of one fp32
+        // chunk hold two packed ones), so that the last of them leave early in the pass
+#pragma unroll
+        for (int q = kAhead * j; q < kAhead * j + kAhead; ++q)
+          if (q < CPL) xr[q] = load_stream(reinterpret_cast<const uint4*>(xn + lane + kWave * q));
         if (AMAX) {
           lane_amax = fold_abs8(lane_amax, y);
           if (j + 1 < CPL) {
