@@ -228,6 +228,25 @@ def test_rms_adaln_unit_sizes(nq, m):
     check_rms(got, x, w, table, idx, 1e-6, 8.0)
 
 
+@pytest.mark.parametrize("m,k,rows_per_frame", [(40000, 1024, 97), (70000, 2048, 41), (33000, 8192, 13)])
+def test_rms_adaln_tail_units(nq, m, k, rows_per_frame):
+    """Tensors whose last round of units is short on 256 CUs, so the rows after the full
+    rounds run in 8-row units (313, 547 and 258 tiles): frames change every few rows, so
+    units straddle frame boundaries (restaged and unstaged rows), with out-of-range frame
+    indices in the tail, the ragged last tile, rstd_out and y_out."""
+    print("rms_adaln tail units", m, k, rows_per_frame, flush=True)
+    frames = (m + rows_per_frame - 1) // rows_per_frame
+    g = np.random.Generator(np.random.PCG64(m + k))
+    x = rand_bf16((m, k), m + 3, 2.0)
+    w = bf16(1 + 0.1 * g.standard_normal(k).astype(np.float32))
+    table = bf16(0.1 * g.standard_normal((frames, 2, k)).astype(np.float32))
+    idx = (np.arange(m) // rows_per_frame).astype(np.int32)
+    idx[[m - 1000, m - 333, m - 2]] = [-1, frames, frames + 7]
+    got = gpu_rms(nq, x, w, table, idx, 1e-6, 8.0)
+    assert got["status"] == 1
+    check_rms(got, x, w, table, idx, 1e-6, 8.0)
+
+
 def test_rms_adaln_tiny_workload(nq):
     wl = workloads.get("rms_adaln_256x2048")
     amax = workloads.calibration_amax(wl.name)
