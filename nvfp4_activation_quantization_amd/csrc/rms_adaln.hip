@@ -385,20 +385,35 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
     load_row<CPL>(xr, x + (r0 < m ? r0 : m - 1) * kChunks, lane);
   }
 
+  // The weight and the first row group's frame are staged together, so a workgroup with
+  // one unit (a short tensor) waits for one round of global loads before its first row
+  // instead of two (the frame used to be staged behind a barrier of its own).
+  int64_t staged = -1;
+  {
+    const int64_t g0 = unit_row(unit_of(0), 0, 0);
+    if (g0 < m) {
+      const int64_t t = frame_idx[g0];
+      if (t >= 0 && t < a.num_frames) staged = t;
+    }
+  }
   const float gsf = call_global_scale(a.global_amax, a.amax_dev);
   float lane_amax = 0.0f;
   fill_inverse_table(inv_tab, gsf, tid);
   for (int c = tid; c < kChunks; c += kThreads) {
-    float f[8];
+    float f[8], o8[8], h8[8];
     unpack8(*reinterpret_cast<const NVFP4_GLOBAL uint4*>(global_ptr(a.w) + 8 * c), f);
+    if (staged >= 0) load_frame_chunk(a, staged, c, o8, h8);
     store_planes(wp, kChunks, c, f);
+    if (staged >= 0) {
+      store_planes(op, kChunks, c, o8);
+      store_planes(hp, kChunks, c, h8);
+    }
   }
   if (TILE)
     for (int i = tid; i < 2 * kUnitLdsBytes / 16; i += kThreads)
       reinterpret_cast<uint4*>(unit_sc)[i] = make_uint4(0, 0, 0, 0);
   __syncthreads();
 
-  int64_t staged = -1;
   int par = 0;                                          // TILE: the unit's scale block
   for (int64_t n = 0; n < mine; ++n) {
     const int64_t v = unit_of(n);
