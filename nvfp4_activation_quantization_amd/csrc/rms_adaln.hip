@@ -346,8 +346,10 @@ __global__ __launch_bounds__(kStagedWaves * kWave) void rms_adaln_staged(RmsArgs
   // whole next row in flight by mid-pass, which short rows need (random input, 63,240 /
   // 150,000 rows: k = 2048 82.0 -> 78.9 / 180.6 -> 172.9 us, k = 3072 110.9 -> 107.4 /
   // 246.0 -> 243.3, k = 4096 136.0 -> 133.4 / 309.3 -> 301.2); from k = 5120 on, where the
-  // pass is long, it gains nothing and costs 1 % at k = 7168 (229.6 -> 233.1 us).
-  constexpr int kAhead = CPL <= 8 ? 2 : 1;
+  // pass is long, it gains nothing and costs 1 % at k = 7168 (229.6 -> 233.1 us).  The amax
+  // pass, whose output pass has no quantizer and no stores, takes two at every k (whole
+  // per-call form at 63,240 / 300,000 x 7168: 403.8 -> 402.3 / 1,849 -> 1,839 us).
+  constexpr int kAhead = (AMAX || CPL <= 8) ? 2 : 1;
   const bool quarter = TILE || a.unit_shift == 7;
   const int ushift = a.unit_shift;
   const int64_t head = quarter ? a.head_units : 0;
