@@ -118,22 +118,28 @@ hipError_t launch_slots(const uint4* x, int64_t m, int64_t k, float global_amax,
 
 // ---- the amax pass of the per-call scale: max |x| over the tensor ----------------------
 //
-// A read-only stream over all m * k / 8 chunks (16-byte loads, kAmaxUnroll per thread in
-// flight), a few workgroups per CU striding over the tensor; each workgroup folds its
-// maximum into *amax with one atomic.
+// A read-only stream over all m * k / 8 chunks: one workgroup per CU, each taking a
+// contiguous run of 64 KiB steps (16-byte loads, kAmaxUnroll per thread in flight, 8 KiB
+// apart); each workgroup folds its maximum into *amax with one atomic.  Two workgroups per
+// CU striding over the whole tensor instead (each thread's loads 2 MiB apart) measured
+// 148 us at 63,240 x 7168 against 129 here; the strided form also swung by 8 % with the
+// grid size (1 MiB and 2 MiB strides the slowest).
 constexpr int kAmaxThreads = 512;
 constexpr int kAmaxUnroll = 8;
+constexpr int64_t kAmaxStep = (int64_t)kAmaxThreads * kAmaxUnroll;   // chunks per workgroup step
 
 __global__ __launch_bounds__(kAmaxThreads) void amax_x_kernel(const uint4* __restrict__ x, int64_t chunks,
                                                               float* amax) {
   __shared__ float red[kAmaxThreads / kWave];
-  const int64_t stride = (int64_t)gridDim.x * kAmaxThreads;
+  const int64_t steps = (chunks + kAmaxStep - 1) / kAmaxStep;
+  const int64_t s0 = blockIdx.x * steps / gridDim.x, s1 = (blockIdx.x + 1) * steps / gridDim.x;
   float t = 0.0f;
-  for (int64_t c = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; c < chunks; c += stride * kAmaxUnroll) {
+  for (int64_t s = s0; s < s1; ++s) {
+    const int64_t c = s * kAmaxStep + threadIdx.x;
     uint4 v[kAmaxUnroll];
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u)
-      v[u] = (c + stride * u < chunks) ? load_stream(x + c + stride * u) : make_uint4(0, 0, 0, 0);
+      v[u] = (c + kAmaxThreads * u < chunks) ? load_stream(x + c + kAmaxThreads * u) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < kAmaxUnroll; ++u) {
       const float y[8] = {bf16_lo(v[u].x), bf16_hi(v[u].x), bf16_lo(v[u].y), bf16_hi(v[u].y),
@@ -159,10 +165,8 @@ hipError_t launch_zero_amax(float* amax, hipStream_t stream) {
 hipError_t launch_amax_x(const void* x, int64_t m, int64_t k, float* amax, const DeviceInfo& dev,
                          hipStream_t stream) {
   const int64_t chunks = m * (k / 8);
-  const int64_t per_block = (int64_t)kAmaxThreads * kAmaxUnroll;
-  int64_t blocks = (chunks + per_block - 1) / per_block;
-  const int64_t cap = (int64_t)dev.cu_count * 2;
-  if (blocks > cap) blocks = cap;
+  int64_t blocks = (chunks + kAmaxStep - 1) / kAmaxStep;
+  if (blocks > dev.cu_count) blocks = dev.cu_count;
   hipLaunchKernelGGL(amax_x_kernel, dim3((uint32_t)blocks), dim3(kAmaxThreads), 0, stream,
                      static_cast<const uint4*>(x), chunks, amax);
   return hipGetLastError();
