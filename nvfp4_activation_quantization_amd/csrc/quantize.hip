@@ -122,7 +122,7 @@ hipError_t launch_slots(const uint4* x, int64_t m, int64_t k, float global_amax,
 // contiguous run of 64 KiB steps (16-byte loads, kAmaxUnroll per thread in flight, 8 KiB
 // apart); each workgroup folds its maximum into *amax with one atomic.  Two workgroups per
 // CU striding over the whole tensor instead (each thread's loads 2 MiB apart) measured
-// 148 us at 63,240 x 7168 against 129 here; the strided form also swung by 8 % with the
+// 148 us at 63,240 x 7168 against 131 here; the strided form also swung by 8 % with the
 // grid size (1 MiB and 2 MiB strides the slowest).
 constexpr int kAmaxThreads = 512;
 constexpr int kAmaxUnroll = 8;
